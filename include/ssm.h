@@ -1,0 +1,141 @@
+/*
+ * ssm.h -- C ABI of the MI355X (gfx950) selective-scan library.
+ *
+ * Two forward operations of selective state-space models, each one call that
+ * enqueues hand-written HIP kernels on the caller's stream:
+ *
+ *   ssm_selective_scan_fwd  -- the S6 selective scan (Mamba-1 layer scan)
+ *   ssm_ssd_chunk_fwd       -- the scalar-decay-per-head SSD form (Mamba-2)
+ *
+ * Conventions shared by every entry point
+ *   - All tensor arguments are DEVICE pointers owned by the caller, row-major
+ *     and contiguous in the stated shape (last axis fastest).  The library
+ *     never allocates, frees or retains them; scratch space is the caller's
+ *     `workspace` whose size comes from the matching *_workspace_bytes query.
+ *   - Large operands (u, delta, z, y, B, C, X, Y) must be 16-byte aligned;
+ *     fp32 parameter vectors 4-byte aligned.  Outputs must not overlap inputs.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls return as
+ *     soon as the kernels are enqueued; they never synchronise.  They keep no
+ *     state between calls and may be issued concurrently on different streams
+ *     with different workspaces.
+ *   - Arithmetic is fp32 throughout (state, accumulation, discretisation);
+ *     storage dtype `dtype` applies to the activation tensors (see each call).
+ *     bf16 outputs are rounded to nearest even from fp32.
+ *   - Validation happens on the host before any HIP call: a nonzero status is
+ *     returned and nothing is launched.  A failed launch returns
+ *     SSM_ERR_HIP; faults inside a kernel surface at the caller's next
+ *     synchronisation, as for any asynchronous HIP work.
+ *   - L = 0 is valid: nothing is written to y, and h_last (if given) receives
+ *     h0 (or zeros).
+ */
+#ifndef SSM_MI355X_H
+#define SSM_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+/* storage dtype of the activation tensors */
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
+
+/* status codes */
+enum {
+    SSM_OK = 0,
+    SSM_ERR_NULL_ARG = 1,      /* a required pointer is NULL */
+    SSM_ERR_BAD_SHAPE = 2,     /* a size is negative/zero where it must not be, or overflows */
+    SSM_ERR_BAD_DTYPE = 3,     /* dtype is not an ssm_dtype */
+    SSM_ERR_UNSUPPORTED = 4,   /* valid request outside what the kernels implement */
+    SSM_ERR_MISALIGNED = 5,    /* a pointer violates the alignment rule above */
+    SSM_ERR_WORKSPACE = 6,     /* workspace NULL or smaller than the query returned */
+    SSM_ERR_HIP = 7            /* a HIP call or kernel launch failed */
+};
+
+/* flags */
+#define SSM_FLAG_DELTA_SOFTPLUS 1u  /* delta <- softplus(delta + delta_bias) */
+#define SSM_FLAG_ZOH            2u  /* exact zero-order-hold input term instead of delta*B */
+
+int ssm_abi_version(void);
+
+/* Static, never-NULL description of a status code. */
+const char* ssm_status_string(int status);
+
+/*
+ * ---------------------------------------------------------------- S6 scan
+ * The selective scan, per batch row b and channel d, with an N-wide state h
+ * carried over tokens t (the per-token discretisation and readout of the
+ * "Discretization becomes a per-token operation" section of the
+ * Transformer-math "Selective state space" article; the gate of section 4 of
+ * the temporalbook "Selective State-Space Models (Mamba)" chapter):
+ *
+ *   dt     = softplus(delta[b,t,d] + delta_bias[d])   (flag set; else delta + bias)
+ *   h[n]   = exp(dt * A[d,n]) * h[n] + dt * B[b,t,n] * u[b,t,d]
+ *            (with SSM_FLAG_ZOH the input term is (exp(dt*A)-1)/A * B * u)
+ *   y      = sum_n C[b,t,n] * h[n]  + Dskip[d] * u[b,t,d]
+ *   y[b,t,d] = y * silu(z[b,t,d])                       (if z given)
+ *
+ * Arguments (shapes in elements):
+ *   u, delta, z, y : [B, L, D]  dtype     (z may be NULL)
+ *   A              : [D, N]     fp32      continuous-time diagonal, normally -exp(A_log)
+ *   Bm, Cm         : [B, L, N]  dtype     shared by all D channels of row b
+ *   Dskip, delta_bias : [D]     fp32 or NULL
+ *   h0             : [B, D, N]  fp32 or NULL (zeros)
+ *   h_last         : [B, D, N]  fp32 or NULL; receives the state after t = L-1
+ *   1 <= N <= 64; B, D >= 1; L >= 0.
+ * Long sequences are split into segments scanned in parallel; each segment's
+ * (decay, offset) pair is carried by a wavefront-level scan.  The workspace
+ * holds those pairs; the query is a pure function of the sizes.
+ */
+size_t ssm_selective_scan_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
+                                          int dtype);
+
+/* Number of sequence segments the planner uses for these sizes (1 = one pass,
+ * no carry); 0 for invalid sizes.  The environment variable SSM_S6_SEGMENTS
+ * (1..64) overrides the choice, for both this query and the call. */
+int ssm_selective_scan_segments(int64_t B, int64_t L, int64_t D, int64_t N);
+
+int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
+                           const void* Bm, const void* Cm, const float* Dskip,
+                           const void* z, const float* delta_bias, unsigned flags,
+                           const float* h0, void* y, float* h_last,
+                           int64_t B, int64_t L, int64_t D, int64_t N, int dtype,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ---------------------------------------------------------------- SSD chunked
+ * The Mamba-2 form with a scalar transition per head (section 3 "Mamba-2 and
+ * State Space Duality" of "Mamba & Mamba-2 Architecture"): per (b, head h),
+ * g = h / (H/G),
+ *   dt   = softplus(delta[b,t,h] + delta_bias[h])       (flag set; else delta + bias)
+ *   S    = exp(dt * A[h]) * S + dt * X[b,t,h,:] (outer) B[b,t,g,:]   (S is P x N)
+ *   Y[b,t,h,:] = (S C[b,t,g,:] + Dskip[h] * X[b,t,h,:]) * silu(z[b,t,h,:])
+ * computed chunk by chunk: within a chunk as the masked product
+ * (M o (C B^T)) (dt o X) on the matrix cores, across chunks through the
+ * carried P x N state.  The chunk length does not change the result beyond
+ * rounding.
+ *   X, Y, z : [B, L, H, P] dtype (z may be NULL)
+ *   delta   : [B, L, H]    dtype
+ *   A       : [H] fp32 (negative);  Dskip, delta_bias : [H] fp32 or NULL
+ *   Bm, Cm  : [B, L, G, N] dtype;  H % G == 0
+ *   h0, h_last : [B, H, P, N] fp32 or NULL
+ *   supported: dtype SSM_BF16, P = 64, N in {64, 128}, chunk in {64, 128, 256}.
+ */
+size_t ssm_ssd_chunk_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P,
+                                     int64_t G, int64_t N, int64_t chunk, int dtype);
+
+int ssm_ssd_chunk_fwd(const void* X, const void* delta, const float* A,
+                      const void* Bm, const void* Cm, const float* Dskip,
+                      const void* z, const float* delta_bias, unsigned flags,
+                      const float* h0, void* Y, float* h_last,
+                      int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                      int64_t N, int64_t chunk, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSM_MI355X_H */

@@ -1,0 +1,160 @@
+"""MI355X-native selective scan (S6) and SSD chunked forward.
+
+Python entry points with the same names as the C ABI in include/ssm.h.  They
+only marshal arguments: every arithmetic step runs in the HIP kernels of
+libssm_mi355x.so.  PyTorch supplies device memory and the current stream.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _native
+from ._native import SSMError
+
+__all__ = ["selective_scan_fwd", "ssd_chunk_fwd", "selective_scan_workspace_bytes",
+           "selective_scan_segments", "ssd_chunk_workspace_bytes", "SSMError"]
+
+_DT = {torch.float32: _native.SSM_F32, torch.bfloat16: _native.SSM_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev_tensor(name, t, dtype=None, device=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream_handle(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def selective_scan_workspace_bytes(B: int, L: int, D: int, N: int, dtype=torch.bfloat16) -> int:
+    return int(_native.load().ssm_selective_scan_workspace_bytes(B, L, D, N, _DT[dtype]))
+
+
+def selective_scan_segments(B: int, L: int, D: int, N: int) -> int:
+    return int(_native.load().ssm_selective_scan_segments(B, L, D, N))
+
+
+def ssd_chunk_workspace_bytes(B, L, H, P, G, N, chunk, dtype=torch.bfloat16) -> int:
+    return int(_native.load().ssm_ssd_chunk_workspace_bytes(B, L, H, P, G, N, chunk, _DT[dtype]))
+
+
+def selective_scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
+                       B: torch.Tensor, C: torch.Tensor, D: Optional[torch.Tensor] = None,
+                       z: Optional[torch.Tensor] = None,
+                       delta_bias: Optional[torch.Tensor] = None,
+                       delta_softplus: bool = True, zoh: bool = False,
+                       h0: Optional[torch.Tensor] = None, return_last_state: bool = True,
+                       out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None
+                       ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """S6 selective scan forward (ssm_selective_scan_fwd).
+
+    u, delta, z: [Bt, L, Dm]; A: [Dm, N] fp32; B, C: [Bt, L, N] (dtype of u);
+    D, delta_bias: [Dm] fp32; h0: [Bt, Dm, N] fp32.  Returns (y, h_last).
+    """
+    lib = _native.load()
+    if u.dtype not in _DT:
+        raise TypeError(f"u must be float32 or bfloat16 (got {u.dtype})")
+    dev = u.device
+    dt = u.dtype
+    u = _dev_tensor("u", u, dt, dev)
+    delta = _dev_tensor("delta", delta, dt, dev)
+    B = _dev_tensor("B", B, dt, dev)
+    C = _dev_tensor("C", C, dt, dev)
+    z = _dev_tensor("z", z, dt, dev)
+    A = _dev_tensor("A", A, torch.float32, dev)
+    D = _dev_tensor("D", D, torch.float32, dev)
+    delta_bias = _dev_tensor("delta_bias", delta_bias, torch.float32, dev)
+    h0 = _dev_tensor("h0", h0, torch.float32, dev)
+    if u.dim() != 3:
+        raise ValueError("u must be [B, L, D]")
+    Bt, L, Dm = u.shape
+    N = A.shape[-1]
+    shapes = {"delta": (delta, (Bt, L, Dm)), "A": (A, (Dm, N)), "B": (B, (Bt, L, N)),
+              "C": (C, (Bt, L, N)), "z": (z, (Bt, L, Dm)), "D": (D, (Dm,)),
+              "delta_bias": (delta_bias, (Dm,)), "h0": (h0, (Bt, Dm, N))}
+    for name, (t, shp) in shapes.items():
+        if t is not None and tuple(t.shape) != shp:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+    y = out if out is not None else torch.empty((Bt, L, Dm), dtype=dt, device=dev)
+    _dev_tensor("out", y, dt, dev)
+    h_last = torch.empty((Bt, Dm, N), dtype=torch.float32, device=dev) if return_last_state else None
+    ws_need = int(lib.ssm_selective_scan_workspace_bytes(Bt, L, Dm, N, _DT[dt]))
+    if ws_need and (workspace is None or workspace.numel() * workspace.element_size() < ws_need):
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    flags = (_native.FLAG_DELTA_SOFTPLUS if delta_softplus else 0) | (_native.FLAG_ZOH if zoh else 0)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.ssm_selective_scan_fwd(
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+        flags, _ptr(h0), _ptr(y), _ptr(h_last), Bt, L, Dm, N, _DT[dt],
+        _ptr(workspace), ws_bytes, _stream_handle(dev))
+    _native.check(rc, "ssm_selective_scan_fwd")
+    return y, h_last
+
+
+def ssd_chunk_fwd(X: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                  C: torch.Tensor, D: Optional[torch.Tensor] = None,
+                  z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
+                  delta_softplus: bool = True, h0: Optional[torch.Tensor] = None,
+                  chunk: int = 256, return_last_state: bool = True,
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
+                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Mamba-2 SSD chunked forward (ssm_ssd_chunk_fwd).
+
+    X, z: [Bt, L, H, P]; delta: [Bt, L, H]; A: [H] fp32; B, C: [Bt, L, G, N];
+    D, delta_bias: [H] fp32; h0: [Bt, H, P, N] fp32.  Returns (Y, h_last).
+    """
+    lib = _native.load()
+    if X.dtype not in _DT:
+        raise TypeError(f"X must be float32 or bfloat16 (got {X.dtype})")
+    dev, dt = X.device, X.dtype
+    X = _dev_tensor("X", X, dt, dev)
+    delta = _dev_tensor("delta", delta, dt, dev)
+    B = _dev_tensor("B", B, dt, dev)
+    C = _dev_tensor("C", C, dt, dev)
+    z = _dev_tensor("z", z, dt, dev)
+    A = _dev_tensor("A", A, torch.float32, dev)
+    D = _dev_tensor("D", D, torch.float32, dev)
+    delta_bias = _dev_tensor("delta_bias", delta_bias, torch.float32, dev)
+    h0 = _dev_tensor("h0", h0, torch.float32, dev)
+    if X.dim() != 4 or B.dim() != 4:
+        raise ValueError("X must be [B, L, H, P] and B/C [B, L, G, N]")
+    Bt, L, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    shapes = {"delta": (delta, (Bt, L, H)), "A": (A, (H,)), "B": (B, (Bt, L, G, N)),
+              "C": (C, (Bt, L, G, N)), "z": (z, (Bt, L, H, P)), "D": (D, (H,)),
+              "delta_bias": (delta_bias, (H,)), "h0": (h0, (Bt, H, P, N))}
+    for name, (t, shp) in shapes.items():
+        if t is not None and tuple(t.shape) != shp:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+    Y = out if out is not None else torch.empty((Bt, L, H, P), dtype=dt, device=dev)
+    _dev_tensor("out", Y, dt, dev)
+    h_last = torch.empty((Bt, H, P, N), dtype=torch.float32, device=dev) if return_last_state else None
+    ws_need = int(lib.ssm_ssd_chunk_workspace_bytes(Bt, L, H, P, G, N, chunk, _DT[dt]))
+    if ws_need and (workspace is None or workspace.numel() * workspace.element_size() < ws_need):
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    flags = _native.FLAG_DELTA_SOFTPLUS if delta_softplus else 0
+    rc = lib.ssm_ssd_chunk_fwd(
+        _ptr(X), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+        flags, _ptr(h0), _ptr(Y), _ptr(h_last), Bt, L, H, P, G, N, chunk, _DT[dt],
+        _ptr(workspace), ws_bytes, _stream_handle(dev))
+    _native.check(rc, "ssm_ssd_chunk_fwd")
+    return Y, h_last

@@ -1,0 +1,153 @@
+// C ABI of the library: argument validation (host only, before any HIP
+// call), planning, and dispatch to the kernel launchers.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "ssm.h"
+#include "ssm_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 60;   // keeps every byte offset in int64
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t esize(int dtype) { return dtype == SSM_BF16 ? 2 : 4; }
+
+// a*b*c without int64 overflow; -1 if it would exceed kMaxElems
+int64_t mul3(int64_t a, int64_t b, int64_t c) {
+    if (a < 0 || b < 0 || c < 0) return -1;
+    if (a == 0 || b == 0 || c == 0) return 0;
+    if (a > kMaxElems / b) return -1;
+    const int64_t ab = a * b;
+    if (ab > kMaxElems / c) return -1;
+    return ab * c;
+}
+
+int s6_check_sizes(int64_t B, int64_t L, int64_t D, int64_t N, int dtype) {
+    if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_BAD_DTYPE;
+    if (B < 1 || D < 1 || N < 1 || L < 0) return SSM_ERR_BAD_SHAPE;
+    if (mul3(B, L, D) < 0 || mul3(B, L, N) < 0 || mul3(B, D, N) < 0) return SSM_ERR_BAD_SHAPE;
+    if (mul3(B, L, D) > kMaxElems / esize(dtype)) return SSM_ERR_BAD_SHAPE;
+    if (N > 64) return SSM_ERR_UNSUPPORTED;
+    if (B > 65535) return SSM_ERR_UNSUPPORTED;                 // grid y
+    if ((D + 63) / 64 > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;
+    return SSM_OK;
+}
+
+int ssd_check_sizes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64_t N,
+                    int64_t chunk, int dtype) {
+    if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_BAD_DTYPE;
+    if (B < 1 || H < 1 || P < 1 || G < 1 || N < 1 || L < 0 || chunk < 1) return SSM_ERR_BAD_SHAPE;
+    if (H % G != 0) return SSM_ERR_BAD_SHAPE;
+    if (mul3(B, L, H) < 0 || mul3(B * H, L, P) < 0 || mul3(B * G, L, N) < 0) return SSM_ERR_BAD_SHAPE;
+    if (mul3(B * H, L, P) > kMaxElems / esize(dtype)) return SSM_ERR_BAD_SHAPE;
+    if (dtype != SSM_BF16 || P != 64 || (N != 64 && N != 128)) return SSM_ERR_UNSUPPORTED;
+    if (chunk != 64 && chunk != 128 && chunk != 256) return SSM_ERR_UNSUPPORTED;
+    if (B * H > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;
+    return SSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char* ssm_status_string(int status) {
+    switch (status) {
+        case SSM_OK: return "ok";
+        case SSM_ERR_NULL_ARG: return "a required pointer argument is NULL";
+        case SSM_ERR_BAD_SHAPE: return "invalid or overflowing tensor size";
+        case SSM_ERR_BAD_DTYPE: return "dtype is not SSM_F32 or SSM_BF16";
+        case SSM_ERR_UNSUPPORTED: return "request outside the sizes/dtypes the kernels implement";
+        case SSM_ERR_MISALIGNED: return "pointer violates the alignment rule (16 B tensors, 4 B fp32 vectors)";
+        case SSM_ERR_WORKSPACE: return "workspace is NULL or smaller than the query returned";
+        case SSM_ERR_HIP: return "a HIP call or kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int ssm_selective_scan_segments(int64_t B, int64_t L, int64_t D, int64_t N) {
+    if (s6_check_sizes(B, L, D, N, SSM_F32) != SSM_OK) return 0;
+    return ssm::plan_s6(B, L, D, N).S;
+}
+
+size_t ssm_selective_scan_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
+                                          int dtype) {
+    if (s6_check_sizes(B, L, D, N, dtype) != SSM_OK) return 0;
+    return ssm::plan_s6(B, L, D, N).workspace_bytes;
+}
+
+int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
+                           const void* Bm, const void* Cm, const float* Dskip,
+                           const void* z, const float* delta_bias, unsigned flags,
+                           const float* h0, void* y, float* h_last,
+                           int64_t B, int64_t L, int64_t D, int64_t N, int dtype,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = s6_check_sizes(B, L, D, N, dtype);
+    if (rc != SSM_OK) return rc;
+    if (flags & ~(unsigned)(SSM_FLAG_DELTA_SOFTPLUS | SSM_FLAG_ZOH)) return SSM_ERR_UNSUPPORTED;
+    if (!A) return SSM_ERR_NULL_ARG;
+    if (L > 0 && (!u || !delta || !Bm || !Cm || !y)) return SSM_ERR_NULL_ARG;
+    const void* big[] = {u, delta, Bm, Cm, z, y};
+    for (const void* p : big)
+        if (p && !aligned(p, 16)) return SSM_ERR_MISALIGNED;
+    const void* vec[] = {A, Dskip, delta_bias, h0, h_last};
+    for (const void* p : vec)
+        if (p && !aligned(p, 4)) return SSM_ERR_MISALIGNED;
+    const ssm::S6Plan plan = ssm::plan_s6(B, L, D, N);
+    if (plan.workspace_bytes > 0) {
+        if (!workspace || workspace_bytes < plan.workspace_bytes) return SSM_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return SSM_ERR_MISALIGNED;
+    }
+    ssm::S6Args a{};
+    a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.z = z;
+    a.delta_bias = delta_bias; a.h0 = h0; a.y = y; a.h_last = h_last;
+    a.B = B; a.L = L; a.D = D; a.N = N;
+    a.S = plan.S; a.seg_len = plan.seg_len; a.flags = flags; a.bf16 = dtype == SSM_BF16;
+    if (plan.S > 1) {
+        a.seg_a = static_cast<float*>(workspace);
+        a.seg_b = a.seg_a + B * D * (int64_t)plan.S * N;
+    }
+    const hipError_t e = ssm::launch_s6(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+size_t ssm_ssd_chunk_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P,
+                                     int64_t G, int64_t N, int64_t chunk, int dtype) {
+    (void)ssd_check_sizes(B, L, H, P, G, N, chunk, dtype);
+    return 0;   // the chunk kernel carries its state on chip
+}
+
+int ssm_ssd_chunk_fwd(const void* X, const void* delta, const float* A,
+                      const void* Bm, const void* Cm, const float* Dskip,
+                      const void* z, const float* delta_bias, unsigned flags,
+                      const float* h0, void* Y, float* h_last,
+                      int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                      int64_t N, int64_t chunk, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    int rc = ssd_check_sizes(B, L, H, P, G, N, chunk, dtype);
+    if (rc != SSM_OK) return rc;
+    if (flags & ~(unsigned)SSM_FLAG_DELTA_SOFTPLUS) return SSM_ERR_UNSUPPORTED;
+    if (!A) return SSM_ERR_NULL_ARG;
+    if (L > 0 && (!X || !delta || !Bm || !Cm || !Y)) return SSM_ERR_NULL_ARG;
+    const void* big[] = {X, delta, Bm, Cm, z, Y};
+    for (const void* p : big)
+        if (p && !aligned(p, 16)) return SSM_ERR_MISALIGNED;
+    const void* vec[] = {A, Dskip, delta_bias, h0, h_last};
+    for (const void* p : vec)
+        if (p && !aligned(p, 4)) return SSM_ERR_MISALIGNED;
+    ssm::SSDArgs a{};
+    a.X = X; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.z = z;
+    a.delta_bias = delta_bias; a.h0 = h0; a.Y = Y; a.h_last = h_last;
+    a.B = B; a.L = L; a.H = H; a.P = P; a.G = G; a.N = N; a.chunk = chunk; a.flags = flags;
+    const hipError_t e = ssm::launch_ssd(a, static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported) return SSM_ERR_UNSUPPORTED;
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // extern "C"

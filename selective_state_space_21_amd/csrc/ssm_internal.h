@@ -1,0 +1,64 @@
+// Internal declarations shared by the C-ABI layer and the kernel launchers.
+// Not part of the public interface (include/ssm.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ssm.h"
+
+namespace ssm {
+
+// One S6 call, fully validated, with the segment plan resolved.
+struct S6Args {
+    const void* u;
+    const void* delta;
+    const float* A;
+    const void* Bm;
+    const void* Cm;
+    const float* Dskip;
+    const void* z;
+    const float* delta_bias;
+    const float* h0;
+    void* y;
+    float* h_last;
+    // workspace: per (b, d, segment, n) decay and offset, fp32 each
+    float* seg_a;
+    float* seg_b;
+    int64_t B, L, D, N;
+    int64_t seg_len;   // tokens per segment (last one may be shorter)
+    int S;             // number of segments along L (1 = no carry)
+    unsigned flags;
+    int bf16;          // storage dtype of activations: 1 = bf16, 0 = fp32
+};
+
+struct S6Plan {
+    int S;
+    int64_t seg_len;
+    size_t workspace_bytes;
+};
+
+// Deterministic in the sizes (plus the SSM_S6_SEGMENTS override).
+S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N);
+
+hipError_t launch_s6(const S6Args& a, hipStream_t stream);
+
+struct SSDArgs {
+    const void* X;
+    const void* delta;
+    const float* A;
+    const void* Bm;
+    const void* Cm;
+    const float* Dskip;
+    const void* z;
+    const float* delta_bias;
+    const float* h0;
+    void* Y;
+    float* h_last;
+    int64_t B, L, H, P, G, N, chunk;
+    unsigned flags;
+};
+
+hipError_t launch_ssd(const SSDArgs& a, hipStream_t stream);
+
+}  // namespace ssm

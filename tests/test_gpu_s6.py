@@ -1,0 +1,221 @@
+"""GPU parity of the S6 selective scan against the fp64 oracle, through the C
+ABI.  Bars: normwise max relative error <= 1e-5 (fp32 storage) and <= 2e-2
+(bf16 storage, fp32 state); bit-exact on integer-valued cases that test
+indexing, segment boundaries and tails."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_21_amd as ssm
+from selective_state_space_21_amd import workloads as W
+
+from _parity import TOL, normwise_err, s6_gpu, s6_oracle, s6_oracle_sampled, to_dev
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _cmp(inp, zoh=False, tol=None, **kw):
+    y, h = s6_gpu(inp, zoh=zoh, **kw)
+    yr, hr = s6_oracle(inp, zoh=zoh)
+    tol = tol if tol is not None else TOL[inp["u"].dtype]
+    ey = normwise_err(y.float().cpu().numpy(), yr)
+    eh = normwise_err(h.cpu().numpy(), hr)
+    assert ey <= tol, f"y err {ey:.3e} > {tol}"
+    assert eh <= max(tol, 1e-5), f"h_last err {eh:.3e}"
+    return ey, eh
+
+
+# ------------------------------------------------ the workloads at oracle-friendly sizes
+@pytest.mark.parametrize("w", [
+    W.S6_SMALL_FP32,                                              # full size
+    W.S6_MAMBA130M.scaled(B=2, L=1000, D=192),                    # ragged L
+    W.S6_MAMBA2P8B.scaled(B=2, L=777, D=320),
+    W.S6_LONG_FP32.scaled(L=20000, D=128),                        # L-split with spikes
+], ids=lambda w: w.name)
+def test_workload_parity_small(w):
+    _cmp(W.make_s6_inputs(w, seed=0))
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 5, 16, 64])
+def test_every_segment_count(S, monkeypatch):
+    monkeypatch.setenv("SSM_S6_SEGMENTS", str(S))
+    w = W.S6_MAMBA130M.scaled(B=2, L=2100, D=64)
+    inp = W.make_s6_inputs(w, seed=1)
+    assert ssm.selective_scan_segments(w.B, w.L, w.D, w.N) == min(S, math.ceil(2100 / 32))
+    _cmp(inp)
+
+
+@pytest.mark.parametrize("N", [1, 3, 4, 5, 8, 15, 16, 17, 32, 33, 64])
+def test_state_sizes(N):
+    w = W.S6_SMALL_FP32.scaled(B=2, L=300, D=70, N=N)
+    _cmp(W.make_s6_inputs(w, seed=N))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zoh_variant(dtype):
+    w = W.S6_MAMBA130M.scaled(B=2, L=500, D=128, dtype=dtype)
+    _cmp(W.make_s6_inputs(w, seed=5), zoh=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_h0_and_chaining(dtype, monkeypatch):
+    w = W.S6_MAMBA130M.scaled(B=2, L=640, D=128, dtype=dtype)
+    inp = W.make_s6_inputs(w, seed=6)
+    inp["h0"] = torch.randn(2, 128, 16, generator=torch.Generator().manual_seed(0))
+    _cmp(inp)
+    # split the sequence across two calls: h_last of the first is h0 of the second
+    d = to_dev(inp)
+    y_all, h_all = ssm.selective_scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], D=d["D"],
+                                          z=d["z"], delta_bias=d["delta_bias"], h0=d["h0"])
+    cut = 256
+    sl = lambda t, a, b: t[:, a:b].contiguous()
+    y1, h1 = ssm.selective_scan_fwd(sl(d["u"], 0, cut), sl(d["delta"], 0, cut), d["A"],
+                                    sl(d["B"], 0, cut), sl(d["C"], 0, cut), D=d["D"],
+                                    z=sl(d["z"], 0, cut), delta_bias=d["delta_bias"], h0=d["h0"])
+    y2, h2 = ssm.selective_scan_fwd(sl(d["u"], cut, 640), sl(d["delta"], cut, 640), d["A"],
+                                    sl(d["B"], cut, 640), sl(d["C"], cut, 640), D=d["D"],
+                                    z=sl(d["z"], cut, 640), delta_bias=d["delta_bias"], h0=h1)
+    torch.cuda.synchronize()
+    tol = TOL[dtype] / 2
+    assert normwise_err(torch.cat([y1, y2], 1).float().cpu(), y_all.float().cpu()) <= tol
+    assert normwise_err(h2.cpu(), h_all.cpu()) <= 1e-5
+
+
+def test_empty_sequence_copies_h0():
+    h0 = torch.randn(2, 64, 16, device="cuda")
+    e = torch.empty(2, 0, 64, device="cuda", dtype=torch.bfloat16)
+    eb = torch.empty(2, 0, 16, device="cuda", dtype=torch.bfloat16)
+    y, h = ssm.selective_scan_fwd(e, e, -torch.ones(64, 16, device="cuda"), eb, eb, h0=h0)
+    torch.cuda.synchronize()
+    assert y.shape == (2, 0, 64) and torch.equal(h, h0)
+
+
+# ------------------------------------------------ bit-exact indexing / boundaries
+def _exact_case(L, Dm, N, dtype, mode, seed):
+    """Integer-valued inputs on which every fp32 step is exact.
+    mode 'prefix': A = 0, dt = 1 -> h_t = sum_{j<=t} B_j u_j (sparse writes keep
+    |values| small); 'reset': A = -1e4, dt = 1 -> h_t = B_t u_t;
+    'mixed': A in {0, -1e4} per (d, n), dt in {0, 1} per (t, d)."""
+    g = torch.Generator().manual_seed(seed)
+    B = 1 if L > 1500 else 2
+    u = torch.randint(-1, 2, (B, L, Dm), generator=g).float()
+    if mode == "prefix":
+        A = torch.zeros(Dm, N)
+        dt = torch.ones(B, L, Dm)
+        mask = (torch.rand(B, L, Dm, generator=g) < 4.0 / max(L, 4)).float()
+        u = u * mask
+    elif mode == "reset":
+        A = torch.full((Dm, N), -1e4)
+        dt = torch.ones(B, L, Dm)
+    else:
+        A = torch.where(torch.rand(Dm, N, generator=g) < 0.5, torch.zeros(Dm, N), torch.full((Dm, N), -1e4))
+        dt = (torch.rand(B, L, Dm, generator=g) < 0.7).float()
+        mask = (torch.rand(B, L, Dm, generator=g) < 4.0 / max(L, 4)).float()
+        u = u * mask
+    Bm = torch.randint(0, 2, (B, L, N), generator=g).float()
+    Cm = torch.randint(-1, 2, (B, L, N), generator=g).float()
+    h0 = torch.randint(-1, 2, (B, Dm, N), generator=g).float()
+    Dsk = torch.randint(-2, 3, (Dm,), generator=g).float()
+    td = W.torch_dtype(dtype)
+    return dict(u=u.to(td), delta=dt.to(td), A=A, B=Bm.to(td), C=Cm.to(td), D=Dsk, z=None,
+                delta_bias=None, h0=h0, delta_softplus=False)
+
+
+@pytest.mark.parametrize("mode", ["prefix", "reset", "mixed"])
+@pytest.mark.parametrize("L", [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 4099])
+@pytest.mark.parametrize("S", [1, 3, 64])
+def test_bit_exact_boundaries(mode, L, S, monkeypatch):
+    monkeypatch.setenv("SSM_S6_SEGMENTS", str(S))
+    for dtype in ("f32", "bf16"):
+        inp = _exact_case(L, 100, 16, dtype, mode, seed=L * 7 + S)
+        y, h = s6_gpu(inp)
+        yr, hr = s6_oracle(inp)
+        assert np.all(np.abs(yr) < 256) and np.all(yr == np.round(yr))
+        np.testing.assert_array_equal(y.float().cpu().numpy(), yr)
+        np.testing.assert_array_equal(h.cpu().numpy(), hr)
+
+
+# ------------------------------------------------ pages' worked values on the GPU
+def _single(u, delta, A=-1.0, h0=None):
+    L = len(u)
+    inp = dict(u=torch.tensor(u, dtype=torch.float32).view(1, L, 1),
+               delta=torch.tensor(delta, dtype=torch.float32).view(1, L, 1),
+               A=torch.tensor([[A]]), B=torch.ones(1, L, 1), C=torch.ones(1, L, 1),
+               D=None, z=None, delta_bias=None,
+               h0=None if h0 is None else torch.tensor([[[h0]]]), delta_softplus=False)
+    return s6_gpu(inp)
+
+
+def test_page_examples_on_gpu():
+    g = json.load(open(os.path.join(GOLDEN, "page2_code_example.json")))
+    y, _ = _single(g["x"], g["delta"], A=g["a_scalar"])
+    y = y.flatten().cpu().numpy()
+    assert round(float(y[0]), 4) == g["printed_outputs"][0]
+    assert round(float(y[1]), 4) == g["printed_outputs"][1]
+    assert abs(float(y[2]) - 3.7931260) < 1e-5
+    g = json.load(open(os.path.join(GOLDEN, "page5_horizon_table.json")))
+    for d, printed in zip(g["delta"], g["printed_retained"]):
+        _, h = _single([0.0], [d], h0=1.0)
+        digits = 4 if printed < 0.01 else 3
+        assert round(float(h.flatten()[0]), digits) == printed
+
+
+# ------------------------------------------------ robustness
+def test_deterministic_and_no_out_of_bounds_writes():
+    w = W.S6_MAMBA130M.scaled(B=3, L=513, D=136)
+    inp = to_dev(W.make_s6_inputs(w, seed=9))
+    n = 3 * 513 * 136
+    pad = 64
+    guard = torch.full((n + 2 * pad,), 12345.0, device="cuda").to(torch.bfloat16)
+    out = guard[pad:pad + n].view(3, 513, 136)
+    y1, _ = ssm.selective_scan_fwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                                   D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"], out=out)
+    y2, _ = ssm.selective_scan_fwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                                   D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    g = guard.float()
+    assert torch.all(g[:pad] == 12352.0) and torch.all(g[pad + n:] == 12352.0)
+
+
+def test_wrapper_rejects_noncontiguous():
+    x = torch.zeros(2, 64, 32, device="cuda").transpose(1, 2)
+    with pytest.raises(ValueError):
+        ssm.selective_scan_fwd(x, x, torch.zeros(64, 16, device="cuda"),
+                               torch.zeros(2, 32, 16, device="cuda"), torch.zeros(2, 32, 16, device="cuda"))
+
+
+# ------------------------------------------------ full-size workloads, sampled channels
+def _sample_channels(w, per_b=24, seed=0):
+    rng = np.random.default_rng(seed)
+    bs = sorted(set([0, w.B - 1] + list(rng.integers(0, w.B, size=min(w.B, 3)))))
+    out = []
+    for b in bs:
+        ds = sorted(set([0, w.D - 1] + list(rng.choice(w.D, size=per_b, replace=False))))
+        out.append((int(b), ds))
+    return out
+
+
+@pytest.mark.parametrize("w", [W.S6_MAMBA130M, W.S6_MAMBA2P8B, W.S6_LONG_FP32], ids=lambda w: w.name)
+def test_full_size_sampled(w):
+    inp = W.make_s6_inputs(w, seed=0)
+    y, h = s6_gpu(inp)
+    y = y.float().cpu().numpy()
+    h = h.cpu().numpy()
+    tol = TOL[w.dtype]
+    ys, yr, hs, hr = [], [], [], []
+    for b, ds, yo, ho in s6_oracle_sampled(inp, _sample_channels(w)):
+        ys.append(y[b][:, ds]); yr.append(yo)
+        hs.append(h[b][ds]); hr.append(ho)
+    ey = normwise_err(np.concatenate(ys, 1), np.concatenate(yr, 1))
+    eh = normwise_err(np.concatenate(hs, 0), np.concatenate(hr, 0))
+    print(f"{w.name}: sampled y err {ey:.3e}, h_last err {eh:.3e}")
+    assert ey <= tol and eh <= max(tol, 1e-5)
+    assert np.all(np.isfinite(y))
