@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective-scan hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one S6 selective-scan forward (softplus step, per-token
+discretisation, state update, readout, skip, silu gate, segment carry) over the
+Mamba-130M-shaped layer workload B=8 L=2048 D=1536 N=16 with bf16 activations
+and fp32 state; inputs are seeded synthetic tensors resident in HBM before the
+timed region.  Before every step a 512 MiB buffer is rewritten (outside the
+timed interval) so that the 203 MB working set is not served from the 256 MB
+Infinity Cache.  Each step is bracketed by HIP events recorded by the library
+itself on the stream it launches on, at its phase boundaries (segment reduce,
+carry scan, segment scan); `value` is the algorithmic bytes of the step
+divided by the mean step time.
+
+The same run also measures the SSD chunked forward on the Mamba-2 workload
+(B=4 L=8192 H=64 P=64 N=128, chunk 256) and times the fp64 CPU oracle on the
+host cores over the whole S6 workload.
+
+Prints one JSON line.  Only one GPU is used; --gpus above 1 exits.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+
+
+def _hip():
+    lib = ctypes.CDLL("libamdhip64.so")
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+def _events(hip, n):
+    evs = (ctypes.c_void_p * n)()
+    for i in range(n):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs[i] = e
+    return evs
+
+
+def _elapsed(hip, a, b):
+    ms = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+    return ms.value
+
+
+def bench_s6(args, torch, ssm, W, native, hip):
+    w = W.S6_MAMBA130M
+    t = W.make_s6_inputs(w, seed=0)
+    dev = torch.device("cuda:0")
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
+    y = torch.empty_like(d["u"])
+    h_last = torch.empty((w.B, w.D, w.N), dtype=torch.float32, device=dev)
+    ws_bytes = ssm.selective_scan_workspace_bytes(w.B, w.L, w.D, w.N, torch.bfloat16)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    segments = ssm.selective_scan_segments(w.B, w.L, w.D, w.N)
+    flush = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+    lib = native.load()
+    stream = torch.cuda.current_stream(dev)
+    evs = _events(hip, 4)
+
+    def step(events):
+        rc = lib.ssm_selective_scan_fwd_timed(
+            d["u"].data_ptr(), d["delta"].data_ptr(), d["A"].data_ptr(), d["B"].data_ptr(),
+            d["C"].data_ptr(), d["D"].data_ptr(), d["z"].data_ptr(), d["delta_bias"].data_ptr(),
+            native.FLAG_DELTA_SOFTPLUS, None, y.data_ptr(), h_last.data_ptr(),
+            w.B, w.L, w.D, w.N, native.SSM_BF16, ws.data_ptr(), ws_bytes, stream.cuda_stream,
+            events)
+        native.check(rc, "ssm_selective_scan_fwd_timed")
+
+    for i in range(args.warmup):
+        flush.fill_(float(i))
+        step(None)
+    torch.cuda.synchronize()
+    phases = [0.0, 0.0, 0.0]
+    total = 0.0
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        flush.fill_(float(i))                      # evict the Infinity Cache (untimed)
+        step(evs)
+        torch.cuda.synchronize()
+        p = [_elapsed(hip, evs[k], evs[k + 1]) for k in range(3)]
+        for k in range(3):
+            phases[k] += p[k]
+        total += _elapsed(hip, evs[0], evs[3])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    # back-to-back steps without the flush (working set may sit in the MALL)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(None)
+    torch.cuda.synchronize()
+    hot_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    ms = total / args.steps
+    nbytes = W.s6_algorithmic_bytes(w)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    elems = w.B * w.L * w.D * w.N
+    scan_ms = phases[2] / args.steps
+    reduce_ms = phases[0] / args.steps
+    carry_ms = phases[1] / args.steps
+    scan_gbs = nbytes / (scan_ms * 1e-3) / 1e9
+    flops = 6.0 * elems                            # mul, mul, fma, fma per state update
+    return dict(
+        w=w, t=t, ms=ms, gbs=gbs, nbytes=nbytes, segments=segments, wall=wall, hot_ms=hot_ms,
+        phases_ms=dict(segment_reduce=reduce_ms, carry_scan=carry_ms, segment_scan=scan_ms),
+        scan_gbs=scan_gbs, scan_tflops=flops / (scan_ms * 1e-3) / 1e12,
+        gtokch=w.tok_ch / (ms * 1e-3) / 1e9, elems=elems)
+
+
+def bench_ssd(args, torch, ssm, W):
+    s = W.SSD_MAMBA2
+    t = W.make_ssd_inputs(s, seed=0)
+    dev = torch.device("cuda:0")
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
+    Y = torch.empty_like(d["X"])
+    flush = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+
+    def step():
+        ssm.ssd_chunk_fwd(d["X"], d["delta"], d["A"], d["B"], d["C"], chunk=s.chunk, out=Y)
+
+    try:
+        step()
+    except ssm.SSMError as e:
+        return dict(status=f"unavailable: {e}")
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    total = 0.0
+    for i in range(args.steps):
+        flush.fill_(float(i))
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        torch.cuda.synchronize()
+        total += a.elapsed_time(b)
+    ms = total / args.steps
+    nbytes = W.ssd_algorithmic_bytes(s)
+    Q = s.chunk
+    nchunks = -(-s.L // Q)
+    # causal chunked-SSD MACs per (b, h, chunk): C B^T lower triangle (Q(Q+1)/2 * N),
+    # masked Y_diag (Q(Q+1)/2 * P), chunk state (P*N*Q), Y_off (Q*P*N)
+    tri = Q * (Q + 1) / 2
+    macs = s.B * s.H * nchunks * (tri * s.N + tri * s.P + 2 * s.P * s.N * Q)
+    return dict(status="ok", workload=s.name, ms=ms, gbs=nbytes / (ms * 1e-3) / 1e9,
+                pct_hbm_peak=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS * 100,
+                tflops=2 * macs / (ms * 1e-3) / 1e12,
+                mfma_util=2 * macs / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                gtokch=s.tok_ch / (ms * 1e-3) / 1e9, algorithmic_bytes=nbytes,
+                causal_gflop=2 * macs / 1e9)
+
+
+def cpu_baseline(r, torch):
+    import oracle
+    w, t = r["w"], r["t"]
+    f64 = {k: (oracle._f64(v) if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.s6_fwd(f64["u"], f64["delta"], f64["A"], f64["B"], f64["C"], D=f64["D"], z=f64["z"],
+                  delta_bias=f64["delta_bias"], threads=threads)
+    sec = time.perf_counter() - t0
+    return {"value": round(r["nbytes"] / sec / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the whole {w.name} workload (B={w.B} L={w.L} D={w.D} N={w.N}), fp64 "
+                      f"sequential loop per channel, channels over {threads} OpenMP threads; "
+                      f"{sec:.2f} s wall, algorithmic bytes of the workload / wall time",
+            "seconds": round(sec, 3),
+            "gtokch_per_s": round(w.tok_ch / sec / 1e9, 6)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ssd", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy three times, the "
+                         "reference for scaling FETCH_SIZE/WRITE_SIZE counters")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the scan is data-parallel over channels and would shard with no "
+              "communication); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import selective_state_space_21_amd as ssm
+    from selective_state_space_21_amd import _native as native
+    from selective_state_space_21_amd import workloads as W
+
+    hip = _hip()
+    if args.calibration_copy:
+        src = torch.ones(64 * 2**20, dtype=torch.float32, device="cuda:0")   # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    r = bench_s6(args, torch, ssm, W, native, hip)
+    ssd = None if args.no_ssd else bench_ssd(args, torch, ssm, W)
+    w = r["w"]
+    line = {
+        "metric": "selective-scan fwd achieved HBM GB/s (% of peak) + Gtoken·channels/s",
+        "value": round(r["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "B": w.B, "L": w.L, "D": w.D, "N": w.N,
+            "io_dtype": "bf16", "state_dtype": "f32", "segments": r["segments"],
+            "pct_of_hbm_peak": round(r["gbs"] / HBM_PEAK_GBS * 100, 2),
+            "gtoken_channels_per_s": round(r["gtokch"], 3),
+            "algorithmic_bytes": r["nbytes"],
+            "phases_ms": {k: round(v, 5) for k, v in r["phases_ms"].items()},
+            "ms_per_step_without_cache_flush": round(r["hot_ms"], 5),
+        },
+        "roofline": {
+            "kernel": "s6_fast segment scan (dominant phase)",
+            "bound": "hbm",
+            "achieved": round(r["scan_gbs"], 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(r["scan_gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "alu_view": {"achieved_tflops": round(r["scan_tflops"], 3),
+                         "peak_tflops": FP32_VECTOR_PEAK_TFLOPS,
+                         "flops_per_state_update": 6, "transcendentals_per_state_update": 1},
+        },
+    }
+    if ssd is not None:
+        line["ssd"] = ssd
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(r, torch)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

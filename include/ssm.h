@@ -106,6 +106,23 @@ int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Same operation, for measurement: `events` is NULL or points to 4 hipEvent_t
+ * created by the caller; they are recorded on `stream` at the phase
+ * boundaries -- before the segment reduce, before the carry scan, before the
+ * segment scan, and after it (with one segment the first three coincide).
+ * Recording is asynchronous; the caller reads the intervals after it has
+ * synchronised.  The arguments and results are otherwise those of
+ * ssm_selective_scan_fwd.
+ */
+int ssm_selective_scan_fwd_timed(const void* u, const void* delta, const float* A,
+                                 const void* Bm, const void* Cm, const float* Dskip,
+                                 const void* z, const float* delta_bias, unsigned flags,
+                                 const float* h0, void* y, float* h_last,
+                                 int64_t B, int64_t L, int64_t D, int64_t N, int dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 void* const* events);
+
+/*
  * ---------------------------------------------------------------- SSD chunked
  * The Mamba-2 form with a scalar transition per head (section 3 "Mamba-2 and
  * State Space Duality" of "Mamba & Mamba-2 Architecture"): per (b, head h),

@@ -87,6 +87,9 @@ def _ptr(a):
 
 
 def default_threads() -> int:
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        return int(env)
     return max(1, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
                else (os.cpu_count() or 1))
 

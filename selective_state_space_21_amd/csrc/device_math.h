@@ -39,15 +39,57 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// log(1 + e^x) = max(x, 0) + log1p(e^-|x|), with the accurate library
-// log1p so that small steps keep full relative precision.
+// log1p(e) for e in [0, 1]: with w = 1 + e rounded to fp32, the rounding
+// error c = e - (w - 1) is exact (Fast2Sum), and log1p(e) = log(w) + c / w to
+// first order in c.  v_log_f32 gives log2(w) to about one ulp, so the result
+// keeps full relative precision even for tiny e (then w = 1, c = e).
+__device__ __forceinline__ float log1p_unit(float e) {
+    const float w = 1.0f + e;
+    const float c = e - (w - 1.0f);
+    return fmaf(fast_log2(w), kLn2, c * fast_rcp(w));
+}
+
+// log(1 + e^x) = max(x, 0) + log1p(e^-|x|).
 __device__ __forceinline__ float softplus_f(float x) {
-    return fmaxf(x, 0.0f) + log1pf(fast_exp2(-fabsf(x) * kLog2e));
+    return fmaxf(x, 0.0f) + log1p_unit(fast_exp2(-fabsf(x) * kLog2e));
 }
 
 // z * sigma(z).  For z < -88 the exponential is +inf and the result -0.
 __device__ __forceinline__ float silu_f(float z) {
     return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e));
 }
+
+// Buffer resources (gfx9 V#): loads through a resource take a per-lane byte
+// offset in a VGPR and a uniform byte offset in an SGPR, so a token-row access
+// costs no vector address arithmetic; accesses past num_records read as zero
+// and stores there are dropped.
+constexpr int kBufferConfig = 0x00020000;   // raw, untyped buffer (gfx9 family)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             kBufferConfig);
+}
+
+template <typename T> struct Buf;
+template <> struct Buf<float> {
+    static __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                 uint32_t soff) {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
+    }
+    static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                 uint32_t soff, float v) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)voff, (int)soff, 0);
+    }
+};
+template <> struct Buf<uint16_t> {
+    static __device__ __forceinline__ float load(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                 uint32_t soff) {
+        return bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0));
+    }
+    static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                 uint32_t soff, float v) {
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(v), r, (int)voff, (int)soff, 0);
+    }
+};
 
 }  // namespace ssm

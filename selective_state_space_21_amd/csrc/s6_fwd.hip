@@ -11,9 +11,19 @@
 //
 // Mapping: one lane owns one (b, d) channel and keeps all N states in VGPRs;
 // a wavefront covers 64 consecutive channels of one batch row, so B_t and C_t
-// are wavefront-uniform (scalar loads, SGPR operands) and every activation
-// access is a contiguous 64-element row.  A is pre-scaled by log2(e) so each
-// discretisation is one multiply and one v_exp_f32.
+// are the same for every lane and every activation access is a contiguous
+// 64-element row.  A is pre-scaled by log2(e) so each discretisation is one
+// multiply and one v_exp_f32.
+//
+// Two kernel bodies:
+//   s6_fast    -- N = 16, first-order input term.  Activations are prefetched
+//                 four tokens ahead through buffer loads with a uniform row
+//                 offset; the B/C rows of 16 tokens sit in lanes 0..15 of each
+//                 16-lane row (one token per lane) and reach every lane through
+//                 DPP row broadcasts folded into the multiplies, so no scalar
+//                 load waits inside the token loop.
+//   s6_generic -- any N <= 64 and the ZOH variant: plain token loop with
+//                 wavefront-uniform scalar loads of B/C.
 //
 // Long sequences: the token axis is cut into S segments ("scan within a
 // block, carry the block's state forward", Transformer-math article, "What it
@@ -31,6 +41,8 @@
 
 #include <stdint.h>
 #include <stdlib.h>
+
+#include <type_traits>
 
 #include "device_math.h"
 #include "ssm_internal.h"
@@ -76,10 +88,234 @@ __device__ __forceinline__ float step_dt(float raw, float bias, unsigned flags) 
     return (flags & SSM_FLAG_DELTA_SOFTPLUS) ? softplus_f(x) : x;
 }
 
-// Segment reduce: for segment s < S-1 of channel (b, d), the pair
-// (prod_t exp(dt_t A), end state from zero).
-template <typename T, int NM, bool FULL, bool ZOH>
-__global__ __launch_bounds__(kWave) void s6_segment_reduce(S6Args p) {
+// Broadcast lane k of each 16-lane row to the whole row (DPP row_newbcast,
+// gfx90a and later).  Used as an operand of a multiply, it folds into the
+// instruction (v_mul_f32_dpp) at no cost.
+template <int K>
+__device__ __forceinline__ float row_bcast_c(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, v), 0x150 + K, 0xf, 0xf, true));
+}
+// k must fold to a constant after unrolling.
+__device__ __forceinline__ float row_bcast(float v, int k) {
+    switch (k) {
+        case 0: return row_bcast_c<0>(v);   case 1: return row_bcast_c<1>(v);
+        case 2: return row_bcast_c<2>(v);   case 3: return row_bcast_c<3>(v);
+        case 4: return row_bcast_c<4>(v);   case 5: return row_bcast_c<5>(v);
+        case 6: return row_bcast_c<6>(v);   case 7: return row_bcast_c<7>(v);
+        case 8: return row_bcast_c<8>(v);   case 9: return row_bcast_c<9>(v);
+        case 10: return row_bcast_c<10>(v); case 11: return row_bcast_c<11>(v);
+        case 12: return row_bcast_c<12>(v); case 13: return row_bcast_c<13>(v);
+        case 14: return row_bcast_c<14>(v); default: return row_bcast_c<15>(v);
+    }
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw (storage-format) B or C row of one token: NM values, as 16-byte loads.
+template <typename T, int NM>
+struct RawRow {
+    static constexpr int kWords = NM * (int)sizeof(T) / 16;   // 16-byte pieces
+    u32x4 w[kWords > 0 ? kWords : 1];
+};
+
+template <typename T, int NM>
+__device__ __forceinline__ void load_raw_row(RawRow<T, NM>& r, __amdgpu_buffer_rsrc_t rs,
+                                             uint32_t voff, uint32_t soff) {
+#pragma unroll
+    for (int k = 0; k < RawRow<T, NM>::kWords; ++k)
+        r.w[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(voff + 16 * k), (int)soff, 0);
+}
+
+template <typename T, int NM>
+__device__ __forceinline__ void unpack_row(const RawRow<T, NM>& r, float (&out)[NM]) {
+#pragma unroll
+    for (int k = 0; k < RawRow<T, NM>::kWords; ++k) {
+        const uint32_t v[4] = {r.w[k].x, r.w[k].y, r.w[k].z, r.w[k].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if constexpr (sizeof(T) == 2) {
+                out[8 * k + 2 * q] = __uint_as_float(v[q] << 16);
+                out[8 * k + 2 * q + 1] = __uint_as_float(v[q] & 0xffff0000u);
+            } else {
+                out[4 * k + q] = __uint_as_float(v[q]);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ fast path
+template <int U>
+struct TokBlock {
+    float u[U], d[U], z[U];
+};
+
+// One pass over segment s of the 64 channels of this wavefront, N = 16.
+//   SCAN = false: reduce the segment to (decay, end state from zero);
+//   SCAN = true : scan from the incoming state, write y (and h_last).
+// RAGGED: D is not a multiple of 64 and the last wavefront of a row has
+// inactive lanes, whose stores are skipped; otherwise every lane stores
+// unconditionally and the token loop has no divergent branch.
+// The tensors come in as __restrict__ arguments so that the compiler knows
+// the y stores cannot alias the inputs.
+template <typename T, bool SCAN, bool HAS_Z, bool RAGGED, bool SOFTPLUS>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3)))
+void s6_fast(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
+             const T* __restrict__ z_, const T* __restrict__ Bm_, const T* __restrict__ Cm_,
+             T* __restrict__ y_) {
+    constexpr int NS = 16;      // states per channel
+    constexpr int U = 4;        // tokens per prefetch block
+    constexpr int G = 16;       // tokens per B/C tile group (one per lane of a row)
+    constexpr uint32_t E = sizeof(T);
+    const int64_t d = (int64_t)blockIdx.x * kWave + threadIdx.x;
+    const int64_t b = blockIdx.y;
+    const int s = blockIdx.z;
+    const bool active = d < p.D;
+    const uint32_t col = (uint32_t)(active ? d : p.D - 1);
+    const int64_t D = p.D;
+    const int64_t t0 = (int64_t)s * p.seg_len;
+    const int64_t t1 = t0 + p.seg_len < p.L ? t0 + p.seg_len : p.L;
+    const int nt = (int)(t1 - t0);                         // segment fits 32-bit offsets
+    const int64_t row0 = (b * p.L + t0) * D;
+    const uint32_t seg_bytes = (uint32_t)nt * (uint32_t)D * E;
+    const uint32_t row_bytes = (uint32_t)D * E;
+    const uint32_t voff = col * E;
+    const auto ru = make_rsrc(u_ + row0, seg_bytes);
+    const auto rd = make_rsrc(delta_ + row0, seg_bytes);
+    const auto rz = make_rsrc(HAS_Z ? z_ + row0 : nullptr, HAS_Z ? seg_bytes : 0u);
+    const auto ry = make_rsrc(SCAN ? y_ + row0 : nullptr, SCAN ? seg_bytes : 0u);
+    const uint32_t bc_row = NS * E;
+    const auto rB = make_rsrc(Bm_ + (b * p.L + t0) * NS, (uint32_t)nt * bc_row);
+    const auto rC = make_rsrc(SCAN ? Cm_ + (b * p.L + t0) * NS : nullptr,
+                              SCAN ? (uint32_t)nt * bc_row : 0u);
+    const float bias = p.delta_bias ? p.delta_bias[col] : 0.0f;
+    const float dsk = (SCAN && p.Dskip) ? p.Dskip[col] : 0.0f;
+    const uint32_t lane16 = threadIdx.x & 15u;
+
+    float A2[NS], h[NS];
+    const int64_t hb = (b * D + col) * NS;
+    const int64_t sb = ((b * D + col) * p.S + s) * NS;
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+        A2[n] = p.A[(int64_t)col * NS + n] * kLog2e;
+        float h_in = 0.0f;
+        if (SCAN) {
+            if (p.S > 1) h_in = p.seg_b[sb + n];
+            else if (p.h0) h_in = p.h0[hb + n];
+        }
+        h[n] = h_in;
+    }
+    float dt_sum = 0.0f;
+
+    // B/C tiles: fp32 rows of the current 16-token group, raw rows of the next.
+    float btile[NS], ctile[SCAN ? NS : 1];
+    RawRow<T, NS> rawB, rawC;
+    auto load_tiles = [&](int jb) {
+        const uint32_t off = (uint32_t)min(jb + (int)lane16, nt - 1) * bc_row;
+        load_raw_row<T, NS>(rawB, rB, off, 0);
+        if constexpr (SCAN) load_raw_row<T, NS>(rawC, rC, off, 0);
+    };
+    auto unpack_tiles = [&]() {
+        unpack_row<T, NS>(rawB, btile);
+        if constexpr (SCAN) unpack_row<T, NS>(rawC, ctile);
+    };
+    auto load_block = [&](TokBlock<U>& k, int jb) {
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const uint32_t soff = (uint32_t)min(jb + j, nt - 1) * row_bytes;
+            k.u[j] = Buf<T>::load(ru, voff, soff);
+            k.d[j] = Buf<T>::load(rd, voff, soff);
+            if constexpr (HAS_Z) k.z[j] = Buf<T>::load(rz, voff, soff);
+        }
+    };
+    // q: which quarter of the tile group (lanes 4q .. 4q+3) holds these tokens
+    auto run_block = [&](const TokBlock<U>& k, int jb, auto guard, int q) {
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const int r = jb + j;
+            if constexpr (decltype(guard)::value) {
+                if (r >= nt) break;
+            }
+            const float x = k.d[j] + bias;
+            float dt;
+            if constexpr (SOFTPLUS) dt = softplus_f(x); else dt = x;
+            const float ut = k.u[j];
+            const float dtu = dt * ut;
+            if constexpr (SCAN) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int n = 0; n < NS; ++n) {
+                    const float dA = fast_exp2(dt * A2[n]);
+                    h[n] = fmaf(dA, h[n], row_bcast(btile[n], 4 * q + j) * dtu);
+                    acc = fmaf(row_bcast(ctile[n], 4 * q + j), h[n], acc);
+                }
+                acc = fmaf(dsk, ut, acc);
+                if constexpr (HAS_Z) acc *= silu_f(k.z[j]);
+                if (!RAGGED || active) Buf<T>::store(ry, voff, (uint32_t)r * row_bytes, acc);
+            } else {
+                dt_sum += dt;
+#pragma unroll
+                for (int n = 0; n < NS; ++n) {
+                    const float dA = fast_exp2(dt * A2[n]);
+                    h[n] = fmaf(dA, h[n], row_bcast(btile[n], 4 * q + j) * dtu);
+                }
+            }
+        }
+    };
+
+    using Full = std::false_type;
+    using Tail = std::true_type;
+    TokBlock<U> ka, kb;
+    int jb = 0;
+    load_tiles(0);
+    load_block(ka, 0);
+    unpack_tiles();
+    while (jb + G <= nt) {
+        load_tiles(jb + G);
+        load_block(kb, jb + 4);
+        run_block(ka, jb, Full{}, 0);
+        load_block(ka, jb + 8);
+        run_block(kb, jb + 4, Full{}, 1);
+        load_block(kb, jb + 12);
+        run_block(ka, jb + 8, Full{}, 2);
+        load_block(ka, jb + 16);
+        run_block(kb, jb + 12, Full{}, 3);
+        unpack_tiles();
+        jb += G;
+    }
+    if (jb < nt) {                       // fewer than 16 tokens left
+        load_block(kb, jb + 4);
+        run_block(ka, jb, Tail{}, 0);
+        if (jb + 4 < nt) {
+            load_block(ka, jb + 8);
+            run_block(kb, jb + 4, Tail{}, 1);
+            if (jb + 8 < nt) {
+                load_block(kb, jb + 12);
+                run_block(ka, jb + 8, Tail{}, 2);
+                if (jb + 12 < nt) run_block(kb, jb + 12, Tail{}, 3);
+            }
+        }
+    }
+
+    if constexpr (SCAN) {
+        if (p.h_last && active && s == p.S - 1) {
+#pragma unroll
+            for (int n = 0; n < NS; ++n) p.h_last[hb + n] = h[n];
+        }
+    } else if (active) {
+#pragma unroll
+        for (int n = 0; n < NS; ++n) {
+            p.seg_a[sb + n] = fast_exp2(A2[n] * dt_sum);
+            p.seg_b[sb + n] = h[n];
+        }
+    }
+}
+
+// --------------------------------------------------------------- generic path
+// Any N <= NM (states past N are zero-padded: A = 0, B = C = 0 keeps them at 0
+// and adds exact zeros to y) and the exact-ZOH input term.
+template <typename T, int NM, bool ZOH, bool SCAN>
+__global__ __launch_bounds__(kWave) void s6_generic(S6Args p) {
     const int64_t d = (int64_t)blockIdx.x * kWave + threadIdx.x;
     const int64_t b = blockIdx.y;
     const int s = blockIdx.z;
@@ -89,41 +325,75 @@ __global__ __launch_bounds__(kWave) void s6_segment_reduce(S6Args p) {
     const T* u = static_cast<const T*>(p.u);
     const T* delta = static_cast<const T*>(p.delta);
     const T* Bm = static_cast<const T*>(p.Bm);
+    const T* Cm = static_cast<const T*>(p.Cm);
+    const T* z = static_cast<const T*>(p.z);
+    T* y = static_cast<T*>(p.y);
     const float bias = p.delta_bias ? p.delta_bias[dd] : 0.0f;
+    const float dsk = (SCAN && p.Dskip) ? p.Dskip[dd] : 0.0f;
+    const bool softplus = (p.flags & SSM_FLAG_DELTA_SOFTPLUS) != 0;
 
     float A1[NM], A2[NM], h[NM];
+    const int64_t hb = (b * p.D + dd) * (int64_t)N;
+    const int64_t sb = ((b * p.D + dd) * p.S + s) * (int64_t)N;
 #pragma unroll
     for (int n = 0; n < NM; ++n) {
-        const float a = (FULL || n < N) ? p.A[dd * N + n] : 0.0f;
+        const float a = n < N ? p.A[dd * N + n] : 0.0f;
         A1[n] = a;
         A2[n] = a * kLog2e;
-        h[n] = 0.0f;
+        float h_in = 0.0f;
+        if (SCAN && n < N) {
+            if (p.S > 1) h_in = p.seg_b[sb + n];
+            else if (p.h0) h_in = p.h0[hb + n];
+        }
+        h[n] = h_in;
     }
     const int64_t t0 = (int64_t)s * p.seg_len;
     const int64_t t1 = t0 + p.seg_len < p.L ? t0 + p.seg_len : p.L;
     float dt_sum = 0.0f;
     for (int64_t t = t0; t < t1; ++t) {
         const int64_t i = (b * p.L + t) * p.D + dd;
-        const float dt = step_dt(Elem<T>::load(delta, i), bias, p.flags);
+        const float x = Elem<T>::load(delta, i) + bias;
+        const float dt = softplus ? softplus_f(x) : x;
         const float ut = Elem<T>::load(u, i);
-        float bt[NM];
-        load_bc_row<T, NM, FULL>(Bm, b * p.L + t, N, bt);
         const float dtu = dt * ut;
-        dt_sum += dt;
+        float bt[NM];
+        load_bc_row<T, NM, false>(Bm, b * p.L + t, N, bt);
+        if constexpr (SCAN) {
+            float ct[NM];
+            load_bc_row<T, NM, false>(Cm, b * p.L + t, N, ct);
+            float acc = 0.0f;
 #pragma unroll
-        for (int n = 0; n < NM; ++n) {
-            const float dA = fast_exp2(dt * A2[n]);
-            const float w = dtu * bt[n] * (ZOH ? zoh_factor(dt * A1[n]) : 1.0f);
-            h[n] = fmaf(dA, h[n], w);
+            for (int n = 0; n < NM; ++n) {
+                const float dA = fast_exp2(dt * A2[n]);
+                const float w = dtu * bt[n] * (ZOH ? zoh_factor(dt * A1[n]) : 1.0f);
+                h[n] = fmaf(dA, h[n], w);
+                acc = fmaf(ct[n], h[n], acc);
+            }
+            acc = fmaf(dsk, ut, acc);
+            if (z) acc *= silu_f(Elem<T>::load(z, i));
+            if (active) Elem<T>::store(y, i, acc);
+        } else {
+            dt_sum += dt;
+#pragma unroll
+            for (int n = 0; n < NM; ++n) {
+                const float dA = fast_exp2(dt * A2[n]);
+                const float w = dtu * bt[n] * (ZOH ? zoh_factor(dt * A1[n]) : 1.0f);
+                h[n] = fmaf(dA, h[n], w);
+            }
         }
     }
-    if (active) {
-        const int64_t o = ((b * p.D + dd) * p.S + s) * (int64_t)N;
+    if constexpr (SCAN) {
+        if (p.h_last && active && s == p.S - 1) {
+#pragma unroll
+            for (int n = 0; n < NM; ++n)
+                if (n < N) p.h_last[hb + n] = h[n];
+        }
+    } else if (active) {
 #pragma unroll
         for (int n = 0; n < NM; ++n) {
-            if (FULL || n < N) {
-                p.seg_a[o + n] = fast_exp2(A2[n] * dt_sum);
-                p.seg_b[o + n] = h[n];
+            if (n < N) {
+                p.seg_a[sb + n] = fast_exp2(A2[n] * dt_sum);
+                p.seg_b[sb + n] = h[n];
             }
         }
     }
@@ -163,112 +433,104 @@ __global__ __launch_bounds__(256) void s6_carry_scan(S6Args p, int SP) {
     if (valid && j < p.S) p.seg_b[o] = fmaf(ae, h0, ce);
 }
 
-// Segment scan with readout: start from the incoming state, write y.
-template <typename T, int NM, bool FULL, bool ZOH>
-__global__ __launch_bounds__(kWave) void s6_segment_scan(S6Args p) {
-    const int64_t d = (int64_t)blockIdx.x * kWave + threadIdx.x;
-    const int64_t b = blockIdx.y;
-    const int s = blockIdx.z;
-    const bool active = d < p.D;
-    const int64_t dd = active ? d : p.D - 1;
-    const int N = (int)p.N;
-    const T* u = static_cast<const T*>(p.u);
-    const T* delta = static_cast<const T*>(p.delta);
-    const T* Bm = static_cast<const T*>(p.Bm);
-    const T* Cm = static_cast<const T*>(p.Cm);
-    const T* z = static_cast<const T*>(p.z);
-    T* y = static_cast<T*>(p.y);
-    const float bias = p.delta_bias ? p.delta_bias[dd] : 0.0f;
-    const float dsk = p.Dskip ? p.Dskip[dd] : 0.0f;
-
-    float A1[NM], A2[NM], h[NM];
-    const int64_t hb = (b * p.D + dd) * (int64_t)N;
-#pragma unroll
-    for (int n = 0; n < NM; ++n) {
-        const float a = (FULL || n < N) ? p.A[dd * N + n] : 0.0f;
-        A1[n] = a;
-        A2[n] = a * kLog2e;
-        float h_in = 0.0f;
-        if (FULL || n < N) {
-            if (p.S > 1)
-                h_in = p.seg_b[((b * p.D + dd) * p.S + s) * (int64_t)N + n];
-            else if (p.h0)
-                h_in = p.h0[hb + n];
-        }
-        h[n] = h_in;
-    }
-    const int64_t t0 = (int64_t)s * p.seg_len;
-    const int64_t t1 = t0 + p.seg_len < p.L ? t0 + p.seg_len : p.L;
-    for (int64_t t = t0; t < t1; ++t) {
-        const int64_t i = (b * p.L + t) * p.D + dd;
-        const float dt = step_dt(Elem<T>::load(delta, i), bias, p.flags);
-        const float ut = Elem<T>::load(u, i);
-        float bt[NM], ct[NM];
-        load_bc_row<T, NM, FULL>(Bm, b * p.L + t, N, bt);
-        load_bc_row<T, NM, FULL>(Cm, b * p.L + t, N, ct);
-        const float dtu = dt * ut;
-        float acc = 0.0f;
-#pragma unroll
-        for (int n = 0; n < NM; ++n) {
-            const float dA = fast_exp2(dt * A2[n]);
-            const float w = dtu * bt[n] * (ZOH ? zoh_factor(dt * A1[n]) : 1.0f);
-            h[n] = fmaf(dA, h[n], w);
-            acc = fmaf(ct[n], h[n], acc);
-        }
-        acc = fmaf(dsk, ut, acc);
-        if (p.z) acc *= silu_f(Elem<T>::load(z, i));
-        if (active) Elem<T>::store(y, i, acc);
-    }
-    if (p.h_last && active && s == p.S - 1) {
-#pragma unroll
-        for (int n = 0; n < NM; ++n)
-            if (FULL || n < N) p.h_last[hb + n] = h[n];
-    }
-}
-
 // h_last = h0 (or zeros) for an empty sequence.
 __global__ void s6_copy_state(const float* h0, float* h_last, int64_t count) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < count) h_last[i] = h0 ? h0[i] : 0.0f;
 }
 
-template <typename T, int NM, bool FULL, bool ZOH>
-hipError_t launch_typed(const S6Args& a, hipStream_t stream) {
-    const dim3 block(kWave);
+void mark(const S6Args& a, int i, hipStream_t stream) {
+    if (a.events) (void)hipEventRecord(a.events[i], stream);
+}
+
+hipError_t launch_carry(const S6Args& a, hipStream_t stream) {
+    int SP = 1;
+    while (SP < a.S) SP <<= 1;
+    const int64_t threads = a.B * a.D * a.N * SP;
+    hipLaunchKernelGGL(s6_carry_scan, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       stream, a, SP);
+    return hipSuccess;
+}
+
+template <typename T, bool SP>
+hipError_t launch_fast_sp(const S6Args& a, hipStream_t stream) {
+    const T* U = static_cast<const T*>(a.u);
+    const T* Dl = static_cast<const T*>(a.delta);
+    const T* Z = static_cast<const T*>(a.z);
+    const T* Bp = static_cast<const T*>(a.Bm);
+    const T* Cp = static_cast<const T*>(a.Cm);
+    T* Y = static_cast<T*>(a.y);
     const unsigned dblocks = (unsigned)((a.D + kWave - 1) / kWave);
-    if (a.S > 1) {
-        hipLaunchKernelGGL((s6_segment_reduce<T, NM, FULL, ZOH>),
-                           dim3(dblocks, (unsigned)a.B, (unsigned)(a.S - 1)), block, 0,
-                           stream, a);
-        int SP = 1;
-        while (SP < a.S) SP <<= 1;
-        const int64_t threads = a.B * a.D * a.N * SP;
-        hipLaunchKernelGGL(s6_carry_scan, dim3((unsigned)((threads + 255) / 256)),
-                           dim3(256), 0, stream, a, SP);
+    const dim3 block(kWave);
+    mark(a, 0, stream);
+    if (a.S > 1)
+        hipLaunchKernelGGL((s6_fast<T, false, false, false, SP>),
+                           dim3(dblocks, (unsigned)a.B, (unsigned)(a.S - 1)), block, 0, stream,
+                           a, U, Dl, Z, Bp, Cp, (T*)nullptr);
+    mark(a, 1, stream);
+    if (a.S > 1) launch_carry(a, stream);
+    mark(a, 2, stream);
+    const dim3 grid(dblocks, (unsigned)a.B, (unsigned)a.S);
+    const bool ragged = (a.D % kWave) != 0;
+    if (a.z) {
+        if (ragged)
+            hipLaunchKernelGGL((s6_fast<T, true, true, true, SP>), grid, block, 0, stream, a, U,
+                               Dl, Z, Bp, Cp, Y);
+        else
+            hipLaunchKernelGGL((s6_fast<T, true, true, false, SP>), grid, block, 0, stream, a, U,
+                               Dl, Z, Bp, Cp, Y);
+    } else {
+        if (ragged)
+            hipLaunchKernelGGL((s6_fast<T, true, false, true, SP>), grid, block, 0, stream, a, U,
+                               Dl, Z, Bp, Cp, Y);
+        else
+            hipLaunchKernelGGL((s6_fast<T, true, false, false, SP>), grid, block, 0, stream, a, U,
+                               Dl, Z, Bp, Cp, Y);
     }
-    hipLaunchKernelGGL((s6_segment_scan<T, NM, FULL, ZOH>),
-                       dim3(dblocks, (unsigned)a.B, (unsigned)a.S), block, 0, stream, a);
+    mark(a, 3, stream);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_fast(const S6Args& a, hipStream_t stream) {
+    return (a.flags & SSM_FLAG_DELTA_SOFTPLUS) ? launch_fast_sp<T, true>(a, stream)
+                                               : launch_fast_sp<T, false>(a, stream);
+}
+
+template <typename T, int NM, bool ZOH>
+hipError_t launch_generic(const S6Args& a, hipStream_t stream) {
+    const unsigned dblocks = (unsigned)((a.D + kWave - 1) / kWave);
+    mark(a, 0, stream);
+    if (a.S > 1)
+        hipLaunchKernelGGL((s6_generic<T, NM, ZOH, false>),
+                           dim3(dblocks, (unsigned)a.B, (unsigned)(a.S - 1)), dim3(kWave), 0,
+                           stream, a);
+    mark(a, 1, stream);
+    if (a.S > 1) launch_carry(a, stream);
+    mark(a, 2, stream);
+    hipLaunchKernelGGL((s6_generic<T, NM, ZOH, true>), dim3(dblocks, (unsigned)a.B, (unsigned)a.S),
+                       dim3(kWave), 0, stream, a);
+    mark(a, 3, stream);
     return hipGetLastError();
 }
 
 template <typename T, bool ZOH>
 hipError_t launch_n(const S6Args& a, hipStream_t stream) {
     const int64_t N = a.N;
-    if (N <= 4) return N == 4 ? launch_typed<T, 4, true, ZOH>(a, stream) : launch_typed<T, 4, false, ZOH>(a, stream);
-    if (N <= 8) return N == 8 ? launch_typed<T, 8, true, ZOH>(a, stream) : launch_typed<T, 8, false, ZOH>(a, stream);
-    if (N <= 16) return N == 16 ? launch_typed<T, 16, true, ZOH>(a, stream) : launch_typed<T, 16, false, ZOH>(a, stream);
-    if (N <= 32) return N == 32 ? launch_typed<T, 32, true, ZOH>(a, stream) : launch_typed<T, 32, false, ZOH>(a, stream);
-    return N == 64 ? launch_typed<T, 64, true, ZOH>(a, stream) : launch_typed<T, 64, false, ZOH>(a, stream);
+    if (N <= 4) return launch_generic<T, 4, ZOH>(a, stream);
+    if (N <= 8) return launch_generic<T, 8, ZOH>(a, stream);
+    if (N <= 16) return launch_generic<T, 16, ZOH>(a, stream);
+    if (N <= 32) return launch_generic<T, 32, ZOH>(a, stream);
+    return launch_generic<T, 64, ZOH>(a, stream);
 }
 
 }  // namespace
-
 S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N) {
     S6Plan pl{1, L > 0 ? L : 1, 0};
     if (L <= 0) return pl;
-    // Enough wavefronts to give every SIMD of the 256 CUs about two.
+    // About three wavefronts per SIMD (256 CUs x 4 SIMDs).
     const int64_t waves = B * ((D + kWave - 1) / kWave);
-    int64_t target = 2048;
+    int64_t target = 3072;
     int64_t S = (target + waves - 1) / waves;
     const char* env = getenv("SSM_S6_SEGMENTS");
     if (env && atoi(env) > 0) S = atoi(env);
@@ -277,7 +539,12 @@ S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N) {
     if (S > maxS) S = maxS;
     if (S > 64) S = 64;
     if (S < 1) S = 1;
-    const int64_t seg_len = (L + S - 1) / S;
+    int64_t seg_len = (L + S - 1) / S;
+    // the kernels address one segment through 32-bit buffer offsets
+    while (seg_len * D * 4 > (int64_t)0xFFFFFFFF && S < 64) {
+        ++S;
+        seg_len = (L + S - 1) / S;
+    }
     S = (L + seg_len - 1) / seg_len;   // no empty trailing segment
     pl.S = (int)S;
     pl.seg_len = seg_len;
@@ -287,14 +554,17 @@ S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N) {
 
 hipError_t launch_s6(const S6Args& a, hipStream_t stream) {
     if (a.L == 0) {
+        for (int i = 0; i < 3; ++i) mark(a, i, stream);
         if (a.h_last) {
             const int64_t count = a.B * a.D * a.N;
             hipLaunchKernelGGL(s6_copy_state, dim3((unsigned)((count + 255) / 256)), dim3(256),
                                0, stream, a.h0, a.h_last, count);
         }
+        mark(a, 3, stream);
         return hipGetLastError();
     }
     const bool zoh = (a.flags & SSM_FLAG_ZOH) != 0;
+    if (a.N == 16 && !zoh) return a.bf16 ? launch_fast<uint16_t>(a, stream) : launch_fast<float>(a, stream);
     if (a.bf16) return zoh ? launch_n<uint16_t, true>(a, stream) : launch_n<uint16_t, false>(a, stream);
     return zoh ? launch_n<float, true>(a, stream) : launch_n<float, false>(a, stream);
 }

@@ -33,6 +33,7 @@ int s6_check_sizes(int64_t B, int64_t L, int64_t D, int64_t N, int dtype) {
     if (N > 64) return SSM_ERR_UNSUPPORTED;
     if (B > 65535) return SSM_ERR_UNSUPPORTED;                 // grid y
     if ((D + 63) / 64 > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;
+    if (((L + 63) / 64) * D * 4 > (int64_t)0xFFFFFFFF) return SSM_ERR_UNSUPPORTED;  // 32-bit segment offsets
     return SSM_OK;
 }
 
@@ -86,6 +87,18 @@ int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
                            const float* h0, void* y, float* h_last,
                            int64_t B, int64_t L, int64_t D, int64_t N, int dtype,
                            void* workspace, size_t workspace_bytes, void* stream) {
+    return ssm_selective_scan_fwd_timed(u, delta, A, Bm, Cm, Dskip, z, delta_bias, flags, h0, y,
+                                        h_last, B, L, D, N, dtype, workspace, workspace_bytes,
+                                        stream, nullptr);
+}
+
+int ssm_selective_scan_fwd_timed(const void* u, const void* delta, const float* A,
+                                 const void* Bm, const void* Cm, const float* Dskip,
+                                 const void* z, const float* delta_bias, unsigned flags,
+                                 const float* h0, void* y, float* h_last,
+                                 int64_t B, int64_t L, int64_t D, int64_t N, int dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 void* const* events) {
     int rc = s6_check_sizes(B, L, D, N, dtype);
     if (rc != SSM_OK) return rc;
     if (flags & ~(unsigned)(SSM_FLAG_DELTA_SOFTPLUS | SSM_FLAG_ZOH)) return SSM_ERR_UNSUPPORTED;
@@ -107,6 +120,7 @@ int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
     a.delta_bias = delta_bias; a.h0 = h0; a.y = y; a.h_last = h_last;
     a.B = B; a.L = L; a.D = D; a.N = N;
     a.S = plan.S; a.seg_len = plan.seg_len; a.flags = flags; a.bf16 = dtype == SSM_BF16;
+    a.events = reinterpret_cast<hipEvent_t const*>(events);
     if (plan.S > 1) {
         a.seg_a = static_cast<float*>(workspace);
         a.seg_b = a.seg_a + B * D * (int64_t)plan.S * N;

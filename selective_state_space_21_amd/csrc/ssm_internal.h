@@ -30,6 +30,7 @@ struct S6Args {
     int S;             // number of segments along L (1 = no carry)
     unsigned flags;
     int bf16;          // storage dtype of activations: 1 = bf16, 0 = fp32
+    hipEvent_t const* events;   // NULL, or 4 events recorded at the phase boundaries
 };
 
 struct S6Plan {
