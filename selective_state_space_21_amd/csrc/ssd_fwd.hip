@@ -5,27 +5,32 @@
 // (plus skip and gate).  Section 3 of "Mamba & Mamba-2 Architecture" gives
 // the same map as a masked product Y = (M o (C B^T)) X with the
 // 1-semiseparable M[t,s] = prod_{k=s+1..t} a_k; the kernel uses that form
-// inside a chunk of Q tokens and the carried state across chunks:
-//   Y_off[t]  = exp(cum_t) * C_t S_prev^T                 (MFMA, K = N)
-//   Y_diag[t] = sum_{s<=t} (C_t . B_s) exp(cum_t - cum_s) dt_s X_s   (MFMA, K = N then K = Q)
-//   S_new     = exp(cum_Q) S_prev + sum_s exp(cum_Q - cum_s) dt_s X_s B_s^T (MFMA, K = Q)
-// with cum the in-chunk inclusive sum of dt * A_h (kept in log2 units).
+// inside a chunk of Q tokens and the carried state across chunks.  With cum
+// the in-chunk inclusive sum of dt * A_h (kept in log2 units), the kernel
+// computes the transposed output tile Y^T (P x Q):
+//   Y_off^T[p][t]  = exp(cum_t) * sum_n S[p][n] C[t][n]              (K = N)
+//   Y_diag^T[p][t] = sum_s X[s][p] M^T[s][t],
+//       M^T[s][t]  = (B_s . C_t) exp(cum_t - cum_s) dt_s for s <= t   (K = N, then K = Q)
+//   S_new[p][n]    = exp(cum_Q) S[p][n] + sum_s X[s][p] w_s B[s][n],
+//       w_s        = exp(cum_Q - cum_s) dt_s                         (K = Q)
 //
-// One workgroup of four wavefronts owns one (b, h) for the whole sequence and
-// walks its chunks in order, so the P x N state never leaves the chip: it
-// sits in fp32 MFMA accumulators (each wavefront owns N/4 columns of it) and
-// a bf16 copy in LDS feeds the next chunk's Y_off.  Per chunk the B rows and
-// the transposed X (plain and decay-weighted) are staged in LDS; each
-// wavefront keeps the C rows of its Q/4 output rows in registers, which serve
-// as the A operand of C S^T and, with the same lane layout, as the B operand
-// of B C^T.  Matrix products use v_mfma_f32_16x16x32_bf16 (bf16 operands,
-// fp32 accumulation); masks, decays, skip and gate are fp32.
+// Work mapping: one workgroup of eight wavefronts owns one (b, h) for the
+// whole sequence and walks its chunks in order, so the P x N state never
+// leaves the chip: it sits in fp32 MFMA accumulators (each wavefront owns 16
+// state columns) with a bf16 copy in LDS for the next chunk's Y_off.  The next
+// chunk's B, X, C and delta are fetched into registers while the current one
+// is computed; barriers wait on LDS only, so those loads stay in flight.  Per
+// chunk, B rows and X^T are staged in LDS and each wavefront keeps the C rows
+// of its output columns in registers (the B operand of both S C^T and B C^T).
+// Output tiles are paired first-with-last so every wavefront does the same
+// share of the causal work.  Products use v_mfma_f32_16x16x32_bf16 (bf16
+// operands, fp32 accumulation); masks, decays, skip and gate are fp32.
 //
-// Operand lane layout of v_mfma_f32_16x16x32_bf16 (lane l, g = l / 16,
-// c = l % 16): A holds row c, k = 8g..8g+7; B holds k = 8g..8g+7 of column c;
-// the result holds rows 4g..4g+3 of column c.  Any permutation of k applied
-// to both operands gives the same product; the masked-score tiles use that
-// to feed the result layout of one product straight into the next.
+// Lane layout of v_mfma_f32_16x16x32_bf16 (lane l, g = l / 16, c = l % 16):
+// A holds row c, k = 8g..8g+7; B holds k = 8g..8g+7 of column c; the result
+// holds rows 4g..4g+3 of column c.  Applying one permutation of k to both
+// operands leaves the product unchanged; the score tiles use that to pass a
+// result straight on as the next product's B operand.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -39,9 +44,11 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kP = 64;          // head dimension
-constexpr int kThreads = 256;   // four wavefronts
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -50,28 +57,46 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ __bf16 bf(float x) { return static_cast<__bf16>(x); }
 __device__ __forceinline__ float f32(__bf16 x) { return static_cast<float>(x); }
 
+// Workgroup barrier that waits for this wavefront's LDS traffic only: global
+// loads issued before it (the next chunk's prefetch) stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int Q, int N>
 struct SsdLds {
-    static constexpr int kBStride = N + 8;       // bf16 elements per B row (16 B pad)
-    static constexpr int kXStride = Q + 8;       // bf16 elements per X^T row
-    static constexpr int kHStride = N + 8;       // bf16 elements per state row
+    static constexpr int kBStride = N + 8;       // bf16 per B row (16-byte pad)
+    static constexpr int kXStride = Q + 8;       // bf16 per X^T row
+    static constexpr int kHStride = N + 8;       // bf16 per state row
     alignas(16) float dt[Q];                      // step per token
     alignas(16) float cum[Q];                     // inclusive sum of dt*A*log2(e)
-    alignas(16) float part[kThreads / 64];        // per-wavefront scan totals
+    alignas(16) float wgt[Q];                     // exp(cum_Q - cum_s) * dt_s
+    alignas(16) float part[kWaves];               // per-wavefront scan totals
     alignas(16) __bf16 B[Q * kBStride];           // B rows of the chunk
-    alignas(16) __bf16 Xt[kP * kXStride];         // X^T
-    alignas(16) __bf16 XWt[kP * kXStride];        // X^T scaled by exp(cum_Q - cum_s) dt_s
-    alignas(16) __bf16 H[kP * kHStride];          // state (bf16) for the next Y_off
+    alignas(16) __bf16 Xt[kP * kXStride];         // X^T of the chunk
+    alignas(16) __bf16 H[kP * kHStride];          // state (bf16) for Y_off
+};
+
+template <int Q, int N>
+struct Tiles {
+    static constexpr int T = Q / 16;                           // output column tiles
+    static constexpr int TPW = T >= 2 * kWaves ? 2 : 1;        // tiles per wavefront
+    static constexpr int NTILE = N / 16;                       // state column tiles
+    static constexpr int KN = N / 32;
+    static constexpr int KQ = Q / 32;
+    static constexpr int BPIECE = (Q * N / 8 + kThreads - 1) / kThreads;   // 16-B pieces / thread
+    static constexpr int XPIECE = (Q * kP / 8 + kThreads - 1) / kThreads;
+    // k-th output tile of wavefront w (-1: none); pairs first with last
+    static __device__ __forceinline__ int tile(int w, int k) {
+        if constexpr (T >= 2 * kWaves) return k == 0 ? w : T - 1 - w;
+        else return w < T ? w : -1;
+    }
 };
 
 template <int Q, int N, bool HAS_Z>
 __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
-    constexpr int RW = Q / 4;        // output rows per wavefront
-    constexpr int TT = RW / 16;      // 16-row tiles per wavefront
-    constexpr int KN = N / 32;       // k-steps over N
-    constexpr int NW = N / 4;        // state columns per wavefront
-    constexpr int NT = NW / 16;      // 16-column state tiles per wavefront
-    constexpr int KQ = Q / 32;       // k-steps over the chunk
+    using TL = Tiles<Q, N>;
+    constexpr int TPW = TL::TPW, KN = TL::KN, KQ = TL::KQ;
     using Lds = SsdLds<Q, N>;
     __shared__ Lds sm;
 
@@ -99,139 +124,151 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
     const float bias = p.delta_bias ? p.delta_bias[h] : 0.0f;
     const float dsk = p.Dskip ? p.Dskip[h] : 0.0f;
     const bool softplus = (p.flags & SSM_FLAG_DELTA_SOFTPLUS) != 0;
+    const int ntile = w < TL::NTILE ? w : -1;      // this wavefront's state columns
 
-    // ---- state: fp32 accumulators hacc[j][nt] = S[p = 16j + 4g + r][n = (NT*w + nt)*16 + c]
-    f32x4 hacc[4][NT];
+    // ---- state: hacc[j] = S[p = 16j + 4g + r][n = 16 * ntile + c]
+    f32x4 hacc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int pp = 16 * j + 4 * g + r;
-                const int nn = (NT * w + nt) * 16 + c;
-                hacc[j][nt][r] = p.h0 ? p.h0[(bh * kP + pp) * N + nn] : 0.0f;
-            }
-        }
-    // bf16 copy of the whole state in LDS
+        for (int r = 0; r < 4; ++r)
+            hacc[j][r] = (p.h0 && ntile >= 0)
+                             ? p.h0[(bh * kP + 16 * j + 4 * g + r) * N + 16 * ntile + c] : 0.0f;
     for (int i = tid; i < kP * N; i += kThreads) {
         const int pp = i / N, nn = i % N;
         sm.H[pp * Lds::kHStride + nn] = bf(p.h0 ? p.h0[(bh * kP + pp) * N + nn] : 0.0f);
     }
 
-    const int64_t nchunks = (L + Q - 1) / Q;
-    for (int64_t ch = 0; ch < nchunks; ++ch) {
-        const int64_t tc = ch * Q;                       // first token of the chunk
-        __syncthreads();                                 // previous chunk done with LDS
-        // ---- 1. steps and in-chunk cumulative decay (log2 units)
-        {
-            float a2 = 0.0f, dtv = 0.0f;
-            if (tid < Q) {
-                const int64_t t = tc + tid;
-                if (t < L) {
-                    const float x = bf16_bits_to_f32(Dl[(b * L + t) * H + h]) + bias;
-                    dtv = softplus ? softplus_f(x) : x;
-                    a2 = dtv * A2;
-                }
-            }
-            // inclusive scan within the wavefront, then across wavefronts
-            float v = a2;
+    // ---- inputs through buffer resources based at batch row b: a read past
+    // the end of the sequence (chunk tail) returns zero, so no load is guarded
+    static_assert((Q * N / 8) % kThreads == 0 && (Q * kP / 8) % kThreads == 0, "piece split");
+    const auto rX = make_rsrc(X + b * L * H * kP, (uint32_t)(L * H * kP * 2));
+    const auto rB = make_rsrc(Bg + b * L * G * N, (uint32_t)(L * G * N * 2));
+    const auto rC = make_rsrc(Cg + b * L * G * N, (uint32_t)(L * G * N * 2));
+    const auto rD = make_rsrc(Dl + b * L * H, (uint32_t)(L * H * 2));
+    float dpre = 0.0f;
+    uint4 bpre[TL::BPIECE];
+    uint4 xpre[TL::XPIECE];
+    // B, X and delta of chunk ch into registers
+    auto prefetch = [&](int64_t ch) {
+        const uint32_t tc = (uint32_t)(ch * Q);
+        dpre = bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(
+            rD, (int)(((tc + min(tid, Q - 1)) * (uint32_t)H + (uint32_t)h) * 2), 0, 0));
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float o = __shfl_up(v, off, 64);
-                if (l >= off) v += o;
+        for (int k = 0; k < TL::BPIECE; ++k) {
+            const uint32_t i = tid + k * kThreads;
+            const uint32_t s = i / (N / 8), k8 = i % (N / 8);
+            bpre[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                rB, (int)((((tc + s) * (uint32_t)G + (uint32_t)grp) * N + 8 * k8) * 2), 0, 0));
+        }
+#pragma unroll
+        for (int k = 0; k < TL::XPIECE; ++k) {
+            const uint32_t i = tid + k * kThreads;
+            const uint32_t s = i / (kP / 8), p8 = i % (kP / 8);
+            xpre[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                rX, (int)((((tc + s) * (uint32_t)H + (uint32_t)h) * kP + 8 * p8) * 2), 0, 0));
+        }
+    };
+    // C rows of this wavefront's output columns, B-operand layout
+    auto load_c = [&](int64_t ch, bf16x8 (&cop)[TPW][KN]) {
+        const uint32_t tc = (uint32_t)(ch * Q);
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) {
+            const int ti = TL::tile(w, k);
+            const uint32_t t = tc + 16 * (ti < 0 ? 0 : ti) + c;
+#pragma unroll
+            for (int kk = 0; kk < KN; ++kk)
+                cop[k][kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                    rC, (int)(((t * (uint32_t)G + (uint32_t)grp) * N + 32 * kk + 8 * g) * 2), 0, 0));
+        }
+    };
+
+    const int64_t nchunks = (L + Q - 1) / Q;
+    if (nchunks > 0) prefetch(0);
+    for (int64_t ch = 0; ch < nchunks; ++ch) {
+        const int64_t tc = ch * Q;
+        lds_barrier();                                   // previous chunk done with LDS
+        bf16x8 cop[TPW][KN];
+        load_c(ch, cop);
+        // ---- 1. steps and in-chunk cumulative decay (log2 units)
+        float dtv = 0.0f, a2 = 0.0f;
+        if (tid < Q && tc + tid < L) {              // past the end: no step, no decay
+            const float x = dpre + bias;
+            dtv = softplus ? softplus_f(x) : x;
+            a2 = dtv * A2;
+        }
+        float v = a2;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float o = __shfl_up(v, off, 64);
+            if (l >= off) v += o;
+        }
+        if (l == 63) sm.part[w] = v;
+        // ---- 2. stage B rows and X^T; C rows to the operand registers
+#pragma unroll
+        for (int k = 0; k < TL::BPIECE; ++k) {
+            const int i = tid + k * kThreads;
+            const int s = i / (N / 8), k8 = i % (N / 8);
+            *reinterpret_cast<uint4*>(&sm.B[s * Lds::kBStride + 8 * k8]) = bpre[k];
+        }
+#pragma unroll
+        for (int k = 0; k < TL::XPIECE; ++k) {
+            const int i = tid + k * kThreads;
+            const int s = i / (kP / 8), p8 = i % (kP / 8);
+            const uint32_t u[4] = {xpre[k].x, xpre[k].y, xpre[k].z, xpre[k].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int pp = 8 * p8 + 2 * q;
+                sm.Xt[pp * Lds::kXStride + s] = __builtin_bit_cast(__bf16, (uint16_t)(u[q] & 0xffffu));
+                sm.Xt[(pp + 1) * Lds::kXStride + s] = __builtin_bit_cast(__bf16, (uint16_t)(u[q] >> 16));
             }
-            if (l == 63) sm.part[w] = v;
-            __syncthreads();
+        }
+        lds_barrier();
+        {
+            const f32x4 p0 = *reinterpret_cast<const f32x4*>(&sm.part[0]);
+            const f32x4 p1 = *reinterpret_cast<const f32x4*>(&sm.part[4]);
             float base = 0.0f;
-            for (int k = 0; k < w; ++k) base += sm.part[k];
+#pragma unroll
+            for (int k = 0; k < kWaves; ++k) base += k < w ? (k < 4 ? p0[k] : p1[k - 4]) : 0.0f;
             if (tid < Q) {
                 sm.dt[tid] = dtv;
                 sm.cum[tid] = base + v;
             }
         }
-        __syncthreads();
+        lds_barrier();
         const float cumQ = sm.cum[Q - 1];
-        // ---- 2. stage B rows, X^T and decay-weighted X^T
-        {
-            constexpr int kBVec = N / 8;                 // 16-byte pieces per B row
-            for (int i = tid; i < Q * kBVec; i += kThreads) {
-                const int s = i / kBVec, k8 = i % kBVec;
-                const int64_t t = tc + s;
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (t < L)
-                    v = *reinterpret_cast<const uint4*>(Bg + ((b * L + t) * G + grp) * N + 8 * k8);
-                *reinterpret_cast<uint4*>(&sm.B[s * Lds::kBStride + 8 * k8]) = v;
-            }
-            constexpr int kXVec = kP / 8;
-            for (int i = tid; i < Q * kXVec; i += kThreads) {
-                const int s = i / kXVec, p8 = i % kXVec;
-                const int64_t t = tc + s;
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (t < L)
-                    v = *reinterpret_cast<const uint4*>(X + ((b * L + t) * H + h) * kP + 8 * p8);
-                const float wgt = fast_exp2(cumQ - sm.cum[s]) * sm.dt[s];
-                const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+        if (tid < Q) sm.wgt[tid] = fast_exp2(cumQ - sm.cum[tid]) * sm.dt[tid];
+        lds_barrier();
+
+        // next chunk's inputs travel while this one is computed
+        if (ch + 1 < nchunks) prefetch(ch + 1);
+
+        // ---- 3. output tiles Y^T[p][t]: yacc[k][j] rows p = 16j + 4g + r, column t = tile*16 + c
+        f32x4 yacc[TPW][4];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int pp = 8 * p8 + 2 * q;
-                    const uint16_t lo = (uint16_t)(u[q] & 0xffffu), hi = (uint16_t)(u[q] >> 16);
-                    sm.Xt[pp * Lds::kXStride + s] = __builtin_bit_cast(__bf16, lo);
-                    sm.Xt[(pp + 1) * Lds::kXStride + s] = __builtin_bit_cast(__bf16, hi);
-                    sm.XWt[pp * Lds::kXStride + s] = bf(bf16_bits_to_f32(lo) * wgt);
-                    sm.XWt[(pp + 1) * Lds::kXStride + s] = bf(bf16_bits_to_f32(hi) * wgt);
+        for (int k = 0; k < TPW; ++k) {
+            const int ti = TL::tile(w, k);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) yacc[k][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (ti < 0) continue;
+            // Y_off^T = S C^T, scaled per column by exp(cum_t)
+#pragma unroll
+            for (int kk = 0; kk < KN; ++kk)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bf16x8 hop = *reinterpret_cast<const bf16x8*>(
+                        &sm.H[(16 * j + c) * Lds::kHStride + 32 * kk + 8 * g]);
+                    yacc[k][j] = mfma(hop, cop[k][kk], yacc[k][j]);
                 }
-            }
-        }
-        // ---- 3. C rows of this wavefront's output tiles, A-operand layout
-        bf16x8 cop[TT][KN];
-#pragma unroll
-        for (int i = 0; i < TT; ++i) {
-            const int64_t t = tc + w * RW + 16 * i + c;
-#pragma unroll
-            for (int kk = 0; kk < KN; ++kk) {
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (t < L)
-                    v = *reinterpret_cast<const uint4*>(Cg + ((b * L + t) * G + grp) * N + 32 * kk + 8 * g);
-                cop[i][kk] = __builtin_bit_cast(bf16x8, v);
-            }
-        }
-        __syncthreads();
-
-        // ---- 4. Y_off = exp(cum_t) * C S^T, then Y_diag accumulated on top
-        f32x4 yacc[TT][4];
-#pragma unroll
-        for (int i = 0; i < TT; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) yacc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kk = 0; kk < KN; ++kk) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                // B operand: S^T[n = 32kk + 8g + e][p = 16j + c] = S[p][n] (bf16 row of the state)
-                const bf16x8 hop = *reinterpret_cast<const bf16x8*>(
-                    &sm.H[(16 * j + c) * Lds::kHStride + 32 * kk + 8 * g]);
-#pragma unroll
-                for (int i = 0; i < TT; ++i) yacc[i][j] = mfma(cop[i][kk], hop, yacc[i][j]);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < TT; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float e = fast_exp2(sm.cum[w * RW + 16 * i + 4 * g + r]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) yacc[i][j][r] *= e;
-            }
-
-#pragma unroll
-        for (int i = 0; i < TT; ++i) {
-            const int t0 = w * RW + 16 * i;              // first row of the tile (in chunk)
-            const int tl = t0 + c;                       // this lane's row in the score tiles
+            const int tl = 16 * ti + c;                  // this lane's column (token in chunk)
             const float cum_t = sm.cum[tl];
-            const int nsb = (t0 + 15) / 32 + 1;          // causal: s-blocks touching s <= t
+            const float eoff = fast_exp2(cum_t);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) yacc[k][j] *= eoff;
+            // Y_diag^T over the causal s-blocks of 32 tokens
+            const int nsb = (16 * ti + 15) / 32 + 1;
             for (int sb = 0; sb < nsb; ++sb) {
-                // scores S^T[s][t] = B_s . C_t for s in two 16-row halves of the block
+                // scores S^T[s][t] = B_s . C_t, two 16-row halves
                 f32x4 st[2];
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
@@ -241,97 +278,106 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
                     for (int kk = 0; kk < KN; ++kk) {
                         const bf16x8 bop = *reinterpret_cast<const bf16x8*>(
                             &sm.B[(s0 + c) * Lds::kBStride + 32 * kk + 8 * g]);
-                        st[hh] = mfma(bop, cop[i][kk], st[hh]);
+                        st[hh] = mfma(bop, cop[k][kk], st[hh]);
                     }
                 }
-                // mask and scale; k-slot e of this lane is s = 32sb + 16(e/4) + 4g + e%4
+                // mask and scale; k-slot e <-> s = 32sb + 16(e/4) + 4g + e%4
                 bf16x8 mop;
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int sq = 32 * sb + 16 * hh + 4 * g;
+                    const f32x4 cs = *reinterpret_cast<const f32x4*>(&sm.cum[sq]);
+                    const f32x4 ds = *reinterpret_cast<const f32x4*>(&sm.dt[sq]);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int s = 32 * sb + 16 * hh + 4 * g + r;
-                        float m = 0.0f;
-                        if (s <= tl) m = st[hh][r] * fast_exp2(cum_t - sm.cum[s]) * sm.dt[s];
-                        mop[4 * hh + r] = bf(m);
+                        float m = st[hh][r] * fast_exp2(cum_t - cs[r]) * ds[r];
+                        mop[4 * hh + r] = bf(sq + r <= tl ? m : 0.0f);
                     }
+                }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const __bf16* xr = &sm.Xt[(16 * j + c) * Lds::kXStride + 32 * sb + 4 * g];
                     const bf16x4 lo = *reinterpret_cast<const bf16x4*>(xr);
                     const bf16x4 hi = *reinterpret_cast<const bf16x4*>(xr + 16);
-                    bf16x8 xop;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        xop[e] = lo[e];
-                        xop[4 + e] = hi[e];
-                    }
-                    yacc[i][j] = mfma(mop, xop, yacc[i][j]);
+                    const bf16x8 xop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    yacc[k][j] = mfma(xop, mop, yacc[k][j]);
                 }
             }
         }
 
-        // ---- 5. state update on this wavefront's columns
-        const float decay = fast_exp2(cumQ);
+        // ---- 4. state update on this wavefront's 16 columns
+        if (ntile >= 0) {
+            const float decay = fast_exp2(cumQ);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < 4; ++j) hacc[j] *= decay;
+            const int nn = 16 * ntile + c;
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) hacc[j][nt] *= decay;
+            for (int ks = 0; ks < KQ; ++ks) {
+                const int s8 = 32 * ks + 8 * g;
+                const f32x4 w0 = *reinterpret_cast<const f32x4*>(&sm.wgt[s8]);
+                const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sm.wgt[s8 + 4]);
+                bf16x8 bcol;
 #pragma unroll
-        for (int ks = 0; ks < KQ; ++ks) {
-            bf16x8 bcol[NT];
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const int nn = (NT * w + nt) * 16 + c;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) bcol[nt][e] = sm.B[(32 * ks + 8 * g + e) * Lds::kBStride + nn];
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bf16x8 xw = *reinterpret_cast<const bf16x8*>(
-                    &sm.XWt[(16 * j + c) * Lds::kXStride + 32 * ks + 8 * g]);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) hacc[j][nt] = mfma(xw, bcol[nt], hacc[j][nt]);
-            }
-        }
-        __syncthreads();                                 // all Y_off reads of sm.H done
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sm.H[(16 * j + 4 * g + r) * Lds::kHStride + (NT * w + nt) * 16 + c] = bf(hacc[j][nt][r]);
-
-        // ---- 6. skip, gate, store Y
-#pragma unroll
-        for (int i = 0; i < TT; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tl = w * RW + 16 * i + 4 * g + r;
-                const int64_t t = tc + tl;
-                if (t >= L) continue;
+                for (int e = 0; e < 8; ++e) {
+                    const float we = e < 4 ? w0[e] : w1[e - 4];
+                    bcol[e] = bf(f32(sm.B[(s8 + e) * Lds::kBStride + nn]) * we);
+                }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int pp = 16 * j + c;
-                    float yv = yacc[i][j][r] + dsk * f32(sm.Xt[pp * Lds::kXStride + tl]);
-                    const int64_t o = ((b * L + t) * H + h) * kP + pp;
-                    if constexpr (HAS_Z) yv *= silu_f(bf16_bits_to_f32(Zg[o]));
-                    Y[o] = f32_to_bf16_bits(yv);
+                    const bf16x8 xa = *reinterpret_cast<const bf16x8*>(
+                        &sm.Xt[(16 * j + c) * Lds::kXStride + s8]);
+                    hacc[j] = mfma(xa, bcol, hacc[j]);
                 }
             }
+        }
+        lds_barrier();                                   // all reads of the old state copy done
+        if (ntile >= 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sm.H[(16 * j + 4 * g + r) * Lds::kHStride + 16 * ntile + c] = bf(hacc[j][r]);
+        }
+
+        // ---- 5. skip, gate, store: lane writes p = 16j + 4g .. +3 of token t
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) {
+            const int ti = TL::tile(w, k);
+            if (ti < 0) continue;
+            const int tl = 16 * ti + c;
+            const int64_t t = tc + tl;
+            if (t >= L) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int p0 = 16 * j + 4 * g;
+                const int64_t o = ((b * L + t) * H + h) * kP + p0;
+                float yv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) yv[r] = yacc[k][j][r];
+                if (p.Dskip) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) yv[r] += dsk * f32(sm.Xt[(p0 + r) * Lds::kXStride + tl]);
+                }
+                if constexpr (HAS_Z) {
+                    const u32x2 zz = *reinterpret_cast<const u32x2*>(Zg + o);
+                    yv[0] *= silu_f(__uint_as_float(zz.x << 16));
+                    yv[1] *= silu_f(__uint_as_float(zz.x & 0xffff0000u));
+                    yv[2] *= silu_f(__uint_as_float(zz.y << 16));
+                    yv[3] *= silu_f(__uint_as_float(zz.y & 0xffff0000u));
+                }
+                u32x2 out;
+                out.x = (uint32_t)f32_to_bf16_bits(yv[0]) | ((uint32_t)f32_to_bf16_bits(yv[1]) << 16);
+                out.y = (uint32_t)f32_to_bf16_bits(yv[2]) | ((uint32_t)f32_to_bf16_bits(yv[3]) << 16);
+                *reinterpret_cast<u32x2*>(Y + o) = out;
+            }
+        }
     }
-    if (p.h_last) {
+    if (p.h_last && ntile >= 0) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int pp = 16 * j + 4 * g + r;
-                    const int nn = (NT * w + nt) * 16 + c;
-                    p.h_last[(bh * kP + pp) * N + nn] = hacc[j][nt][r];
-                }
+            for (int r = 0; r < 4; ++r)
+                p.h_last[(bh * kP + 16 * j + 4 * g + r) * N + 16 * ntile + c] = hacc[j][r];
     }
 }
 
