@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <type_traits>
 
 #include "device_math.h"
 #include "ssm_internal.h"
@@ -70,10 +71,12 @@ struct SsdLds {
     static constexpr int kHStride = N + 8;       // bf16 per state row
     alignas(16) float dt[Q];                      // step per token
     alignas(16) float cum[Q];                     // inclusive sum of dt*A*log2(e)
-    alignas(16) float wgt[Q];                     // exp(cum_Q - cum_s) * dt_s
+    alignas(16) float fblk[Q];                    // exp(cum_{32 floor(s/32)} - cum_s) * dt_s
     alignas(16) float part[kWaves];               // per-wavefront scan totals
+    alignas(16) int wide[kWaves];                 // per-wavefront: a 32-token block spans > 2^64
     alignas(16) __bf16 B[Q * kBStride];           // B rows of the chunk
     alignas(16) __bf16 Xt[kP * kXStride];         // X^T of the chunk
+    alignas(16) __bf16 XWt[kP * kXStride];        // X^T with column s scaled by exp(cum_Q - cum_s) dt_s
     alignas(16) __bf16 H[kP * kHStride];          // state (bf16) for Y_off
 };
 
@@ -85,7 +88,11 @@ struct Tiles {
     static constexpr int KN = N / 32;
     static constexpr int KQ = Q / 32;
     static constexpr int BPIECE = (Q * N / 8 + kThreads - 1) / kThreads;   // 16-B pieces / thread
-    static constexpr int XPIECE = (Q * kP / 8 + kThreads - 1) / kThreads;
+    static constexpr int XGROUP = (Q / 4) * (kP / 8);          // (4 tokens x 8 p) groups
+    static constexpr int XPIECE = 4;                           // 16-B rows per group
+    // B pieces fetched ahead of the output tiles; the rest after them, which
+    // keeps the largest tile shape inside the register file
+    static constexpr int BEARLY = (Q == 256 && N == 128) ? BPIECE / 2 : BPIECE;
     // k-th output tile of wavefront w (-1: none); pairs first with last
     static __device__ __forceinline__ int tile(int w, int k) {
         if constexpr (T >= 2 * kWaves) return k == 0 ? w : T - 1 - w;
@@ -93,19 +100,62 @@ struct Tiles {
     }
 };
 
+// 4 tokens x 8 head-dim values (bf16 pairs xs[token][pair]) -> rows 8 p8 .. 8 p8 + 7
+// of a transposed [p][s] tile, columns 4 sg .. 4 sg + 3: eight 8-byte writes
+template <int XSTRIDE>
+__device__ __forceinline__ void stage_xt_rows(__bf16* xt, int sg, int p8, const uint32_t (&xs)[4][4]) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        u32x2 even, odd;       // values 2m and 2m+1 of the group, tokens 0..3
+        even.x = __builtin_amdgcn_perm(xs[1][m], xs[0][m], 0x05040100u);
+        even.y = __builtin_amdgcn_perm(xs[3][m], xs[2][m], 0x05040100u);
+        odd.x = __builtin_amdgcn_perm(xs[1][m], xs[0][m], 0x07060302u);
+        odd.y = __builtin_amdgcn_perm(xs[3][m], xs[2][m], 0x07060302u);
+        const int pp = 8 * p8 + 2 * m;
+        *reinterpret_cast<u32x2*>(&xt[pp * XSTRIDE + 4 * sg]) = even;
+        *reinterpret_cast<u32x2*>(&xt[(pp + 1) * XSTRIDE + 4 * sg]) = odd;
+    }
+}
+
+// two bf16 (round to nearest even) in one dword, a in the low half
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){a, b}, b2));
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane 4q + m receives in
+// element j the 16-bit word m of the 8 bytes addressed by lane 4j + q.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    const s4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s4*)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
 template <int Q, int N, bool HAS_Z>
 __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
     using TL = Tiles<Q, N>;
     constexpr int TPW = TL::TPW, KN = TL::KN, KQ = TL::KQ;
     using Lds = SsdLds<Q, N>;
     __shared__ Lds sm;
+    auto stage_xt = [](__bf16* xt, int sg, int p8, const uint32_t (&xs)[4][4]) {
+        stage_xt_rows<Lds::kXStride>(xt, sg, p8, xs);
+    };
 
     const int tid = threadIdx.x;
     const int w = tid / 64;
     const int l = tid % 64;
     const int g = l / 16;
     const int c = l % 16;
-    const int64_t bh = blockIdx.x;
+    // Workgroups are dealt to the 8 XCDs round robin (i -> XCD i % 8); renumber
+    // them so that each XCD receives a contiguous range of (batch, head) pairs.
+    // Heads of one batch row share B and C, so those rows are then fetched
+    // into about two of the eight L2 caches instead of all eight.
+    const int64_t bh = [] {
+        const uint32_t n = gridDim.x, i = blockIdx.x, x = i % 8, q = n / 8, r = n % 8;
+        return (int64_t)(x * q + min(x, r) + i / 8);
+    }();
     const int64_t b = bh / p.H;
     const int64_t h = bh % p.H;
     const int64_t grp = h / (p.H / p.G);
@@ -141,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
 
     // ---- inputs through buffer resources based at batch row b: a read past
     // the end of the sequence (chunk tail) returns zero, so no load is guarded
-    static_assert((Q * N / 8) % kThreads == 0 && (Q * kP / 8) % kThreads == 0, "piece split");
+    static_assert((Q * N / 8) % kThreads == 0 && TL::XGROUP <= kThreads, "piece split");
     const auto rX = make_rsrc(X + b * L * H * kP, (uint32_t)(L * H * kP * 2));
     const auto rB = make_rsrc(Bg + b * L * G * N, (uint32_t)(L * G * N * 2));
     const auto rC = make_rsrc(Cg + b * L * G * N, (uint32_t)(L * G * N * 2));
@@ -149,24 +199,30 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
     float dpre = 0.0f;
     uint4 bpre[TL::BPIECE];
     uint4 xpre[TL::XPIECE];
-    // B, X and delta of chunk ch into registers
-    auto prefetch = [&](int64_t ch) {
+    // B pieces [k0, k1), X and delta of chunk ch into registers
+    auto prefetch_b = [&](int64_t ch, auto k0, auto k1) {
         const uint32_t tc = (uint32_t)(ch * Q);
-        dpre = bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(
-            rD, (int)(((tc + min(tid, Q - 1)) * (uint32_t)H + (uint32_t)h) * 2), 0, 0));
 #pragma unroll
-        for (int k = 0; k < TL::BPIECE; ++k) {
+        for (int k = decltype(k0)::value; k < decltype(k1)::value; ++k) {
             const uint32_t i = tid + k * kThreads;
             const uint32_t s = i / (N / 8), k8 = i % (N / 8);
             bpre[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                 rB, (int)((((tc + s) * (uint32_t)G + (uint32_t)grp) * N + 8 * k8) * 2), 0, 0));
         }
+    };
+    auto prefetch = [&](int64_t ch) {
+        const uint32_t tc = (uint32_t)(ch * Q);
+        dpre = bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(
+            rD, (int)(((tc + min(tid, Q - 1)) * (uint32_t)H + (uint32_t)h) * 2), 0, 0));
+        prefetch_b(ch, std::integral_constant<int, 0>{}, std::integral_constant<int, TL::BEARLY>{});
+        {
+            // thread -> tokens 4*sg .. 4*sg+3, head-dim values 8*p8 .. 8*p8+7
+            const uint32_t sg = min(tid, TL::XGROUP - 1) / (kP / 8), p8 = tid % (kP / 8);
 #pragma unroll
-        for (int k = 0; k < TL::XPIECE; ++k) {
-            const uint32_t i = tid + k * kThreads;
-            const uint32_t s = i / (kP / 8), p8 = i % (kP / 8);
-            xpre[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                rX, (int)((((tc + s) * (uint32_t)H + (uint32_t)h) * kP + 8 * p8) * 2), 0, 0));
+            for (int q = 0; q < 4; ++q)
+                xpre[q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                    rX, (int)((((tc + 4 * sg + q) * (uint32_t)H + (uint32_t)h) * kP + 8 * p8) * 2),
+                    0, 0));
         }
     };
     // C rows of this wavefront's output columns, B-operand layout
@@ -184,7 +240,11 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
     };
 
     const int64_t nchunks = (L + Q - 1) / Q;
-    if (nchunks > 0) prefetch(0);
+    if (nchunks > 0) {
+        prefetch(0);
+        prefetch_b(0, std::integral_constant<int, TL::BEARLY>{},
+                   std::integral_constant<int, TL::BPIECE>{});
+    }
     for (int64_t ch = 0; ch < nchunks; ++ch) {
         const int64_t tc = ch * Q;
         lds_barrier();                                   // previous chunk done with LDS
@@ -211,17 +271,14 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
             const int s = i / (N / 8), k8 = i % (N / 8);
             *reinterpret_cast<uint4*>(&sm.B[s * Lds::kBStride + 8 * k8]) = bpre[k];
         }
-#pragma unroll
-        for (int k = 0; k < TL::XPIECE; ++k) {
-            const int i = tid + k * kThreads;
-            const int s = i / (kP / 8), p8 = i % (kP / 8);
-            const uint32_t u[4] = {xpre[k].x, xpre[k].y, xpre[k].z, xpre[k].w};
+        if (tid < TL::XGROUP) {
+            const int sg = tid / (kP / 8), p8 = tid % (kP / 8);
+            uint32_t xs[4][4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int pp = 8 * p8 + 2 * q;
-                sm.Xt[pp * Lds::kXStride + s] = __builtin_bit_cast(__bf16, (uint16_t)(u[q] & 0xffffu));
-                sm.Xt[(pp + 1) * Lds::kXStride + s] = __builtin_bit_cast(__bf16, (uint16_t)(u[q] >> 16));
+                xs[q][0] = xpre[q].x; xs[q][1] = xpre[q].y; xs[q][2] = xpre[q].z; xs[q][3] = xpre[q].w;
             }
+            stage_xt(sm.Xt, sg, p8, xs);
         }
         lds_barrier();
         {
@@ -237,123 +294,55 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
         }
         lds_barrier();
         const float cumQ = sm.cum[Q - 1];
-        if (tid < Q) sm.wgt[tid] = fast_exp2(cumQ - sm.cum[tid]) * sm.dt[tid];
+        bool far = false;
+        if (tid < Q) {
+            const float cs = sm.cum[tid], ds = sm.dt[tid];
+            const float rel = sm.cum[tid & ~31] - cs;
+            far = fabsf(rel) > 64.0f;
+            sm.fblk[tid] = fast_exp2(rel) * ds;
+        }
+        if (tid < TL::XGROUP) {
+            // X^T scaled per token by its weight in the chunk's final state
+            const int sg = tid / (kP / 8), p8 = tid % (kP / 8);
+            const f32x4 cs = *reinterpret_cast<const f32x4*>(&sm.cum[4 * sg]);
+            const f32x4 ds = *reinterpret_cast<const f32x4*>(&sm.dt[4 * sg]);
+            uint32_t xs[4][4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float wq = fast_exp2(cumQ - cs[q]) * ds[q];
+                const uint32_t v[4] = {xpre[q].x, xpre[q].y, xpre[q].z, xpre[q].w};
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    xs[q][m] = pack_bf16x2(__uint_as_float(v[m] << 16) * wq,
+                                           __uint_as_float(v[m] & 0xffff0000u) * wq);
+            }
+            stage_xt(sm.XWt, sg, p8, xs);
+        }
+        far = __any(far);
+        if (l == 0) sm.wide[w] = far;
         lds_barrier();
+        bool wide;
+        {
+            const int4 f0 = *reinterpret_cast<const int4*>(&sm.wide[0]);
+            const int4 f1 = *reinterpret_cast<const int4*>(&sm.wide[4]);
+            wide = (f0.x | f0.y | f0.z | f0.w | f1.x | f1.y | f1.z | f1.w) != 0;
+        }
 
         // next chunk's inputs travel while this one is computed
         if (ch + 1 < nchunks) prefetch(ch + 1);
 
-        // ---- 3. output tiles Y^T[p][t]: yacc[k][j] rows p = 16j + 4g + r, column t = tile*16 + c
-        f32x4 yacc[TPW][4];
-#pragma unroll
-        for (int k = 0; k < TPW; ++k) {
-            const int ti = TL::tile(w, k);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) yacc[k][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            if (ti < 0) continue;
-            // Y_off^T = S C^T, scaled per column by exp(cum_t)
-#pragma unroll
-            for (int kk = 0; kk < KN; ++kk)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const bf16x8 hop = *reinterpret_cast<const bf16x8*>(
-                        &sm.H[(16 * j + c) * Lds::kHStride + 32 * kk + 8 * g]);
-                    yacc[k][j] = mfma(hop, cop[k][kk], yacc[k][j]);
-                }
-            const int tl = 16 * ti + c;                  // this lane's column (token in chunk)
-            const float cum_t = sm.cum[tl];
-            const float eoff = fast_exp2(cum_t);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) yacc[k][j] *= eoff;
-            // Y_diag^T over the causal s-blocks of 32 tokens
-            const int nsb = (16 * ti + 15) / 32 + 1;
-            for (int sb = 0; sb < nsb; ++sb) {
-                // scores S^T[s][t] = B_s . C_t, two 16-row halves
-                f32x4 st[2];
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    st[hh] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                    const int s0 = 32 * sb + 16 * hh;
-#pragma unroll
-                    for (int kk = 0; kk < KN; ++kk) {
-                        const bf16x8 bop = *reinterpret_cast<const bf16x8*>(
-                            &sm.B[(s0 + c) * Lds::kBStride + 32 * kk + 8 * g]);
-                        st[hh] = mfma(bop, cop[k][kk], st[hh]);
-                    }
-                }
-                // mask and scale; k-slot e <-> s = 32sb + 16(e/4) + 4g + e%4
-                bf16x8 mop;
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const int sq = 32 * sb + 16 * hh + 4 * g;
-                    const f32x4 cs = *reinterpret_cast<const f32x4*>(&sm.cum[sq]);
-                    const f32x4 ds = *reinterpret_cast<const f32x4*>(&sm.dt[sq]);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        float m = st[hh][r] * fast_exp2(cum_t - cs[r]) * ds[r];
-                        mop[4 * hh + r] = bf(sq + r <= tl ? m : 0.0f);
-                    }
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const __bf16* xr = &sm.Xt[(16 * j + c) * Lds::kXStride + 32 * sb + 4 * g];
-                    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(xr);
-                    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(xr + 16);
-                    const bf16x8 xop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                    yacc[k][j] = mfma(xop, mop, yacc[k][j]);
-                }
-            }
-        }
-
-        // ---- 4. state update on this wavefront's 16 columns
-        if (ntile >= 0) {
-            const float decay = fast_exp2(cumQ);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) hacc[j] *= decay;
-            const int nn = 16 * ntile + c;
-#pragma unroll
-            for (int ks = 0; ks < KQ; ++ks) {
-                const int s8 = 32 * ks + 8 * g;
-                const f32x4 w0 = *reinterpret_cast<const f32x4*>(&sm.wgt[s8]);
-                const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sm.wgt[s8 + 4]);
-                bf16x8 bcol;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float we = e < 4 ? w0[e] : w1[e - 4];
-                    bcol[e] = bf(f32(sm.B[(s8 + e) * Lds::kBStride + nn]) * we);
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const bf16x8 xa = *reinterpret_cast<const bf16x8*>(
-                        &sm.Xt[(16 * j + c) * Lds::kXStride + s8]);
-                    hacc[j] = mfma(xa, bcol, hacc[j]);
-                }
-            }
-        }
-        lds_barrier();                                   // all reads of the old state copy done
-        if (ntile >= 0) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sm.H[(16 * j + 4 * g + r) * Lds::kHStride + 16 * ntile + c] = bf(hacc[j][r]);
-        }
-
-        // ---- 5. skip, gate, store: lane writes p = 16j + 4g .. +3 of token t
-#pragma unroll
-        for (int k = 0; k < TPW; ++k) {
-            const int ti = TL::tile(w, k);
-            if (ti < 0) continue;
+        // ---- 5. skip, gate, store of one output tile: lane writes p = 16j + 4g .. +3 of token t
+        auto store_tile = [&](int ti, const f32x4 (&yacc)[4]) __attribute__((always_inline)) {
             const int tl = 16 * ti + c;
             const int64_t t = tc + tl;
-            if (t >= L) continue;
+            if (t >= L) return;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int p0 = 16 * j + 4 * g;
                 const int64_t o = ((b * L + t) * H + h) * kP + p0;
                 float yv[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) yv[r] = yacc[k][j][r];
+                for (int r = 0; r < 4; ++r) yv[r] = yacc[j][r];
                 if (p.Dskip) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) yv[r] += dsk * f32(sm.Xt[(p0 + r) * Lds::kXStride + tl]);
@@ -370,7 +359,137 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
                 out.y = (uint32_t)f32_to_bf16_bits(yv[2]) | ((uint32_t)f32_to_bf16_bits(yv[3]) << 16);
                 *reinterpret_cast<u32x2*>(Y + o) = out;
             }
+        };
+
+        // ---- 3. output tiles Y^T[p][t]: yacc[j] rows p = 16j + 4g + r, column t = tile*16 + c
+        // Mask and scale of the intra-chunk scores by exp(cum_t - cum_s) dt_s.
+        // Factored as E_t * fblk[s] with E_t = exp(cum_t - cum_{32 sb}): one
+        // exponential per lane and block instead of one per element.  fblk holds
+        // up to one 32-token block's decay, so a chunk where that exceeds 2^64
+        // takes the per-element form (a separately compiled copy of the loop).
+        auto out_tiles = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < TPW; ++k) {
+            const int ti = TL::tile(w, k);
+            if (ti < 0) continue;
+            f32x4 yacc[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) yacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            // Y_off^T = S C^T, scaled per column by exp(cum_t)
+#pragma unroll
+            for (int kk = 0; kk < KN; ++kk)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bf16x8 hop = *reinterpret_cast<const bf16x8*>(
+                        &sm.H[(16 * j + c) * Lds::kHStride + 32 * kk + 8 * g]);
+                    yacc[j] = mfma(hop, cop[k][kk], yacc[j]);
+                }
+            const int tl = 16 * ti + c;                  // this lane's column (token in chunk)
+            const float cum_t = sm.cum[tl];
+            const float eoff = fast_exp2(cum_t);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) yacc[j] *= eoff;
+            auto diag_blocks = [&](auto wide_tag) __attribute__((always_inline)) {
+            constexpr bool kWide = decltype(wide_tag)::value;
+            // Y_diag^T over the causal s-blocks of 32 tokens
+            const int nsb = (16 * ti + 15) / 32 + 1;
+            for (int sb = 0; sb < nsb; ++sb) {
+                // scores S^T[s][t] = B_s . C_t, two 16-row halves
+                f32x4 st[2];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    st[hh] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                    const int s0 = 32 * sb + 16 * hh;
+#pragma unroll
+                    for (int kk = 0; kk < KN; ++kk) {
+                        const bf16x8 bop = *reinterpret_cast<const bf16x8*>(
+                            &sm.B[(s0 + c) * Lds::kBStride + 32 * kk + 8 * g]);
+                        st[hh] = mfma(bop, cop[k][kk], st[hh]);
+                    }
+                }
+                // k-slot e <-> s = 32sb + 16(e/4) + 4g + e%4
+                const bool diag = 32 * sb + 31 > 16 * ti;    // block reaches the tile's first row
+                f32x4 fac[2];
+                if constexpr (!kWide) {
+                    const float et = fast_exp2(cum_t - sm.cum[32 * sb]);
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh)
+                        fac[hh] = *reinterpret_cast<const f32x4*>(&sm.fblk[32 * sb + 16 * hh + 4 * g]) * et;
+                } else {
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int sq = 32 * sb + 16 * hh + 4 * g;
+                        const f32x4 cs = *reinterpret_cast<const f32x4*>(&sm.cum[sq]);
+                        const f32x4 ds = *reinterpret_cast<const f32x4*>(&sm.dt[sq]);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) fac[hh][r] = fast_exp2(cum_t - cs[r]) * ds[r];
+                    }
+                }
+                bf16x8 mop;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int sq = 32 * sb + 16 * hh + 4 * g;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float m = st[hh][r] * fac[hh][r];
+                        if (diag && sq + r > tl) m = 0.0f;
+                        mop[4 * hh + r] = bf(m);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const __bf16* xr = &sm.Xt[(16 * j + c) * Lds::kXStride + 32 * sb + 4 * g];
+                    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(xr);
+                    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(xr + 16);
+                    const bf16x8 xop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    yacc[j] = mfma(xop, mop, yacc[j]);
+                }
+            }
+            };
+            if (wide) diag_blocks(std::true_type{});
+            else diag_blocks(std::false_type{});
+            store_tile(ti, yacc);
         }
+        };
+        out_tiles();
+        if constexpr (TL::BEARLY < TL::BPIECE) {
+            if (ch + 1 < nchunks)
+                prefetch_b(ch + 1, std::integral_constant<int, TL::BEARLY>{},
+                           std::integral_constant<int, TL::BPIECE>{});
+        }
+
+        // ---- 4. state update on this wavefront's 16 columns
+        if (ntile >= 0) {
+            const float decay = fast_exp2(cumQ);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) hacc[j] *= decay;
+            // B operand B[s][n = 16 ntile + c] for 8 consecutive s through two
+            // transposed reads; as supplier this lane addresses row 8g + c/4 (+4),
+            // columns 16 ntile + 4 (c % 4) .. +3
+            const __bf16* bsrc = &sm.B[(8 * g + c / 4) * Lds::kBStride + 16 * ntile + 4 * (c % 4)];
+#pragma unroll
+            for (int ks = 0; ks < KQ; ++ks) {
+                const int s8 = 32 * ks + 8 * g;
+                const bf16x4 lo = lds_read_tr16(bsrc + 32 * ks * Lds::kBStride);
+                const bf16x4 hi = lds_read_tr16(bsrc + (32 * ks + 4) * Lds::kBStride);
+                const bf16x8 bcol = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bf16x8 xa = *reinterpret_cast<const bf16x8*>(
+                        &sm.XWt[(16 * j + c) * Lds::kXStride + s8]);
+                    hacc[j] = mfma(xa, bcol, hacc[j]);
+                }
+            }
+        }
+        lds_barrier();                                   // all reads of the old state copy done
+        if (ntile >= 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sm.H[(16 * j + 4 * g + r) * Lds::kHStride + 16 * ntile + c] = bf(hacc[j][r]);
+        }
+
     }
     if (p.h_last && ntile >= 0) {
 #pragma unroll
