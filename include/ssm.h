@@ -152,6 +152,36 @@ int ssm_ssd_chunk_fwd(const void* X, const void* delta, const float* A,
                       int64_t N, int64_t chunk, int dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * ---------------------------------------------------------------- S6 decode
+ * One token of the selective scan against a resident state, for
+ * autoregressive generation: the plain recurrence, one token at a time, with
+ * a constant D x N state per sequence (Transformer-math "Selective state
+ * space" article, section "What it costs at inference, and on a CPU").  Per
+ * (b, d), with the formulas of ssm_selective_scan_fwd at a single t:
+ *
+ *   dt     = softplus(delta[b,d] + delta_bias[d])     (flag set; else delta + bias)
+ *   state[b,d,n] = exp(dt * A[d,n]) * state[b,d,n] + dt * B[b,n] * u[b,d]
+ *   y[b,d] = (sum_n C[b,n] * state[b,d,n] + Dskip[d] * u[b,d]) * silu(z[b,d])
+ *
+ * Arguments:
+ *   state          : [B, D, N]  fp32, read and overwritten in place (owned by
+ *                    the caller; a sequence's state after token t is its
+ *                    input for token t + 1, as h_last / h0 of the scan)
+ *   u, delta, z, y : [B, D]     dtype (z may be NULL)
+ *   A              : [D, N]     fp32
+ *   Bm, Cm         : [B, N]     dtype, shared by all D channels of row b
+ *   Dskip, delta_bias : [D]     fp32 or NULL
+ *   flags          : SSM_FLAG_DELTA_SOFTPLUS, SSM_FLAG_ZOH as for the scan
+ *   1 <= N <= 64 (N in {4, 8, 16, 32, 64} takes the vectorised path).
+ * Alignment: state, A and the dtype tensors 16 B; Dskip and delta_bias 4 B.
+ * `state` must not overlap any input.  No workspace; asynchronous on stream.
+ */
+int ssm_selective_state_update(float* state, const void* u, const void* delta, const float* A,
+                               const void* Bm, const void* Cm, const float* Dskip,
+                               const void* z, const float* delta_bias, unsigned flags, void* y,
+                               int64_t B, int64_t D, int64_t N, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

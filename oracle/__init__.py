@@ -11,6 +11,8 @@ What is here:
     tokens in double precision, `ssm_oracle.c`).
   * `ssd_fwd` -- the scalar-decay-per-head recurrence whose unrolled matrix is
     the 1-semiseparable SSD matrix (same file).
+  * `s6_step` -- one decode step: the same recurrence over a single token,
+    starting from and returning the caller's state.
   * `scans`   -- the affine-pair scans (sequential, Hillis-Steele doubling,
     Blelloch up/down sweep, chunked with carry) used as pins of the carry
     logic.
@@ -161,3 +163,22 @@ def ssd_fwd(X, delta, A, B, C, D=None, z=None, delta_bias=None,
     if rc != 0:
         raise ValueError("oracle_ssd_fwd rejected its arguments")
     return Y, h_last
+
+
+def s6_step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
+            delta_softplus=True, zoh=False, threads=None):
+    """One decode step in fp64: the recurrence of `s6_fwd` over a single token.
+
+    Decoding runs the plain recurrence one token at a time against a constant
+    D x N state per sequence (Transformer-math "Selective state space"
+    article, section "What it costs at inference, and on a CPU"), so a step is
+    `s6_fwd` with L = 1 and h0 = state.
+    state: [Bt, Dm, N]; u, delta, z: [Bt, Dm]; A: [Dm, N]; B, C: [Bt, N];
+    D, delta_bias: [Dm].  Returns (y [Bt, Dm], new_state [Bt, Dm, N]), float64.
+    """
+    state, u, delta, A, B, C = map(_f64, (state, u, delta, A, B, C))
+    D, z, delta_bias = map(_f64, (D, z, delta_bias))
+    y, h = s6_fwd(u[:, None, :], delta[:, None, :], A, B[:, None, :], C[:, None, :], D=D,
+                  z=None if z is None else z[:, None, :], delta_bias=delta_bias,
+                  delta_softplus=delta_softplus, zoh=zoh, h0=state, threads=threads)
+    return y[:, 0, :], h

@@ -13,7 +13,8 @@ import torch
 from . import _native
 from ._native import SSMError
 
-__all__ = ["selective_scan_fwd", "ssd_chunk_fwd", "selective_scan_workspace_bytes",
+__all__ = ["selective_scan_fwd", "ssd_chunk_fwd", "selective_state_update",
+           "selective_scan_workspace_bytes",
            "selective_scan_segments", "ssd_chunk_workspace_bytes", "SSMError"]
 
 _DT = {torch.float32: _native.SSM_F32, torch.bfloat16: _native.SSM_BF16}
@@ -158,3 +159,48 @@ def ssd_chunk_fwd(X: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torc
         _ptr(workspace), ws_bytes, _stream_handle(dev))
     _native.check(rc, "ssm_ssd_chunk_fwd")
     return Y, h_last
+
+
+def selective_state_update(state: torch.Tensor, u: torch.Tensor, delta: torch.Tensor,
+                           A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                           D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                           delta_bias: Optional[torch.Tensor] = None,
+                           delta_softplus: bool = True, zoh: bool = False,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step of the selective scan (ssm_selective_state_update).
+
+    state: [Bt, Dm, N] fp32, updated in place; u, delta, z: [Bt, Dm];
+    A: [Dm, N] fp32; B, C: [Bt, N] (dtype of u); D, delta_bias: [Dm] fp32.
+    Returns y [Bt, Dm].
+    """
+    lib = _native.load()
+    if u.dtype not in _DT:
+        raise TypeError(f"u must be float32 or bfloat16 (got {u.dtype})")
+    dev, dt = u.device, u.dtype
+    state = _dev_tensor("state", state, torch.float32, dev)
+    u = _dev_tensor("u", u, dt, dev)
+    delta = _dev_tensor("delta", delta, dt, dev)
+    B = _dev_tensor("B", B, dt, dev)
+    C = _dev_tensor("C", C, dt, dev)
+    z = _dev_tensor("z", z, dt, dev)
+    A = _dev_tensor("A", A, torch.float32, dev)
+    D = _dev_tensor("D", D, torch.float32, dev)
+    delta_bias = _dev_tensor("delta_bias", delta_bias, torch.float32, dev)
+    if u.dim() != 2:
+        raise ValueError("u must be [B, D]")
+    Bt, Dm = u.shape
+    N = A.shape[-1]
+    shapes = {"state": (state, (Bt, Dm, N)), "delta": (delta, (Bt, Dm)), "A": (A, (Dm, N)),
+              "B": (B, (Bt, N)), "C": (C, (Bt, N)), "z": (z, (Bt, Dm)), "D": (D, (Dm,)),
+              "delta_bias": (delta_bias, (Dm,))}
+    for name, (t, shp) in shapes.items():
+        if t is not None and tuple(t.shape) != shp:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+    y = out if out is not None else torch.empty((Bt, Dm), dtype=dt, device=dev)
+    _dev_tensor("out", y, dt, dev)
+    flags = (_native.FLAG_DELTA_SOFTPLUS if delta_softplus else 0) | (_native.FLAG_ZOH if zoh else 0)
+    rc = lib.ssm_selective_state_update(
+        _ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+        _ptr(delta_bias), flags, _ptr(y), Bt, Dm, N, _DT[dt], _stream_handle(dev))
+    _native.check(rc, "ssm_selective_state_update")
+    return y

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ssm.h"
+
 namespace ssm {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -57,6 +59,18 @@ __device__ __forceinline__ float softplus_f(float x) {
 // z * sigma(z).  For z < -88 the exponential is +inf and the result -0.
 __device__ __forceinline__ float silu_f(float z) {
     return z * fast_rcp(1.0f + fast_exp2(-z * kLog2e));
+}
+
+// (e^x - 1) / x, the exact zero-order-hold input factor for x = dt * A;
+// its limit 1 at x = 0.
+__device__ __forceinline__ float zoh_factor(float x) {
+    return x != 0.0f ? expm1f(x) / x : 1.0f;
+}
+
+// The step size of one token: softplus(raw + bias) when the flag is set.
+__device__ __forceinline__ float step_dt(float raw, float bias, unsigned flags) {
+    const float x = raw + bias;
+    return (flags & SSM_FLAG_DELTA_SOFTPLUS) ? softplus_f(x) : x;
 }
 
 // Buffer resources (gfx9 V#): loads through a resource take a per-lane byte

@@ -79,15 +79,6 @@ __device__ __forceinline__ void load_bc_row(const T* base, int64_t row, int N,
 // Exact zero-order hold: dB = (exp(dt*A) - 1) / A * B = dt*B * expm1(x)/x,
 // x = dt*A (the ZOH formula of the Transformer-math article's discretisation
 // section); expm1 keeps small x accurate.
-__device__ __forceinline__ float zoh_factor(float x) {
-    return x != 0.0f ? expm1f(x) / x : 1.0f;
-}
-
-__device__ __forceinline__ float step_dt(float raw, float bias, unsigned flags) {
-    const float x = raw + bias;
-    return (flags & SSM_FLAG_DELTA_SOFTPLUS) ? softplus_f(x) : x;
-}
-
 // Broadcast lane k of each 16-lane row to the whole row (DPP row_newbcast,
 // gfx90a and later).  Used as an operand of a multiply, it folds into the
 // instruction (v_mul_f32_dpp) at no cost.

@@ -168,4 +168,29 @@ int ssm_ssd_chunk_fwd(const void* X, const void* delta, const float* A,
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+int ssm_selective_state_update(float* state, const void* u, const void* delta, const float* A,
+                               const void* Bm, const void* Cm, const float* Dskip,
+                               const void* z, const float* delta_bias, unsigned flags, void* y,
+                               int64_t B, int64_t D, int64_t N, int dtype, void* stream) {
+    if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_BAD_DTYPE;
+    if (B < 1 || D < 1 || N < 1) return SSM_ERR_BAD_SHAPE;
+    if (mul3(B, D, N) < 0 || mul3(B, D, N) > kMaxElems / 4) return SSM_ERR_BAD_SHAPE;
+    if (N > 64) return SSM_ERR_UNSUPPORTED;
+    if ((B * D * N + 255) / 256 > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;   // grid x
+    if (flags & ~(unsigned)(SSM_FLAG_DELTA_SOFTPLUS | SSM_FLAG_ZOH)) return SSM_ERR_UNSUPPORTED;
+    if (!state || !u || !delta || !A || !Bm || !Cm || !y) return SSM_ERR_NULL_ARG;
+    const void* big[] = {state, A, u, delta, Bm, Cm, z, y};
+    for (const void* p : big)
+        if (p && !aligned(p, 16)) return SSM_ERR_MISALIGNED;
+    const void* vec[] = {Dskip, delta_bias};
+    for (const void* p : vec)
+        if (p && !aligned(p, 4)) return SSM_ERR_MISALIGNED;
+    ssm::StepArgs a{};
+    a.state = state; a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip;
+    a.z = z; a.delta_bias = delta_bias; a.y = y;
+    a.B = B; a.D = D; a.N = N; a.flags = flags; a.bf16 = dtype == SSM_BF16;
+    const hipError_t e = ssm::launch_s6_step(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 }  // extern "C"

@@ -62,4 +62,23 @@ struct SSDArgs {
 
 hipError_t launch_ssd(const SSDArgs& a, hipStream_t stream);
 
+// One decode step of the selective scan against a resident state.
+struct StepArgs {
+    float* state;          // [B, D, N] fp32, read and written in place
+    const void* u;         // [B, D]
+    const void* delta;     // [B, D]
+    const float* A;        // [D, N]
+    const void* Bm;        // [B, N]
+    const void* Cm;        // [B, N]
+    const float* Dskip;
+    const void* z;
+    const float* delta_bias;
+    void* y;               // [B, D]
+    int64_t B, D, N;
+    unsigned flags;
+    int bf16;
+};
+
+hipError_t launch_s6_step(const StepArgs& a, hipStream_t stream);
+
 }  // namespace ssm

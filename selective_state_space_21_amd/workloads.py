@@ -8,6 +8,7 @@ Generator: numpy PCG64 (`default_rng(seed)`), drawn in float32 in a fixed
 order so that a given (workload, seed, shape) is reproducible byte for byte:
   S6  : u, delta_raw, B, C, z, Dskip, delta_bias, spike positions
   SSD : X, delta_raw, B, C, A
+  decode step : state, u, delta_raw, B, C, z, Dskip, delta_bias
 bf16 tensors are produced from float32 by torch's round-to-nearest-even cast.
 
 Parameterisation conventions (stated on the pages, not part of the kernel):
@@ -73,6 +74,20 @@ class SSDWorkload:
         return self.B * self.L * self.H * self.P
 
 
+@dataclasses.dataclass(frozen=True)
+class StepWorkload:
+    """One decode step of B sequences against a resident [B, D, N] state."""
+    name: str
+    B: int
+    D: int
+    N: int
+    dtype: str
+    desc: str = ""
+
+    def scaled(self, **kw) -> "StepWorkload":
+        return dataclasses.replace(self, **kw)
+
+
 S6_SMALL_FP32 = S6Workload(
     "s6_small_fp32", B=1, L=256, D=64, N=16, dtype="f32", delta_mean=-2.0,
     delta_std=0.5, bias_range=None, skip="ones", gate=False,
@@ -94,6 +109,11 @@ S6_LONG_FP32 = S6Workload(
 SSD_MAMBA2 = SSDWorkload(
     "ssd_mamba2_bf16", B=4, L=8192, H=64, P=64, N=128, G=1, chunk=256,
     dtype="bf16", desc="Mamba-2 SSD, B=4 L=8192 H=64 P=64 N=128 G=1 chunk 256, bf16")
+
+S6_DECODE_2P8B = StepWorkload(
+    "s6_decode_mamba2.8b_bf16", B=64, D=5120, N=16, dtype="bf16",
+    desc="decode step of 64 sequences through a Mamba-2.8B-shaped layer, D=5120 N=16, "
+         "bf16 activations, fp32 state")
 
 S6_WORKLOADS = {w.name: w for w in (S6_SMALL_FP32, S6_MAMBA130M, S6_MAMBA2P8B, S6_LONG_FP32)}
 SSD_WORKLOADS = {w.name: w for w in (SSD_MAMBA2,)}
@@ -168,6 +188,40 @@ def make_ssd_inputs(w: SSDWorkload, seed: int = 0) -> dict:
         A=torch.from_numpy(A), B=_cast(Bm, w.dtype), C=_cast(Cm, w.dtype),
         D=None, z=None, delta_bias=None, h0=None, delta_softplus=True,
         chunk=w.chunk)
+
+
+def make_step_inputs(w: StepWorkload, seed: int = 0) -> dict:
+    """Tensors on the CPU for one decode step: state [B, D, N] fp32 ~ N(0, 1)
+    (a state left by earlier tokens), u, delta_raw ~ N(0, 1), B, C, z ~ N(0, 1),
+    Dskip ~ N(1, 0.1), delta_bias ~ U(-4, -2), A = -exp(log(n + 1)); softplus on."""
+    rng = np.random.default_rng(seed)
+    f32 = np.float32
+    state = rng.standard_normal((w.B, w.D, w.N), dtype=f32)
+    u = rng.standard_normal((w.B, w.D), dtype=f32)
+    delta = rng.standard_normal((w.B, w.D), dtype=f32)
+    Bm = rng.standard_normal((w.B, w.N), dtype=f32)
+    Cm = rng.standard_normal((w.B, w.N), dtype=f32)
+    z = rng.standard_normal((w.B, w.D), dtype=f32)
+    Dskip = (1.0 + 0.1 * rng.standard_normal(w.D)).astype(f32)
+    bias = rng.uniform(-4.0, -2.0, size=w.D).astype(f32)
+    A = np.broadcast_to(-np.exp(np.log(np.arange(1, w.N + 1, dtype=np.float64))),
+                        (w.D, w.N)).astype(f32)
+    return dict(
+        state=torch.from_numpy(state), u=_cast(u, w.dtype), delta=_cast(delta, w.dtype),
+        A=torch.from_numpy(np.ascontiguousarray(A)), B=_cast(Bm, w.dtype), C=_cast(Cm, w.dtype),
+        D=torch.from_numpy(Dskip), z=_cast(z, w.dtype), delta_bias=torch.from_numpy(bias),
+        delta_softplus=True)
+
+
+def step_algorithmic_bytes(w: StepWorkload) -> int:
+    """State read and written once; A, u, delta, z, B, C, Dskip, bias read once; y written."""
+    e = 4 if w.dtype == "f32" else 2
+    n = 2 * w.B * w.D * w.N * 4          # state in and out
+    n += w.D * w.N * 4                   # A
+    n += 4 * w.B * w.D * e               # u, delta, z, y
+    n += 2 * w.B * w.N * e               # B, C
+    n += 2 * w.D * 4                     # Dskip, delta_bias
+    return n
 
 
 def s6_algorithmic_bytes(w: S6Workload, with_h_last: bool = True) -> int:

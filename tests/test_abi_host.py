@@ -120,6 +120,30 @@ def test_ssd_validation_errors(lib):
     assert lib.ssm_ssd_chunk_workspace_bytes(4, 8192, 64, 64, 1, 128, 256, 1) == 0
 
 
+def step(lib, **kw):
+    a = dict(state=FAKE, u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None,
+             flags=1, y=FAKE, Bt=4, Dm=256, N=16, dtype=1, stream=None)
+    a.update(kw)
+    return lib.ssm_selective_state_update(
+        a["state"], a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"],
+        a["flags"], a["y"], a["Bt"], a["Dm"], a["N"], a["dtype"], a["stream"])
+
+
+def test_step_validation_errors(lib):
+    assert step(lib, state=None) == 1
+    assert step(lib, A=None) == 1
+    assert step(lib, y=None) == 1
+    assert step(lib, Bt=0) == 2
+    assert step(lib, N=-1) == 2
+    assert step(lib, Dm=1 << 40, N=1 << 30) == 2
+    assert step(lib, dtype=7) == 3
+    assert step(lib, N=65) == 4
+    assert step(lib, flags=8) == 4
+    assert step(lib, state=FAKE_MIS) == 5
+    assert step(lib, A=FAKE + 4) == 5
+    assert step(lib, D=FAKE + 2) == 5
+
+
 def test_python_wrapper_rejects_host_tensors():
     import torch
     import selective_state_space_21_amd as ssm

@@ -69,6 +69,23 @@ def test_p2_page2_worked_example():
     assert h == pytest.approx(retained + y_in[0], abs=1e-12)
 
 
+def test_p2_as_two_decode_steps():
+    """The worked example is itself a two-token decode: each step starts from
+    the state the previous one returned."""
+    g = _golden("page2_worked_example.json")
+    one = np.ones((1, 1))
+    st = np.zeros((1, 1, 1))
+    y1, st = oracle.s6_step(st, np.array([[g["x"][0]]]), np.array([[g["delta"][0]]]),
+                            g["A"] * one, one, one, delta_softplus=False)
+    assert y1[0, 0] == pytest.approx(20.0, abs=1e-12) and st[0, 0, 0] == y1[0, 0]
+    y2, st = oracle.s6_step(st, np.array([[g["x"][1]]]), np.array([[g["delta"][1]]]),
+                            g["A"] * one, one, one, delta_softplus=False)
+    retained = 20.0 * math.exp(-g["delta"][1])
+    assert round(retained, 2) == g["printed_retained_h1"]
+    assert round(y2[0, 0] - retained, 2) == g["printed_input_term_step2"]
+    assert y2[0, 0] == pytest.approx(retained + g["delta"][1] * g["x"][1], abs=1e-12)
+
+
 # ---------------------------------------------------------------- P3
 def test_p3_horizon_table():
     g = _golden("page5_horizon_table.json")
