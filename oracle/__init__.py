@@ -13,6 +13,8 @@ What is here:
     the 1-semiseparable SSD matrix (same file).
   * `s6_step` -- one decode step: the same recurrence over a single token,
     starting from and returning the caller's state.
+  * `backward.s6_bwd` -- gradients of the selective scan by fp64 reverse-mode
+    differentiation of the per-token definition (plain PyTorch CPU ops).
   * `scans`   -- the affine-pair scans (sequential, Hillis-Steele doubling,
     Blelloch up/down sweep, chunked with carry) used as pins of the carry
     logic.

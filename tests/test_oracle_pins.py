@@ -414,3 +414,52 @@ def test_oracle_rejects_bad_arguments():
     with pytest.raises(ValueError):
         oracle.ssd_fwd(np.zeros((1, 4, 3, 2)), np.zeros((1, 4, 3)), -np.ones(3),
                        np.zeros((1, 4, 2, 2)), np.zeros((1, 4, 2, 2)))   # H % G != 0
+
+
+# ---------------------------------------------------------------- backward
+def _fd_case(seed=0, Bt=2, L=5, Dm=3, N=4):
+    g = torch.Generator().manual_seed(seed)
+    r = lambda *s: torch.randn(*s, generator=g, dtype=torch.float64)
+    return dict(u=r(Bt, L, Dm), delta=r(Bt, L, Dm), A=-2.0 * torch.rand(Dm, N, generator=g,
+                dtype=torch.float64), B=r(Bt, L, N), C=r(Bt, L, N), D=r(Dm), z=r(Bt, L, Dm),
+                delta_bias=r(Dm), h0=r(Bt, Dm, N)), r(Bt, L, Dm), r(Bt, Dm, N), g
+
+
+def test_backward_matches_finite_differences_of_the_c_oracle():
+    """Directional derivatives of sum(dy*y) + sum(dh*h_last), by central
+    differences of the C oracle (separate code), against the autodiff
+    gradients, for every input."""
+    from oracle.backward import s6_bwd
+    inp, dy, dh, g = _fd_case()
+    gr = s6_bwd(inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], dy, D=inp["D"], z=inp["z"],
+                delta_bias=inp["delta_bias"], h0=inp["h0"], dh_last=dh)
+
+    def f(**kw):
+        a = dict(inp)
+        a.update(kw)
+        y, hl = oracle.s6_fwd(a["u"], a["delta"], a["A"], a["B"], a["C"], D=a["D"], z=a["z"],
+                              delta_bias=a["delta_bias"], h0=a["h0"])
+        return float((y * dy.numpy()).sum() + (hl * dh.numpy()).sum())
+
+    eps = 1e-6
+    for k, x in inp.items():
+        v = torch.randn(x.shape, generator=g, dtype=torch.float64)
+        fd = (f(**{k: x + eps * v}) - f(**{k: x - eps * v})) / (2 * eps)
+        an = float((gr["dh0" if k == "h0" else "d" + k] * v).sum())
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (k, fd, an)
+
+
+def test_backward_one_step_closed_form():
+    """N = 1, L = 1, no softplus, skip or gate: y = C (e^{dt A} h0 + dt B u)."""
+    from oracle.backward import s6_bwd
+    u, dt, a, b, c, h0 = 0.7, 0.3, -1.5, 1.1, -0.8, 0.4
+    T = lambda v: torch.tensor(v, dtype=torch.float64)
+    gr = s6_bwd(T([[[u]]]), T([[[dt]]]), T([[a]]), T([[[b]]]), T([[[c]]]), T([[[1.0]]]),
+                delta_softplus=False, h0=T([[[h0]]]))
+    e = math.exp(dt * a)
+    assert gr["du"].item() == pytest.approx(c * dt * b, rel=1e-14)
+    assert gr["ddelta"].item() == pytest.approx(c * (a * e * h0 + b * u), rel=1e-14)
+    assert gr["dA"].item() == pytest.approx(c * h0 * dt * e, rel=1e-14)
+    assert gr["dB"].item() == pytest.approx(c * dt * u, rel=1e-14)
+    assert gr["dC"].item() == pytest.approx(e * h0 + dt * b * u, rel=1e-14)
+    assert gr["dh0"].item() == pytest.approx(c * e, rel=1e-14)
