@@ -153,6 +153,43 @@ int ssm_ssd_chunk_fwd(const void* X, const void* delta, const float* A,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ---------------------------------------------------------------- S6 backward
+ * Gradients of the selective scan (the operation of ssm_selective_scan_fwd,
+ * Euler input term) for L = sum(dy * y) + sum(dh_last * h_last).  The states
+ * are not stored by the forward call: they are recomputed from the saved
+ * inputs (the backward pass by recomputation of the Transformer-math
+ * "Selective state space" article, "Why the fused kernel is the real
+ * contribution").
+ *
+ * Inputs: those of the forward call (u, delta, A, Bm, Cm, Dskip, z,
+ * delta_bias, flags, h0; same shapes and dtype), plus
+ *   dy       : [B, L, D]  dtype       gradient of y
+ *   dh_last  : [B, D, N]  fp32 or NULL (zeros)
+ * Outputs (all written, never accumulated into):
+ *   du, ddelta     : [B, L, D] dtype  (ddelta is the gradient of the raw delta)
+ *   dz             : [B, L, D] dtype, required when z is given
+ *   dA             : [D, N]    fp32
+ *   dB, dC         : [B, L, N] fp32   (summed over the D channels)
+ *   dDskip, ddelta_bias : [D]  fp32 or NULL (not computed)
+ *   dh0            : [B, D, N] fp32 or NULL
+ * Supported: 1 <= N <= 16; flags SSM_FLAG_DELTA_SOFTPLUS only (no ZOH).
+ * The workspace (query below; 256-byte aligned) holds a state checkpoint
+ * every 16 tokens and per-channel-group partial sums; results are
+ * deterministic (no atomics).
+ */
+size_t ssm_selective_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
+                                              int dtype);
+
+int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* Bm,
+                           const void* Cm, const float* Dskip, const void* z,
+                           const float* delta_bias, unsigned flags, const float* h0,
+                           const void* dy, const float* dh_last, void* du, void* ddelta,
+                           float* dA, float* dB, float* dC, float* dDskip, void* dz,
+                           float* ddelta_bias, float* dh0, int64_t B, int64_t L, int64_t D,
+                           int64_t N, int dtype, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
  * ---------------------------------------------------------------- S6 decode
  * One token of the selective scan against a resident state, for
  * autoregressive generation: the plain recurrence, one token at a time, with

@@ -13,7 +13,7 @@ import torch
 from . import _native
 from ._native import SSMError
 
-__all__ = ["selective_scan_fwd", "ssd_chunk_fwd", "selective_state_update",
+__all__ = ["selective_scan_fwd", "selective_scan_bwd", "ssd_chunk_fwd", "selective_state_update",
            "selective_scan_workspace_bytes",
            "selective_scan_segments", "ssd_chunk_workspace_bytes", "SSMError"]
 
@@ -204,3 +204,70 @@ def selective_state_update(state: torch.Tensor, u: torch.Tensor, delta: torch.Te
         _ptr(delta_bias), flags, _ptr(y), Bt, Dm, N, _DT[dt], _stream_handle(dev))
     _native.check(rc, "ssm_selective_state_update")
     return y
+
+
+def selective_scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                       C: torch.Tensor, dy: torch.Tensor, D: Optional[torch.Tensor] = None,
+                       z: Optional[torch.Tensor] = None,
+                       delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = True,
+                       h0: Optional[torch.Tensor] = None, dh_last: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None) -> dict:
+    """Gradients of the S6 scan (ssm_selective_scan_bwd), states recomputed.
+
+    Inputs as selective_scan_fwd plus dy [Bt, L, Dm] (dtype of u) and
+    dh_last [Bt, Dm, N] fp32.  Returns a dict with du, ddelta (dtype of u),
+    dA [Dm, N], dB, dC [Bt, L, N] (fp32), and dD, dz, ddelta_bias, dh0 for the
+    optional inputs that were given.
+    """
+    lib = _native.load()
+    if u.dtype not in _DT:
+        raise TypeError(f"u must be float32 or bfloat16 (got {u.dtype})")
+    dev, dt = u.device, u.dtype
+    u = _dev_tensor("u", u, dt, dev)
+    delta = _dev_tensor("delta", delta, dt, dev)
+    B = _dev_tensor("B", B, dt, dev)
+    C = _dev_tensor("C", C, dt, dev)
+    z = _dev_tensor("z", z, dt, dev)
+    dy = _dev_tensor("dy", dy, dt, dev)
+    A = _dev_tensor("A", A, torch.float32, dev)
+    D = _dev_tensor("D", D, torch.float32, dev)
+    delta_bias = _dev_tensor("delta_bias", delta_bias, torch.float32, dev)
+    h0 = _dev_tensor("h0", h0, torch.float32, dev)
+    dh_last = _dev_tensor("dh_last", dh_last, torch.float32, dev)
+    if u.dim() != 3:
+        raise ValueError("u must be [B, L, D]")
+    Bt, L, Dm = u.shape
+    N = A.shape[-1]
+    shapes = {"delta": (delta, (Bt, L, Dm)), "A": (A, (Dm, N)), "B": (B, (Bt, L, N)),
+              "C": (C, (Bt, L, N)), "z": (z, (Bt, L, Dm)), "dy": (dy, (Bt, L, Dm)),
+              "D": (D, (Dm,)), "delta_bias": (delta_bias, (Dm,)), "h0": (h0, (Bt, Dm, N)),
+              "dh_last": (dh_last, (Bt, Dm, N))}
+    for name, (t, shp) in shapes.items():
+        if t is not None and tuple(t.shape) != shp:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+    f32 = torch.float32
+    out = {"du": torch.empty_like(u), "ddelta": torch.empty_like(u),
+           "dA": torch.empty((Dm, N), dtype=f32, device=dev),
+           "dB": torch.empty((Bt, L, N), dtype=f32, device=dev),
+           "dC": torch.empty((Bt, L, N), dtype=f32, device=dev)}
+    if D is not None:
+        out["dD"] = torch.empty((Dm,), dtype=f32, device=dev)
+    if z is not None:
+        out["dz"] = torch.empty_like(z)
+    if delta_bias is not None:
+        out["ddelta_bias"] = torch.empty((Dm,), dtype=f32, device=dev)
+    if h0 is not None:
+        out["dh0"] = torch.empty((Bt, Dm, N), dtype=f32, device=dev)
+    need = int(lib.ssm_selective_scan_bwd_workspace_bytes(Bt, L, Dm, N, _DT[dt]))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    flags = _native.FLAG_DELTA_SOFTPLUS if delta_softplus else 0
+    rc = lib.ssm_selective_scan_bwd(
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+        flags, _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(out["du"]), _ptr(out["ddelta"]),
+        _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out.get("dD")),
+        _ptr(out.get("dz")), _ptr(out.get("ddelta_bias")), _ptr(out.get("dh0")),
+        Bt, L, Dm, N, _DT[dt], _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream_handle(dev))
+    _native.check(rc, "ssm_selective_scan_bwd")
+    return out

@@ -54,6 +54,18 @@ int ssd_check_sizes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64
     return SSM_OK;
 }
 
+int s6_bwd_check_sizes(int64_t B, int64_t L, int64_t D, int64_t N, int dtype) {
+    int rc = s6_check_sizes(B, L, D, N, dtype);
+    if (rc != SSM_OK) return rc;
+    if (N > 16) return SSM_ERR_UNSUPPORTED;
+    const int64_t G = (D + 31) / 32;
+    if (G > 0x7fffffffLL || 2 * B * L * N + D * N + D > (int64_t)0x7fffffff * 256)
+        return SSM_ERR_UNSUPPORTED;
+    if (mul3(2 * G, B * L, N) < 0) return SSM_ERR_BAD_SHAPE;
+    if ((L + 16) * N * esize(dtype) >= (int64_t)0x80000000LL) return SSM_ERR_UNSUPPORTED;  // B/C row offsets
+    return SSM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -190,6 +202,47 @@ int ssm_selective_state_update(float* state, const void* u, const void* delta, c
     a.z = z; a.delta_bias = delta_bias; a.y = y;
     a.B = B; a.D = D; a.N = N; a.flags = flags; a.bf16 = dtype == SSM_BF16;
     const hipError_t e = ssm::launch_s6_step(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+size_t ssm_selective_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
+                                              int dtype) {
+    if (s6_bwd_check_sizes(B, L, D, N, dtype) != SSM_OK) return 0;
+    return ssm::s6_bwd_workspace_bytes(B, L, D, N);
+}
+
+int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* Bm,
+                           const void* Cm, const float* Dskip, const void* z,
+                           const float* delta_bias, unsigned flags, const float* h0,
+                           const void* dy, const float* dh_last, void* du, void* ddelta,
+                           float* dA, float* dB, float* dC, float* dDskip, void* dz,
+                           float* ddelta_bias, float* dh0, int64_t B, int64_t L, int64_t D,
+                           int64_t N, int dtype, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    int rc = s6_bwd_check_sizes(B, L, D, N, dtype);
+    if (rc != SSM_OK) return rc;
+    if (flags & ~(unsigned)SSM_FLAG_DELTA_SOFTPLUS) return SSM_ERR_UNSUPPORTED;
+    if (!A || !dA) return SSM_ERR_NULL_ARG;
+    if (L > 0 && (!u || !delta || !Bm || !Cm || !dy || !du || !ddelta || !dB || !dC))
+        return SSM_ERR_NULL_ARG;
+    if (L > 0 && z && !dz) return SSM_ERR_NULL_ARG;
+    const void* big[] = {u, delta, Bm, Cm, z, dy, du, ddelta, dB, dC, dz};
+    for (const void* p : big)
+        if (p && !aligned(p, 16)) return SSM_ERR_MISALIGNED;
+    const void* vec[] = {A, Dskip, delta_bias, h0, dh_last, dA, dDskip, ddelta_bias, dh0};
+    for (const void* p : vec)
+        if (p && !aligned(p, 4)) return SSM_ERR_MISALIGNED;
+    const size_t need = ssm::s6_bwd_workspace_bytes(B, L, D, N);
+    if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return SSM_ERR_MISALIGNED;
+    ssm::S6BwdArgs a{};
+    a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip;
+    a.z = L > 0 ? z : nullptr; a.delta_bias = delta_bias; a.h0 = h0; a.dy = dy;
+    a.dh_last = dh_last; a.du = du; a.ddelta = ddelta; a.dA = dA; a.dB = dB; a.dC = dC;
+    a.dDskip = dDskip; a.dz = dz; a.ddelta_bias = ddelta_bias; a.dh0 = dh0;
+    a.B = B; a.L = L; a.D = D; a.N = N; a.flags = flags; a.bf16 = dtype == SSM_BF16;
+    ssm::s6_bwd_carve(a, workspace);
+    const hipError_t e = ssm::launch_s6_bwd(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

@@ -81,4 +81,41 @@ struct StepArgs {
 
 hipError_t launch_s6_step(const StepArgs& a, hipStream_t stream);
 
+// Backward pass of the selective scan (states recomputed, not stored).
+struct S6BwdArgs {
+    const void* u;
+    const void* delta;
+    const float* A;
+    const void* Bm;
+    const void* Cm;
+    const float* Dskip;
+    const void* z;
+    const float* delta_bias;
+    const float* h0;
+    const void* dy;
+    const float* dh_last;
+    void* du;
+    void* ddelta;
+    float* dA;
+    float* dB;
+    float* dC;
+    float* dDskip;
+    void* dz;
+    float* ddelta_bias;
+    float* dh0;
+    int64_t B, L, D, N;
+    unsigned flags;
+    int bf16;
+    // workspace, carved by s6_bwd_carve
+    float* ckpt;       // [B, D, ceil(L/16), N] state before each 16-token tile
+    float* part_bc;    // [2][ceil(D/32)][B, L, N] per-channel-group dB, dC
+    float* part_dA;    // [B, D, N]
+    float* part_dD;    // [B, D]
+    float* part_db;    // [B, D]
+};
+
+size_t s6_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N);
+void s6_bwd_carve(S6BwdArgs& a, void* workspace);
+hipError_t launch_s6_bwd(const S6BwdArgs& a, hipStream_t stream);
+
 }  // namespace ssm

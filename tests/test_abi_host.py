@@ -144,6 +144,36 @@ def test_step_validation_errors(lib):
     assert step(lib, D=FAKE + 2) == 5
 
 
+def bwd(lib, **kw):
+    a = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, flags=1,
+             h0=None, dy=FAKE, dh=None, du=FAKE, dd=FAKE, dA=FAKE, dB=FAKE, dC=FAKE, dD=None,
+             dz=None, dbias=None, dh0=None, Bt=2, L=64, Dm=128, N=16, dtype=1, ws=0x100000,
+             ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.ssm_selective_scan_bwd(
+        a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["flags"],
+        a["h0"], a["dy"], a["dh"], a["du"], a["dd"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"],
+        a["dbias"], a["dh0"], a["Bt"], a["L"], a["Dm"], a["N"], a["dtype"], a["ws"],
+        a["ws_bytes"], a["stream"])
+
+
+def test_bwd_validation_errors(lib):
+    assert bwd(lib, dy=None) == 1
+    assert bwd(lib, dA=None) == 1
+    assert bwd(lib, z=FAKE, dz=None) == 1
+    assert bwd(lib, Bt=0) == 2
+    assert bwd(lib, dtype=9) == 3
+    assert bwd(lib, N=17) == 4
+    assert bwd(lib, flags=3) == 4
+    assert bwd(lib, du=FAKE_MIS) == 5
+    assert bwd(lib, ws=0x100010) == 5
+    assert bwd(lib, ws_bytes=16) == 6
+    assert bwd(lib, ws=None) == 6
+    need = lib.ssm_selective_scan_bwd_workspace_bytes(8, 2048, 1536, 16, 1)
+    assert need > 8 * 1536 * 128 * 16 * 4          # the state checkpoints alone
+    assert lib.ssm_selective_scan_bwd_workspace_bytes(8, 2048, 1536, 17, 1) == 0
+
+
 def test_python_wrapper_rejects_host_tensors():
     import torch
     import selective_state_space_21_amd as ssm
