@@ -16,7 +16,7 @@
 //   du_t  = g_t D + dt_t sum_n m_t B_t;  dz_t = dy_t r_t silu'(z_t)
 //   dA   += m_t h_{t-1} dt_t a_t;  dD += g_t u_t;  dbias += ddelta_t;  dh0 = a_0 m_0
 //
-// Mapping: a workgroup of 8 wavefronts covers 32 channels of one batch row;
+// Mapping: a workgroup of 4 wavefronts covers 16 channels of one batch row;
 // each 16-lane row of a wavefront is one channel and lane n holds state n
 // (N <= 16), so a lane carries one state and one adjoint.  Per-channel,
 // per-token scalars (dt, u, g, ...) of a 16-token tile are computed by lane j
@@ -25,7 +25,7 @@
 //   2. s6_bwd_main: tiles in reverse; each tile recomputes its 16 states
 //      from the checkpoint into registers, then runs the adjoint backwards.
 //      Sums over n are row all-reduces (4 DPP adds); dB and dC are summed
-//      over the wavefront's 4 rows (xor swizzles) and the workgroup's 8
+//      over the wavefront's 4 rows (xor swizzles) and the workgroup's 4
 //      wavefronts (LDS), giving one partial per (channel group, b, t, n).
 //   3. s6_bwd_reduce: sums the channel-group partials of dB and dC and the
 //      batch partials of dA, D and bias.  No atomics: results are
@@ -41,7 +41,7 @@
 namespace ssm {
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kChans = 4 * kWaves;     // channels per workgroup
 constexpr int kTile = 16;              // tokens per tile = per checkpoint
@@ -82,41 +82,72 @@ __device__ __forceinline__ float row_sum(float v) {
     return v;
 }
 
+// Reduce-scatter over the 16 lanes of each row: v[i] is this lane's term for
+// token i; the result in lane j is the row's sum for token j.  Four halving
+// exchanges (lane distance 8, 4, 2, 1): each lane keeps the half of its
+// tokens whose index bit matches its own lane bit, adding the partner's copy.
+__device__ __forceinline__ float row_reduce_scatter(const float (&v)[16], int j) {
+    const bool b3 = j & 8, b2 = j & 4, b1 = j & 2, b0 = j & 1;
+    float a[8], c[4], e[2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        a[i] = (b3 ? v[i + 8] : v[i]) + dpp_mov<0x128>(b3 ? v[i] : v[i + 8]);   // row_ror 8 = xor 8
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        c[i] = (b2 ? a[i + 4] : a[i]) + lane_xor<4>(b2 ? a[i] : a[i + 4]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        e[i] = (b1 ? c[i + 2] : c[i]) + dpp_mov<0x4E>(b1 ? c[i] : c[i + 2]);  // quad xor 2
+    return (b0 ? e[1] : e[0]) + dpp_mov<0xB1>(b0 ? e[0] : e[1]);               // quad xor 1
+}
+
 __device__ __forceinline__ float sigmoid_f(float x) {
     return fast_rcp(1.0f + fast_exp2(-x * kLog2e));
 }
 
-// Per-channel scalars of token t0 + j, computed by lane j of the row.
-template <typename T, bool HAS_Z, bool SOFTPLUS, bool FULL>
-struct TileScalars {
-    float dt, dtu, u, g, sig, z, dy;
-
-    __device__ __forceinline__ void load(const S6BwdArgs& p, const LaneId& id, int64_t t0,
-                                         float bias) {
+// Per-channel inputs of token t0 + j, loaded by lane j of the row (raw, so
+// that they can be fetched a tile ahead), and the scalars derived from them.
+template <typename T, bool HAS_Z, bool FULL>
+struct TileRaw {
+    float delta, u, z, dy;
+    __device__ __forceinline__ void load(const S6BwdArgs& p, const LaneId& id, int64_t t0) {
         const int64_t t = t0 + id.n;
         const bool in = id.chan_ok && t < p.L;
         const int64_t i = (id.b * p.L + (in ? t : 0)) * p.D + id.dc;
-        const float x = Elem<T>::load(static_cast<const T*>(p.delta), i) + bias;
+        delta = in ? Elem<T>::load(static_cast<const T*>(p.delta), i) : 0.0f;
         u = in ? Elem<T>::load(static_cast<const T*>(p.u), i) : 0.0f;
-        dt = in ? (SOFTPLUS ? softplus_f(x) : x) : 0.0f;
-        dtu = dt * u;
         if constexpr (FULL) {
-            sig = SOFTPLUS ? sigmoid_f(x) : 1.0f;
             dy = in ? Elem<T>::load(static_cast<const T*>(p.dy), i) : 0.0f;
-            if constexpr (HAS_Z) {
-                z = Elem<T>::load(static_cast<const T*>(p.z), i);
-                g = dy * silu_f(z);
-            } else {
-                z = 0.0f;
-                g = dy;
-            }
+            z = HAS_Z ? Elem<T>::load(static_cast<const T*>(p.z), i) : 0.0f;
         }
     }
 };
 
-// B or C [B, L, N] of tokens t0 .. t0 + 15 for this lane's state n, through a
-// buffer resource over batch row b: reads past the row (tokens t >= L, and
-// lanes n >= N, pointed past the end) return zero.
+template <bool HAS_Z, bool SOFTPLUS, bool FULL>
+struct TileScalars {
+    float dt, dtu, u, g, sig, z, dy;
+
+    template <typename R>
+    __device__ __forceinline__ void from(const R& r, const S6BwdArgs& p, const LaneId& id,
+                                         int64_t t0, float bias) {
+        const bool in = id.chan_ok && t0 + id.n < p.L;
+        const float x = r.delta + bias;
+        u = r.u;
+        dt = in ? (SOFTPLUS ? softplus_f(x) : x) : 0.0f;
+        dtu = dt * u;
+        if constexpr (FULL) {
+            sig = SOFTPLUS ? sigmoid_f(x) : 1.0f;
+            dy = r.dy;
+            z = r.z;
+            g = HAS_Z ? dy * silu_f(z) : dy;
+        }
+    }
+};
+
+// B or C [B, L, N] of a tile is shared by every channel of the workgroup:
+// thread (j, n) = (tid / 16, tid % 16) loads element (t0 + j, n) through a
+// buffer resource over batch row b (tokens past L and n >= N read as zero),
+// and the tile is staged in LDS as [token][n].
 template <typename T>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t bc_rsrc(const S6BwdArgs& p, int64_t b,
                                                           const void* src) {
@@ -124,17 +155,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t bc_rsrc(const S6BwdArgs& p, in
 }
 
 template <typename T>
-__device__ __forceinline__ void load_bc(const S6BwdArgs& p, const LaneId& id, int64_t t0,
-                                        __amdgpu_buffer_rsrc_t r, float (&v)[kTile]) {
-    const uint32_t vn = id.n < p.N ? (uint32_t)(id.n * sizeof(T)) : 0x80000000u;
-    const uint32_t row = (uint32_t)(p.N * sizeof(T));
-#pragma unroll
-    for (int j = 0; j < kTile; ++j)
-        v[j] = Buf<T>::load(r, vn + (uint32_t)(t0 + j) * row, 0);
+__device__ __forceinline__ float load_bc_elem(const S6BwdArgs& p, int64_t t0,
+                                              __amdgpu_buffer_rsrc_t r) {
+    const int j = threadIdx.x / 16, n = threadIdx.x % 16;
+    const uint32_t off = n < p.N ? (uint32_t)(((t0 + j) * p.N + n) * sizeof(T)) : 0x80000000u;
+    return Buf<T>::load(r, off, 0);
 }
 
 template <typename T, bool SOFTPLUS>
 __global__ __launch_bounds__(kThreads) void s6_bwd_ckpt(S6BwdArgs p) {
+    static_assert(kThreads == kTile * 16, "one tile element per thread");
+    __shared__ float bt[kTile][16];
     const LaneId id = lane_id(p);
     const float a2 = id.ok ? p.A[id.dc * p.N + id.n] * kLog2e : 0.0f;
     const float bias = p.delta_bias ? p.delta_bias[id.dc] : 0.0f;
@@ -142,24 +173,37 @@ __global__ __launch_bounds__(kThreads) void s6_bwd_ckpt(S6BwdArgs p) {
     float h = (id.ok && p.h0) ? p.h0[(id.b * p.D + id.d) * p.N + id.n] : 0.0f;
     const auto rB = bc_rsrc<T>(p, id.b, p.Bm);
     float* ck = p.ckpt + (id.b * p.D + id.dc) * nblk * p.N + id.n;
+    TileRaw<T, false, false> raw;
+    float bpre = 0.0f;
+    if (nblk > 0) {
+        raw.load(p, id, 0);
+        bpre = load_bc_elem<T>(p, 0, rB);
+    }
     for (int64_t k = 0; k < nblk; ++k) {
         if (id.ok) ck[k * p.N] = h;
         const int64_t t0 = k * kTile;
-        TileScalars<T, false, SOFTPLUS, false> s;
-        s.load(p, id, t0, bias);
-        float bv[kTile];
-        load_bc<T>(p, id, t0, rB, bv);
+        TileScalars<false, SOFTPLUS, false> s;
+        s.from(raw, p, id, t0, bias);
+        __syncthreads();                    // previous tile's B reads done
+        bt[threadIdx.x / 16][threadIdx.x % 16] = bpre;
+        __syncthreads();
+        if (k + 1 < nblk) {                 // next tile's inputs travel during this one
+            raw.load(p, id, t0 + kTile);
+            bpre = load_bc_elem<T>(p, t0 + kTile, rB);
+        }
 #pragma unroll
         for (int j = 0; j < kTile; ++j) {
             const float dA = fast_exp2(row_bcast(s.dt, j) * a2);
-            h = fmaf(dA, h, bv[j] * row_bcast(s.dtu, j));
+            h = fmaf(dA, h, bt[j][id.n] * row_bcast(s.dtu, j));
         }
     }
 }
 
 template <typename T, bool HAS_Z, bool SOFTPLUS>
-__global__ __launch_bounds__(kThreads) void s6_bwd_main(S6BwdArgs p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void s6_bwd_main(S6BwdArgs p) {
     __shared__ float red[2][kWaves][kTile][16];     // [dB|dC][wave][token][n]
+    __shared__ float bct[2][kTile][16];             // B, C of the tile, [token][n]
     const LaneId id = lane_id(p);
     const float an = id.ok ? p.A[id.dc * p.N + id.n] : 0.0f;
     const float a2 = an * kLog2e;
@@ -171,19 +215,35 @@ __global__ __launch_bounds__(kThreads) void s6_bwd_main(S6BwdArgs p) {
     T* du_out = static_cast<T*>(p.du);
     T* dd_out = static_cast<T*>(p.ddelta);
     T* dz_out = static_cast<T*>(p.dz);
-
     const auto rB = bc_rsrc<T>(p, id.b, p.Bm);
     const auto rC = bc_rsrc<T>(p, id.b, p.Cm);
+    const bool lowhalf = id.row < 2;               // rows 0-1 gather dB, rows 2-3 dC
+
     float mu = (id.ok && p.dh_last) ? p.dh_last[(id.b * p.D + id.d) * p.N + id.n] : 0.0f;
     float dA_acc = 0.0f, dD_acc = 0.0f, db_acc = 0.0f;
+    TileRaw<T, HAS_Z, true> raw;
+    float bpre = 0.0f, cpre = 0.0f, hck = 0.0f;
+    if (nblk > 0) {
+        raw.load(p, id, (nblk - 1) * kTile);
+        bpre = load_bc_elem<T>(p, (nblk - 1) * kTile, rB);
+        cpre = load_bc_elem<T>(p, (nblk - 1) * kTile, rC);
+        hck = id.ok ? ck[(nblk - 1) * p.N] : 0.0f;
+    }
     for (int64_t k = nblk - 1; k >= 0; --k) {
         const int64_t t0 = k * kTile;
-        const float hprev0 = id.ok ? ck[k * p.N] : 0.0f;
-        TileScalars<T, HAS_Z, SOFTPLUS, true> s;
-        s.load(p, id, t0, bias);
-        float bv[kTile], cv[kTile];
-        load_bc<T>(p, id, t0, rB, bv);
-        load_bc<T>(p, id, t0, rC, cv);
+        const float hprev0 = hck;
+        TileScalars<HAS_Z, SOFTPLUS, true> s;
+        s.from(raw, p, id, t0, bias);
+        __syncthreads();                   // previous tile's LDS reads done
+        bct[0][threadIdx.x / 16][threadIdx.x % 16] = bpre;
+        bct[1][threadIdx.x / 16][threadIdx.x % 16] = cpre;
+        __syncthreads();
+        if (k > 0) {                       // previous tile's inputs travel during this one
+            raw.load(p, id, t0 - kTile);
+            bpre = load_bc_elem<T>(p, t0 - kTile, rB);
+            cpre = load_bc_elem<T>(p, t0 - kTile, rC);
+            hck = id.ok ? ck[(k - 1) * p.N] : 0.0f;
+        }
         // states of the tile, recomputed from its checkpoint
         float hs[kTile], da[kTile];
         {
@@ -191,32 +251,39 @@ __global__ __launch_bounds__(kThreads) void s6_bwd_main(S6BwdArgs p) {
 #pragma unroll
             for (int j = 0; j < kTile; ++j) {
                 da[j] = fast_exp2(row_bcast(s.dt, j) * a2);
-                h = fmaf(da[j], h, bv[j] * row_bcast(s.dtu, j));
+                h = fmaf(da[j], h, bct[0][j][id.n] * row_bcast(s.dtu, j));
                 hs[j] = h;
             }
         }
-        // adjoint, token by token backwards; lane j keeps the row sums of token j
-        float r_ddt = 0.0f, r_su = 0.0f, r_y = 0.0f;
-        float pb[kTile], pc[kTile];
+        // The reverse loop re-reads B and C from LDS and re-broadcasts the
+        // per-token scalars instead of keeping the recompute's copies alive:
+        // empty asm statements (no instruction) make the values opaque to
+        // common-subexpression elimination across the two loops.
+        asm volatile("" ::: "memory");
+        asm volatile("" : "+v"(s.dt), "+v"(s.dtu), "+v"(s.u), "+v"(s.g));
+        // adjoint, token by token backwards.  Per-lane terms of the sums over n
+        // (pt: ddt, pu: sum m B, py: readout) are reduced after the loop;
+        // wbc[j]: dB (rows 0-1) or dC (rows 2-3) of token j summed over the wavefront
+        float pt[kTile], pu[kTile], py[kTile], wbc[kTile];
 #pragma unroll
         for (int j = kTile - 1; j >= 0; --j) {
+            const float bj = bct[0][j][id.n], cj = bct[1][j][id.n];
             const float gj = row_bcast(s.g, j);
-            const float dtj = row_bcast(s.dt, j);
-            const float m = fmaf(gj, cv[j], mu);
+            const float m = fmaf(gj, cj, mu);
             const float hp = j > 0 ? hs[j - 1] : hprev0;
-            pc[j] = gj * hs[j];
-            pb[j] = m * row_bcast(s.dtu, j);
-            const float vt = row_sum(m * fmaf(hp, an * da[j], bv[j] * row_bcast(s.u, j)));
-            const float vu = row_sum(m * bv[j]);
-            const float vy = row_sum(cv[j] * hs[j]);
-            if (id.n == j) {
-                r_ddt = vt;
-                r_su = vu;
-                r_y = vy;
-            }
-            dA_acc = fmaf(m * hp, dtj * da[j], dA_acc);
+            const float pc = gj * hs[j];
+            const float pb = m * row_bcast(s.dtu, j);
+            pt[j] = m * fmaf(hp, an * da[j], bj * row_bcast(s.u, j));
+            pu[j] = m * bj;
+            py[j] = cj * hs[j];
+            dA_acc = fmaf(m * hp, row_bcast(s.dt, j) * da[j], dA_acc);
             mu = da[j] * m;
+            const float v = (lowhalf ? pb : pc) + __shfl_xor(lowhalf ? pc : pb, 32, 64);
+            wbc[j] = v + lane_xor<16>(v);
         }
+        const float r_ddt = row_reduce_scatter(pt, id.n);
+        const float r_su = row_reduce_scatter(pu, id.n);
+        const float r_y = row_reduce_scatter(py, id.n);
         // per-channel results of token t0 + j in lane j
         {
             const int64_t t = t0 + id.n;
@@ -234,34 +301,23 @@ __global__ __launch_bounds__(kThreads) void s6_bwd_main(S6BwdArgs p) {
                 dD_acc = fmaf(s.g, s.u, dD_acc);
             }
         }
-        // dB, dC: rows 0-1 of the wavefront gather dB, rows 2-3 dC (xor 32), then
-        // both rows of a pair hold the wavefront sum (xor 16)
-#pragma unroll
-        for (int j = 0; j < kTile; ++j) {
-            const bool lowhalf = id.row < 2;
-            const float keep = lowhalf ? pb[j] : pc[j];
-            const float send = lowhalf ? pc[j] : pb[j];
-            float v = keep + __shfl_xor(send, 32, 64);
-            v += lane_xor<16>(v);
-            pb[j] = v;
-        }
-        __syncthreads();                     // previous tile's partials consumed
         if (id.row == 0 || id.row == 2) {
             const int q = id.row / 2;
 #pragma unroll
-            for (int j = 0; j < kTile; ++j) red[q][id.w][j][id.n] = pb[j];
+            for (int j = 0; j < kTile; ++j) red[q][id.w][j][id.n] = wbc[j];
         }
         __syncthreads();
         {
-            // thread -> (q, token, n); sum over the workgroup's wavefronts
-            const int tid = threadIdx.x;
-            const int q = tid / (kTile * 16), j = (tid / 16) % kTile, n = tid % 16;
-            float v = 0.0f;
+            // thread -> (q, token, n) for half of them; sum over the wavefronts
+            for (int e = threadIdx.x; e < 2 * kTile * 16; e += kThreads) {
+                const int q = e / (kTile * 16), j = (e / 16) % kTile, n = e % 16;
+                float v = 0.0f;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) v += red[q][w][j][n];
-            const int64_t t = t0 + j;
-            if (t < p.L && n < p.N)
-                p.part_bc[(((int64_t)q * G + blockIdx.x) * p.B + id.b) * p.L * p.N + t * p.N + n] = v;
+                for (int w = 0; w < kWaves; ++w) v += red[q][w][j][n];
+                const int64_t t = t0 + j;
+                if (t < p.L && n < p.N)
+                    p.part_bc[(((int64_t)q * G + blockIdx.x) * p.B + id.b) * p.L * p.N + t * p.N + n] = v;
+            }
         }
     }
     if (id.ok) {

@@ -58,7 +58,7 @@ int s6_bwd_check_sizes(int64_t B, int64_t L, int64_t D, int64_t N, int dtype) {
     int rc = s6_check_sizes(B, L, D, N, dtype);
     if (rc != SSM_OK) return rc;
     if (N > 16) return SSM_ERR_UNSUPPORTED;
-    const int64_t G = (D + 31) / 32;
+    const int64_t G = (D + 15) / 16;
     if (G > 0x7fffffffLL || 2 * B * L * N + D * N + D > (int64_t)0x7fffffff * 256)
         return SSM_ERR_UNSUPPORTED;
     if (mul3(2 * G, B * L, N) < 0) return SSM_ERR_BAD_SHAPE;

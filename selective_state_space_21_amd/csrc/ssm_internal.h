@@ -108,7 +108,7 @@ struct S6BwdArgs {
     int bf16;
     // workspace, carved by s6_bwd_carve
     float* ckpt;       // [B, D, ceil(L/16), N] state before each 16-token tile
-    float* part_bc;    // [2][ceil(D/32)][B, L, N] per-channel-group dB, dC
+    float* part_bc;    // [2][ceil(D/16)][B, L, N] per-channel-group dB, dC
     float* part_dA;    // [B, D, N]
     float* part_dD;    // [B, D]
     float* part_db;    // [B, D]
