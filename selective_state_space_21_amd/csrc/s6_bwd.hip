@@ -162,39 +162,62 @@ __device__ __forceinline__ float load_bc_elem(const S6BwdArgs& p, int64_t t0,
     return Buf<T>::load(r, off, 0);
 }
 
+// Inputs of kSuper consecutive tiles, fetched together so that one memory
+// round trip covers 128 tokens of the sequential sweep.
+constexpr int kSuper = 8;
+
+template <typename T>
+struct SuperRaw {
+    float delta[kSuper], u[kSuper], b[kSuper];
+    __device__ __forceinline__ void load(const S6BwdArgs& p, const LaneId& id, int64_t t0,
+                                         __amdgpu_buffer_rsrc_t rB) {
+#pragma unroll
+        for (int i = 0; i < kSuper; ++i) {
+            TileRaw<T, false, false> r;
+            r.load(p, id, t0 + i * kTile);
+            delta[i] = r.delta;
+            u[i] = r.u;
+            b[i] = load_bc_elem<T>(p, t0 + i * kTile, rB);
+        }
+    }
+};
+
 template <typename T, bool SOFTPLUS>
 __global__ __launch_bounds__(kThreads) void s6_bwd_ckpt(S6BwdArgs p) {
     static_assert(kThreads == kTile * 16, "one tile element per thread");
-    __shared__ float bt[kTile][16];
+    __shared__ float bt[kSuper][kTile][16];
     const LaneId id = lane_id(p);
     const float a2 = id.ok ? p.A[id.dc * p.N + id.n] * kLog2e : 0.0f;
     const float bias = p.delta_bias ? p.delta_bias[id.dc] : 0.0f;
     const int64_t nblk = (p.L + kTile - 1) / kTile;
+    const int64_t nsup = (nblk + kSuper - 1) / kSuper;
     float h = (id.ok && p.h0) ? p.h0[(id.b * p.D + id.d) * p.N + id.n] : 0.0f;
     const auto rB = bc_rsrc<T>(p, id.b, p.Bm);
     float* ck = p.ckpt + (id.b * p.D + id.dc) * nblk * p.N + id.n;
-    TileRaw<T, false, false> raw;
-    float bpre = 0.0f;
-    if (nblk > 0) {
-        raw.load(p, id, 0);
-        bpre = load_bc_elem<T>(p, 0, rB);
-    }
-    for (int64_t k = 0; k < nblk; ++k) {
-        if (id.ok) ck[k * p.N] = h;
-        const int64_t t0 = k * kTile;
-        TileScalars<false, SOFTPLUS, false> s;
-        s.from(raw, p, id, t0, bias);
-        __syncthreads();                    // previous tile's B reads done
-        bt[threadIdx.x / 16][threadIdx.x % 16] = bpre;
-        __syncthreads();
-        if (k + 1 < nblk) {                 // next tile's inputs travel during this one
-            raw.load(p, id, t0 + kTile);
-            bpre = load_bc_elem<T>(p, t0 + kTile, rB);
-        }
+    SuperRaw<T> nxt;
+    if (nsup > 0) nxt.load(p, id, 0, rB);
+    for (int64_t sg = 0; sg < nsup; ++sg) {
+        const SuperRaw<T> cur = nxt;
+        __syncthreads();                    // previous super-tile's B reads done
 #pragma unroll
-        for (int j = 0; j < kTile; ++j) {
-            const float dA = fast_exp2(row_bcast(s.dt, j) * a2);
-            h = fmaf(dA, h, bt[j][id.n] * row_bcast(s.dtu, j));
+        for (int i = 0; i < kSuper; ++i) bt[i][threadIdx.x / 16][threadIdx.x % 16] = cur.b[i];
+        __syncthreads();
+        if (sg + 1 < nsup) nxt.load(p, id, (sg + 1) * kSuper * kTile, rB);   // travels meanwhile
+#pragma unroll
+        for (int i = 0; i < kSuper; ++i) {
+            const int64_t k = sg * kSuper + i;
+            if (k >= nblk) break;
+            if (id.ok) ck[k * p.N] = h;
+            TileRaw<T, false, false> r;
+            r.delta = cur.delta[i];
+            r.u = cur.u[i];
+            TileScalars<false, SOFTPLUS, false> s;
+            s.from(r, p, id, k * kTile, bias);
+#pragma unroll
+            for (int j = 0; j < kTile; ++j) {
+                const float dA = fast_exp2(row_bcast(s.dt, j) * a2);
+                h = fmaf(dA, h, bt[i][j][id.n] * row_bcast(s.dtu, j));
+            }
         }
     }
 }
