@@ -13,6 +13,8 @@ What is here:
     the 1-semiseparable SSD matrix (same file).
   * `s6_step` -- one decode step: the same recurrence over a single token,
     starting from and returning the caller's state.
+  * `causal_conv1d_silu` -- the short causal depthwise convolution and SiLU
+    that produce the scan input u (numpy, float64).
   * `backward.s6_bwd` -- gradients of the selective scan by fp64 reverse-mode
     differentiation of the per-token definition (plain PyTorch CPU ops).
   * `scans`   -- the affine-pair scans (sequential, Hillis-Steele doubling,
@@ -184,3 +186,29 @@ def s6_step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
                   z=None if z is None else z[:, None, :], delta_bias=delta_bias,
                   delta_softplus=delta_softplus, zoh=zoh, h0=state, threads=threads)
     return y[:, 0, :], h
+
+
+def causal_conv1d_silu(x, weight, bias=None, state=None, silu=True):
+    """Causal depthwise convolution over tokens, then SiLU, in fp64.
+
+    The Mamba block passes one branch through a short causal depthwise
+    convolution and a SiLU before the selective SSM (temporalbook "Selective
+    State-Space Models (Mamba)", section 4; width d_conv = 4 in the block
+    constructor of section 5).  Reading: per channel d,
+        s[b,t,d] = bias[d] + sum_{k<K} weight[d,k] * x[b, t-(K-1)+k, d]
+    (the last tap multiplies the current token), with x at negative times taken
+    from `state` [B, D, K-1] (oldest first) or zero; u = s * sigmoid(s).
+    x: [B, L, D]; weight: [D, K].  Returns (u [B, L, D], new_state [B, D, K-1]),
+    the new state being the last K-1 inputs (with the old state before them).
+    """
+    x, weight, bias, state = map(_f64, (x, weight, bias, state))
+    Bt, L, Dm = x.shape
+    K = weight.shape[1]
+    hist = np.zeros((Bt, K - 1, Dm)) if state is None else np.transpose(state, (0, 2, 1))
+    xe = np.concatenate([hist, x], axis=1)             # [B, K-1+L, D]
+    s = np.zeros((Bt, L, Dm)) if bias is None else np.broadcast_to(bias, (Bt, L, Dm)).copy()
+    for k in range(K):
+        s += weight[:, k][None, None, :] * xe[:, k:k + L, :]
+    u = s * (1.0 / (1.0 + np.exp(-s))) if silu else s
+    new_state = np.transpose(xe[:, L:, :], (0, 2, 1)).copy() if K > 1 else np.zeros((Bt, Dm, 0))
+    return u, new_state

@@ -463,3 +463,49 @@ def test_backward_one_step_closed_form():
     assert gr["dB"].item() == pytest.approx(c * dt * u, rel=1e-14)
     assert gr["dC"].item() == pytest.approx(e * h0 + dt * b * u, rel=1e-14)
     assert gr["dh0"].item() == pytest.approx(c * e, rel=1e-14)
+
+
+# ---------------------------------------------------------------- conv1d + SiLU
+def test_conv1d_matches_torch_conv1d():
+    """The causal depthwise convolution is torch's grouped conv1d (a
+    cross-correlation) with K-1 zeros of left padding, truncated to L."""
+    rng = np.random.default_rng(0)
+    for (Bt, L, Dm, K) in [(2, 11, 5, 4), (1, 3, 7, 4), (3, 9, 4, 2), (1, 6, 3, 1)]:
+        x = rng.standard_normal((Bt, L, Dm))
+        w = rng.standard_normal((Dm, K))
+        b = rng.standard_normal(Dm)
+        u, _ = oracle.causal_conv1d_silu(x, w, b)
+        s = torch.nn.functional.conv1d(torch.tensor(x).permute(0, 2, 1), torch.tensor(w)[:, None, :],
+                                       torch.tensor(b), padding=K - 1, groups=Dm)[:, :, :L]
+        ref = torch.nn.functional.silu(s).permute(0, 2, 1).numpy()
+        np.testing.assert_allclose(u, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_conv1d_impulse_response_and_causality():
+    """A unit impulse at t0 gives silu(w[d, K-1-(t-t0)]) for t0 <= t < t0+K,
+    silu(0) = 0 elsewhere: the last tap multiplies the current token, and
+    nothing reaches earlier times."""
+    L, Dm, K, t0 = 12, 3, 4, 5
+    w = np.arange(1.0, 1.0 + Dm * K).reshape(Dm, K) / 10.0
+    x = np.zeros((1, L, Dm))
+    x[0, t0, :] = 1.0
+    u, _ = oracle.causal_conv1d_silu(x, w, silu=False)
+    for t in range(L):
+        expect = w[:, K - 1 - (t - t0)] if t0 <= t < t0 + K else np.zeros(Dm)
+        np.testing.assert_array_equal(u[0, t], expect)
+
+
+def test_conv1d_state_carries_chunks():
+    """Splitting the sequence and passing the returned state reproduces one
+    call (chunked prefill)."""
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((2, 20, 6))
+    w = rng.standard_normal((6, 4))
+    b = rng.standard_normal(6)
+    u, st = oracle.causal_conv1d_silu(x, w, b)
+    u1, s1 = oracle.causal_conv1d_silu(x[:, :7], w, b)
+    u2, s2 = oracle.causal_conv1d_silu(x[:, 7:9], w, b, state=s1)
+    u3, s3 = oracle.causal_conv1d_silu(x[:, 9:], w, b, state=s2)
+    np.testing.assert_allclose(np.concatenate([u1, u2, u3], 1), u, rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(s3, st)
+    np.testing.assert_array_equal(st, np.transpose(x[:, -3:, :], (0, 2, 1)))
