@@ -219,6 +219,29 @@ int ssm_selective_state_update(float* state, const void* u, const void* delta, c
                                const void* z, const float* delta_bias, unsigned flags, void* y,
                                int64_t B, int64_t D, int64_t N, int dtype, void* stream);
 
+/*
+ * ---------------------------------------------------------------- conv1d + SiLU
+ * The short causal depthwise convolution over tokens, then SiLU, that turns
+ * the inner branch of a Mamba block into the scan input u (temporalbook
+ * "Selective State-Space Models (Mamba)", section 4; width d_conv = 4 in the
+ * block constructor of section 5).  Per (b, channel d):
+ *
+ *   s[b,t,d] = bias[d] + sum_{k<K} weight[d,k] * x[b, t-(K-1)+k, d]
+ *   u[b,t,d] = silu(s) = s * sigmoid(s)        (silu != 0; else u = s)
+ *
+ * The last tap multiplies the current token.  Inputs before t = 0 come from
+ * state_in (the previous chunk's last K-1 inputs, oldest first) or are zero;
+ * state_out receives this call's last K-1 inputs, so chunked prefill is
+ * exact when each call passes the previous state_out as its state_in.
+ *   x, u      : [B, L, D] dtype (channels contiguous, the layout of the scan's u)
+ *   weight    : [D, K] fp32;  bias : [D] fp32 or NULL
+ *   state_in, state_out : [B, D, K-1] fp32 or NULL (must not overlap)
+ *   1 <= K <= 4;  L >= 0 (L = 0 copies state_in, or zeros, to state_out).
+ */
+int ssm_causal_conv1d_silu(const void* x, const float* weight, const float* bias,
+                           const float* state_in, int silu, void* u, float* state_out,
+                           int64_t B, int64_t L, int64_t D, int64_t K, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,6 +14,7 @@ from . import _native
 from ._native import SSMError
 
 __all__ = ["selective_scan_fwd", "selective_scan_bwd", "ssd_chunk_fwd", "selective_state_update",
+           "causal_conv1d_silu",
            "selective_scan_workspace_bytes",
            "selective_scan_segments", "ssd_chunk_workspace_bytes", "SSMError"]
 
@@ -271,3 +272,38 @@ def selective_scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B:
         _stream_handle(dev))
     _native.check(rc, "ssm_selective_scan_bwd")
     return out
+
+
+def causal_conv1d_silu(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                       state: Optional[torch.Tensor] = None, silu: bool = True,
+                       return_state: bool = False, out: Optional[torch.Tensor] = None):
+    """Causal depthwise conv1d over tokens, then SiLU (ssm_causal_conv1d_silu).
+
+    x: [Bt, L, Dm] (float32 or bfloat16); weight: [Dm, K] fp32; bias: [Dm]
+    fp32; state: [Bt, Dm, K-1] fp32 (previous chunk's last inputs).  Returns u
+    (same dtype as x), or (u, new_state) with return_state.
+    """
+    lib = _native.load()
+    if x.dtype not in _DT:
+        raise TypeError(f"x must be float32 or bfloat16 (got {x.dtype})")
+    dev, dt = x.device, x.dtype
+    x = _dev_tensor("x", x, dt, dev)
+    weight = _dev_tensor("weight", weight, torch.float32, dev)
+    bias = _dev_tensor("bias", bias, torch.float32, dev)
+    state = _dev_tensor("state", state, torch.float32, dev)
+    if x.dim() != 3 or weight.dim() != 2:
+        raise ValueError("x must be [B, L, D] and weight [D, K]")
+    Bt, L, Dm = x.shape
+    K = weight.shape[1]
+    shapes = {"weight": (weight, (Dm, K)), "bias": (bias, (Dm,)), "state": (state, (Bt, Dm, K - 1))}
+    for name, (t, shp) in shapes.items():
+        if t is not None and tuple(t.shape) != shp:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+    u = out if out is not None else torch.empty_like(x)
+    _dev_tensor("out", u, dt, dev)
+    new_state = torch.empty((Bt, Dm, K - 1), dtype=torch.float32, device=dev) if return_state else None
+    rc = lib.ssm_causal_conv1d_silu(_ptr(x), _ptr(weight), _ptr(bias), _ptr(state), int(bool(silu)),
+                                    _ptr(u), _ptr(new_state), Bt, L, Dm, K, _DT[dt],
+                                    _stream_handle(dev))
+    _native.check(rc, "ssm_causal_conv1d_silu")
+    return (u, new_state) if return_state else u

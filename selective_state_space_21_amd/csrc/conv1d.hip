@@ -1,0 +1,173 @@
+// Short causal depthwise convolution over tokens followed by SiLU: the
+// branch of the Mamba block that produces the scan input u (temporalbook
+// "Selective State-Space Models (Mamba)", section 4; width d_conv = 4 in the
+// block constructor of section 5).  Per (b, channel d):
+//   s_t = bias[d] + sum_{k<K} w[d,k] x_{t-(K-1)+k},   u_t = s_t sigmoid(s_t)
+// with x at negative times taken from the carried state (the previous call's
+// last K-1 inputs) or zero.
+//
+// The layout is [B, L, D] with channels contiguous, so a thread owns VEC
+// consecutive channels (one 16-byte vector) and streams a run of kRun tokens,
+// keeping the last K-1 inputs in registers: x is read once (plus a K-1 token
+// halo per run) and u written once -- the kernel is bound by those bytes.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "device_math.h"
+#include "ssm_internal.h"
+
+namespace ssm {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kRun = 32;       // tokens per thread
+constexpr int kUnroll = 8;     // tokens whose loads are in flight together
+
+template <typename T, int VEC> struct Vec;
+template <> struct Vec<uint16_t, 8> {
+    static __device__ __forceinline__ void load(const uint16_t* p, float (&v)[8]) {
+        const uint4 r = *reinterpret_cast<const uint4*>(p);
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    static __device__ __forceinline__ void store(uint16_t* p, const float (&v)[8]) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = (uint32_t)f32_to_bf16_bits(v[2 * i]) | ((uint32_t)f32_to_bf16_bits(v[2 * i + 1]) << 16);
+        *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+};
+template <> struct Vec<float, 4> {
+    static __device__ __forceinline__ void load(const float* p, float (&v)[4]) {
+        const float4 r = *reinterpret_cast<const float4*>(p);
+        v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
+    }
+    static __device__ __forceinline__ void store(float* p, const float (&v)[4]) {
+        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+};
+template <typename T> struct Vec<T, 1> {
+    static __device__ __forceinline__ void load(const T* p, float (&v)[1]) { v[0] = Elem<T>::load(p, 0); }
+    static __device__ __forceinline__ void store(T* p, const float (&v)[1]) { Elem<T>::store(p, 0, v[0]); }
+};
+
+// one thread per (channel vector, b, run), channel vectors fastest
+template <typename T, int VEC, int K, bool SILU>
+__global__ __launch_bounds__(kBlock) void conv1d_silu_kernel(ConvArgs p) {
+    const int64_t groups = (p.D + VEC - 1) / VEC;
+    const int64_t nrun = (p.L + kRun - 1) / kRun;
+    const int64_t gi = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (gi >= groups * p.B * nrun) return;
+    const int64_t d0 = (gi % groups) * VEC;
+    const int64_t br = gi / groups;
+    const int64_t b = br / nrun, run = br % nrun;
+    const int64_t t0 = run * kRun;
+    const T* x = static_cast<const T*>(p.x) + b * p.L * p.D + d0;
+    T* u = static_cast<T*>(p.u) + b * p.L * p.D + d0;
+
+    float w[VEC][K], bias[VEC];
+#pragma unroll
+    for (int c = 0; c < VEC; ++c) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) w[c][k] = p.weight[(d0 + c) * K + k];
+        bias[c] = p.bias ? p.bias[d0 + c] : 0.0f;
+    }
+    // window[i] = x_{t-(K-1)+i} for the next output t; i = K-1 is filled per token
+    float win[K][VEC];
+#pragma unroll
+    for (int i = 0; i < K - 1; ++i) {
+        const int64_t t = t0 - (K - 1) + i;
+        if (t >= 0) {
+            Vec<T, VEC>::load(x + t * p.D, win[i]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < VEC; ++c)
+                win[i][c] = p.state_in ? p.state_in[((b * p.D) + d0 + c) * (K - 1) + (t + K - 1)] : 0.0f;
+        }
+    }
+    const int64_t tend = t0 + kRun < p.L ? t0 + kRun : p.L;
+    for (int64_t tb = t0; tb < tend; tb += kUnroll) {
+        float xs[kUnroll][VEC];
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j)
+            if (tb + j < tend) Vec<T, VEC>::load(x + (tb + j) * p.D, xs[j]);
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) {
+            if (tb + j >= tend) break;
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) win[K - 1][c] = xs[j][c];
+            float o[VEC];
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) {
+                float s = bias[c];
+#pragma unroll
+                for (int k = 0; k < K; ++k) s = fmaf(w[c][k], win[k][c], s);
+                o[c] = SILU ? silu_f(s) : s;
+            }
+            Vec<T, VEC>::store(u + (tb + j) * p.D, o);
+#pragma unroll
+            for (int i = 0; i < K - 1; ++i)
+#pragma unroll
+                for (int c = 0; c < VEC; ++c) win[i][c] = win[i + 1][c];
+        }
+    }
+    // the last run leaves the final K-1 inputs in the window
+    if (p.state_out && run == nrun - 1) {
+#pragma unroll
+        for (int i = 0; i < K - 1; ++i)
+#pragma unroll
+            for (int c = 0; c < VEC; ++c)
+                p.state_out[((b * p.D) + d0 + c) * (K - 1) + i] = win[i][c];
+    }
+}
+
+template <typename T, int VEC, int K>
+hipError_t launch_k(const ConvArgs& a, hipStream_t stream) {
+    const int64_t groups = (a.D + VEC - 1) / VEC;
+    const int64_t nrun = (a.L + kRun - 1) / kRun;
+    const unsigned grid = (unsigned)((groups * a.B * nrun + kBlock - 1) / kBlock);
+    if (a.silu) conv1d_silu_kernel<T, VEC, K, true><<<grid, kBlock, 0, stream>>>(a);
+    else conv1d_silu_kernel<T, VEC, K, false><<<grid, kBlock, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+template <typename T, int VEC>
+hipError_t launch_v(const ConvArgs& a, hipStream_t stream) {
+    switch (a.K) {
+        case 1: return launch_k<T, VEC, 1>(a, stream);
+        case 2: return launch_k<T, VEC, 2>(a, stream);
+        case 3: return launch_k<T, VEC, 3>(a, stream);
+        default: return launch_k<T, VEC, 4>(a, stream);
+    }
+}
+
+// no tokens: the carried state passes through unchanged (zeros without one)
+__global__ __launch_bounds__(kBlock) void conv_state_pass(ConvArgs p) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i < p.B * p.D * (p.K - 1)) p.state_out[i] = p.state_in ? p.state_in[i] : 0.0f;
+}
+
+}  // namespace
+
+hipError_t launch_conv1d(const ConvArgs& a, hipStream_t stream) {
+    if (a.L == 0) {
+        const int64_t n = a.B * a.D * (a.K - 1);
+        if (a.state_out && n > 0)
+            conv_state_pass<<<(unsigned)((n + kBlock - 1) / kBlock), kBlock, 0, stream>>>(a);
+        return hipGetLastError();
+    }
+    if (a.bf16) {
+        if (a.D % 8 == 0) return launch_v<uint16_t, 8>(a, stream);
+        return launch_v<uint16_t, 1>(a, stream);
+    }
+    if (a.D % 4 == 0) return launch_v<float, 4>(a, stream);
+    return launch_v<float, 1>(a, stream);
+}
+
+}  // namespace ssm

@@ -246,4 +246,28 @@ int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, con
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+int ssm_causal_conv1d_silu(const void* x, const float* weight, const float* bias,
+                           const float* state_in, int silu, void* u, float* state_out,
+                           int64_t B, int64_t L, int64_t D, int64_t K, int dtype, void* stream) {
+    if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_BAD_DTYPE;
+    if (B < 1 || D < 1 || L < 0 || K < 1) return SSM_ERR_BAD_SHAPE;
+    if (mul3(B, L, D) < 0 || mul3(B, L, D) > kMaxElems / esize(dtype)) return SSM_ERR_BAD_SHAPE;
+    if (K > 4) return SSM_ERR_UNSUPPORTED;
+    if (D * B * ((L + 31) / 32) / 256 > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;   // grid x
+    if (!weight) return SSM_ERR_NULL_ARG;
+    if (L > 0 && (!x || !u)) return SSM_ERR_NULL_ARG;
+    const void* big[] = {x, u};
+    for (const void* p : big)
+        if (p && !aligned(p, 16)) return SSM_ERR_MISALIGNED;
+    const void* vec[] = {weight, bias, state_in, state_out};
+    for (const void* p : vec)
+        if (p && !aligned(p, 4)) return SSM_ERR_MISALIGNED;
+    ssm::ConvArgs a{};
+    a.x = x; a.weight = weight; a.bias = bias; a.state_in = state_in; a.u = u;
+    a.state_out = state_out; a.B = B; a.L = L; a.D = D; a.K = K; a.silu = silu != 0;
+    a.bf16 = dtype == SSM_BF16;
+    const hipError_t e = ssm::launch_conv1d(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 }  // extern "C"

@@ -118,4 +118,19 @@ size_t s6_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N);
 void s6_bwd_carve(S6BwdArgs& a, void* workspace);
 hipError_t launch_s6_bwd(const S6BwdArgs& a, hipStream_t stream);
 
+// Causal depthwise conv1d (+ SiLU) over tokens.
+struct ConvArgs {
+    const void* x;            // [B, L, D]
+    const float* weight;      // [D, K]
+    const float* bias;        // [D] or NULL
+    const float* state_in;    // [B, D, K-1] or NULL
+    void* u;                  // [B, L, D]
+    float* state_out;         // [B, D, K-1] or NULL
+    int64_t B, L, D, K;
+    int silu;
+    int bf16;
+};
+
+hipError_t launch_conv1d(const ConvArgs& a, hipStream_t stream);
+
 }  // namespace ssm

@@ -9,6 +9,7 @@ order so that a given (workload, seed, shape) is reproducible byte for byte:
   S6  : u, delta_raw, B, C, z, Dskip, delta_bias, spike positions
   SSD : X, delta_raw, B, C, A
   decode step : state, u, delta_raw, B, C, z, Dskip, delta_bias
+  conv1d      : x, weight, bias
 bf16 tensors are produced from float32 by torch's round-to-nearest-even cast.
 
 Parameterisation conventions (stated on the pages, not part of the kernel):
@@ -88,6 +89,21 @@ class StepWorkload:
         return dataclasses.replace(self, **kw)
 
 
+@dataclasses.dataclass(frozen=True)
+class ConvWorkload:
+    """Causal depthwise conv1d + SiLU over [B, L, D] inputs, width K."""
+    name: str
+    B: int
+    L: int
+    D: int
+    K: int
+    dtype: str
+    desc: str = ""
+
+    def scaled(self, **kw) -> "ConvWorkload":
+        return dataclasses.replace(self, **kw)
+
+
 S6_SMALL_FP32 = S6Workload(
     "s6_small_fp32", B=1, L=256, D=64, N=16, dtype="f32", delta_mean=-2.0,
     delta_std=0.5, bias_range=None, skip="ones", gate=False,
@@ -114,6 +130,10 @@ S6_DECODE_2P8B = StepWorkload(
     "s6_decode_mamba2.8b_bf16", B=64, D=5120, N=16, dtype="bf16",
     desc="decode step of 64 sequences through a Mamba-2.8B-shaped layer, D=5120 N=16, "
          "bf16 activations, fp32 state")
+
+CONV_MAMBA130M = ConvWorkload(
+    "conv1d_mamba130m_layer_bf16", B=8, L=2048, D=1536, K=4, dtype="bf16",
+    desc="conv1d (d_conv=4) + SiLU in front of a Mamba-130M-shaped scan, B=8 L=2048 D=1536, bf16")
 
 S6_WORKLOADS = {w.name: w for w in (S6_SMALL_FP32, S6_MAMBA130M, S6_MAMBA2P8B, S6_LONG_FP32)}
 SSD_WORKLOADS = {w.name: w for w in (SSD_MAMBA2,)}
@@ -211,6 +231,24 @@ def make_step_inputs(w: StepWorkload, seed: int = 0) -> dict:
         A=torch.from_numpy(np.ascontiguousarray(A)), B=_cast(Bm, w.dtype), C=_cast(Cm, w.dtype),
         D=torch.from_numpy(Dskip), z=_cast(z, w.dtype), delta_bias=torch.from_numpy(bias),
         delta_softplus=True)
+
+
+def make_conv_inputs(w: ConvWorkload, seed: int = 0) -> dict:
+    """x ~ N(0, 1); weight, bias ~ U(-1/sqrt(K), 1/sqrt(K)) (the usual fan-in
+    bound of a depthwise convolution with K taps)."""
+    rng = np.random.default_rng(seed)
+    f32 = np.float32
+    x = rng.standard_normal((w.B, w.L, w.D), dtype=f32)
+    bound = 1.0 / math.sqrt(w.K)
+    weight = rng.uniform(-bound, bound, size=(w.D, w.K)).astype(f32)
+    bias = rng.uniform(-bound, bound, size=w.D).astype(f32)
+    return dict(x=_cast(x, w.dtype), weight=torch.from_numpy(weight), bias=torch.from_numpy(bias))
+
+
+def conv_algorithmic_bytes(w: ConvWorkload) -> int:
+    """x read once, u written once, weight and bias read once."""
+    e = 4 if w.dtype == "f32" else 2
+    return 2 * w.B * w.L * w.D * e + w.D * (w.K + 1) * 4
 
 
 def step_algorithmic_bytes(w: StepWorkload) -> int:

@@ -174,6 +174,25 @@ def test_bwd_validation_errors(lib):
     assert lib.ssm_selective_scan_bwd_workspace_bytes(8, 2048, 1536, 17, 1) == 0
 
 
+def conv(lib, **kw):
+    a = dict(x=FAKE, w=FAKE, b=None, si=None, silu=1, u=FAKE, so=None, Bt=2, L=64, Dm=128, K=4,
+             dtype=1, stream=None)
+    a.update(kw)
+    return lib.ssm_causal_conv1d_silu(a["x"], a["w"], a["b"], a["si"], a["silu"], a["u"], a["so"],
+                                      a["Bt"], a["L"], a["Dm"], a["K"], a["dtype"], a["stream"])
+
+
+def test_conv_validation_errors(lib):
+    assert conv(lib, w=None) == 1
+    assert conv(lib, x=None) == 1
+    assert conv(lib, K=0) == 2
+    assert conv(lib, L=-1) == 2
+    assert conv(lib, dtype=3) == 3
+    assert conv(lib, K=5) == 4
+    assert conv(lib, u=FAKE_MIS) == 5
+    assert conv(lib, b=FAKE + 2) == 5
+
+
 def test_python_wrapper_rejects_host_tensors():
     import torch
     import selective_state_space_21_amd as ssm
