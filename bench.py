@@ -14,10 +14,14 @@ itself on the stream it launches on, at its phase boundaries (segment reduce,
 carry scan, segment scan); `value` is the algorithmic bytes of the step
 divided by the mean step time.
 
-The same run also measures the SSD chunked forward on the Mamba-2 workload
-(B=4 L=8192 H=64 P=64 N=128, chunk 256) and times the fp64 CPU oracle on the
-host cores over the whole S6 workload.
+The same run also measures, under "paths", the other calls of the library on
+their own workloads (each flushed and timed the same way): the SSD chunked
+forward (Mamba-2, B=4 L=8192 H=64 P=64 N=128, chunk 256), the decode step
+(64 sequences, D=5120 N=16), the backward pass with recomputation and the
+causal conv1d + SiLU (both on the Mamba-130M layer shape), and it times the
+fp64 CPU oracle on the host cores over the whole S6 workload.
 
+`--only PART` runs one part alone and prints its result (for profiling).
 Prints one JSON line.  Only one GPU is used; --gpus above 1 exits.
 """
 from __future__ import annotations
@@ -35,6 +39,14 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 FP32_VECTOR_PEAK_TFLOPS = 157.3
+
+# HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per
+# dispatch), scaled by what the same counters read for a 256 MiB copy
+# (fetch x2.000, write x1.000); profiles/s6_scan_mamba130m_layer_bf16.md and
+# profiles/ssd_chunk_mamba2_bf16.md.  Valid for the kernels as profiled: to be
+# re-taken (or set to None) when those kernels change.
+S6_SCAN_TRAFFIC_BYTES = int((84538.5 * 2.0 + 49920.0) * 1024)
+SSD_CHUNK_TRAFFIC_BYTES = int((151673.2 * 2.0 + 270336.0) * 1024)
 
 
 def _hip():
@@ -161,29 +173,117 @@ def bench_ssd(args, torch, ssm, W):
     # masked Y_diag (Q(Q+1)/2 * P), chunk state (P*N*Q), Y_off (Q*P*N)
     tri = Q * (Q + 1) / 2
     macs = s.B * s.H * nchunks * (tri * s.N + tri * s.P + 2 * s.P * s.N * Q)
-    return dict(status="ok", workload=s.name, ms=ms, gbs=nbytes / (ms * 1e-3) / 1e9,
-                pct_hbm_peak=nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS * 100,
-                tflops=2 * macs / (ms * 1e-3) / 1e12,
-                mfma_util=2 * macs / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
-                gtokch=s.tok_ch / (ms * 1e-3) / 1e9, algorithmic_bytes=nbytes,
-                causal_gflop=2 * macs / 1e9)
+    return dict(status="ok", workload=s.name, ms=round(ms, 5),
+                gbs=round(nbytes / (ms * 1e-3) / 1e9, 2),
+                pct_hbm_peak=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS * 100, 2),
+                tflops=round(2 * macs / (ms * 1e-3) / 1e12, 2),
+                mfma_util=round(2 * macs / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                gtokch=round(s.tok_ch / (ms * 1e-3) / 1e9, 3), algorithmic_bytes=nbytes,
+                causal_gflop=round(2 * macs / 1e9, 3), hbm_traffic_bytes=SSD_CHUNK_TRAFFIC_BYTES)
 
 
-def cpu_baseline(r, torch):
+def _time_flushed(torch, fn, steps, warmup):
+    """Mean ms of fn() over `steps` calls, each after rewriting a 512 MiB
+    buffer (untimed), bracketed by events on the current stream."""
+    flush = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device="cuda:0")
+    for _ in range(max(1, warmup)):
+        fn()
+    torch.cuda.synchronize()
+    total = 0.0
+    for i in range(steps):
+        flush.fill_(float(i))
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        total += a.elapsed_time(b)
+    return total / steps
+
+
+def bench_decode(args, torch, ssm, W):
+    w = W.S6_DECODE_2P8B
+    t = W.make_step_inputs(w, seed=0)
+    d = {k: (v.to("cuda:0") if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
+    y = torch.empty((w.B, w.D), dtype=torch.bfloat16, device="cuda:0")
+
+    def step():
+        ssm.selective_state_update(d["state"], d["u"], d["delta"], d["A"], d["B"], d["C"],
+                                   D=d["D"], z=d["z"], delta_bias=d["delta_bias"], out=y)
+
+    ms = _time_flushed(torch, step, args.steps, args.warmup)
+    nbytes = W.step_algorithmic_bytes(w)
+    return dict(status="ok", workload=w.name, ms=round(ms, 5), algorithmic_bytes=nbytes,
+                gbs=round(nbytes / (ms * 1e-3) / 1e9, 2),
+                pct_hbm_peak=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS * 100, 2),
+                state_updates_per_s=round(w.B * w.D * w.N / (ms * 1e-3), 1))
+
+
+def bench_bwd(args, torch, ssm, W):
+    w = W.S6_MAMBA130M
+    t = W.make_s6_inputs(w, seed=0)
+    d = {k: (v.to("cuda:0") if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
+    g = torch.Generator().manual_seed(1)
+    dy = torch.randn(w.B, w.L, w.D, generator=g).to(torch.bfloat16).to("cuda:0")
+    need = int(ssm._native.load().ssm_selective_scan_bwd_workspace_bytes(w.B, w.L, w.D, w.N, 1))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+
+    def step():
+        ssm.selective_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], dy, D=d["D"],
+                               z=d["z"], delta_bias=d["delta_bias"], workspace=ws)
+
+    ms = _time_flushed(torch, step, args.steps, args.warmup)
+    e = 2
+    # inputs u, delta, z, dy, B, C read and du, ddelta, dz written once (bf16);
+    # dB, dC fp32; A, dA and the per-channel vectors are negligible
+    nbytes = 7 * w.B * w.L * w.D * e + 2 * w.B * w.L * w.N * (e + 4)
+    return dict(status="ok", workload=w.name, ms=round(ms, 5), algorithmic_bytes=nbytes,
+                gbs=round(nbytes / (ms * 1e-3) / 1e9, 2),
+                gtokch=round(w.tok_ch / (ms * 1e-3) / 1e9, 3), workspace_bytes=need)
+
+
+def bench_conv(args, torch, ssm, W):
+    w = W.CONV_MAMBA130M
+    t = W.make_conv_inputs(w, seed=0)
+    d = {k: v.to("cuda:0") for k, v in t.items()}
+    u = torch.empty_like(d["x"])
+
+    def step():
+        ssm.causal_conv1d_silu(d["x"], d["weight"], d["bias"], out=u)
+
+    ms = _time_flushed(torch, step, args.steps, args.warmup)
+    nbytes = W.conv_algorithmic_bytes(w)
+    return dict(status="ok", workload=w.name, ms=round(ms, 5), algorithmic_bytes=nbytes,
+                gbs=round(nbytes / (ms * 1e-3) / 1e9, 2),
+                pct_hbm_peak=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS * 100, 2))
+
+
+def cpu_baseline(r, torch, min_seconds=10.0):
+    """The fp64 oracle over the whole S6 workload on the host cores, repeated
+    until at least `min_seconds` of wall time (the workload alone takes well
+    under a second); value = algorithmic bytes per workload / mean seconds."""
     import oracle
     w, t = r["w"], r["t"]
     f64 = {k: (oracle._f64(v) if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
     threads = oracle.default_threads()
+    runs = 0
     t0 = time.perf_counter()
-    oracle.s6_fwd(f64["u"], f64["delta"], f64["A"], f64["B"], f64["C"], D=f64["D"], z=f64["z"],
-                  delta_bias=f64["delta_bias"], threads=threads)
-    sec = time.perf_counter() - t0
+    while True:
+        oracle.s6_fwd(f64["u"], f64["delta"], f64["A"], f64["B"], f64["C"], D=f64["D"],
+                      z=f64["z"], delta_bias=f64["delta_bias"], threads=threads)
+        runs += 1
+        total = time.perf_counter() - t0
+        if total >= min_seconds:
+            break
+    sec = total / runs
     return {"value": round(r["nbytes"] / sec / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"the whole {w.name} workload (B={w.B} L={w.L} D={w.D} N={w.N}), fp64 "
-                      f"sequential loop per channel, channels over {threads} OpenMP threads; "
-                      f"{sec:.2f} s wall, algorithmic bytes of the workload / wall time",
-            "seconds": round(sec, 3),
+            "sample": f"the whole {w.name} workload (B={w.B} L={w.L} D={w.D} N={w.N}), run "
+                      f"{runs} times ({total:.1f} s wall); fp64 sequential loop per channel, "
+                      f"channels over {threads} OpenMP threads; algorithmic bytes of the "
+                      f"workload / mean seconds per run",
+            "seconds_per_run": round(sec, 4),
             "gtokch_per_s": round(w.tok_ch / sec / 1e9, 6)}
 
 
@@ -193,7 +293,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-ssd", action="store_true")
+    ap.add_argument("--no-ssd", action="store_true", help="skip every path but the S6 scan")
+    ap.add_argument("--only", choices=["s6", "ssd", "decode", "bwd", "conv"],
+                    help="run one part alone and print its result")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 256 MiB device copy three times, the "
                          "reference for scaling FETCH_SIZE/WRITE_SIZE counters")
@@ -218,8 +320,18 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.only and args.only != "s6":
+        fn = {"ssd": bench_ssd, "decode": bench_decode, "bwd": bench_bwd, "conv": bench_conv}
+        res = fn[args.only](args, torch, ssm, W)
+        print(json.dumps({"part": args.only, **{k: v for k, v in res.items()}}), flush=True)
+        return
     r = bench_s6(args, torch, ssm, W, native, hip)
-    ssd = None if args.no_ssd else bench_ssd(args, torch, ssm, W)
+    paths = {}
+    if not args.no_ssd and not args.only:
+        paths["ssd_chunk_fwd"] = bench_ssd(args, torch, ssm, W)
+        paths["selective_state_update"] = bench_decode(args, torch, ssm, W)
+        paths["selective_scan_bwd"] = bench_bwd(args, torch, ssm, W)
+        paths["causal_conv1d_silu"] = bench_conv(args, torch, ssm, W)
     w = r["w"]
     line = {
         "metric": "selective-scan fwd achieved HBM GB/s (% of peak) + Gtoken·channels/s",
@@ -250,15 +362,15 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(r["scan_gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": S6_SCAN_TRAFFIC_BYTES,
             "alu_view": {"achieved_tflops": round(r["scan_tflops"], 3),
                          "peak_tflops": FP32_VECTOR_PEAK_TFLOPS,
                          "flops_per_state_update": 6, "transcendentals_per_state_update": 1},
         },
     }
-    if ssd is not None:
-        line["ssd"] = ssd
-    if not args.no_cpu_baseline:
+    if paths:
+        line["paths"] = paths
+    if not args.no_cpu_baseline and not args.only:
         line["cpu_baseline"] = cpu_baseline(r, torch)
     print(json.dumps(line), flush=True)
 
