@@ -106,19 +106,53 @@ __device__ __forceinline__ float sigmoid_f(float x) {
 }
 
 // Per-channel inputs of token t0 + j, loaded by lane j of the row (raw, so
-// that they can be fetched a tile ahead), and the scalars derived from them.
+// that they can be fetched a tile ahead).  Buffer resources over batch row b
+// make every load unconditional: tokens past L read as zero, so no branch
+// (and no wait at its join) separates a prefetch from the work it overlaps.
+struct RowRsrc {
+    __amdgpu_buffer_rsrc_t delta, u, z, dy;
+};
+
+template <typename T>
+__device__ __forceinline__ RowRsrc row_rsrc(const S6BwdArgs& p, int64_t b) {
+    const uint32_t bytes = (uint32_t)(p.L * p.D * sizeof(T));
+    const int64_t off = b * p.L * p.D;
+    RowRsrc r;
+    r.delta = make_rsrc(static_cast<const T*>(p.delta) + off, bytes);
+    r.u = make_rsrc(static_cast<const T*>(p.u) + off, bytes);
+    r.z = make_rsrc(p.z ? static_cast<const T*>(p.z) + off : static_cast<const T*>(p.u) + off, bytes);
+    r.dy = make_rsrc(p.dy ? static_cast<const T*>(p.dy) + off : static_cast<const T*>(p.u) + off, bytes);
+    return r;
+}
+
+// Loaded storage bits, widened to fp32 only where they are used: a
+// conversion next to the load would make the compiler wait for the load
+// there, in the iteration that issues the prefetch.
+template <typename T> struct Bits;
+template <> struct Bits<float> {
+    static __device__ __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+    }
+    static __device__ __forceinline__ float f32(uint32_t v) { return __uint_as_float(v); }
+};
+template <> struct Bits<uint16_t> {
+    static __device__ __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+    }
+    static __device__ __forceinline__ float f32(uint32_t v) { return __uint_as_float(v << 16); }
+};
+
 template <typename T, bool HAS_Z, bool FULL>
 struct TileRaw {
-    float delta, u, z, dy;
-    __device__ __forceinline__ void load(const S6BwdArgs& p, const LaneId& id, int64_t t0) {
-        const int64_t t = t0 + id.n;
-        const bool in = id.chan_ok && t < p.L;
-        const int64_t i = (id.b * p.L + (in ? t : 0)) * p.D + id.dc;
-        delta = in ? Elem<T>::load(static_cast<const T*>(p.delta), i) : 0.0f;
-        u = in ? Elem<T>::load(static_cast<const T*>(p.u), i) : 0.0f;
+    uint32_t delta, u, z, dy;
+    __device__ __forceinline__ void load(const S6BwdArgs& p, const LaneId& id, const RowRsrc& r,
+                                         int64_t t0) {
+        const uint32_t off = (uint32_t)(((t0 + id.n) * p.D + id.dc) * sizeof(T));
+        delta = Bits<T>::load(r.delta, off);
+        u = Bits<T>::load(r.u, off);
         if constexpr (FULL) {
-            dy = in ? Elem<T>::load(static_cast<const T*>(p.dy), i) : 0.0f;
-            z = HAS_Z ? Elem<T>::load(static_cast<const T*>(p.z), i) : 0.0f;
+            dy = Bits<T>::load(r.dy, off);
+            z = HAS_Z ? Bits<T>::load(r.z, off) : 0u;
         }
     }
 };
@@ -127,18 +161,18 @@ template <bool HAS_Z, bool SOFTPLUS, bool FULL>
 struct TileScalars {
     float dt, dtu, u, g, sig, z, dy;
 
-    template <typename R>
+    template <typename T, typename R>
     __device__ __forceinline__ void from(const R& r, const S6BwdArgs& p, const LaneId& id,
                                          int64_t t0, float bias) {
         const bool in = id.chan_ok && t0 + id.n < p.L;
-        const float x = r.delta + bias;
-        u = r.u;
+        const float x = Bits<T>::f32(r.delta) + bias;
+        u = in ? Bits<T>::f32(r.u) : 0.0f;
         dt = in ? (SOFTPLUS ? softplus_f(x) : x) : 0.0f;
         dtu = dt * u;
         if constexpr (FULL) {
             sig = SOFTPLUS ? sigmoid_f(x) : 1.0f;
-            dy = r.dy;
-            z = r.z;
+            dy = in ? Bits<T>::f32(r.dy) : 0.0f;
+            z = Bits<T>::f32(r.z);
             g = HAS_Z ? dy * silu_f(z) : dy;
         }
     }
@@ -154,12 +188,25 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t bc_rsrc(const S6BwdArgs& p, in
     return make_rsrc(static_cast<const T*>(src) + b * p.L * p.N, (uint32_t)(p.L * p.N * sizeof(T)));
 }
 
+// LDS tile of B or C stored per state n as 16 consecutive tokens, rows padded
+// to 20 floats: the transposed store by thread (j, n) is conflict-free and
+// lane n reads its 16 tokens as four 16-byte loads.
+constexpr int kPitch = kTile + 4;
+
+__device__ __forceinline__ void tile_row(const float* tile, int n, float (&v)[kTile]) {
+#pragma unroll
+    for (int q = 0; q < kTile / 4; ++q) {
+        const float4 x = *reinterpret_cast<const float4*>(tile + n * kPitch + 4 * q);
+        v[4 * q] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
+    }
+}
+
 template <typename T>
-__device__ __forceinline__ float load_bc_elem(const S6BwdArgs& p, int64_t t0,
-                                              __amdgpu_buffer_rsrc_t r) {
+__device__ __forceinline__ uint32_t load_bc_bits(const S6BwdArgs& p, int64_t t0,
+                                                 __amdgpu_buffer_rsrc_t r) {
     const int j = threadIdx.x / 16, n = threadIdx.x % 16;
     const uint32_t off = n < p.N ? (uint32_t)(((t0 + j) * p.N + n) * sizeof(T)) : 0x80000000u;
-    return Buf<T>::load(r, off, 0);
+    return Bits<T>::load(r, off);
 }
 
 // Inputs of kSuper consecutive tiles, fetched together so that one memory
@@ -168,16 +215,16 @@ constexpr int kSuper = 8;
 
 template <typename T>
 struct SuperRaw {
-    float delta[kSuper], u[kSuper], b[kSuper];
-    __device__ __forceinline__ void load(const S6BwdArgs& p, const LaneId& id, int64_t t0,
-                                         __amdgpu_buffer_rsrc_t rB) {
+    uint32_t delta[kSuper], u[kSuper], b[kSuper];
+    __device__ __forceinline__ void load(const S6BwdArgs& p, const LaneId& id, const RowRsrc& rr,
+                                         int64_t t0, __amdgpu_buffer_rsrc_t rB) {
 #pragma unroll
         for (int i = 0; i < kSuper; ++i) {
             TileRaw<T, false, false> r;
-            r.load(p, id, t0 + i * kTile);
+            r.load(p, id, rr, t0 + i * kTile);
             delta[i] = r.delta;
             u[i] = r.u;
-            b[i] = load_bc_elem<T>(p, t0 + i * kTile, rB);
+            b[i] = load_bc_bits<T>(p, t0 + i * kTile, rB);
         }
     }
 };
@@ -185,7 +232,7 @@ struct SuperRaw {
 template <typename T, bool SOFTPLUS>
 __global__ __launch_bounds__(kThreads) void s6_bwd_ckpt(S6BwdArgs p) {
     static_assert(kThreads == kTile * 16, "one tile element per thread");
-    __shared__ float bt[kSuper][kTile][16];
+    __shared__ __attribute__((aligned(16))) float bt[kSuper][16 * kPitch];
     const LaneId id = lane_id(p);
     const float a2 = id.ok ? p.A[id.dc * p.N + id.n] * kLog2e : 0.0f;
     const float bias = p.delta_bias ? p.delta_bias[id.dc] : 0.0f;
@@ -194,15 +241,17 @@ __global__ __launch_bounds__(kThreads) void s6_bwd_ckpt(S6BwdArgs p) {
     float h = (id.ok && p.h0) ? p.h0[(id.b * p.D + id.d) * p.N + id.n] : 0.0f;
     const auto rB = bc_rsrc<T>(p, id.b, p.Bm);
     float* ck = p.ckpt + (id.b * p.D + id.dc) * nblk * p.N + id.n;
+    const RowRsrc rr = row_rsrc<T>(p, id.b);
     SuperRaw<T> nxt;
-    if (nsup > 0) nxt.load(p, id, 0, rB);
+    if (nsup > 0) nxt.load(p, id, rr, 0, rB);
     for (int64_t sg = 0; sg < nsup; ++sg) {
         const SuperRaw<T> cur = nxt;
         __syncthreads();                    // previous super-tile's B reads done
 #pragma unroll
-        for (int i = 0; i < kSuper; ++i) bt[i][threadIdx.x / 16][threadIdx.x % 16] = cur.b[i];
+        for (int i = 0; i < kSuper; ++i)
+            bt[i][(threadIdx.x % 16) * kPitch + threadIdx.x / 16] = Bits<T>::f32(cur.b[i]);
         __syncthreads();
-        if (sg + 1 < nsup) nxt.load(p, id, (sg + 1) * kSuper * kTile, rB);   // travels meanwhile
+        if (sg + 1 < nsup) nxt.load(p, id, rr, (sg + 1) * kSuper * kTile, rB);   // travels meanwhile
 #pragma unroll
         for (int i = 0; i < kSuper; ++i) {
             const int64_t k = sg * kSuper + i;
@@ -212,12 +261,18 @@ __global__ __launch_bounds__(kThreads) void s6_bwd_ckpt(S6BwdArgs p) {
             r.delta = cur.delta[i];
             r.u = cur.u[i];
             TileScalars<false, SOFTPLUS, false> s;
-            s.from(r, p, id, k * kTile, bias);
+            s.template from<T>(r, p, id, k * kTile, bias);
+            float bv[kTile], dA[kTile];
+            tile_row(bt[i], id.n, bv);
+            // all decay factors and input terms first, then the dependent chain
 #pragma unroll
             for (int j = 0; j < kTile; ++j) {
-                const float dA = fast_exp2(row_bcast(s.dt, j) * a2);
-                h = fmaf(dA, h, bt[i][j][id.n] * row_bcast(s.dtu, j));
+                dA[j] = fast_exp2(row_bcast(s.dt, j) * a2);
+                bv[j] *= row_bcast(s.dtu, j);
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < kTile; ++j) h = fmaf(dA[j], h, bv[j]);
         }
     }
 }
@@ -226,15 +281,17 @@ template <typename T, bool HAS_Z, bool SOFTPLUS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void s6_bwd_main(S6BwdArgs p) {
     __shared__ float red[2][kWaves][kTile][16];     // [dB|dC][wave][token][n]
-    __shared__ float bct[2][kTile][16];             // B, C of the tile, [token][n]
+    __shared__ __attribute__((aligned(16))) float bct[2][16 * kPitch];   // B, C: [n][token]
     const LaneId id = lane_id(p);
     const float an = id.ok ? p.A[id.dc * p.N + id.n] : 0.0f;
     const float a2 = an * kLog2e;
     const float bias = p.delta_bias ? p.delta_bias[id.dc] : 0.0f;
     const float dsk = p.Dskip ? p.Dskip[id.dc] : 0.0f;
     const int64_t nblk = (p.L + kTile - 1) / kTile;
-    const float* ck = p.ckpt + (id.b * p.D + id.dc) * nblk * p.N + id.n;
+    // n clamped: lanes past N read a valid (ignored) checkpoint
+    const float* ck = p.ckpt + (id.b * p.D + id.dc) * nblk * p.N + (id.n < p.N ? id.n : 0);
     const int64_t G = (p.D + kChans - 1) / kChans;
+    const RowRsrc rr = row_rsrc<T>(p, id.b);
     T* du_out = static_cast<T*>(p.du);
     T* dd_out = static_cast<T*>(p.ddelta);
     T* dz_out = static_cast<T*>(p.dz);
@@ -245,36 +302,44 @@ void s6_bwd_main(S6BwdArgs p) {
     float mu = (id.ok && p.dh_last) ? p.dh_last[(id.b * p.D + id.d) * p.N + id.n] : 0.0f;
     float dA_acc = 0.0f, dD_acc = 0.0f, db_acc = 0.0f;
     TileRaw<T, HAS_Z, true> raw;
-    float bpre = 0.0f, cpre = 0.0f, hck = 0.0f;
+    uint32_t bpre = 0, cpre = 0;
+    float hck = 0.0f;
     if (nblk > 0) {
-        raw.load(p, id, (nblk - 1) * kTile);
-        bpre = load_bc_elem<T>(p, (nblk - 1) * kTile, rB);
-        cpre = load_bc_elem<T>(p, (nblk - 1) * kTile, rC);
-        hck = id.ok ? ck[(nblk - 1) * p.N] : 0.0f;
+        raw.load(p, id, rr, (nblk - 1) * kTile);
+        bpre = load_bc_bits<T>(p, (nblk - 1) * kTile, rB);
+        cpre = load_bc_bits<T>(p, (nblk - 1) * kTile, rC);
+        hck = ck[(nblk - 1) * p.N];
     }
     for (int64_t k = nblk - 1; k >= 0; --k) {
         const int64_t t0 = k * kTile;
-        const float hprev0 = hck;
+        const float hprev0 = id.ok ? hck : 0.0f;
         TileScalars<HAS_Z, SOFTPLUS, true> s;
-        s.from(raw, p, id, t0, bias);
+        s.template from<T>(raw, p, id, t0, bias);
         __syncthreads();                   // previous tile's LDS reads done
-        bct[0][threadIdx.x / 16][threadIdx.x % 16] = bpre;
-        bct[1][threadIdx.x / 16][threadIdx.x % 16] = cpre;
+        bct[0][(threadIdx.x % 16) * kPitch + threadIdx.x / 16] = Bits<T>::f32(bpre);
+        bct[1][(threadIdx.x % 16) * kPitch + threadIdx.x / 16] = Bits<T>::f32(cpre);
         __syncthreads();
         if (k > 0) {                       // previous tile's inputs travel during this one
-            raw.load(p, id, t0 - kTile);
-            bpre = load_bc_elem<T>(p, t0 - kTile, rB);
-            cpre = load_bc_elem<T>(p, t0 - kTile, rC);
-            hck = id.ok ? ck[(k - 1) * p.N] : 0.0f;
+            raw.load(p, id, rr, t0 - kTile);
+            bpre = load_bc_bits<T>(p, t0 - kTile, rB);
+            cpre = load_bc_bits<T>(p, t0 - kTile, rC);
+            hck = ck[(k - 1) * p.N];
         }
         // states of the tile, recomputed from its checkpoint
         float hs[kTile], da[kTile];
         {
-            float h = hprev0;
+            float bv[kTile];
+            tile_row(bct[0], id.n, bv);
 #pragma unroll
             for (int j = 0; j < kTile; ++j) {
                 da[j] = fast_exp2(row_bcast(s.dt, j) * a2);
-                h = fmaf(da[j], h, bct[0][j][id.n] * row_bcast(s.dtu, j));
+                bv[j] *= row_bcast(s.dtu, j);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            float h = hprev0;
+#pragma unroll
+            for (int j = 0; j < kTile; ++j) {
+                h = fmaf(da[j], h, bv[j]);
                 hs[j] = h;
             }
         }
@@ -288,9 +353,12 @@ void s6_bwd_main(S6BwdArgs p) {
         // (pt: ddt, pu: sum m B, py: readout) are reduced after the loop;
         // wbc[j]: dB (rows 0-1) or dC (rows 2-3) of token j summed over the wavefront
         float pt[kTile], pu[kTile], py[kTile], wbc[kTile];
+        float bv[kTile], cv[kTile];
+        tile_row(bct[0], id.n, bv);
+        tile_row(bct[1], id.n, cv);
 #pragma unroll
         for (int j = kTile - 1; j >= 0; --j) {
-            const float bj = bct[0][j][id.n], cj = bct[1][j][id.n];
+            const float bj = bv[j], cj = cv[j];
             const float gj = row_bcast(s.g, j);
             const float m = fmaf(gj, cj, mu);
             const float hp = j > 0 ? hs[j - 1] : hprev0;

@@ -63,6 +63,7 @@ int s6_bwd_check_sizes(int64_t B, int64_t L, int64_t D, int64_t N, int dtype) {
         return SSM_ERR_UNSUPPORTED;
     if (mul3(2 * G, B * L, N) < 0) return SSM_ERR_BAD_SHAPE;
     if ((L + 16) * N * esize(dtype) >= (int64_t)0x80000000LL) return SSM_ERR_UNSUPPORTED;  // B/C row offsets
+    if ((L + 16) * D * esize(dtype) >= (int64_t)0x80000000LL) return SSM_ERR_UNSUPPORTED;  // activation row offsets
     return SSM_OK;
 }
 
