@@ -17,8 +17,9 @@ divided by the mean step time.
 The same run also measures, under "paths", the other calls of the library on
 their own workloads (each flushed and timed the same way): the SSD chunked
 forward (Mamba-2, B=4 L=8192 H=64 P=64 N=128, chunk 256), the decode step
-(64 sequences, D=5120 N=16), the backward pass with recomputation and the
-causal conv1d + SiLU (both on the Mamba-130M layer shape), and it times the
+(64 sequences, D=5120 N=16), the backward pass with recomputation, the
+causal conv1d + SiLU, and the conv1d fused in front of the scan (all three on
+the Mamba-130M layer shape), and it times the
 fp64 CPU oracle on the host cores over the whole S6 workload.
 
 `--only PART` runs one part alone and prints its result (for profiling).
@@ -259,6 +260,30 @@ def bench_conv(args, torch, ssm, W):
                 pct_hbm_peak=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS * 100, 2))
 
 
+def bench_conv_scan(args, torch, ssm, W):
+    """The conv1d + SiLU fused in front of the S6 scan, on the Mamba-130M layer
+    shape with a K = 4 convolution: x replaces u as the input, so the
+    algorithmic bytes are those of the scan plus the convolution weights."""
+    w = W.S6_MAMBA130M
+    t = W.make_s6_inputs(w, seed=0)
+    cv = W.make_conv_inputs(W.CONV_MAMBA130M, seed=1)
+    d = {k: (v.to("cuda:0") if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
+    x, cw, cb = (cv[k].to("cuda:0") for k in ("x", "weight", "bias"))
+    y = torch.empty_like(d["u"])
+    ws = torch.empty(max(1, ssm.selective_scan_workspace_bytes(w.B, w.L, w.D, w.N)),
+                     dtype=torch.uint8, device="cuda:0")
+
+    def step():
+        ssm.selective_scan_conv_fwd(x, cw, cb, d["delta"], d["A"], d["B"], d["C"], D=d["D"],
+                                    z=d["z"], delta_bias=d["delta_bias"], out=y, workspace=ws)
+
+    ms = _time_flushed(torch, step, args.steps, args.warmup)
+    nbytes = W.s6_algorithmic_bytes(w) + W.CONV_MAMBA130M.D * (W.CONV_MAMBA130M.K + 1) * 4
+    return dict(status="ok", workload=w.name + "+conv1d_k4", ms=round(ms, 5),
+                algorithmic_bytes=nbytes, gbs=round(nbytes / (ms * 1e-3) / 1e9, 2),
+                gtokch=round(w.tok_ch / (ms * 1e-3) / 1e9, 3))
+
+
 def cpu_baseline(r, torch, min_seconds=10.0):
     """The fp64 oracle over the whole S6 workload on the host cores, repeated
     until at least `min_seconds` of wall time (the workload alone takes well
@@ -294,7 +319,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ssd", action="store_true", help="skip every path but the S6 scan")
-    ap.add_argument("--only", choices=["s6", "ssd", "decode", "bwd", "conv"],
+    ap.add_argument("--only", choices=["s6", "ssd", "decode", "bwd", "conv", "conv_scan"],
                     help="run one part alone and print its result")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 256 MiB device copy three times, the "
@@ -321,7 +346,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if args.only and args.only != "s6":
-        fn = {"ssd": bench_ssd, "decode": bench_decode, "bwd": bench_bwd, "conv": bench_conv}
+        fn = {"ssd": bench_ssd, "decode": bench_decode, "bwd": bench_bwd, "conv": bench_conv,
+              "conv_scan": bench_conv_scan}
         res = fn[args.only](args, torch, ssm, W)
         print(json.dumps({"part": args.only, **{k: v for k, v in res.items()}}), flush=True)
         return
@@ -332,6 +358,7 @@ def main():
         paths["selective_state_update"] = bench_decode(args, torch, ssm, W)
         paths["selective_scan_bwd"] = bench_bwd(args, torch, ssm, W)
         paths["causal_conv1d_silu"] = bench_conv(args, torch, ssm, W)
+        paths["selective_scan_conv_fwd"] = bench_conv_scan(args, torch, ssm, W)
     w = r["w"]
     line = {
         "metric": "selective-scan fwd achieved HBM GB/s (% of peak) + Gtoken·channels/s",

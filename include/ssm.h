@@ -123,6 +123,30 @@ int ssm_selective_scan_fwd_timed(const void* u, const void* delta, const float* 
                                  void* const* events);
 
 /*
+ * The same scan with the causal depthwise conv1d + SiLU of ssm_causal_conv1d_silu
+ * fused in front of it: the call reads the convolution's input x [B, L, D]
+ * and forms u = silu(bias + sum_k weight[d,k] x_{t-(K-1)+k}) per token in
+ * registers, so u never round-trips through memory (the Mamba block applies
+ * the short convolution and SiLU just before the selective SSM: temporalbook
+ * "Selective State-Space Models (Mamba)", section 4).
+ *   x              : [B, L, D] dtype (the place of u)
+ *   conv_weight    : [D, K] fp32; conv_bias : [D] fp32 or NULL; 1 <= K <= 4
+ *   conv_state_in  : [B, D, K-1] fp32 or NULL (zeros): inputs before t = 0
+ *   conv_state_out : [B, D, K-1] fp32 or NULL: the last K-1 inputs
+ *   u_out          : [B, L, D] dtype or NULL: the convolution's output u
+ *                    (what the backward pass takes as u)
+ * Everything else as ssm_selective_scan_fwd (same workspace query).
+ * Supported: N = 16; flags SSM_FLAG_DELTA_SOFTPLUS only.
+ */
+int ssm_selective_scan_conv_fwd(const void* x, const float* conv_weight, const float* conv_bias,
+                                const float* conv_state_in, float* conv_state_out, int64_t K,
+                                void* u_out, const void* delta, const float* A, const void* Bm,
+                                const void* Cm, const float* Dskip, const void* z,
+                                const float* delta_bias, unsigned flags, const float* h0, void* y,
+                                float* h_last, int64_t B, int64_t L, int64_t D, int64_t N,
+                                int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * ---------------------------------------------------------------- SSD chunked
  * The Mamba-2 form with a scalar transition per head (section 3 "Mamba-2 and
  * State Space Duality" of "Mamba & Mamba-2 Architecture"): per (b, head h),

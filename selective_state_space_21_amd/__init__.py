@@ -13,7 +13,7 @@ import torch
 from . import _native
 from ._native import SSMError
 
-__all__ = ["selective_scan_fwd", "selective_scan_bwd", "ssd_chunk_fwd", "selective_state_update",
+__all__ = ["selective_scan_fwd", "selective_scan_conv_fwd", "selective_scan_bwd", "ssd_chunk_fwd", "selective_state_update",
            "causal_conv1d_silu",
            "selective_scan_workspace_bytes",
            "selective_scan_segments", "ssd_chunk_workspace_bytes", "SSMError"]
@@ -307,3 +307,73 @@ def causal_conv1d_silu(x: torch.Tensor, weight: torch.Tensor, bias: Optional[tor
                                     _stream_handle(dev))
     _native.check(rc, "ssm_causal_conv1d_silu")
     return (u, new_state) if return_state else u
+
+
+def selective_scan_conv_fwd(x: torch.Tensor, conv_weight: torch.Tensor,
+                            conv_bias: Optional[torch.Tensor], delta: torch.Tensor,
+                            A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                            D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                            delta_bias: Optional[torch.Tensor] = None,
+                            delta_softplus: bool = True, h0: Optional[torch.Tensor] = None,
+                            conv_state: Optional[torch.Tensor] = None,
+                            return_u: bool = False, return_conv_state: bool = False,
+                            out: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None) -> dict:
+    """Causal conv1d + SiLU fused in front of the S6 scan (ssm_selective_scan_conv_fwd).
+
+    x: [Bt, L, Dm] (the convolution's input, in place of u); conv_weight:
+    [Dm, K] fp32; conv_bias: [Dm] fp32; conv_state: [Bt, Dm, K-1] fp32; the
+    rest as selective_scan_fwd (N = 16).  Returns a dict with y and h_last,
+    plus u and conv_state when requested.
+    """
+    lib = _native.load()
+    if x.dtype not in _DT:
+        raise TypeError(f"x must be float32 or bfloat16 (got {x.dtype})")
+    dev, dt = x.device, x.dtype
+    x = _dev_tensor("x", x, dt, dev)
+    conv_weight = _dev_tensor("conv_weight", conv_weight, torch.float32, dev)
+    conv_bias = _dev_tensor("conv_bias", conv_bias, torch.float32, dev)
+    conv_state = _dev_tensor("conv_state", conv_state, torch.float32, dev)
+    delta = _dev_tensor("delta", delta, dt, dev)
+    B = _dev_tensor("B", B, dt, dev)
+    C = _dev_tensor("C", C, dt, dev)
+    z = _dev_tensor("z", z, dt, dev)
+    A = _dev_tensor("A", A, torch.float32, dev)
+    D = _dev_tensor("D", D, torch.float32, dev)
+    delta_bias = _dev_tensor("delta_bias", delta_bias, torch.float32, dev)
+    h0 = _dev_tensor("h0", h0, torch.float32, dev)
+    if x.dim() != 3 or conv_weight.dim() != 2:
+        raise ValueError("x must be [B, L, D] and conv_weight [D, K]")
+    Bt, L, Dm = x.shape
+    N = A.shape[-1]
+    K = conv_weight.shape[1]
+    shapes = {"delta": (delta, (Bt, L, Dm)), "A": (A, (Dm, N)), "B": (B, (Bt, L, N)),
+              "C": (C, (Bt, L, N)), "z": (z, (Bt, L, Dm)), "D": (D, (Dm,)),
+              "delta_bias": (delta_bias, (Dm,)), "h0": (h0, (Bt, Dm, N)),
+              "conv_weight": (conv_weight, (Dm, K)), "conv_bias": (conv_bias, (Dm,)),
+              "conv_state": (conv_state, (Bt, Dm, K - 1))}
+    for name, (t, shp) in shapes.items():
+        if t is not None and tuple(t.shape) != shp:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shp}")
+    y = out if out is not None else torch.empty((Bt, L, Dm), dtype=dt, device=dev)
+    _dev_tensor("out", y, dt, dev)
+    h_last = torch.empty((Bt, Dm, N), dtype=torch.float32, device=dev)
+    u = torch.empty_like(x) if return_u else None
+    cs = torch.empty((Bt, Dm, K - 1), dtype=torch.float32, device=dev) if return_conv_state else None
+    ws_need = int(lib.ssm_selective_scan_workspace_bytes(Bt, L, Dm, N, _DT[dt]))
+    if ws_need and (workspace is None or workspace.numel() * workspace.element_size() < ws_need):
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    flags = _native.FLAG_DELTA_SOFTPLUS if delta_softplus else 0
+    rc = lib.ssm_selective_scan_conv_fwd(
+        _ptr(x), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state), _ptr(cs), K, _ptr(u),
+        _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), flags,
+        _ptr(h0), _ptr(y), _ptr(h_last), Bt, L, Dm, N, _DT[dt], _ptr(workspace), ws_bytes,
+        _stream_handle(dev))
+    _native.check(rc, "ssm_selective_scan_conv_fwd")
+    res = {"y": y, "h_last": h_last}
+    if return_u:
+        res["u"] = u
+    if return_conv_state:
+        res["conv_state"] = cs
+    return res

@@ -128,7 +128,7 @@ struct TokBlock {
 // unconditionally and the token loop has no divergent branch.
 // The tensors come in as __restrict__ arguments so that the compiler knows
 // the y stores cannot alias the inputs.
-template <typename T, bool SCAN, bool HAS_Z, bool RAGGED, bool SOFTPLUS>
+template <typename T, bool SCAN, bool HAS_Z, bool RAGGED, bool SOFTPLUS, bool CONV>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3)))
 void s6_fast(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
              const T* __restrict__ z_, const T* __restrict__ Bm_, const T* __restrict__ Cm_,
@@ -177,6 +177,43 @@ void s6_fast(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
     }
     float dt_sum = 0.0f;
 
+    // Causal conv1d + SiLU in front of the scan (CONV): u_ holds its input x.
+    // Four taps (a width K < 4 is padded with leading zero weights); the
+    // window holds x_{t-3}, x_{t-2}, x_{t-1}, starting from the tokens before
+    // the segment, the carried state, or zeros.
+    float cw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, cb = 0.0f, xw[3] = {0.0f, 0.0f, 0.0f};
+    if constexpr (CONV) {
+        const int K = (int)p.conv_K;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int kk = k - (4 - K);
+            cw[k] = kk >= 0 ? p.conv_w[(int64_t)col * K + kk] : 0.0f;
+        }
+        cb = p.conv_b ? p.conv_b[col] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int64_t tt = t0 - 3 + i;
+            const int slot = (int)tt + K - 1;           // index into the carried state
+            if (tt >= 0)
+                xw[i] = Elem<T>::load(u_, (b * p.L + tt) * D + col);
+            else if (p.conv_state_in && slot >= 0)
+                xw[i] = p.conv_state_in[(b * D + col) * (K - 1) + slot];
+        }
+    }
+    const auto ruo = make_rsrc((CONV && SCAN && p.u_out) ? static_cast<T*>(p.u_out) + row0 : nullptr,
+                               (CONV && SCAN && p.u_out) ? seg_bytes : 0u);
+    auto input_u = [&](float xt) -> float {
+        if constexpr (CONV) {
+            const float sc = fmaf(cw[3], xt, fmaf(cw[2], xw[2], fmaf(cw[1], xw[1], fmaf(cw[0], xw[0], cb))));
+            xw[0] = xw[1];
+            xw[1] = xw[2];
+            xw[2] = xt;
+            return silu_f(sc);
+        } else {
+            return xt;
+        }
+    };
+
     // B/C tiles: fp32 rows of the current 16-token group, raw rows of the next.
     float btile[NS], ctile[SCAN ? NS : 1];
     RawRow<T, NS> rawB, rawC;
@@ -209,9 +246,12 @@ void s6_fast(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
             const float x = k.d[j] + bias;
             float dt;
             if constexpr (SOFTPLUS) dt = softplus_f(x); else dt = x;
-            const float ut = k.u[j];
+            const float ut = input_u(k.u[j]);
             const float dtu = dt * ut;
             if constexpr (SCAN) {
+                if constexpr (CONV) {
+                    if (p.u_out && (!RAGGED || active)) Buf<T>::store(ruo, voff, (uint32_t)r * row_bytes, ut);
+                }
                 float acc = 0.0f;
 #pragma unroll
                 for (int n = 0; n < NS; ++n) {
@@ -271,6 +311,14 @@ void s6_fast(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
         if (p.h_last && active && s == p.S - 1) {
 #pragma unroll
             for (int n = 0; n < NS; ++n) p.h_last[hb + n] = h[n];
+        }
+        if constexpr (CONV) {
+            // the last K-1 inputs of the sequence, oldest first
+            if (p.conv_state_out && active && s == p.S - 1) {
+                const int K = (int)p.conv_K;
+                for (int i = 0; i < K - 1; ++i)
+                    p.conv_state_out[(b * D + col) * (K - 1) + i] = xw[4 - K + i];
+            }
         }
     } else if (active) {
 #pragma unroll
@@ -422,7 +470,7 @@ hipError_t launch_carry(const S6Args& a, hipStream_t stream) {
     return hipSuccess;
 }
 
-template <typename T, bool SP>
+template <typename T, bool SP, bool CV>
 hipError_t launch_fast_sp(const S6Args& a, hipStream_t stream) {
     const T* U = static_cast<const T*>(a.u);
     const T* Dl = static_cast<const T*>(a.delta);
@@ -434,7 +482,7 @@ hipError_t launch_fast_sp(const S6Args& a, hipStream_t stream) {
     const dim3 block(kWave);
     mark(a, 0, stream);
     if (a.S > 1)
-        hipLaunchKernelGGL((s6_fast<T, false, false, false, SP>),
+        hipLaunchKernelGGL((s6_fast<T, false, false, false, SP, CV>),
                            dim3(dblocks, (unsigned)a.B, (unsigned)(a.S - 1)), block, 0, stream,
                            a, U, Dl, Z, Bp, Cp, (T*)nullptr);
     mark(a, 1, stream);
@@ -444,17 +492,17 @@ hipError_t launch_fast_sp(const S6Args& a, hipStream_t stream) {
     const bool ragged = (a.D % kWave) != 0;
     if (a.z) {
         if (ragged)
-            hipLaunchKernelGGL((s6_fast<T, true, true, true, SP>), grid, block, 0, stream, a, U,
+            hipLaunchKernelGGL((s6_fast<T, true, true, true, SP, CV>), grid, block, 0, stream, a, U,
                                Dl, Z, Bp, Cp, Y);
         else
-            hipLaunchKernelGGL((s6_fast<T, true, true, false, SP>), grid, block, 0, stream, a, U,
+            hipLaunchKernelGGL((s6_fast<T, true, true, false, SP, CV>), grid, block, 0, stream, a, U,
                                Dl, Z, Bp, Cp, Y);
     } else {
         if (ragged)
-            hipLaunchKernelGGL((s6_fast<T, true, false, true, SP>), grid, block, 0, stream, a, U,
+            hipLaunchKernelGGL((s6_fast<T, true, false, true, SP, CV>), grid, block, 0, stream, a, U,
                                Dl, Z, Bp, Cp, Y);
         else
-            hipLaunchKernelGGL((s6_fast<T, true, false, false, SP>), grid, block, 0, stream, a, U,
+            hipLaunchKernelGGL((s6_fast<T, true, false, false, SP, CV>), grid, block, 0, stream, a, U,
                                Dl, Z, Bp, Cp, Y);
     }
     mark(a, 3, stream);
@@ -463,8 +511,10 @@ hipError_t launch_fast_sp(const S6Args& a, hipStream_t stream) {
 
 template <typename T>
 hipError_t launch_fast(const S6Args& a, hipStream_t stream) {
-    return (a.flags & SSM_FLAG_DELTA_SOFTPLUS) ? launch_fast_sp<T, true>(a, stream)
-                                               : launch_fast_sp<T, false>(a, stream);
+    const bool sp = (a.flags & SSM_FLAG_DELTA_SOFTPLUS) != 0;
+    if (a.conv_w)
+        return sp ? launch_fast_sp<T, true, true>(a, stream) : launch_fast_sp<T, false, true>(a, stream);
+    return sp ? launch_fast_sp<T, true, false>(a, stream) : launch_fast_sp<T, false, false>(a, stream);
 }
 
 template <typename T, int NM, bool ZOH>
@@ -530,6 +580,10 @@ hipError_t launch_s6(const S6Args& a, hipStream_t stream) {
             hipLaunchKernelGGL(s6_copy_state, dim3((unsigned)((count + 255) / 256)), dim3(256),
                                0, stream, a.h0, a.h_last, count);
         }
+        const int64_t ccount = a.B * a.D * (a.conv_K - 1);
+        if (a.conv_w && a.conv_state_out && ccount > 0)
+            hipLaunchKernelGGL(s6_copy_state, dim3((unsigned)((ccount + 255) / 256)), dim3(256),
+                               0, stream, a.conv_state_in, a.conv_state_out, ccount);
         mark(a, 3, stream);
         return hipGetLastError();
     }

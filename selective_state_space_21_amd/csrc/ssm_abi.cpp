@@ -146,6 +146,48 @@ int ssm_selective_scan_fwd_timed(const void* u, const void* delta, const float* 
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+int ssm_selective_scan_conv_fwd(const void* x, const float* conv_weight, const float* conv_bias,
+                                const float* conv_state_in, float* conv_state_out, int64_t K,
+                                void* u_out, const void* delta, const float* A, const void* Bm,
+                                const void* Cm, const float* Dskip, const void* z,
+                                const float* delta_bias, unsigned flags, const float* h0, void* y,
+                                float* h_last, int64_t B, int64_t L, int64_t D, int64_t N,
+                                int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = s6_check_sizes(B, L, D, N, dtype);
+    if (rc != SSM_OK) return rc;
+    if (flags & ~(unsigned)SSM_FLAG_DELTA_SOFTPLUS) return SSM_ERR_UNSUPPORTED;
+    if (N != 16) return SSM_ERR_UNSUPPORTED;
+    if (K < 1) return SSM_ERR_BAD_SHAPE;
+    if (K > 4) return SSM_ERR_UNSUPPORTED;
+    if (!A || !conv_weight) return SSM_ERR_NULL_ARG;
+    if (L > 0 && (!x || !delta || !Bm || !Cm || !y)) return SSM_ERR_NULL_ARG;
+    const void* big[] = {x, delta, Bm, Cm, z, y, u_out};
+    for (const void* p : big)
+        if (p && !aligned(p, 16)) return SSM_ERR_MISALIGNED;
+    const void* vec[] = {A, Dskip, delta_bias, h0, h_last, conv_weight, conv_bias, conv_state_in,
+                         conv_state_out};
+    for (const void* p : vec)
+        if (p && !aligned(p, 4)) return SSM_ERR_MISALIGNED;
+    const ssm::S6Plan plan = ssm::plan_s6(B, L, D, N);
+    if (plan.workspace_bytes > 0) {
+        if (!workspace || workspace_bytes < plan.workspace_bytes) return SSM_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return SSM_ERR_MISALIGNED;
+    }
+    ssm::S6Args a{};
+    a.u = x; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.z = z;
+    a.delta_bias = delta_bias; a.h0 = h0; a.y = y; a.h_last = h_last;
+    a.B = B; a.L = L; a.D = D; a.N = N;
+    a.S = plan.S; a.seg_len = plan.seg_len; a.flags = flags; a.bf16 = dtype == SSM_BF16;
+    a.conv_w = conv_weight; a.conv_b = conv_bias; a.conv_state_in = conv_state_in;
+    a.conv_state_out = conv_state_out; a.u_out = u_out; a.conv_K = K;
+    if (plan.S > 1) {
+        a.seg_a = static_cast<float*>(workspace);
+        a.seg_b = a.seg_a + B * D * (int64_t)plan.S * N;
+    }
+    const hipError_t e = ssm::launch_s6(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 size_t ssm_ssd_chunk_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t P,
                                      int64_t G, int64_t N, int64_t chunk, int dtype) {
     (void)ssd_check_sizes(B, L, H, P, G, N, chunk, dtype);

@@ -31,6 +31,13 @@ struct S6Args {
     unsigned flags;
     int bf16;          // storage dtype of activations: 1 = bf16, 0 = fp32
     hipEvent_t const* events;   // NULL, or 4 events recorded at the phase boundaries
+    // causal conv1d + SiLU fused in front of the scan (u then holds its input x)
+    const float* conv_w;        // [D, conv_K] or NULL (no convolution)
+    const float* conv_b;        // [D] or NULL
+    const float* conv_state_in; // [B, D, conv_K - 1] or NULL
+    float* conv_state_out;      // [B, D, conv_K - 1] or NULL
+    void* u_out;                // [B, L, D] or NULL: the convolution's output u
+    int64_t conv_K;
 };
 
 struct S6Plan {

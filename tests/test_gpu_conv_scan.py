@@ -1,0 +1,139 @@
+"""GPU parity of the causal conv1d + SiLU fused in front of the S6 scan
+(ssm_selective_scan_conv_fwd) through the C ABI.
+
+Reference: the composition of the two pinned fp64 oracles (conv1d + SiLU,
+then the scan).  Bar: normwise 1e-5 (fp32 storage) / 2e-2 (bf16).  With
+fp32 storage the fused call equals the two separate calls bit for bit (the
+same per-token arithmetic), and its u output equals the separate conv1d's."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_21_amd as ssm
+from selective_state_space_21_amd import workloads as W
+
+from _parity import TOL, normwise_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(Bt, L, Dm, K, dtype, seed, gate=True, skip=True, bias=True):
+    w = W.S6_MAMBA130M.scaled(B=Bt, L=L, D=Dm, dtype=dtype, gate=gate,
+                              skip="normal" if skip else None,
+                              bias_range=(-4.0, -2.0) if bias else None)
+    inp = W.make_s6_inputs(w, seed)
+    cv = W.make_conv_inputs(W.CONV_MAMBA130M.scaled(B=Bt, L=L, D=Dm, K=K, dtype=dtype), seed + 1)
+    inp["x"] = cv["x"]
+    inp["conv_w"] = cv["weight"]
+    inp["conv_b"] = cv["bias"]
+    return inp
+
+
+def _fused(d, conv_state=None, h0=None, **kw):
+    r = ssm.selective_scan_conv_fwd(d["x"], d["conv_w"], d["conv_b"], d["delta"], d["A"], d["B"],
+                                    d["C"], D=d["D"], z=d["z"], delta_bias=d["delta_bias"],
+                                    h0=h0, conv_state=conv_state, return_u=True,
+                                    return_conv_state=True, **kw)
+    torch.cuda.synchronize()
+    return r
+
+
+def _oracle(inp, conv_state=None, h0=None):
+    u, cs = oracle.causal_conv1d_silu(inp["x"], inp["conv_w"], inp["conv_b"], state=conv_state)
+    y, h = oracle.s6_fwd(u, inp["delta"], inp["A"], inp["B"], inp["C"], D=inp["D"], z=inp["z"],
+                         delta_bias=inp["delta_bias"], h0=h0)
+    return y, h, u, cs
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(2, 300, 128, 4), (1, 1000, 100, 4), (2, 77, 64, 3),
+                                   (1, 2, 64, 4), (3, 129, 70, 2), (1, 64, 64, 1)])
+def test_fused_parity(dtype, shape):
+    Bt, L, Dm, K = shape
+    inp = _case(Bt, L, Dm, K, dtype, seed=L + K)
+    g = torch.Generator().manual_seed(L)
+    cs0 = torch.randn(Bt, Dm, K - 1, generator=g) if K > 1 else None
+    h0 = 0.3 * torch.randn(Bt, Dm, 16, generator=g)
+    r = _fused(to_dev(inp), conv_state=None if cs0 is None else cs0.cuda(), h0=h0.cuda())
+    y, h, u, cs = _oracle(inp, conv_state=cs0, h0=h0)
+    tol = TOL[dtype]
+    assert normwise_err(r["y"].float().cpu().numpy(), y) <= tol
+    assert normwise_err(r["h_last"].cpu().numpy(), h) <= (1e-5 if dtype == "f32" else 2e-2)
+    assert normwise_err(r["u"].float().cpu().numpy(), u) <= tol
+    np.testing.assert_array_equal(r["conv_state"].cpu().numpy(), cs)
+
+
+@pytest.mark.parametrize("segments", [1, 3, 16])
+def test_fused_equals_separate_calls_fp32(monkeypatch, segments):
+    monkeypatch.setenv("SSM_S6_SEGMENTS", str(segments))
+    inp = _case(2, 600, 96, 4, "f32", seed=segments)
+    d = to_dev(inp)
+    r = _fused(d)
+    u = ssm.causal_conv1d_silu(d["x"], d["conv_w"], d["conv_b"])
+    y, h = ssm.selective_scan_fwd(u, d["delta"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
+                                  delta_bias=d["delta_bias"])
+    torch.cuda.synchronize()
+    assert ssm.selective_scan_segments(2, 600, 96, 16) == segments
+    assert torch.equal(r["u"], u)
+    assert torch.equal(r["y"], y)
+    assert torch.equal(r["h_last"], h)
+
+
+def test_fused_u_equals_conv_kernel_bf16():
+    inp = _case(2, 200, 128, 4, "bf16", seed=9)
+    d = to_dev(inp)
+    r = _fused(d)
+    u = ssm.causal_conv1d_silu(d["x"], d["conv_w"], d["conv_b"])
+    torch.cuda.synchronize()
+    assert torch.equal(r["u"], u)
+
+
+def test_fused_chunked_prefill_equals_one_call():
+    """Chunks chained through conv_state and h_last reproduce one call."""
+    inp = _case(2, 330, 64, 4, "f32", seed=4)
+    d = to_dev(inp)
+    one = _fused(d)
+    ys, cs, h = [], None, None
+    for a, b in [(0, 100), (100, 101), (101, 330)]:
+        sub = dict(d)
+        for k in ("x", "delta", "B", "C", "z"):
+            sub[k] = d[k][:, a:b].contiguous()
+        r = _fused(sub, conv_state=cs, h0=h)
+        ys.append(r["y"])
+        cs, h = r["conv_state"], r["h_last"]
+    y = torch.cat(ys, 1)
+    assert normwise_err(y.cpu().numpy(), one["y"].cpu().numpy()) <= 1e-6
+    assert normwise_err(h.cpu().numpy(), one["h_last"].cpu().numpy()) <= 1e-6
+    assert torch.equal(cs, one["conv_state"])
+
+
+def test_fused_empty_sequence():
+    d = to_dev(_case(2, 4, 64, 4, "bf16", seed=1))
+    e = {k: (v[:, :0].contiguous() if k in ("x", "delta", "B", "C", "z") else v) for k, v in d.items()}
+    cs0 = torch.randn(2, 64, 3, device="cuda")
+    h0 = torch.randn(2, 64, 16, device="cuda")
+    r = _fused(e, conv_state=cs0, h0=h0)
+    assert torch.equal(r["conv_state"], cs0) and torch.equal(r["h_last"], h0)
+
+
+def test_fused_full_size_sampled():
+    """Mamba-130M layer shape with a K = 4 convolution in front; sampled
+    channels of every batch row against the oracle composition."""
+    w = W.S6_MAMBA130M
+    inp = W.make_s6_inputs(w, seed=0)
+    cv = W.make_conv_inputs(W.CONV_MAMBA130M, seed=1)
+    inp.update(x=cv["x"], conv_w=cv["weight"], conv_b=cv["bias"])
+    r = _fused(to_dev(inp))
+    y = r["y"].float().cpu().numpy()
+    ds = np.array([0, 1, 63, 64, 700, 1535])
+    errs = []
+    for b in range(w.B):
+        xs = inp["x"][b:b + 1, :, ds]
+        u, _ = oracle.causal_conv1d_silu(xs, inp["conv_w"][ds], inp["conv_b"][ds])
+        yr, _ = oracle.s6_fwd(u, inp["delta"][b:b + 1, :, ds], inp["A"][ds], inp["B"][b:b + 1],
+                              inp["C"][b:b + 1], D=inp["D"][ds], z=inp["z"][b:b + 1, :, ds],
+                              delta_bias=inp["delta_bias"][ds])
+        errs.append(normwise_err(y[b:b + 1][:, :, ds], yr))
+    print(f"fused conv+scan {w.name}: sampled y err {max(errs):.3e}")
+    assert max(errs) <= 2e-2
