@@ -106,6 +106,22 @@ int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Variable-length batch: row b runs only its first seq_lens[b] tokens
+ * (seq_lens: device int32 [B], values clamped to [0, L]); y at positions
+ * t >= seq_lens[b] is left untouched and h_last is the state after the row's
+ * last token.  Sequences of different lengths share one launch with the
+ * layout [B, L, ...] right-padded to the longest.  Otherwise as
+ * ssm_selective_scan_fwd (same workspace query).
+ */
+int ssm_selective_scan_fwd_varlen(const void* u, const void* delta, const float* A,
+                                  const void* Bm, const void* Cm, const float* Dskip,
+                                  const void* z, const float* delta_bias, unsigned flags,
+                                  const float* h0, void* y, float* h_last,
+                                  const int32_t* seq_lens, int64_t B, int64_t L, int64_t D,
+                                  int64_t N, int dtype, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/*
  * Same operation, for measurement: `events` is NULL or points to 4 hipEvent_t
  * created by the caller; they are recorded on `stream` at the phase
  * boundaries -- before the segment reduce, before the carry scan, before the

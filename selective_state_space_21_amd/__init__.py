@@ -64,12 +64,15 @@ def selective_scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
                        delta_softplus: bool = True, zoh: bool = False,
                        h0: Optional[torch.Tensor] = None, return_last_state: bool = True,
                        out: Optional[torch.Tensor] = None,
-                       workspace: Optional[torch.Tensor] = None
+                       workspace: Optional[torch.Tensor] = None,
+                       seq_lens: Optional[torch.Tensor] = None
                        ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """S6 selective scan forward (ssm_selective_scan_fwd).
 
     u, delta, z: [Bt, L, Dm]; A: [Dm, N] fp32; B, C: [Bt, L, N] (dtype of u);
     D, delta_bias: [Dm] fp32; h0: [Bt, Dm, N] fp32.  Returns (y, h_last).
+    seq_lens: optional int32 [Bt] -- row b runs its first seq_lens[b] tokens
+    (ssm_selective_scan_fwd_varlen); later positions of y are left untouched.
     """
     lib = _native.load()
     if u.dtype not in _DT:
@@ -103,6 +106,16 @@ def selective_scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
         workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
     flags = (_native.FLAG_DELTA_SOFTPLUS if delta_softplus else 0) | (_native.FLAG_ZOH if zoh else 0)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if seq_lens is not None:
+        seq_lens = _dev_tensor("seq_lens", seq_lens, torch.int32, dev)
+        if tuple(seq_lens.shape) != (Bt,):
+            raise ValueError(f"seq_lens has shape {tuple(seq_lens.shape)}, expected {(Bt,)}")
+        rc = lib.ssm_selective_scan_fwd_varlen(
+            _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            flags, _ptr(h0), _ptr(y), _ptr(h_last), _ptr(seq_lens), Bt, L, Dm, N, _DT[dt],
+            _ptr(workspace), ws_bytes, _stream_handle(dev))
+        _native.check(rc, "ssm_selective_scan_fwd_varlen")
+        return y, h_last
     rc = lib.ssm_selective_scan_fwd(
         _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
         flags, _ptr(h0), _ptr(y), _ptr(h_last), Bt, L, Dm, N, _DT[dt],

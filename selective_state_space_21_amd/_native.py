@@ -36,6 +36,8 @@ SIGNATURES = {
     "ssm_selective_scan_segments": (_i, [_i64, _i64, _i64, _i64]),
     "ssm_selective_scan_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _u, _vp, _vp, _vp,
                                     _i64, _i64, _i64, _i64, _i, _vp, _sz, _vp]),
+    "ssm_selective_scan_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _u, _vp, _vp,
+                                           _vp, _vp, _i64, _i64, _i64, _i64, _i, _vp, _sz, _vp]),
     "ssm_selective_scan_fwd_timed": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _u, _vp, _vp, _vp,
                                           _i64, _i64, _i64, _i64, _i, _vp, _sz, _vp, _vp]),
     "ssm_selective_scan_conv_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp,

@@ -80,6 +80,15 @@ __device__ __forceinline__ void load_bc_row(const T* base, int64_t row, int N,
 // Exact zero-order hold: dB = (exp(dt*A) - 1) / A * B = dt*B * expm1(x)/x,
 // x = dt*A (the ZOH formula of the Transformer-math article's discretisation
 // section); expm1 keeps small x accurate.
+// Tokens of batch row b: the row's length when lengths are given (clamped to
+// [0, L]), else L.  Rows shorter than L leave their later positions of y
+// untouched and end (h_last) at their own last token.
+__device__ __forceinline__ int64_t row_len(const S6Args& p, int64_t b) {
+    if (!p.seq_lens) return p.L;
+    const int64_t n = p.seq_lens[b];
+    return n < 0 ? 0 : (n > p.L ? p.L : n);
+}
+
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Raw (storage-format) B or C row of one token: NM values, as 16-byte loads.
@@ -144,8 +153,9 @@ void s6_fast(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
     const uint32_t col = (uint32_t)(active ? d : p.D - 1);
     const int64_t D = p.D;
     const int64_t t0 = (int64_t)s * p.seg_len;
-    const int64_t t1 = t0 + p.seg_len < p.L ? t0 + p.seg_len : p.L;
-    const int nt = (int)(t1 - t0);                         // segment fits 32-bit offsets
+    const int64_t Lb = row_len(p, b);                      // this row's tokens
+    const int64_t t1 = t0 + p.seg_len < Lb ? t0 + p.seg_len : Lb;
+    const int nt = t1 > t0 ? (int)(t1 - t0) : 0;           // segment fits 32-bit offsets
     const int64_t row0 = (b * p.L + t0) * D;
     const uint32_t seg_bytes = (uint32_t)nt * (uint32_t)D * E;
     const uint32_t row_bytes = (uint32_t)D * E;
@@ -190,9 +200,11 @@ void s6_fast(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
             cw[k] = kk >= 0 ? p.conv_w[(int64_t)col * K + kk] : 0.0f;
         }
         cb = p.conv_b ? p.conv_b[col] : 0.0f;
+        // a segment past the row's end starts (and ends) at the row's last inputs
+        const int64_t ts = t0 < Lb ? t0 : Lb;
 #pragma unroll
         for (int i = 0; i < 3; ++i) {
-            const int64_t tt = t0 - 3 + i;
+            const int64_t tt = ts - 3 + i;
             const int slot = (int)tt + K - 1;           // index into the carried state
             if (tt >= 0)
                 xw[i] = Elem<T>::load(u_, (b * p.L + tt) * D + col);
@@ -366,7 +378,8 @@ __global__ __launch_bounds__(kWave) void s6_generic(S6Args p) {
         h[n] = h_in;
     }
     const int64_t t0 = (int64_t)s * p.seg_len;
-    const int64_t t1 = t0 + p.seg_len < p.L ? t0 + p.seg_len : p.L;
+    const int64_t Lb = row_len(p, b);
+    const int64_t t1 = t0 + p.seg_len < Lb ? t0 + p.seg_len : Lb;
     float dt_sum = 0.0f;
     for (int64_t t = t0; t < t1; ++t) {
         const int64_t i = (b * p.L + t) * p.D + dd;

@@ -25,6 +25,12 @@ int64_t mul3(int64_t a, int64_t b, int64_t c) {
     return ab * c;
 }
 
+int s6_fwd_impl(const void* u, const void* delta, const float* A, const void* Bm, const void* Cm,
+                const float* Dskip, const void* z, const float* delta_bias, unsigned flags,
+                const float* h0, void* y, float* h_last, const int32_t* seq_lens,
+                int64_t B, int64_t L, int64_t D, int64_t N, int dtype,
+                void* workspace, size_t workspace_bytes, void* stream, void* const* events);
+
 int s6_check_sizes(int64_t B, int64_t L, int64_t D, int64_t N, int dtype) {
     if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_BAD_DTYPE;
     if (B < 1 || D < 1 || N < 1 || L < 0) return SSM_ERR_BAD_SHAPE;
@@ -109,6 +115,19 @@ int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
                                         stream, nullptr);
 }
 
+int ssm_selective_scan_fwd_varlen(const void* u, const void* delta, const float* A,
+                                  const void* Bm, const void* Cm, const float* Dskip,
+                                  const void* z, const float* delta_bias, unsigned flags,
+                                  const float* h0, void* y, float* h_last,
+                                  const int32_t* seq_lens, int64_t B, int64_t L, int64_t D,
+                                  int64_t N, int dtype, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+    if (!seq_lens) return SSM_ERR_NULL_ARG;
+    if (!aligned(seq_lens, 4)) return SSM_ERR_MISALIGNED;
+    return s6_fwd_impl(u, delta, A, Bm, Cm, Dskip, z, delta_bias, flags, h0, y, h_last, seq_lens,
+                       B, L, D, N, dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
 int ssm_selective_scan_fwd_timed(const void* u, const void* delta, const float* A,
                                  const void* Bm, const void* Cm, const float* Dskip,
                                  const void* z, const float* delta_bias, unsigned flags,
@@ -116,6 +135,19 @@ int ssm_selective_scan_fwd_timed(const void* u, const void* delta, const float* 
                                  int64_t B, int64_t L, int64_t D, int64_t N, int dtype,
                                  void* workspace, size_t workspace_bytes, void* stream,
                                  void* const* events) {
+    return s6_fwd_impl(u, delta, A, Bm, Cm, Dskip, z, delta_bias, flags, h0, y, h_last, nullptr,
+                       B, L, D, N, dtype, workspace, workspace_bytes, stream, events);
+}
+
+}  // extern "C"
+
+namespace {
+
+int s6_fwd_impl(const void* u, const void* delta, const float* A, const void* Bm, const void* Cm,
+                const float* Dskip, const void* z, const float* delta_bias, unsigned flags,
+                const float* h0, void* y, float* h_last, const int32_t* seq_lens,
+                int64_t B, int64_t L, int64_t D, int64_t N, int dtype,
+                void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
     int rc = s6_check_sizes(B, L, D, N, dtype);
     if (rc != SSM_OK) return rc;
     if (flags & ~(unsigned)(SSM_FLAG_DELTA_SOFTPLUS | SSM_FLAG_ZOH)) return SSM_ERR_UNSUPPORTED;
@@ -138,6 +170,7 @@ int ssm_selective_scan_fwd_timed(const void* u, const void* delta, const float* 
     a.B = B; a.L = L; a.D = D; a.N = N;
     a.S = plan.S; a.seg_len = plan.seg_len; a.flags = flags; a.bf16 = dtype == SSM_BF16;
     a.events = reinterpret_cast<hipEvent_t const*>(events);
+    a.seq_lens = seq_lens;
     if (plan.S > 1) {
         a.seg_a = static_cast<float*>(workspace);
         a.seg_b = a.seg_a + B * D * (int64_t)plan.S * N;
@@ -145,6 +178,10 @@ int ssm_selective_scan_fwd_timed(const void* u, const void* delta, const float* 
     const hipError_t e = ssm::launch_s6(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
+
+}  // namespace
+
+extern "C" {
 
 int ssm_selective_scan_conv_fwd(const void* x, const float* conv_weight, const float* conv_bias,
                                 const float* conv_state_in, float* conv_state_out, int64_t K,

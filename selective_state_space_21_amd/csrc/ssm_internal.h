@@ -38,6 +38,7 @@ struct S6Args {
     float* conv_state_out;      // [B, D, conv_K - 1] or NULL
     void* u_out;                // [B, L, D] or NULL: the convolution's output u
     int64_t conv_K;
+    const int32_t* seq_lens;    // [B] tokens per batch row (device), or NULL: all L
 };
 
 struct S6Plan {

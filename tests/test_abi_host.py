@@ -215,6 +215,18 @@ def test_conv_scan_validation_errors(lib):
     assert conv_scan(lib, si=FAKE + 2) == 5
 
 
+def test_varlen_validation_errors(lib):
+    def call(sl, **kw):
+        a = dict(Bt=2, L=64, Dm=128, N=16, dtype=1)
+        a.update(kw)
+        return lib.ssm_selective_scan_fwd_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 1,
+                                                 None, FAKE, None, sl, a["Bt"], a["L"], a["Dm"],
+                                                 a["N"], a["dtype"], FAKE, 1 << 30, None)
+    assert call(None) == 1
+    assert call(FAKE + 2) == 5
+    assert call(FAKE, Bt=0) == 2
+
+
 def test_python_wrapper_rejects_host_tensors():
     import torch
     import selective_state_space_21_amd as ssm
