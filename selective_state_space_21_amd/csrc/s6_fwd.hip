@@ -17,8 +17,9 @@
 //
 // Two kernel bodies:
 //   s6_fast    -- N = 16, first-order input term.  Activations are prefetched
-//                 four tokens ahead through buffer loads with a uniform row
-//                 offset; the B/C rows of 16 tokens sit in lanes 0..15 of each
+//                 twelve tokens ahead (the gate four) through buffer loads
+//                 with a uniform row offset, kept as stored bits until their
+//                 token comes up; the B/C rows of 16 tokens sit in lanes 0..15 of each
 //                 16-lane row (one token per lane) and reach every lane through
 //                 DPP row broadcasts folded into the multiplies, so no scalar
 //                 load waits inside the token loop.
@@ -30,10 +31,10 @@
 // costs at inference").  Three launches:
 //   1. s6_segment_reduce: each segment but the last reduces to the affine pair
 //      (decay = exp(A * sum dt), offset = its end state from h = 0);
-//   2. s6_carry_scan:    a wavefront-level inclusive scan of those pairs with
-//      the composition (a1,b1) then (a2,b2) = (a2 a1, a2 b1 + b2) (section 3
-//      of the temporalbook chapter), one lane per segment, giving each
-//      segment's incoming state;
+//   2. s6_carry_scan:    folds those pairs in segment order with the
+//      composition (a1,b1) then (a2,b2) = (a2 a1, a2 b1 + b2) (section 3 of
+//      the temporalbook chapter), one lane per (b, d, n) and 64 of them per
+//      wavefront, giving each segment's incoming state;
 //   3. s6_segment_scan:  every segment reruns from its incoming state, writes
 //      y, and the last one writes h_last.
 // With S = 1 only launch 3 runs.
@@ -42,6 +43,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "device_math.h"
@@ -52,6 +54,10 @@ namespace ssm {
 namespace {
 
 constexpr int kWave = 64;
+// s6_fast workgroups hold four independent wavefronts (256 channels): the
+// dispatcher then places one on each SIMD of a CU, where single-wavefront
+// workgroups were seen to pile up unevenly on the SIMDs.
+constexpr int kFastBlock = 4 * kWave;
 
 // Row t of B (or C) for batch row b: NM floats, zero past N (zero-padded
 // states keep h = 0 and add exact zeros to y).
@@ -124,10 +130,32 @@ __device__ __forceinline__ void unpack_row(const RawRow<T, NM>& r, float (&out)[
 }
 
 // ------------------------------------------------------------------ fast path
+// Per-token inputs of U consecutive tokens as loaded (storage bits): they are
+// widened to fp32 only where they are used, so that a load still in flight
+// stalls nothing until its own token comes up.
 template <int U>
 struct TokBlock {
-    float u[U], d[U], z[U];
+    uint32_t u[U], d[U];
 };
+template <int U>
+struct GateBlock {
+    uint32_t z[U];
+};
+
+template <typename T>
+__device__ __forceinline__ uint32_t load_bits(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                              uint32_t soff) {
+    if constexpr (sizeof(T) == 2)
+        return __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+    else
+        return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ float widen(uint32_t bits) {
+    if constexpr (sizeof(T) == 2) return __uint_as_float(bits << 16);
+    else return __uint_as_float(bits);
+}
 
 // One pass over segment s of the 64 channels of this wavefront, N = 16.
 //   SCAN = false: reduce the segment to (decay, end state from zero);
@@ -138,7 +166,7 @@ struct TokBlock {
 // The tensors come in as __restrict__ arguments so that the compiler knows
 // the y stores cannot alias the inputs.
 template <typename T, bool SCAN, bool HAS_Z, bool RAGGED, bool SOFTPLUS, bool CONV>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(kFastBlock) __attribute__((amdgpu_waves_per_eu(3)))
 void s6_fast(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
              const T* __restrict__ z_, const T* __restrict__ Bm_, const T* __restrict__ Cm_,
              T* __restrict__ y_) {
@@ -146,7 +174,11 @@ void s6_fast(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
     constexpr int U = 4;        // tokens per prefetch block
     constexpr int G = 16;       // tokens per B/C tile group (one per lane of a row)
     constexpr uint32_t E = sizeof(T);
-    const int64_t d = (int64_t)blockIdx.x * kWave + threadIdx.x;
+    // a wavefront whose channels all lie past D has nothing to do
+    const int64_t wave0 = (int64_t)blockIdx.x * kFastBlock +
+                          kWave * (int64_t)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    if (wave0 >= p.D) return;
+    const int64_t d = (int64_t)blockIdx.x * kFastBlock + threadIdx.x;
     const int64_t b = blockIdx.y;
     const int s = blockIdx.z;
     const bool active = d < p.D;
@@ -174,7 +206,7 @@ void s6_fast(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
 
     float A2[NS], h[NS];
     const int64_t hb = (b * D + col) * NS;
-    const int64_t sb = ((b * D + col) * p.S + s) * NS;
+    const int64_t sb = (int64_t)s * (p.B * D * NS) + hb;    // segment-major pairs
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
         A2[n] = p.A[(int64_t)col * NS + n] * kLog2e;
@@ -242,25 +274,44 @@ void s6_fast(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             const uint32_t soff = (uint32_t)min(jb + j, nt - 1) * row_bytes;
-            k.u[j] = Buf<T>::load(ru, voff, soff);
-            k.d[j] = Buf<T>::load(rd, voff, soff);
-            if constexpr (HAS_Z) k.z[j] = Buf<T>::load(rz, voff, soff);
+            k.u[j] = load_bits<T>(ru, voff, soff);
+            k.d[j] = load_bits<T>(rd, voff, soff);
+        }
+    };
+    // the gate is needed last in a token and is requested one block ahead
+    auto load_gate = [&](GateBlock<U>& g, int jb) {
+        if constexpr (HAS_Z) {
+#pragma unroll
+            for (int j = 0; j < U; ++j)
+                g.z[j] = load_bits<T>(rz, voff, (uint32_t)min(jb + j, nt - 1) * row_bytes);
         }
     };
     // q: which quarter of the tile group (lanes 4q .. 4q+3) holds these tokens
-    auto run_block = [&](const TokBlock<U>& k, int jb, auto guard, int q) {
+    // The step sizes of a block's tokens are formed first, as independent
+    // chains, then the state updates run token by token.
+    auto run_block = [&](const TokBlock<U>& k, const GateBlock<U>& g, int jb, auto guard, int q) {
+        constexpr bool kGuard = decltype(guard)::value;
+        float dtv[U], utv[U], dtu[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            if constexpr (kGuard) {
+                if (jb + j >= nt) break;
+            }
+            const float x = widen<T>(k.d[j]) + bias;
+            if constexpr (SOFTPLUS) dtv[j] = softplus_f(x); else dtv[j] = x;
+            utv[j] = input_u(widen<T>(k.u[j]));
+            dtu[j] = dtv[j] * utv[j];
+            if constexpr (!SCAN) dt_sum += dtv[j];
+        }
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             const int r = jb + j;
-            if constexpr (decltype(guard)::value) {
+            if constexpr (kGuard) {
                 if (r >= nt) break;
             }
-            const float x = k.d[j] + bias;
-            float dt;
-            if constexpr (SOFTPLUS) dt = softplus_f(x); else dt = x;
-            const float ut = input_u(k.u[j]);
-            const float dtu = dt * ut;
+            const float dt = dtv[j];
             if constexpr (SCAN) {
+                const float ut = utv[j];
                 if constexpr (CONV) {
                     if (p.u_out && (!RAGGED || active)) Buf<T>::store(ruo, voff, (uint32_t)r * row_bytes, ut);
                 }
@@ -268,18 +319,17 @@ void s6_fast(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
 #pragma unroll
                 for (int n = 0; n < NS; ++n) {
                     const float dA = fast_exp2(dt * A2[n]);
-                    h[n] = fmaf(dA, h[n], row_bcast(btile[n], 4 * q + j) * dtu);
+                    h[n] = fmaf(dA, h[n], row_bcast(btile[n], 4 * q + j) * dtu[j]);
                     acc = fmaf(row_bcast(ctile[n], 4 * q + j), h[n], acc);
                 }
                 acc = fmaf(dsk, ut, acc);
-                if constexpr (HAS_Z) acc *= silu_f(k.z[j]);
+                if constexpr (HAS_Z) acc *= silu_f(widen<T>(g.z[j]));
                 if (!RAGGED || active) Buf<T>::store(ry, voff, (uint32_t)r * row_bytes, acc);
             } else {
-                dt_sum += dt;
 #pragma unroll
                 for (int n = 0; n < NS; ++n) {
                     const float dA = fast_exp2(dt * A2[n]);
-                    h[n] = fmaf(dA, h[n], row_bcast(btile[n], 4 * q + j) * dtu);
+                    h[n] = fmaf(dA, h[n], row_bcast(btile[n], 4 * q + j) * dtu[j]);
                 }
             }
         }
@@ -287,34 +337,57 @@ void s6_fast(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
 
     using Full = std::false_type;
     using Tail = std::true_type;
-    TokBlock<U> ka, kb;
+    // Four rotating blocks: the block three ahead (12 tokens) is requested
+    // before a block is run, the B/C rows one 16-token group ahead.
+    TokBlock<U> k0, k1, k2, k3;
+    GateBlock<U> g0, g1;
     int jb = 0;
     load_tiles(0);
-    load_block(ka, 0);
+    load_block(k0, 0);
+    load_block(k1, 4);
+    load_block(k2, 8);
+    load_gate(g0, 0);
     unpack_tiles();
-    while (jb + G <= nt) {
+    // The scheduling fences keep each refill after the last use of the
+    // registers it refills, so that no loop-carried copy of a value still in
+    // flight (and no wait for it) is needed at the back edge.
+    // Written as a bottom-tested loop: the exit then sits at the latch and
+    // the loop-carried registers need no renaming copies.
+    const int groups = nt / G;
+    if (groups > 0) do {
         load_tiles(jb + G);
-        load_block(kb, jb + 4);
-        run_block(ka, jb, Full{}, 0);
-        load_block(ka, jb + 8);
-        run_block(kb, jb + 4, Full{}, 1);
-        load_block(kb, jb + 12);
-        run_block(ka, jb + 8, Full{}, 2);
-        load_block(ka, jb + 16);
-        run_block(kb, jb + 12, Full{}, 3);
+        load_block(k3, jb + 12);
+        load_gate(g1, jb + 4);
+        run_block(k0, g0, jb, Full{}, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_block(k0, jb + 16);
+        load_gate(g0, jb + 8);
+        run_block(k1, g1, jb + 4, Full{}, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_block(k1, jb + 20);
+        load_gate(g1, jb + 12);
+        run_block(k2, g0, jb + 8, Full{}, 2);
+        __builtin_amdgcn_sched_barrier(0);
+        load_block(k2, jb + 24);
+        load_gate(g0, jb + 16);
+        run_block(k3, g1, jb + 12, Full{}, 3);
+        __builtin_amdgcn_sched_barrier(0);
         unpack_tiles();
         jb += G;
-    }
+    } while (jb < groups * G);
     if (jb < nt) {                       // fewer than 16 tokens left
-        load_block(kb, jb + 4);
-        run_block(ka, jb, Tail{}, 0);
+        load_gate(g1, jb + 4);
+        run_block(k0, g0, jb, Tail{}, 0);
         if (jb + 4 < nt) {
-            load_block(ka, jb + 8);
-            run_block(kb, jb + 4, Tail{}, 1);
+            load_gate(g0, jb + 8);
+            run_block(k1, g1, jb + 4, Tail{}, 1);
             if (jb + 8 < nt) {
-                load_block(kb, jb + 12);
-                run_block(ka, jb + 8, Tail{}, 2);
-                if (jb + 12 < nt) run_block(kb, jb + 12, Tail{}, 3);
+                load_gate(g1, jb + 12);
+                run_block(k2, g0, jb + 8, Tail{}, 2);
+                if (jb + 12 < nt) {
+                    load_block(k3, jb + 12);
+                    run_block(k3, g1, jb + 12, Tail{}, 3);
+                }
             }
         }
     }
@@ -364,7 +437,7 @@ __global__ __launch_bounds__(kWave) void s6_generic(S6Args p) {
 
     float A1[NM], A2[NM], h[NM];
     const int64_t hb = (b * p.D + dd) * (int64_t)N;
-    const int64_t sb = ((b * p.D + dd) * p.S + s) * (int64_t)N;
+    const int64_t sb = (int64_t)s * (p.B * p.D * N) + hb;  // segment-major pairs
 #pragma unroll
     for (int n = 0; n < NM; ++n) {
         const float a = n < N ? p.A[dd * N + n] : 0.0f;
@@ -430,38 +503,37 @@ __global__ __launch_bounds__(kWave) void s6_generic(S6Args p) {
     }
 }
 
-// Wavefront-level scan over segments.  Lane j of a group of SP lanes (SP a
-// power of two >= S) holds segment j of one (b, d, n); after log2(SP) steps
-// of __shfl_up it holds the inclusive composition of segments 0..j.  The
-// incoming state of segment j is the exclusive one applied to h0; it
-// overwrites seg_b (each lane reads its pair before any lane writes).
-__global__ __launch_bounds__(256) void s6_carry_scan(S6Args p, int SP) {
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int j = (int)(gid % SP);
-    const int64_t bdn = gid / SP;
-    const int64_t total = p.B * p.D * p.N;
-    const bool valid = bdn < total;
-    const int64_t bd = valid ? bdn / p.N : 0;
-    const int n = valid ? (int)(bdn % p.N) : 0;
-    const int64_t o = (bd * p.S + j) * p.N + n;
-    float a = 1.0f, c = 0.0f;                     // identity map
-    if (valid && j < p.S - 1) {
-        a = p.seg_a[o];
-        c = p.seg_b[o];
-    }
-    for (int off = 1; off < SP; off <<= 1) {
-        const float ap = __shfl_up(a, off, SP);
-        const float cp = __shfl_up(c, off, SP);
-        if (j >= off) {                           // earlier segments first, then ours
-            c = fmaf(a, cp, c);
-            a = a * ap;
+// Carry over segments.  The pairs are stored segment-major, pair s of chain
+// i = (b*D + d)*N + n at s*B*D*N + i, so that for one segment a wavefront
+// reads 64 consecutive chains.  Each lane folds the pairs of its chain in
+// order, h <- a_s h + b_s starting from h0, and overwrites b_s with the state
+// entering segment s (the composition (a1,b1) then (a2,b2) = (a2 a1,
+// a2 b1 + b2) of section 3 of the temporalbook chapter, applied to h0).  With
+// at most 64 segments the fold is short; the pairs of up to eight segments are
+// loaded before any is used or overwritten.
+__global__ __launch_bounds__(256) void s6_carry_scan(const float* __restrict__ seg_a,
+                                                     float* __restrict__ seg_b,
+                                                     const float* __restrict__ h0,
+                                                     int64_t chains, int S) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= chains) return;
+    float h = h0 ? h0[i] : 0.0f;
+    constexpr int kBatch = 8;
+    for (int s0 = 0; s0 < S - 1; s0 += kBatch) {
+        float a[kBatch], c[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const bool in = s0 + k < S - 1;
+            a[k] = in ? seg_a[(int64_t)(s0 + k) * chains + i] : 1.0f;
+            c[k] = in ? seg_b[(int64_t)(s0 + k) * chains + i] : 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            if (s0 + k < S - 1) seg_b[(int64_t)(s0 + k) * chains + i] = h;
+            h = fmaf(a[k], h, c[k]);
         }
     }
-    const float h0 = (valid && p.h0) ? p.h0[bd * p.N + n] : 0.0f;
-    float ae = __shfl_up(a, 1, SP);
-    float ce = __shfl_up(c, 1, SP);
-    if (j == 0) { ae = 1.0f; ce = 0.0f; }
-    if (valid && j < p.S) p.seg_b[o] = fmaf(ae, h0, ce);
+    seg_b[(int64_t)(S - 1) * chains + i] = h;      // entering the last segment
 }
 
 // h_last = h0 (or zeros) for an empty sequence.
@@ -474,13 +546,11 @@ void mark(const S6Args& a, int i, hipStream_t stream) {
     if (a.events) (void)hipEventRecord(a.events[i], stream);
 }
 
-hipError_t launch_carry(const S6Args& a, hipStream_t stream) {
-    int SP = 1;
-    while (SP < a.S) SP <<= 1;
-    const int64_t threads = a.B * a.D * a.N * SP;
-    hipLaunchKernelGGL(s6_carry_scan, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                       stream, a, SP);
-    return hipSuccess;
+// launch errors surface through the caller's hipGetLastError
+void launch_carry(const S6Args& a, hipStream_t stream) {
+    const int64_t chains = a.B * a.D * a.N;
+    hipLaunchKernelGGL(s6_carry_scan, dim3((unsigned)((chains + 255) / 256)), dim3(256), 0,
+                       stream, a.seg_a, a.seg_b, a.h0, chains, (int)a.S);
 }
 
 template <typename T, bool SP, bool CV>
@@ -491,8 +561,8 @@ hipError_t launch_fast_sp(const S6Args& a, hipStream_t stream) {
     const T* Bp = static_cast<const T*>(a.Bm);
     const T* Cp = static_cast<const T*>(a.Cm);
     T* Y = static_cast<T*>(a.y);
-    const unsigned dblocks = (unsigned)((a.D + kWave - 1) / kWave);
-    const dim3 block(kWave);
+    const unsigned dblocks = (unsigned)((a.D + kFastBlock - 1) / kFastBlock);
+    const dim3 block(kFastBlock);
     mark(a, 0, stream);
     if (a.S > 1)
         hipLaunchKernelGGL((s6_fast<T, false, false, false, SP, CV>),
@@ -557,20 +627,43 @@ hipError_t launch_n(const S6Args& a, hipStream_t stream) {
     return launch_generic<T, 64, ZOH>(a, stream);
 }
 
+// SIMDs of the current device (four per CU), read once per device.
+int64_t simd_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    const int slot = dev < 64 ? dev : 63;
+    int cus = cached[slot].load(std::memory_order_relaxed);
+    if (cus <= 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        cached[slot].store(cus, std::memory_order_relaxed);
+    }
+    return 4 * (int64_t)cus;
+}
+
 }  // namespace
 S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N) {
     S6Plan pl{1, L > 0 ? L : 1, 0};
     if (L <= 0) return pl;
-    // About three wavefronts per SIMD (256 CUs x 4 SIMDs).
+    // Wavefronts per segment.  With at least one per SIMD the sequence is not
+    // split (a split adds a second pass over the tokens); otherwise the
+    // segment count is the smallest that gives every SIMD at least three
+    // wavefronts and all SIMDs the same number (a whole multiple of the SIMD
+    // count), else the one nearest three per SIMD.
     const int64_t waves = B * ((D + kWave - 1) / kWave);
-    int64_t target = 3072;
-    int64_t S = (target + waves - 1) / waves;
-    const char* env = getenv("SSM_S6_SEGMENTS");
-    if (env && atoi(env) > 0) S = atoi(env);
+    const int64_t simds = simd_count();
     const int64_t min_seg = 32;
     int64_t maxS = (L + min_seg - 1) / min_seg;
+    if (maxS > 64) maxS = 64;
+    int64_t S = waves >= simds ? 1 : 0;
+    for (int64_t c = 1; c <= maxS && S == 0; ++c)
+        if (waves * c >= 3 * simds && (waves * c) % simds == 0) S = c;
+    if (S == 0) S = (3 * simds + waves - 1) / waves;
+    const char* env = getenv("SSM_S6_SEGMENTS");
+    if (env && atoi(env) > 0) S = atoi(env);
     if (S > maxS) S = maxS;
-    if (S > 64) S = 64;
     if (S < 1) S = 1;
     int64_t seg_len = (L + S - 1) / S;
     // the kernels address one segment through 32-bit buffer offsets
