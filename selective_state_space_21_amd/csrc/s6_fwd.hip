@@ -19,10 +19,12 @@
 //   s6_fast    -- N = 16, first-order input term.  Activations are prefetched
 //                 twelve tokens ahead (the gate four) through buffer loads
 //                 with a uniform row offset, kept as stored bits until their
-//                 token comes up; the B/C rows of 16 tokens sit in lanes 0..15 of each
-//                 16-lane row (one token per lane) and reach every lane through
-//                 DPP row broadcasts folded into the multiplies, so no scalar
-//                 load waits inside the token loop.
+//                 token comes up.  The B/C rows of the next 16 tokens are
+//                 loaded one token per lane (lanes 0..15 of each 16-lane
+//                 row); the reduce broadcasts B from there with DPP row
+//                 broadcasts folded into the multiplies, the scan stages B and
+//                 C in LDS and reads each token's rows as broadcasts.  No
+//                 scalar load waits inside the token loop.
 //   s6_generic -- any N <= 64 and the ZOH variant: plain token loop with
 //                 wavefront-uniform scalar loads of B/C.
 //
@@ -259,16 +261,40 @@ void s6_fast(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
     };
 
     // B/C tiles: fp32 rows of the current 16-token group, raw rows of the next.
-    float btile[NS], ctile[SCAN ? NS : 1];
+    float btile[SCAN ? 1 : NS];
     RawRow<T, NS> rawB, rawC;
+    // The scan keeps the B and C rows of the current 16-token group in LDS,
+    // one 1 KiB slice each per wavefront ([token][state], fp32): every lane
+    // reads the rows of the token at hand with the same address (a
+    // broadcast), so neither the input term nor the readout needs a
+    // cross-lane move, and no registers hold the group's rows.  Only this
+    // wavefront touches its slices, and its LDS accesses are performed in
+    // program order, so no barrier is needed.  The reduce keeps B in
+    // registers and broadcasts it with DPP, folded into the multiply.
+    __shared__ float4 cshare[SCAN ? (kFastBlock / kWave) * G * (NS / 4) : 1];
+    float4* const cslice = cshare + (SCAN ? (threadIdx.x / kWave) * G * (NS / 4) : 0);
+    __shared__ float4 bshare[SCAN ? (kFastBlock / kWave) * G * (NS / 4) : 1];
+    float4* const bslice = bshare + (SCAN ? (threadIdx.x / kWave) * G * (NS / 4) : 0);
+    const bool c_writer = (threadIdx.x & (kWave - 1)) < (uint32_t)G;
     auto load_tiles = [&](int jb) {
         const uint32_t off = (uint32_t)min(jb + (int)lane16, nt - 1) * bc_row;
         load_raw_row<T, NS>(rawB, rB, off, 0);
         if constexpr (SCAN) load_raw_row<T, NS>(rawC, rC, off, 0);
     };
     auto unpack_tiles = [&]() {
-        unpack_row<T, NS>(rawB, btile);
-        if constexpr (SCAN) unpack_row<T, NS>(rawC, ctile);
+        if constexpr (!SCAN) unpack_row<T, NS>(rawB, btile);
+        if constexpr (SCAN) {
+            float c[NS], bb[NS];
+            unpack_row<T, NS>(rawC, c);
+            unpack_row<T, NS>(rawB, bb);
+            if (c_writer) {
+#pragma unroll
+                for (int k = 0; k < NS / 4; ++k) {
+                    cslice[lane16 * (NS / 4) + k] = make_float4(c[4 * k], c[4 * k + 1], c[4 * k + 2], c[4 * k + 3]);
+                    bslice[lane16 * (NS / 4) + k] = make_float4(bb[4 * k], bb[4 * k + 1], bb[4 * k + 2], bb[4 * k + 3]);
+                }
+            }
+        }
     };
     auto load_block = [&](TokBlock<U>& k, int jb) {
 #pragma unroll
@@ -315,12 +341,20 @@ void s6_fast(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
                 if constexpr (CONV) {
                     if (p.u_out && (!RAGGED || active)) Buf<T>::store(ruo, voff, (uint32_t)r * row_bytes, ut);
                 }
+                float ct[NS], bt[NS];
+#pragma unroll
+                for (int k = 0; k < NS / 4; ++k) {
+                    const float4 v = cslice[(4 * q + j) * (NS / 4) + k];
+                    ct[4 * k] = v.x; ct[4 * k + 1] = v.y; ct[4 * k + 2] = v.z; ct[4 * k + 3] = v.w;
+                    const float4 w = bslice[(4 * q + j) * (NS / 4) + k];
+                    bt[4 * k] = w.x; bt[4 * k + 1] = w.y; bt[4 * k + 2] = w.z; bt[4 * k + 3] = w.w;
+                }
                 float acc = 0.0f;
 #pragma unroll
                 for (int n = 0; n < NS; ++n) {
                     const float dA = fast_exp2(dt * A2[n]);
-                    h[n] = fmaf(dA, h[n], row_bcast(btile[n], 4 * q + j) * dtu[j]);
-                    acc = fmaf(row_bcast(ctile[n], 4 * q + j), h[n], acc);
+                    h[n] = fmaf(dA, h[n], bt[n] * dtu[j]);
+                    acc = fmaf(ct[n], h[n], acc);
                 }
                 acc = fmaf(dsk, ut, acc);
                 if constexpr (HAS_Z) acc *= silu_f(widen<T>(g.z[j]));
