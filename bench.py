@@ -46,7 +46,7 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3
 # (fetch x2.000, write x1.000); profiles/s6_scan_mamba130m_layer_bf16.md and
 # profiles/ssd_chunk_mamba2_bf16.md.  Valid for the kernels as profiled: to be
 # re-taken (or set to None) when those kernels change.
-S6_SCAN_TRAFFIC_BYTES = int((84538.5 * 2.0 + 49920.0) * 1024)
+S6_SCAN_TRAFFIC_BYTES = int((83273.4 * 2.0 + 49920.0) * 1024)
 SSD_CHUNK_TRAFFIC_BYTES = int((151673.2 * 2.0 + 270336.0) * 1024)
 
 
