@@ -12,7 +12,9 @@ timed interval) so that the 203 MB working set is not served from the 256 MB
 Infinity Cache.  Each step is bracketed by HIP events recorded by the library
 itself on the stream it launches on, at its phase boundaries (segment reduce,
 carry scan, segment scan); `value` is the algorithmic bytes of the step
-divided by the mean step time.
+divided by the mean step time.  The default 60 untimed warm-up steps bring the
+GPU to its steady clock first (the first ~40 calls of a cold process run up to
+~10% slower).
 
 The same run also measures, under "paths", the other calls of the library on
 their own workloads (each flushed and timed the same way): the SSD chunked
@@ -315,8 +317,10 @@ def cpu_baseline(r, torch, min_seconds=10.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the GPU reaches its steady clock after ~30-40 back-to-back calls
+    # (~15 ms): the first calls of a cold process run ~10% slower
+    ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ssd", action="store_true", help="skip every path but the S6 scan")
     ap.add_argument("--only", choices=["s6", "ssd", "decode", "bwd", "conv", "conv_scan"],
