@@ -172,17 +172,24 @@ def bench_ssd(args, torch, ssm, W):
     nbytes = W.ssd_algorithmic_bytes(s)
     Q = s.chunk
     nchunks = -(-s.L // Q)
-    # causal chunked-SSD MACs per (b, h, chunk): C B^T lower triangle (Q(Q+1)/2 * N),
-    # masked Y_diag (Q(Q+1)/2 * P), chunk state (P*N*Q), Y_off (Q*P*N)
+    # causal chunked-SSD MACs: the scores C B^T (lower triangle, Q(Q+1)/2 * N)
+    # once per (b, group, chunk), as they depend on the group only; per (b, h,
+    # chunk) the masked Y_diag (Q(Q+1)/2 * P), chunk state (P*N*Q) and Y_off
+    # (Q*P*N).  The kernel forms the scores per head, so it executes more.
     tri = Q * (Q + 1) / 2
-    macs = s.B * s.H * nchunks * (tri * s.N + tri * s.P + 2 * s.P * s.N * Q)
+    per_head = tri * s.P + 2 * s.P * s.N * Q
+    macs = s.B * nchunks * (s.G * tri * s.N + s.H * per_head)
+    macs_exec = s.B * nchunks * s.H * (tri * s.N + per_head)
     return dict(status="ok", workload=s.name, ms=round(ms, 5),
                 gbs=round(nbytes / (ms * 1e-3) / 1e9, 2),
                 pct_hbm_peak=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS * 100, 2),
                 tflops=round(2 * macs / (ms * 1e-3) / 1e12, 2),
                 mfma_util=round(2 * macs / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                 gtokch=round(s.tok_ch / (ms * 1e-3) / 1e9, 3), algorithmic_bytes=nbytes,
-                causal_gflop=round(2 * macs / 1e9, 3), hbm_traffic_bytes=SSD_CHUNK_TRAFFIC_BYTES)
+                causal_gflop=round(2 * macs / 1e9, 3),
+                executed_gflop=round(2 * macs_exec / 1e9, 3),
+                executed_tflops=round(2 * macs_exec / (ms * 1e-3) / 1e12, 2),
+                hbm_traffic_bytes=SSD_CHUNK_TRAFFIC_BYTES)
 
 
 def _time_flushed(torch, fn, steps, warmup):
