@@ -251,7 +251,9 @@ __global__ __launch_bounds__(kThreads) void s6_bwd_ckpt(S6BwdArgs p) {
         for (int i = 0; i < kSuper; ++i)
             bt[i][(threadIdx.x % 16) * kPitch + threadIdx.x / 16] = Bits<T>::f32(cur.b[i]);
         __syncthreads();
-        if (sg + 1 < nsup) nxt.load(p, id, rr, (sg + 1) * kSuper * kTile, rB);   // travels meanwhile
+        // travels meanwhile; issued unconditionally (past the end it reads
+        // zeros) so that no branch join makes the compiler wait for it here
+        nxt.load(p, id, rr, (sg + 1) * kSuper * kTile, rB);
 #pragma unroll
         for (int i = 0; i < kSuper; ++i) {
             const int64_t k = sg * kSuper + i;
@@ -319,12 +321,15 @@ void s6_bwd_main(S6BwdArgs p) {
         bct[0][(threadIdx.x % 16) * kPitch + threadIdx.x / 16] = Bits<T>::f32(bpre);
         bct[1][(threadIdx.x % 16) * kPitch + threadIdx.x / 16] = Bits<T>::f32(cpre);
         __syncthreads();
-        if (k > 0) {                       // previous tile's inputs travel during this one
-            raw.load(p, id, rr, t0 - kTile);
-            bpre = load_bc_bits<T>(p, t0 - kTile, rB);
-            cpre = load_bc_bits<T>(p, t0 - kTile, rC);
-            hck = ck[(k - 1) * p.N];
-        }
+        // The previous tile's inputs travel during this one.  The loads are
+        // unconditional (for k = 0 the buffer loads fall before the row and
+        // read zeros, the checkpoint load repeats tile 0): a branch around
+        // them would join the loaded and the old values, and the compiler
+        // waits for the loads at that join, in the tile that issues them.
+        raw.load(p, id, rr, t0 - kTile);
+        bpre = load_bc_bits<T>(p, t0 - kTile, rB);
+        cpre = load_bc_bits<T>(p, t0 - kTile, rC);
+        hck = ck[(k > 0 ? k - 1 : 0) * p.N];
         // states of the tile, recomputed from its checkpoint
         float hs[kTile], da[kTile];
         {
