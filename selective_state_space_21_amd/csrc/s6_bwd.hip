@@ -283,6 +283,11 @@ template <typename T, bool HAS_Z, bool SOFTPLUS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void s6_bwd_main(S6BwdArgs p) {
     __shared__ float red[2][kWaves][kTile][16];     // [dB|dC][wave][token][n]
+    // du, ddelta, dz of the tile as stored ([output][token][channel]): written
+    // per lane, then stored as 16-byte rows pieces, so that one store covers
+    // a run of the workgroup's channels instead of one 2-byte element
+    constexpr int kOut = HAS_Z ? 3 : 2;
+    __shared__ __attribute__((aligned(16))) T outst[kOut][kTile][kChans];
     __shared__ __attribute__((aligned(16))) float bct[2][16 * kPitch];   // B, C: [n][token]
     const LaneId id = lane_id(p);
     const float an = id.ok ? p.A[id.dc * p.N + id.n] : 0.0f;
@@ -380,19 +385,19 @@ void s6_bwd_main(S6BwdArgs p) {
         const float r_ddt = row_reduce_scatter(pt, id.n);
         const float r_su = row_reduce_scatter(pu, id.n);
         const float r_y = row_reduce_scatter(py, id.n);
-        // per-channel results of token t0 + j in lane j
+        // per-channel results of token t0 + j in lane j, staged in LDS
         {
             const int64_t t = t0 + id.n;
+            const int cl = 4 * id.w + id.row;                  // channel in the workgroup
+            const float r = r_y + dsk * s.u;
+            const float dd = r_ddt * s.sig;
+            Elem<T>::store(&outst[0][id.n][0], cl, fmaf(s.g, dsk, s.dt * r_su));
+            Elem<T>::store(&outst[1][id.n][0], cl, dd);
+            if constexpr (HAS_Z) {
+                const float sz = sigmoid_f(s.z);
+                Elem<T>::store(&outst[2][id.n][0], cl, s.dy * r * (sz * fmaf(s.z, 1.0f - sz, 1.0f)));
+            }
             if (id.chan_ok && t < p.L) {
-                const int64_t i = (id.b * p.L + t) * p.D + id.d;
-                const float r = r_y + dsk * s.u;
-                if constexpr (HAS_Z) {
-                    const float sz = sigmoid_f(s.z);
-                    Elem<T>::store(dz_out, i, s.dy * r * (sz * fmaf(s.z, 1.0f - sz, 1.0f)));
-                }
-                Elem<T>::store(du_out, i, fmaf(s.g, dsk, s.dt * r_su));
-                const float dd = r_ddt * s.sig;
-                Elem<T>::store(dd_out, i, dd);
                 db_acc += dd;
                 dD_acc = fmaf(s.g, s.u, dD_acc);
             }
@@ -404,6 +409,24 @@ void s6_bwd_main(S6BwdArgs p) {
         }
         __syncthreads();
         {
+            // the staged rows: thread -> (output, token, 16-byte piece)
+            constexpr int kPieces = kChans * (int)sizeof(T) / 16;
+            const int64_t d0 = (int64_t)blockIdx.x * kChans;
+            const bool vec = d0 + kChans <= p.D && (p.D * (int64_t)sizeof(T)) % 16 == 0;
+            for (int e = threadIdx.x; e < kOut * kTile * kPieces; e += kThreads) {
+                const int o = e / (kTile * kPieces), j = (e / kPieces) % kTile, pc = e % kPieces;
+                const int64_t t = t0 + j;
+                if (t >= p.L) continue;
+                constexpr int kPer = 16 / (int)sizeof(T);           // elements per piece
+                T* dst = (o == 0 ? du_out : o == 1 ? dd_out : dz_out) + (id.b * p.L + t) * p.D + d0 + pc * kPer;
+                const T* src = &outst[o][j][pc * kPer];
+                if (vec) {
+                    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+                } else {
+                    for (int c = 0; c < kPer; ++c)
+                        if (d0 + pc * kPer + c < p.D) dst[c] = src[c];
+                }
+            }
             // thread -> (q, token, n) for half of them; sum over the wavefronts
             for (int e = threadIdx.x; e < 2 * kTile * 16; e += kThreads) {
                 const int q = e / (kTile * 16), j = (e / 16) % kTile, n = e % 16;
