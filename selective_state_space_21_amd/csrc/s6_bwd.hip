@@ -48,7 +48,7 @@ constexpr int kTile = 16;              // tokens per tile = per checkpoint
 
 struct LaneId {
     int w, l, row, n;
-    int64_t b, d, dc;      // dc: d clamped into range for addressing
+    int64_t b, grp, d, dc; // grp: channel group; dc: d clamped into range for addressing
     bool chan_ok, ok;      // channel exists; channel and state exist
 };
 
@@ -59,8 +59,17 @@ __device__ __forceinline__ LaneId lane_id(const S6BwdArgs& p) {
     id.l = tid % 64;
     id.row = id.l / 16;
     id.n = id.l % 16;
-    id.b = blockIdx.y;
-    id.d = (int64_t)blockIdx.x * kChans + 4 * id.w + id.row;
+    // Workgroups are dealt to the 8 XCDs round robin (i -> XCD i % 8).  A
+    // workgroup's 16 channels are a quarter of a 128-byte row of u, delta, z
+    // and dy (bf16), so the id is renumbered to give each XCD a contiguous
+    // range of channel groups: the four that share a row then fetch it into
+    // one L2 instead of four.
+    const uint32_t n = gridDim.x * gridDim.y, i = blockIdx.x + gridDim.x * blockIdx.y;
+    const uint32_t x = i % 8, q = n / 8, r = n % 8;
+    const uint32_t lid = x * q + min(x, r) + i / 8;
+    id.b = lid / gridDim.x;
+    id.grp = lid % gridDim.x;
+    id.d = (int64_t)id.grp * kChans + 4 * id.w + id.row;
     id.chan_ok = id.d < p.D;
     id.dc = id.chan_ok ? id.d : p.D - 1;
     id.ok = id.chan_ok && id.n < p.N;
@@ -411,7 +420,7 @@ void s6_bwd_main(S6BwdArgs p) {
         {
             // the staged rows: thread -> (output, token, 16-byte piece)
             constexpr int kPieces = kChans * (int)sizeof(T) / 16;
-            const int64_t d0 = (int64_t)blockIdx.x * kChans;
+            const int64_t d0 = id.grp * kChans;
             const bool vec = d0 + kChans <= p.D && (p.D * (int64_t)sizeof(T)) % 16 == 0;
             for (int e = threadIdx.x; e < kOut * kTile * kPieces; e += kThreads) {
                 const int o = e / (kTile * kPieces), j = (e / kPieces) % kTile, pc = e % kPieces;
@@ -435,7 +444,7 @@ void s6_bwd_main(S6BwdArgs p) {
                 for (int w = 0; w < kWaves; ++w) v += red[q][w][j][n];
                 const int64_t t = t0 + j;
                 if (t < p.L && n < p.N)
-                    p.part_bc[(((int64_t)q * G + blockIdx.x) * p.B + id.b) * p.L * p.N + t * p.N + n] = v;
+                    p.part_bc[(((int64_t)q * G + id.grp) * p.B + id.b) * p.L * p.N + t * p.N + n] = v;
             }
         }
     }

@@ -67,6 +67,7 @@ int s6_bwd_check_sizes(int64_t B, int64_t L, int64_t D, int64_t N, int dtype) {
     const int64_t G = (D + 15) / 16;
     if (G > 0x7fffffffLL || 2 * B * L * N + D * N + D > (int64_t)0x7fffffff * 256)
         return SSM_ERR_UNSUPPORTED;
+    if (G * B > 0xffffffffLL) return SSM_ERR_UNSUPPORTED;   // workgroup ids are 32-bit
     if (mul3(2 * G, B * L, N) < 0) return SSM_ERR_BAD_SHAPE;
     if ((L + 16) * N * esize(dtype) >= (int64_t)0x80000000LL) return SSM_ERR_UNSUPPORTED;  // B/C row offsets
     if ((L + 16) * D * esize(dtype) >= (int64_t)0x80000000LL) return SSM_ERR_UNSUPPORTED;  // activation row offsets
