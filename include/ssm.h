@@ -86,9 +86,12 @@ const char* ssm_status_string(int status);
  *   h0             : [B, D, N]  fp32 or NULL (zeros)
  *   h_last         : [B, D, N]  fp32 or NULL; receives the state after t = L-1
  *   1 <= N <= 64; B, D >= 1; L >= 0.
- * Long sequences are split into segments scanned in parallel; each segment's
- * (decay, offset) pair is carried by a wavefront-level scan.  The workspace
- * holds those pairs; the query is a pure function of the sizes.
+ * Long sequences are split into segments scanned in parallel; the segments'
+ * (decay, offset) pairs are carried by a wavefront-level scan in which each
+ * lane composes the pairs of one (b, d, n) chain in segment order.  The
+ * workspace holds those pairs.  The query depends on the sizes and on the
+ * CU count of the current device (the segment count balances wavefronts over
+ * its SIMDs): query and call on the same device.
  */
 size_t ssm_selective_scan_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
                                           int dtype);
