@@ -98,7 +98,7 @@ size_t ssm_selective_scan_workspace_bytes(int64_t B, int64_t L, int64_t D, int64
 
 /* Number of sequence segments the planner uses for these sizes (1 = one pass,
  * no carry); 0 for invalid sizes.  The environment variable SSM_S6_SEGMENTS
- * (1..64) overrides the choice, for both this query and the call. */
+ * (1..256) overrides the choice, for both this query and the call. */
 int ssm_selective_scan_segments(int64_t B, int64_t L, int64_t D, int64_t N);
 
 int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A,

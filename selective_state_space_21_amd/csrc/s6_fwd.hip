@@ -60,6 +60,7 @@ constexpr int kWave = 64;
 // dispatcher then places one on each SIMD of a CU, where single-wavefront
 // workgroups were seen to pile up unevenly on the SIMDs.
 constexpr int kFastBlock = 4 * kWave;
+constexpr int64_t kMaxSegments = 256;    // segments per sequence (each >= 32 tokens)
 
 // Row t of B (or C) for batch row b: NM floats, zero past N (zero-padded
 // states keep h = 0 and add exact zeros to y).
@@ -690,7 +691,7 @@ S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N) {
     const int64_t simds = simd_count();
     const int64_t min_seg = 32;
     int64_t maxS = (L + min_seg - 1) / min_seg;
-    if (maxS > 64) maxS = 64;
+    if (maxS > kMaxSegments) maxS = kMaxSegments;
     int64_t S = waves >= simds ? 1 : 0;
     for (int64_t c = 1; c <= maxS && S == 0; ++c)
         if (waves * c >= 3 * simds && (waves * c) % simds == 0) S = c;
@@ -701,7 +702,7 @@ S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N) {
     if (S < 1) S = 1;
     int64_t seg_len = (L + S - 1) / S;
     // the kernels address one segment through 32-bit buffer offsets
-    while (seg_len * D * 4 > (int64_t)0xFFFFFFFF && S < 64) {
+    while (seg_len * D * 4 > (int64_t)0xFFFFFFFF && S < kMaxSegments) {
         ++S;
         seg_len = (L + S - 1) / S;
     }

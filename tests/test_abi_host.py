@@ -78,9 +78,9 @@ def test_s6_workspace_and_plan(lib):
     # one segment when there are plenty of channels
     assert lib.ssm_selective_scan_segments(64, 2048, 4096, 16) == 1
     assert lib.ssm_selective_scan_workspace_bytes(64, 2048, 4096, 16, 1) == 0
-    # few channels, long sequence: split up to 64 segments
+    # few channels, long sequence: split into up to 256 segments
     S = lib.ssm_selective_scan_segments(1, 131072, 2048, 16)
-    assert 2 <= S <= 64
+    assert 2 <= S <= 256
     assert lib.ssm_selective_scan_workspace_bytes(1, 131072, 2048, 16, 0) == 2 * 4 * 2048 * 16 * S
     # never more segments than ceil(L / 32)
     assert lib.ssm_selective_scan_segments(1, 40, 64, 16) <= 2
@@ -92,7 +92,7 @@ def test_s6_plan_env_override(lib, monkeypatch):
     monkeypatch.setenv("SSM_S6_SEGMENTS", "7")
     assert lib.ssm_selective_scan_segments(1, 7000, 64, 16) == 7
     monkeypatch.setenv("SSM_S6_SEGMENTS", "500")
-    assert lib.ssm_selective_scan_segments(1, 70000, 64, 16) == 64
+    assert lib.ssm_selective_scan_segments(1, 70000, 64, 16) == 256
 
 
 def ssd(lib, **kw):

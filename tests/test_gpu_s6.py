@@ -52,6 +52,16 @@ def test_every_segment_count(S, monkeypatch):
     _cmp(inp)
 
 
+@pytest.mark.parametrize("S", [96, 200, 256])
+def test_more_than_64_segments(S, monkeypatch):
+    # the segment carry folds up to 256 (decay, offset) pairs per chain
+    monkeypatch.setenv("SSM_S6_SEGMENTS", str(S))
+    w = W.S6_LONG_FP32.scaled(L=9000, D=64)
+    inp = W.make_s6_inputs(w, seed=3)
+    assert ssm.selective_scan_segments(w.B, w.L, w.D, w.N) == min(S, math.ceil(9000 / math.ceil(9000 / S)))
+    _cmp(inp)
+
+
 @pytest.mark.parametrize("N", [1, 3, 4, 5, 8, 15, 16, 17, 32, 33, 64])
 def test_state_sizes(N):
     w = W.S6_SMALL_FP32.scaled(B=2, L=300, D=70, N=N)
