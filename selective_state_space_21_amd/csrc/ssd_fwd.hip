@@ -68,6 +68,13 @@ template <int Q, int N>
 struct SsdLds {
     static constexpr int kBStride = N + 8;       // bf16 per B row (16-byte pad)
     static constexpr int kXStride = Q + 8;       // bf16 per X^T row
+    // X^T rows are swizzled by 32-token blocks: element (p, s) sits in column
+    // s ^ 32 * ((p / 16) % KX).  The staging writes put eight rows 8 apart in
+    // one instruction; unswizzled those rows start on two LDS banks only (a
+    // 4-way conflict), swizzled they spread over four.  The product reads take
+    // 32-token blocks of one row range, which the swizzle only renumbers.
+    static constexpr int KX = Q / 32 < 4 ? Q / 32 : 4;
+    static __device__ __forceinline__ int xcol(int p, int s) { return s ^ (32 * ((p / 16) % KX)); }
     static constexpr int kHStride = N + 8;       // bf16 per state row
     alignas(16) float dt[Q];                      // step per token
     alignas(16) float cum[Q];                     // inclusive sum of dt*A*log2(e)
@@ -102,8 +109,9 @@ struct Tiles {
 
 // 4 tokens x 8 head-dim values (bf16 pairs xs[token][pair]) -> rows 8 p8 .. 8 p8 + 7
 // of a transposed [p][s] tile, columns 4 sg .. 4 sg + 3: eight 8-byte writes
-template <int XSTRIDE>
+template <typename Lds>
 __device__ __forceinline__ void stage_xt_rows(__bf16* xt, int sg, int p8, const uint32_t (&xs)[4][4]) {
+    constexpr int XSTRIDE = Lds::kXStride;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         u32x2 even, odd;       // values 2m and 2m+1 of the group, tokens 0..3
@@ -111,9 +119,10 @@ __device__ __forceinline__ void stage_xt_rows(__bf16* xt, int sg, int p8, const 
         even.y = __builtin_amdgcn_perm(xs[3][m], xs[2][m], 0x05040100u);
         odd.x = __builtin_amdgcn_perm(xs[1][m], xs[0][m], 0x07060302u);
         odd.y = __builtin_amdgcn_perm(xs[3][m], xs[2][m], 0x07060302u);
-        const int pp = 8 * p8 + 2 * m;
-        *reinterpret_cast<u32x2*>(&xt[pp * XSTRIDE + 4 * sg]) = even;
-        *reinterpret_cast<u32x2*>(&xt[(pp + 1) * XSTRIDE + 4 * sg]) = odd;
+        const int pp = 8 * p8 + 2 * m;                  // pp and pp + 1 share the swizzle
+        const int col = Lds::xcol(pp, 4 * sg);
+        *reinterpret_cast<u32x2*>(&xt[pp * XSTRIDE + col]) = even;
+        *reinterpret_cast<u32x2*>(&xt[(pp + 1) * XSTRIDE + col]) = odd;
     }
 }
 
@@ -140,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
     using Lds = SsdLds<Q, N>;
     __shared__ Lds sm;
     auto stage_xt = [](__bf16* xt, int sg, int p8, const uint32_t (&xs)[4][4]) {
-        stage_xt_rows<Lds::kXStride>(xt, sg, p8, xs);
+        stage_xt_rows<Lds>(xt, sg, p8, xs);
     };
 
     const int tid = threadIdx.x;
@@ -349,7 +358,8 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
                 for (int r = 0; r < 4; ++r) yv[r] = yacc[j][r];
                 if (p.Dskip) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) yv[r] += dsk * f32(sm.Xt[(p0 + r) * Lds::kXStride + tl]);
+                    for (int r = 0; r < 4; ++r)
+                        yv[r] += dsk * f32(sm.Xt[(p0 + r) * Lds::kXStride + Lds::xcol(p0 + r, tl)]);
                 }
                 if constexpr (HAS_Z) {
                     const u32x2 zz = *reinterpret_cast<const u32x2*>(Zg + o);
@@ -442,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
                 }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const __bf16* xr = &sm.Xt[(16 * j + c) * Lds::kXStride + 32 * sb + 4 * g];
+                    const __bf16* xr = &sm.Xt[(16 * j + c) * Lds::kXStride + Lds::xcol(16 * j + c, 32 * sb + 4 * g)];
                     const bf16x4 lo = *reinterpret_cast<const bf16x4*>(xr);
                     const bf16x4 hi = *reinterpret_cast<const bf16x4*>(xr + 16);
                     const bf16x8 xop = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -480,7 +490,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const bf16x8 xa = *reinterpret_cast<const bf16x8*>(
-                        &sm.XWt[(16 * j + c) * Lds::kXStride + s8]);
+                        &sm.XWt[(16 * j + c) * Lds::kXStride + Lds::xcol(16 * j + c, s8)]);
                     hacc[j] = mfma(xa, bcol, hacc[j]);
                 }
             }
