@@ -49,7 +49,7 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3
 # profiles/ssd_chunk_mamba2_bf16.md.  Valid for the kernels as profiled: to be
 # re-taken (or set to None) when those kernels change.
 S6_SCAN_TRAFFIC_BYTES = int((83273.4 * 2.0 + 49920.0) * 1024)
-SSD_CHUNK_TRAFFIC_BYTES = int((151672.4 * 2.0 + 270336.0) * 1024)
+SSD_CHUNK_TRAFFIC_BYTES = int((151674.5 * 2.0 + 270336.0) * 1024)
 
 
 def _hip():
