@@ -48,6 +48,7 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3
 # (fetch x2.000, write x1.000); profiles/s6_scan_mamba130m_layer_bf16.md and
 # profiles/ssd_chunk_mamba2_bf16.md.  Valid for the kernels as profiled: to be
 # re-taken (or set to None) when those kernels change.
+S6_LANES_TRAFFIC_BYTES = None
 S6_SCAN_TRAFFIC_BYTES = int((83273.4 * 2.0 + 49920.0) * 1024)
 SSD_CHUNK_TRAFFIC_BYTES = int((151674.5 * 2.0 + 270336.0) * 1024)
 
@@ -58,6 +59,7 @@ def _hip():
     lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                         ctypes.c_void_p]
     lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     return lib
 
 
@@ -85,7 +87,8 @@ def bench_s6(args, torch, ssm, W, native, hip):
     h_last = torch.empty((w.B, w.D, w.N), dtype=torch.float32, device=dev)
     ws_bytes = ssm.selective_scan_workspace_bytes(w.B, w.L, w.D, w.N, torch.bfloat16)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    segments = ssm.selective_scan_segments(w.B, w.L, w.D, w.N)
+    lanes = ssm.selective_scan_lanes(w.B, w.L, w.D, w.N)
+    segments = 1 if lanes else ssm.selective_scan_segments(w.B, w.L, w.D, w.N)
     flush = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
     lib = native.load()
     stream = torch.cuda.current_stream(dev)
@@ -104,19 +107,27 @@ def bench_s6(args, torch, ssm, W, native, hip):
         flush.fill_(float(i))
         step(None)
     torch.cuda.synchronize()
-    phases = [0.0, 0.0, 0.0]
+    # the call as a whole, between two events on its stream
     total = 0.0
     wall0 = time.perf_counter()
     for i in range(args.steps):
         flush.fill_(float(i))                      # evict the Infinity Cache (untimed)
-        step(evs)
+        hip.hipEventRecord(evs[0], stream.cuda_stream)
+        step(None)
+        hip.hipEventRecord(evs[1], stream.cuda_stream)
         torch.cuda.synchronize()
-        p = [_elapsed(hip, evs[k], evs[k + 1]) for k in range(3)]
-        for k in range(3):
-            phases[k] += p[k]
-        total += _elapsed(hip, evs[0], evs[3])
+        total += _elapsed(hip, evs[0], evs[1])
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    # the split path's phases (the library records an event at each boundary;
+    # a recorded event costs a few microseconds, so this loop is kept apart)
+    phases = [0.0, 0.0, 0.0]
+    for i in range(args.steps):
+        flush.fill_(float(i))
+        step(evs)
+        torch.cuda.synchronize()
+        for k in range(3):
+            phases[k] += _elapsed(hip, evs[k], evs[k + 1])
     # back-to-back steps without the flush (working set may sit in the MALL)
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -128,14 +139,17 @@ def bench_s6(args, torch, ssm, W, native, hip):
     nbytes = W.s6_algorithmic_bytes(w)
     gbs = nbytes / (ms * 1e-3) / 1e9
     elems = w.B * w.L * w.D * w.N
-    scan_ms = phases[2] / args.steps
+    # the state-per-lane call is one kernel: its time is the call's
+    scan_ms = ms if lanes else phases[2] / args.steps
     reduce_ms = phases[0] / args.steps
     carry_ms = phases[1] / args.steps
     scan_gbs = nbytes / (scan_ms * 1e-3) / 1e9
     flops = 6.0 * elems                            # mul, mul, fma, fma per state update
     return dict(
-        w=w, t=t, ms=ms, gbs=gbs, nbytes=nbytes, segments=segments, wall=wall, hot_ms=hot_ms,
-        phases_ms=dict(segment_reduce=reduce_ms, carry_scan=carry_ms, segment_scan=scan_ms),
+        w=w, t=t, ms=ms, gbs=gbs, nbytes=nbytes, segments=segments, lanes=lanes, wall=wall,
+        hot_ms=hot_ms,
+        phases_ms=(dict(state_per_lane=scan_ms) if lanes else
+                   dict(segment_reduce=reduce_ms, carry_scan=carry_ms, segment_scan=scan_ms)),
         scan_gbs=scan_gbs, scan_tflops=flops / (scan_ms * 1e-3) / 1e12,
         gtokch=w.tok_ch / (ms * 1e-3) / 1e9, elems=elems)
 
@@ -386,7 +400,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": w.name, "B": w.B, "L": w.L, "D": w.D, "N": w.N,
-            "io_dtype": "bf16", "state_dtype": "f32", "segments": r["segments"],
+            "io_dtype": "bf16", "state_dtype": "f32",
+            "path": "state_per_lane" if r["lanes"] else "split", "segments": r["segments"],
             "pct_of_hbm_peak": round(r["gbs"] / HBM_PEAK_GBS * 100, 2),
             "gtoken_channels_per_s": round(r["gtokch"], 3),
             "algorithmic_bytes": r["nbytes"],
@@ -394,13 +409,14 @@ def main():
             "ms_per_step_without_cache_flush": round(r["hot_ms"], 5),
         },
         "roofline": {
-            "kernel": "s6_fast segment scan (dominant phase)",
+            "kernel": ("s6_lanes (state per lane, the only kernel of the call)" if r["lanes"]
+                       else "s6_fast segment scan (dominant phase)"),
             "bound": "hbm",
             "achieved": round(r["scan_gbs"], 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(r["scan_gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": S6_SCAN_TRAFFIC_BYTES,
+            "traffic": S6_LANES_TRAFFIC_BYTES if r["lanes"] else S6_SCAN_TRAFFIC_BYTES,
             "alu_view": {"achieved_tflops": round(r["scan_tflops"], 3),
                          "peak_tflops": FP32_VECTOR_PEAK_TFLOPS,
                          "flops_per_state_update": 6, "transcendentals_per_state_update": 1},

@@ -86,12 +86,19 @@ const char* ssm_status_string(int status);
  *   h0             : [B, D, N]  fp32 or NULL (zeros)
  *   h_last         : [B, D, N]  fp32 or NULL; receives the state after t = L-1
  *   1 <= N <= 64; B, D >= 1; L >= 0.
- * Long sequences are split into segments scanned in parallel; the segments'
- * (decay, offset) pairs are carried by a wavefront-level scan in which each
- * lane composes the pairs of one (b, d, n) chain in segment order.  The
- * workspace holds those pairs.  The query depends on the sizes and on the
- * CU count of the current device (the segment count balances wavefronts over
- * its SIMDs): query and call on the same device.
+ * Two execution paths, chosen from the sizes:
+ *   - state per lane (N = 16, D a multiple of 16, B*D/4 wavefronts at least
+ *     two per SIMD; see ssm_selective_scan_lanes): one lane per (channel,
+ *     state), the whole sequence in one pass, no workspace used;
+ *   - split: one lane per channel; long sequences are split into segments
+ *     scanned in parallel, and the segments' (decay, offset) pairs are carried
+ *     by a wavefront-level scan in which each lane composes the pairs of one
+ *     (b, d, n) chain in segment order.  The workspace holds those pairs.
+ * The workspace query returns the split path's size (calls with a fused
+ * convolution or SSM_FLAG_ZOH take that path at any size).  It depends on
+ * the sizes and on the CU count of the current device (the segment count and
+ * the path balance wavefronts over its SIMDs): query and call on the same
+ * device.
  */
 size_t ssm_selective_scan_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
                                           int dtype);
@@ -100,6 +107,14 @@ size_t ssm_selective_scan_workspace_bytes(int64_t B, int64_t L, int64_t D, int64
  * no carry); 0 for invalid sizes.  The environment variable SSM_S6_SEGMENTS
  * (1..256) overrides the choice, for both this query and the call. */
 int ssm_selective_scan_segments(int64_t B, int64_t L, int64_t D, int64_t N);
+
+/* 1 if a forward call at these sizes without a fused convolution and without
+ * SSM_FLAG_ZOH runs the state-per-lane kernel (unsplit: the segment count
+ * above then applies only to the other calls), else 0 (also for invalid
+ * sizes).  The environment variable SSM_S6_LANES=0 turns that kernel off,
+ * SSM_S6_LANES=1 takes it whenever N = 16, D is a multiple of 16 and the
+ * offsets fit, for both this query and the call. */
+int ssm_selective_scan_lanes(int64_t B, int64_t L, int64_t D, int64_t N);
 
 int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
                            const void* Bm, const void* Cm, const float* Dskip,

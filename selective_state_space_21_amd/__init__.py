@@ -16,7 +16,7 @@ from ._native import SSMError
 __all__ = ["selective_scan_fwd", "selective_scan_conv_fwd", "selective_scan_bwd", "ssd_chunk_fwd", "selective_state_update",
            "causal_conv1d_silu",
            "selective_scan_workspace_bytes",
-           "selective_scan_segments", "ssd_chunk_workspace_bytes", "SSMError"]
+           "selective_scan_segments", "selective_scan_lanes", "ssd_chunk_workspace_bytes", "SSMError"]
 
 _DT = {torch.float32: _native.SSM_F32, torch.bfloat16: _native.SSM_BF16}
 
@@ -51,6 +51,12 @@ def selective_scan_workspace_bytes(B: int, L: int, D: int, N: int, dtype=torch.b
 
 def selective_scan_segments(B: int, L: int, D: int, N: int) -> int:
     return int(_native.load().ssm_selective_scan_segments(B, L, D, N))
+
+
+def selective_scan_lanes(B: int, L: int, D: int, N: int) -> bool:
+    """True if a forward call at these sizes (no fused conv, no ZOH) runs the
+    state-per-lane kernel, unsplit."""
+    return bool(_native.load().ssm_selective_scan_lanes(B, L, D, N))
 
 
 def ssd_chunk_workspace_bytes(B, L, H, P, G, N, chunk, dtype=torch.bfloat16) -> int:

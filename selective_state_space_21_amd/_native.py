@@ -34,6 +34,7 @@ SIGNATURES = {
     "ssm_status_string": (ctypes.c_char_p, [_i]),
     "ssm_selective_scan_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i]),
     "ssm_selective_scan_segments": (_i, [_i64, _i64, _i64, _i64]),
+    "ssm_selective_scan_lanes": (_i, [_i64, _i64, _i64, _i64]),
     "ssm_selective_scan_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _u, _vp, _vp, _vp,
                                     _i64, _i64, _i64, _i64, _i, _vp, _sz, _vp]),
     "ssm_selective_scan_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _u, _vp, _vp,

@@ -76,12 +76,6 @@ __device__ __forceinline__ LaneId lane_id(const S6BwdArgs& p) {
     return id;
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-        0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
-}
-
 // sum over the 16 lanes of each row, result in every lane of the row
 __device__ __forceinline__ float row_sum(float v) {
     v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
@@ -89,25 +83,6 @@ __device__ __forceinline__ float row_sum(float v) {
     v += dpp_mov<0x124>(v);   // row_ror 4: quads q and q+1
     v += dpp_mov<0x128>(v);   // row_ror 8: all four quads
     return v;
-}
-
-// Reduce-scatter over the 16 lanes of each row: v[i] is this lane's term for
-// token i; the result in lane j is the row's sum for token j.  Four halving
-// exchanges (lane distance 8, 4, 2, 1): each lane keeps the half of its
-// tokens whose index bit matches its own lane bit, adding the partner's copy.
-__device__ __forceinline__ float row_reduce_scatter(const float (&v)[16], int j) {
-    const bool b3 = j & 8, b2 = j & 4, b1 = j & 2, b0 = j & 1;
-    float a[8], c[4], e[2];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        a[i] = (b3 ? v[i + 8] : v[i]) + dpp_mov<0x128>(b3 ? v[i] : v[i + 8]);   // row_ror 8 = xor 8
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        c[i] = (b2 ? a[i + 4] : a[i]) + lane_xor<4>(b2 ? a[i] : a[i + 4]);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-        e[i] = (b1 ? c[i + 2] : c[i]) + dpp_mov<0x4E>(b1 ? c[i] : c[i + 2]);  // quad xor 2
-    return (b0 ? e[1] : e[0]) + dpp_mov<0xB1>(b0 ? e[0] : e[1]);               // quad xor 1
 }
 
 __device__ __forceinline__ float sigmoid_f(float x) {
@@ -255,11 +230,11 @@ __global__ __launch_bounds__(kThreads) void s6_bwd_ckpt(S6BwdArgs p) {
     if (nsup > 0) nxt.load(p, id, rr, 0, rB);
     for (int64_t sg = 0; sg < nsup; ++sg) {
         const SuperRaw<T> cur = nxt;
-        __syncthreads();                    // previous super-tile's B reads done
+        lds_barrier();                    // previous super-tile's B reads done
 #pragma unroll
         for (int i = 0; i < kSuper; ++i)
             bt[i][(threadIdx.x % 16) * kPitch + threadIdx.x / 16] = Bits<T>::f32(cur.b[i]);
-        __syncthreads();
+        lds_barrier();
         // travels meanwhile; issued unconditionally (past the end it reads
         // zeros) so that no branch join makes the compiler wait for it here
         nxt.load(p, id, rr, (sg + 1) * kSuper * kTile, rB);
@@ -331,10 +306,10 @@ void s6_bwd_main(S6BwdArgs p) {
         const float hprev0 = id.ok ? hck : 0.0f;
         TileScalars<HAS_Z, SOFTPLUS, true> s;
         s.template from<T>(raw, p, id, t0, bias);
-        __syncthreads();                   // previous tile's LDS reads done
+        lds_barrier();                   // previous tile's LDS reads done
         bct[0][(threadIdx.x % 16) * kPitch + threadIdx.x / 16] = Bits<T>::f32(bpre);
         bct[1][(threadIdx.x % 16) * kPitch + threadIdx.x / 16] = Bits<T>::f32(cpre);
-        __syncthreads();
+        lds_barrier();
         // The previous tile's inputs travel during this one.  The loads are
         // unconditional (for k = 0 the buffer loads fall before the row and
         // read zeros, the checkpoint load repeats tile 0): a branch around
@@ -391,9 +366,9 @@ void s6_bwd_main(S6BwdArgs p) {
             const float v = (lowhalf ? pb : pc) + __shfl_xor(lowhalf ? pc : pb, 32, 64);
             wbc[j] = v + lane_xor<16>(v);
         }
-        const float r_ddt = row_reduce_scatter(pt, id.n);
-        const float r_su = row_reduce_scatter(pu, id.n);
-        const float r_y = row_reduce_scatter(py, id.n);
+        const float r_ddt = row_reduce_scatter16(pt, id.n);
+        const float r_su = row_reduce_scatter16(pu, id.n);
+        const float r_y = row_reduce_scatter16(py, id.n);
         // per-channel results of token t0 + j in lane j, staged in LDS
         {
             const int64_t t = t0 + id.n;
@@ -416,7 +391,7 @@ void s6_bwd_main(S6BwdArgs p) {
 #pragma unroll
             for (int j = 0; j < kTile; ++j) red[q][id.w][j][id.n] = wbc[j];
         }
-        __syncthreads();
+        lds_barrier();
         {
             // the staged rows: thread -> (output, token, 16-byte piece)
             constexpr int kPieces = kChans * (int)sizeof(T) / 16;

@@ -99,6 +99,7 @@ __device__ __forceinline__ int64_t row_len(const S6Args& p, int64_t b) {
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Raw (storage-format) B or C row of one token: NM values, as 16-byte loads.
 template <typename T, int NM>
@@ -449,6 +450,199 @@ void s6_fast(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
     }
 }
 
+// -------------------------------------------------------- state-per-lane path
+// N = 16, first-order input term, D a multiple of 16, no fused convolution.
+// One lane per (channel, state): each 16-lane row of a wavefront is one
+// channel and lane n holds its state n, so a workgroup of four wavefronts
+// covers 16 channels of one batch row.  With B*D/4 wavefronts the chip is
+// filled without splitting the sequence, so every decay factor is computed
+// once (the split path computes it in the segment reduce and again in the
+// segment scan) and there is no carry launch.
+//
+// The sequence is walked in super-tiles of 128 tokens.  Per super-tile the
+// workgroup loads u, delta, z (the 16 channels' 32-byte run of each token)
+// and the B and C rows as 16-byte pieces, one of each per thread, and stages
+// them in LDS: the activations as [channel][token], B and C as fp32
+// [tile][state][token].  A lane loading its own 2-byte element instead
+// touches 16 cache lines per instruction, which ran 1.7x slower.
+// Per 16-token tile, lane j of a row forms the per-channel scalars of token j
+// (step size, dt*u, skip, gate); the decay exp(dt*A) and input term dt*u*B of
+// each token reach the row through DPP row broadcasts folded into the
+// multiplies.  All 16 decay factors of a tile are formed before the state
+// chain h <- a*h + b runs through them.  The readout terms C*h of the tile are
+// summed over the row by a reduce-scatter that leaves token j's y in lane j,
+// which adds skip and gate and stages y in LDS; y leaves as 16-byte pieces of
+// the workgroup's channel run when the next super-tile starts.
+// The next super-tile's pieces are loaded while this one is computed.
+namespace lanes {
+constexpr int kTile = 16;                 // tokens per tile (one per lane of a row)
+constexpr int kSuper = 8;                 // tiles per super-tile
+constexpr int kSpan = kTile * kSuper;     // tokens per super-tile
+constexpr int kChans = 16;                // channels per workgroup
+constexpr int kPitch = kTile + 4;         // staged B/C row of one state (floats)
+
+template <typename T> __device__ __forceinline__ uint32_t elem_bits(T v);
+template <> __device__ __forceinline__ uint32_t elem_bits<uint16_t>(uint16_t v) { return v; }
+template <> __device__ __forceinline__ uint32_t elem_bits<float>(float v) { return __float_as_uint(v); }
+
+// One super-tile's inputs as loaded: 16-byte pieces, kPer per thread and tensor.
+template <typename T, bool HAS_Z>
+struct Pieces {
+    static constexpr int kPerToken = kChans * (int)sizeof(T) / 16;   // channels' run of a token
+    static constexpr int kPer = kSpan * kPerToken / 256;
+    u32x4 u[kPer], d[kPer], z[HAS_Z ? kPer : 1], b[kPer], c[kPer];
+};
+}  // namespace lanes
+
+template <typename T, bool HAS_Z, bool SOFTPLUS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
+              const T* __restrict__ z_, const T* __restrict__ Bm_, const T* __restrict__ Cm_,
+              T* __restrict__ y_) {
+    using namespace lanes;
+    using Raw = Pieces<T, HAS_Z>;
+    constexpr uint32_t E = sizeof(T);
+    constexpr int kPerToken = Raw::kPerToken, kPer = Raw::kPer;
+    constexpr int kVals = 16 / (int)E;                  // elements per piece
+    // activation rows padded so the four rows a wavefront reads start 8 banks apart
+    constexpr int kActPitch = kSpan + 2 * kVals;
+    __shared__ __attribute__((aligned(16))) float bct[2][kSuper][16 * kPitch];
+    __shared__ __attribute__((aligned(16))) T act[HAS_Z ? 3 : 2][kChans][kActPitch];
+    __shared__ __attribute__((aligned(16))) T yst[kSpan][kChans];
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, row = (tid >> 4) & 3, n = tid & 15;
+    // Workgroups are dealt to the 8 XCDs round robin (i -> XCD i % 8); the id
+    // is renumbered so each XCD runs a contiguous range of channel groups, and
+    // the four groups that share a 128-byte activation row share one L2.
+    const uint32_t groups = gridDim.x, total = gridDim.x * gridDim.y;
+    const uint32_t bi = blockIdx.x + gridDim.x * blockIdx.y;
+    const uint32_t xcd = bi % 8, per = total / 8, extra = total % 8;
+    const uint32_t lid = xcd * per + min(xcd, extra) + bi / 8;
+    const int64_t b = lid / groups;
+    const int64_t grp = lid % groups;
+    const int chan = 4 * w + row;
+    const int64_t D = p.D;
+    const int64_t d = grp * kChans + chan;
+    const int64_t Lb = row_len(p, b);
+    const float a2 = p.A[d * 16 + n] * kLog2e;
+    const float bias = p.delta_bias ? p.delta_bias[d] : 0.0f;
+    const float dsk = p.Dskip ? p.Dskip[d] : 0.0f;
+    float h = p.h0 ? p.h0[(b * D + d) * 16 + n] : 0.0f;
+    // buffer resources over this row's tokens: loads past the row's end read
+    // zero, stores there are dropped (the planner keeps offsets in 32 bits)
+    const int64_t rowoff = b * p.L * D;
+    const uint32_t act_bytes = (uint32_t)(Lb * D * E);
+    const auto ru = make_rsrc(u_ + rowoff, act_bytes);
+    const auto rd = make_rsrc(delta_ + rowoff, act_bytes);
+    const auto rz = make_rsrc(HAS_Z ? z_ + rowoff : nullptr, HAS_Z ? act_bytes : 0u);
+    const auto ry = make_rsrc(y_ + rowoff, act_bytes);
+    const uint32_t bc_bytes = (uint32_t)(Lb * 16 * E);
+    const auto rB = make_rsrc(Bm_ + b * p.L * 16, bc_bytes);
+    const auto rC = make_rsrc(Cm_ + b * p.L * 16, bc_bytes);
+    const uint32_t row_bytes = (uint32_t)(D * E);
+    const uint32_t grp_bytes = (uint32_t)(grp * kChans * E);
+
+    // thread -> (token idx / kPerToken, piece idx % kPerToken) of the super-tile
+    auto load = [&](Raw& r, int64_t st0) {
+        const uint32_t soff = (uint32_t)st0 * row_bytes;
+        const uint32_t bsoff = (uint32_t)st0 * (16 * E);
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const uint32_t idx = tid + 256 * k, t = idx / kPerToken, pc = idx % kPerToken;
+            const uint32_t voff = t * row_bytes + grp_bytes + 16 * pc;
+            r.u[k] = __builtin_amdgcn_raw_buffer_load_b128(ru, (int)voff, (int)soff, 0);
+            r.d[k] = __builtin_amdgcn_raw_buffer_load_b128(rd, (int)voff, (int)soff, 0);
+            if constexpr (HAS_Z)
+                r.z[k] = __builtin_amdgcn_raw_buffer_load_b128(rz, (int)voff, (int)soff, 0);
+            const uint32_t bvoff = t * (16 * E) + 16 * pc;
+            r.b[k] = __builtin_amdgcn_raw_buffer_load_b128(rB, (int)bvoff, (int)bsoff, 0);
+            r.c[k] = __builtin_amdgcn_raw_buffer_load_b128(rC, (int)bvoff, (int)bsoff, 0);
+        }
+    };
+    auto stage = [&](const Raw& r) {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int idx = tid + 256 * k, t = idx / kPerToken, pc = idx % kPerToken;
+            const T* vu = reinterpret_cast<const T*>(&r.u[k]);
+            const T* vd = reinterpret_cast<const T*>(&r.d[k]);
+            const T* vz = reinterpret_cast<const T*>(&r.z[k]);
+            const T* vb = reinterpret_cast<const T*>(&r.b[k]);
+            const T* vc = reinterpret_cast<const T*>(&r.c[k]);
+#pragma unroll
+            for (int e = 0; e < kVals; ++e) {
+                const int ch = kVals * pc + e;           // channel, or state for B/C
+                act[0][ch][t] = vu[e];
+                act[1][ch][t] = vd[e];
+                if constexpr (HAS_Z) act[2][ch][t] = vz[e];
+                bct[0][t / kTile][ch * kPitch + t % kTile] = widen<T>(elem_bits<T>(vb[e]));
+                bct[1][t / kTile][ch * kPitch + t % kTile] = widen<T>(elem_bits<T>(vc[e]));
+            }
+        }
+    };
+    constexpr int kPerY = kSpan * kPerToken / 256;
+    auto store_y = [&](int64_t st0) {
+#pragma unroll
+        for (int k = 0; k < kPerY; ++k) {
+            const uint32_t idx = tid + 256 * k, t = idx / kPerToken, pc = idx % kPerToken;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(
+                reinterpret_cast<const char*>(&yst[t][0]) + 16 * pc);
+            __builtin_amdgcn_raw_buffer_store_b128(v, ry, (int)(t * row_bytes + grp_bytes + 16 * pc),
+                                                   (int)((uint32_t)st0 * row_bytes), 0);
+        }
+    };
+
+    const int64_t nsup = (Lb + kSpan - 1) / kSpan;
+    Raw nxt;
+    if (nsup > 0) load(nxt, 0);
+    for (int64_t sg = 0; sg < nsup; ++sg) {
+        const Raw cur = nxt;
+        const int64_t st0 = sg * kSpan;
+        lds_barrier();                      // previous super-tile's LDS reads and y staging done
+        if (sg > 0) store_y(st0 - kSpan);
+        stage(cur);
+        lds_barrier();
+        load(nxt, st0 + kSpan);             // travels while this super-tile is computed
+#pragma unroll
+        for (int i = 0; i < kSuper; ++i) {
+            const int tl = kTile * i + n;   // this lane's token within the super-tile
+            const bool in = st0 + tl < Lb;  // past the row's end: dt = 0 leaves h unchanged
+            const float xr = widen<T>(elem_bits<T>(act[1][chan][tl])) + bias;
+            const float dt = in ? (SOFTPLUS ? softplus_f(xr) : xr) : 0.0f;
+            const float ut = widen<T>(elem_bits<T>(act[0][chan][tl]));
+            const float dtu = dt * ut;
+            float bv[kTile], cv[kTile], dA[kTile], pr[kTile];
+#pragma unroll
+            for (int q = 0; q < kTile / 4; ++q) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(&bct[0][i][n * kPitch + 4 * q]);
+                const f32x4 c = *reinterpret_cast<const f32x4*>(&bct[1][i][n * kPitch + 4 * q]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    bv[4 * q + r] = x[r];
+                    cv[4 * q + r] = c[r];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kTile; ++j) {
+                dA[j] = fast_exp2(row_bcast(dt, j) * a2);
+                bv[j] *= row_bcast(dtu, j);
+            }
+#pragma unroll
+            for (int j = 0; j < kTile; ++j) {
+                h = fmaf(dA[j], h, bv[j]);
+                pr[j] = cv[j] * h;
+            }
+            float yv = row_reduce_scatter16(pr, n);
+            yv = fmaf(dsk, ut, yv);
+            if constexpr (HAS_Z) yv *= silu_f(widen<T>(elem_bits<T>(act[2][chan][tl])));
+            if constexpr (sizeof(T) == 2) yst[tl][chan] = f32_to_bf16_bits(yv);
+            else yst[tl][chan] = yv;
+        }
+    }
+    lds_barrier();
+    if (nsup > 0) store_y((nsup - 1) * kSpan);
+    if (p.h_last) p.h_last[(b * D + d) * 16 + n] = h;
+}
+
 // --------------------------------------------------------------- generic path
 // Any N <= NM (states past N are zero-padded: A = 0, B = C = 0 keeps them at 0
 // and adds exact zeros to y) and the exact-ZOH input term.
@@ -628,7 +822,30 @@ hipError_t launch_fast_sp(const S6Args& a, hipStream_t stream) {
 }
 
 template <typename T>
+hipError_t launch_lanes(const S6Args& a, hipStream_t stream) {
+    const bool sp = (a.flags & SSM_FLAG_DELTA_SOFTPLUS) != 0;
+    const T* U = static_cast<const T*>(a.u);
+    const T* Dl = static_cast<const T*>(a.delta);
+    const T* Z = static_cast<const T*>(a.z);
+    const T* Bp = static_cast<const T*>(a.Bm);
+    const T* Cp = static_cast<const T*>(a.Cm);
+    T* Y = static_cast<T*>(a.y);
+    const dim3 grid((unsigned)(a.D / lanes::kChans), (unsigned)a.B), block(256);
+    for (int i = 0; i < 3; ++i) mark(a, i, stream);     // no reduce or carry phase
+    if (a.z) {
+        if (sp) hipLaunchKernelGGL((s6_lanes<T, true, true>), grid, block, 0, stream, a, U, Dl, Z, Bp, Cp, Y);
+        else hipLaunchKernelGGL((s6_lanes<T, true, false>), grid, block, 0, stream, a, U, Dl, Z, Bp, Cp, Y);
+    } else {
+        if (sp) hipLaunchKernelGGL((s6_lanes<T, false, true>), grid, block, 0, stream, a, U, Dl, Z, Bp, Cp, Y);
+        else hipLaunchKernelGGL((s6_lanes<T, false, false>), grid, block, 0, stream, a, U, Dl, Z, Bp, Cp, Y);
+    }
+    mark(a, 3, stream);
+    return hipGetLastError();
+}
+
+template <typename T>
 hipError_t launch_fast(const S6Args& a, hipStream_t stream) {
+    if (a.lanes && !a.conv_w) return launch_lanes<T>(a, stream);
     const bool sp = (a.flags & SSM_FLAG_DELTA_SOFTPLUS) != 0;
     if (a.conv_w)
         return sp ? launch_fast_sp<T, true, true>(a, stream) : launch_fast_sp<T, false, true>(a, stream);
@@ -680,8 +897,20 @@ int64_t simd_count() {
 
 }  // namespace
 S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N) {
-    S6Plan pl{1, L > 0 ? L : 1, 0};
+    S6Plan pl{1, L > 0 ? L : 1, 0, false};
     if (L <= 0) return pl;
+    // State-per-lane kernel: N = 16, D a multiple of 16, a batch row's
+    // activations (plus one super-tile) within 32-bit buffer offsets at 4
+    // bytes per element, and its B*D/4 wavefronts at least two per SIMD.
+    // SSM_S6_LANES=0 turns it off, =1 takes it whenever the shape allows.
+    {
+        const bool shape_ok = N == 16 && D % lanes::kChans == 0 &&
+                              (L + 2 * lanes::kSpan) * D * 4 <= (int64_t)0xFFFFFFFF;
+        pl.lanes = shape_ok && B * D / 4 >= 2 * simd_count();
+        const char* env = getenv("SSM_S6_LANES");
+        if (env && env[0] == '0') pl.lanes = false;
+        if (env && env[0] == '1') pl.lanes = shape_ok;
+    }
     // Wavefronts per segment.  With at least one per SIMD the sequence is not
     // split (a split adds a second pass over the tokens); otherwise the
     // segment count is the smallest that gives every SIMD at least three

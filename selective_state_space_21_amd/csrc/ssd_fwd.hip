@@ -37,6 +37,7 @@
 #include <type_traits>
 
 #include "device_math.h"
+#include "lane_ops.h"
 #include "ssm_internal.h"
 
 namespace ssm {
@@ -58,11 +59,8 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ __bf16 bf(float x) { return static_cast<__bf16>(x); }
 __device__ __forceinline__ float f32(__bf16 x) { return static_cast<float>(x); }
 
-// Workgroup barrier that waits for this wavefront's LDS traffic only: global
-// loads issued before it (the next chunk's prefetch) stay in flight.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
+// lds_barrier() (lane_ops.h) waits for this wavefront's LDS traffic only:
+// global loads issued before it (the next chunk's prefetch) stay in flight.
 
 template <int Q, int N>
 struct SsdLds {

@@ -99,6 +99,11 @@ int ssm_selective_scan_segments(int64_t B, int64_t L, int64_t D, int64_t N) {
     return ssm::plan_s6(B, L, D, N).S;
 }
 
+int ssm_selective_scan_lanes(int64_t B, int64_t L, int64_t D, int64_t N) {
+    if (s6_check_sizes(B, L, D, N, SSM_F32) != SSM_OK) return 0;
+    return ssm::plan_s6(B, L, D, N).lanes ? 1 : 0;
+}
+
 size_t ssm_selective_scan_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
                                           int dtype) {
     if (s6_check_sizes(B, L, D, N, dtype) != SSM_OK) return 0;
@@ -170,6 +175,7 @@ int s6_fwd_impl(const void* u, const void* delta, const float* A, const void* Bm
     a.delta_bias = delta_bias; a.h0 = h0; a.y = y; a.h_last = h_last;
     a.B = B; a.L = L; a.D = D; a.N = N;
     a.S = plan.S; a.seg_len = plan.seg_len; a.flags = flags; a.bf16 = dtype == SSM_BF16;
+    a.lanes = plan.lanes;
     a.events = reinterpret_cast<hipEvent_t const*>(events);
     a.seq_lens = seq_lens;
     if (plan.S > 1) {
@@ -216,6 +222,7 @@ int ssm_selective_scan_conv_fwd(const void* x, const float* conv_weight, const f
     a.delta_bias = delta_bias; a.h0 = h0; a.y = y; a.h_last = h_last;
     a.B = B; a.L = L; a.D = D; a.N = N;
     a.S = plan.S; a.seg_len = plan.seg_len; a.flags = flags; a.bf16 = dtype == SSM_BF16;
+    a.lanes = plan.lanes;
     a.conv_w = conv_weight; a.conv_b = conv_bias; a.conv_state_in = conv_state_in;
     a.conv_state_out = conv_state_out; a.u_out = u_out; a.conv_K = K;
     if (plan.S > 1) {

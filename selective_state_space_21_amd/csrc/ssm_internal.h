@@ -39,15 +39,17 @@ struct S6Args {
     void* u_out;                // [B, L, D] or NULL: the convolution's output u
     int64_t conv_K;
     const int32_t* seq_lens;    // [B] tokens per batch row (device), or NULL: all L
+    bool lanes;                 // state-per-lane kernel (unsplit) when no convolution is fused
 };
 
 struct S6Plan {
-    int S;
+    int S;                  // segments of the split path
     int64_t seg_len;
-    size_t workspace_bytes;
+    size_t workspace_bytes; // of the split path (also required when lanes is set)
+    bool lanes;             // a call without fused convolution or ZOH takes the state-per-lane kernel
 };
 
-// Deterministic in the sizes (plus the SSM_S6_SEGMENTS override).
+// Deterministic in the sizes (plus the SSM_S6_SEGMENTS / SSM_S6_LANES overrides).
 S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N);
 
 hipError_t launch_s6(const S6Args& a, hipStream_t stream);

@@ -95,6 +95,28 @@ def test_s6_plan_env_override(lib, monkeypatch):
     assert lib.ssm_selective_scan_segments(1, 70000, 64, 16) == 256
 
 
+def test_s6_lanes_plan(lib, monkeypatch):
+    # Without a GPU the planner assumes 256 CUs (1024 SIMDs): the state-per-lane
+    # kernel needs N = 16, D % 16 == 0 and B*D/4 >= 2048 wavefronts
+    monkeypatch.delenv("SSM_S6_LANES", raising=False)
+    assert lib.ssm_selective_scan_lanes(8, 2048, 1536, 16) == 1
+    assert lib.ssm_selective_scan_lanes(4, 4096, 5120, 16) == 1
+    assert lib.ssm_selective_scan_lanes(1, 131072, 2048, 16) == 0      # too few channels
+    assert lib.ssm_selective_scan_lanes(8, 2048, 1544, 16) == 0        # D % 16 != 0
+    assert lib.ssm_selective_scan_lanes(8, 2048, 1536, 32) == 0        # N != 16
+    assert lib.ssm_selective_scan_lanes(0, 2048, 1536, 16) == 0        # invalid sizes
+    # offsets of one batch row (plus a super-tile) must fit 32 bits at 4 B per element
+    assert lib.ssm_selective_scan_lanes(2, 2**20, 1024, 16) == 0
+    # the split plan (segments, workspace) is unchanged: other calls still use it
+    assert lib.ssm_selective_scan_segments(8, 2048, 1536, 16) > 1
+    monkeypatch.setenv("SSM_S6_LANES", "0")
+    assert lib.ssm_selective_scan_lanes(8, 2048, 1536, 16) == 0
+    monkeypatch.setenv("SSM_S6_LANES", "1")
+    assert lib.ssm_selective_scan_lanes(1, 40, 64, 16) == 1
+    assert lib.ssm_selective_scan_lanes(1, 40, 72, 16) == 0
+    assert lib.ssm_selective_scan_lanes(1, 40, 64, 8) == 0
+
+
 def ssd(lib, **kw):
     a = dict(X=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, flags=1,
              h0=None, Y=FAKE, h_last=None, Bt=1, L=256, H=8, P=64, G=1, N=128, chunk=256,

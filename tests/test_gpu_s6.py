@@ -213,8 +213,15 @@ def _sample_channels(w, per_b=24, seed=0):
     return out
 
 
+@pytest.mark.parametrize("path", ["planned", "split"])
 @pytest.mark.parametrize("w", [W.S6_MAMBA130M, W.S6_MAMBA2P8B, W.S6_LONG_FP32], ids=lambda w: w.name)
-def test_full_size_sampled(w):
+def test_full_size_sampled(w, path, monkeypatch):
+    # "planned": the layer shapes take the state-per-lane kernel, the long fp32
+    # shape the split path; "split": the split path forced at every shape
+    if path == "split":
+        monkeypatch.setenv("SSM_S6_LANES", "0")
+        if w is W.S6_LONG_FP32:
+            pytest.skip("the planned run already takes the split path")
     inp = W.make_s6_inputs(w, seed=0)
     y, h = s6_gpu(inp)
     y = y.float().cpu().numpy()
