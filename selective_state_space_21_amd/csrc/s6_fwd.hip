@@ -605,9 +605,13 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
 #pragma unroll
         for (int i = 0; i < kSuper; ++i) {
             const int tl = kTile * i + n;   // this lane's token within the super-tile
-            const bool in = st0 + tl < Lb;  // past the row's end: dt = 0 leaves h unchanged
+            // past the row's end dt = 0 leaves h unchanged; the step is formed
+            // unconditionally and masked, so no branch splits the super-tile
+            // into one basic block per tile (which kept the scheduler from
+            // overlapping a tile's exponentials with the previous tile's chain)
+            const uint32_t keep = st0 + tl < Lb ? 0xffffffffu : 0u;
             const float xr = widen<T>(elem_bits<T>(act[1][chan][tl])) + bias;
-            const float dt = in ? (SOFTPLUS ? softplus_f(xr) : xr) : 0.0f;
+            const float dt = __uint_as_float(__float_as_uint(SOFTPLUS ? softplus_f(xr) : xr) & keep);
             const float ut = widen<T>(elem_bits<T>(act[0][chan][tl]));
             const float dtu = dt * ut;
             float bv[kTile], cv[kTile], dA[kTile], pr[kTile];
