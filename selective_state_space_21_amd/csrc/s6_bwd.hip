@@ -162,6 +162,55 @@ struct TileScalars {
     }
 };
 
+// Activations of the workgroup's 16 channels, loaded cooperatively as 16-byte
+// pieces of each token's channel run (32 bytes in bf16, 64 in fp32) and
+// staged in LDS as [tensor][channel][token].  A lane loading its own 2-byte
+// element touches 16 cache lines per load instruction; a piece covers 8 (or
+// 4) channels of one token.  Used when D * sizeof(T) is a multiple of 16, so
+// that every piece is aligned; tokens outside [0, L) read as zero.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct Run {
+    static constexpr int kPerToken = kChans * (int)sizeof(T) / 16;   // pieces per token
+    static constexpr int kVals = 16 / (int)sizeof(T);                 // elements per piece
+};
+
+template <typename T>
+__device__ __forceinline__ uint32_t piece_off(const S6BwdArgs& p, int64_t grp, int64_t t, int pc) {
+    return (t < 0 || t >= p.L) ? 0xFFFFFFF0u
+                               : (uint32_t)((t * p.D + grp * kChans) * (int64_t)sizeof(T) + 16 * pc);
+}
+
+// Four consecutive channels of one token (8 bytes in bf16, 16 in fp32).
+template <typename T>
+__device__ __forceinline__ uint32_t quad_off(const S6BwdArgs& p, int64_t grp, int64_t t, int q) {
+    return (t < 0 || t >= p.L) ? 0xFFFFFFF0u
+                               : (uint32_t)((t * p.D + grp * kChans + 4 * q) * (int64_t)sizeof(T));
+}
+template <typename T> struct Quad;
+template <> struct Quad<uint16_t> {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 v = {0u, 0u};
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+    }
+    __device__ __forceinline__ uint16_t elem(int q) const {
+        return (uint16_t)(v[q >> 1] >> (16 * (q & 1)));
+    }
+};
+template <> struct Quad<float> {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+        v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    }
+    __device__ __forceinline__ float elem(int q) const { return __uint_as_float(v[q]); }
+};
+
+template <typename T> __device__ __forceinline__ uint32_t elem_bits(T v);
+template <> __device__ __forceinline__ uint32_t elem_bits<uint16_t>(uint16_t v) { return v; }
+template <> __device__ __forceinline__ uint32_t elem_bits<float>(float v) { return __float_as_uint(v); }
+
 // B or C [B, L, N] of a tile is shared by every channel of the workgroup:
 // thread (j, n) = (tid / 16, tid % 16) loads element (t0 + j, n) through a
 // buffer resource over batch row b (tokens past L and n >= N read as zero),
@@ -197,27 +246,47 @@ __device__ __forceinline__ uint32_t load_bc_bits(const S6BwdArgs& p, int64_t t0,
 // round trip covers 128 tokens of the sequential sweep.
 constexpr int kSuper = 8;
 
-template <typename T>
+template <typename T, bool VEC>
 struct SuperRaw {
-    uint32_t delta[kSuper], u[kSuper], b[kSuper];
+    // VEC: this lane's pieces of the super-tile (wave w: tensor w / 2, tokens
+    // 64 (w % 2) .. +63); otherwise its own element of every tile
+    u32x4 a[VEC ? Run<T>::kPerToken : 1];
+    uint32_t delta[VEC ? 1 : kSuper], u[VEC ? 1 : kSuper], b[kSuper];
     __device__ __forceinline__ void load(const S6BwdArgs& p, const LaneId& id, const RowRsrc& rr,
                                          int64_t t0, __amdgpu_buffer_rsrc_t rB) {
+        if constexpr (VEC) {
+            constexpr int kPT = Run<T>::kPerToken;
+            const int wu = __builtin_amdgcn_readfirstlane(id.w);
+            const __amdgpu_buffer_rsrc_t rs = (wu >> 1) == 0 ? rr.delta : rr.u;
+#pragma unroll
+            for (int i = 0; i < kPT; ++i) {
+                const int idx = id.l + 64 * i;
+                const int64_t t = t0 + 64 * (wu & 1) + idx / kPT;
+                a[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rs, (int)piece_off<T>(p, id.grp, t, idx % kPT), 0, 0);
+            }
+        }
 #pragma unroll
         for (int i = 0; i < kSuper; ++i) {
-            TileRaw<T, false, false> r;
-            r.load(p, id, rr, t0 + i * kTile);
-            delta[i] = r.delta;
-            u[i] = r.u;
+            if constexpr (!VEC) {
+                TileRaw<T, false, false> r;
+                r.load(p, id, rr, t0 + i * kTile);
+                delta[i] = r.delta;
+                u[i] = r.u;
+            }
             b[i] = load_bc_bits<T>(p, t0 + i * kTile, rB);
         }
     }
 };
 
-template <typename T, bool SOFTPLUS>
+template <typename T, bool SOFTPLUS, bool VEC>
 __global__ __launch_bounds__(kThreads) void s6_bwd_ckpt(S6BwdArgs p) {
     static_assert(kThreads == kTile * 16, "one tile element per thread");
+    constexpr int kSpan = kSuper * kTile;
     __shared__ __attribute__((aligned(16))) float bt[kSuper][16 * kPitch];
+    __shared__ __attribute__((aligned(16))) T actc[VEC ? 2 : 1][kChans][kSpan + 8];
     const LaneId id = lane_id(p);
+    const int cl = 4 * id.w + id.row;                    // channel in the workgroup
     const float a2 = id.ok ? p.A[id.dc * p.N + id.n] * kLog2e : 0.0f;
     const float bias = p.delta_bias ? p.delta_bias[id.dc] : 0.0f;
     const int64_t nblk = (p.L + kTile - 1) / kTile;
@@ -226,26 +295,43 @@ __global__ __launch_bounds__(kThreads) void s6_bwd_ckpt(S6BwdArgs p) {
     const auto rB = bc_rsrc<T>(p, id.b, p.Bm);
     float* ck = p.ckpt + (id.b * p.D + id.dc) * nblk * p.N + id.n;
     const RowRsrc rr = row_rsrc<T>(p, id.b);
-    SuperRaw<T> nxt;
+    SuperRaw<T, VEC> nxt;
     if (nsup > 0) nxt.load(p, id, rr, 0, rB);
     for (int64_t sg = 0; sg < nsup; ++sg) {
-        const SuperRaw<T> cur = nxt;
-        lds_barrier();                    // previous super-tile's B reads done
+        const SuperRaw<T, VEC> cur = nxt;
+        lds_barrier();                    // previous super-tile's LDS reads done
 #pragma unroll
         for (int i = 0; i < kSuper; ++i)
             bt[i][(threadIdx.x % 16) * kPitch + threadIdx.x / 16] = Bits<T>::f32(cur.b[i]);
+        if constexpr (VEC) {
+            constexpr int kPT = Run<T>::kPerToken, kVals = Run<T>::kVals;
+            const int wu = id.w;
+#pragma unroll
+            for (int i = 0; i < kPT; ++i) {
+                const int idx = id.l + 64 * i;
+                const int j = 64 * (wu & 1) + idx / kPT, pc = idx % kPT;
+                const T* e = reinterpret_cast<const T*>(&cur.a[i]);
+#pragma unroll
+                for (int q = 0; q < kVals; ++q) actc[wu >> 1][kVals * pc + q][j] = e[q];
+            }
+        }
         lds_barrier();
         // travels meanwhile; issued unconditionally (past the end it reads
         // zeros) so that no branch join makes the compiler wait for it here
-        nxt.load(p, id, rr, (sg + 1) * kSuper * kTile, rB);
+        nxt.load(p, id, rr, (sg + 1) * kSpan, rB);
 #pragma unroll
         for (int i = 0; i < kSuper; ++i) {
             const int64_t k = sg * kSuper + i;
             if (k >= nblk) break;
             if (id.ok) ck[k * p.N] = h;
             TileRaw<T, false, false> r;
-            r.delta = cur.delta[i];
-            r.u = cur.u[i];
+            if constexpr (VEC) {
+                r.delta = elem_bits<T>(actc[0][cl][kTile * i + id.n]);
+                r.u = elem_bits<T>(actc[1][cl][kTile * i + id.n]);
+            } else {
+                r.delta = cur.delta[i];
+                r.u = cur.u[i];
+            }
             TileScalars<false, SOFTPLUS, false> s;
             s.template from<T>(r, p, id, k * kTile, bias);
             float bv[kTile], dA[kTile];
@@ -263,7 +349,7 @@ __global__ __launch_bounds__(kThreads) void s6_bwd_ckpt(S6BwdArgs p) {
     }
 }
 
-template <typename T, bool HAS_Z, bool SOFTPLUS>
+template <typename T, bool HAS_Z, bool SOFTPLUS, bool VEC>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void s6_bwd_main(S6BwdArgs p) {
     __shared__ float red[2][kWaves][kTile][16];     // [dB|dC][wave][token][n]
@@ -273,7 +359,12 @@ void s6_bwd_main(S6BwdArgs p) {
     constexpr int kOut = HAS_Z ? 3 : 2;
     __shared__ __attribute__((aligned(16))) T outst[kOut][kTile][kChans];
     __shared__ __attribute__((aligned(16))) float bct[2][16 * kPitch];   // B, C: [n][token]
+    // VEC: delta, u, dy (, z) of the tile as [tensor][channel][token]; wave w
+    // loads tensor w: lane l loads channels 4 (l % 4) .. +3 of token l / 4
+    constexpr int kNT = HAS_Z ? 4 : 3;
+    __shared__ __attribute__((aligned(16))) T actst[VEC ? kNT : 1][kChans][kTile + 8];
     const LaneId id = lane_id(p);
+    const int cl = 4 * id.w + id.row;                    // channel in the workgroup
     const float an = id.ok ? p.A[id.dc * p.N + id.n] : 0.0f;
     const float a2 = an * kLog2e;
     const float bias = p.delta_bias ? p.delta_bias[id.dc] : 0.0f;
@@ -295,8 +386,19 @@ void s6_bwd_main(S6BwdArgs p) {
     TileRaw<T, HAS_Z, true> raw;
     uint32_t bpre = 0, cpre = 0;
     float hck = 0.0f;
+    const int wu = __builtin_amdgcn_readfirstlane(id.w);
+    const __amdgpu_buffer_rsrc_t rs_act = wu == 0 ? rr.delta : wu == 1 ? rr.u : wu == 2 ? rr.dy : rr.z;
+    const bool act_lane = wu < kNT;
+    Quad<T> apre;
+    // every lane loads (a wavefront without a tensor at an offset past the
+    // resource), so no branch separates the prefetch from the work it overlaps
+    auto load_act = [&](int64_t t0) {
+        const int64_t t = act_lane ? t0 + (id.l >> 2) : -1;
+        apre.load(rs_act, quad_off<T>(p, id.grp, t, id.l & 3));
+    };
     if (nblk > 0) {
-        raw.load(p, id, rr, (nblk - 1) * kTile);
+        if constexpr (VEC) load_act((nblk - 1) * kTile);
+        else raw.load(p, id, rr, (nblk - 1) * kTile);
         bpre = load_bc_bits<T>(p, (nblk - 1) * kTile, rB);
         cpre = load_bc_bits<T>(p, (nblk - 1) * kTile, rC);
         hck = ck[(nblk - 1) * p.N];
@@ -305,17 +407,31 @@ void s6_bwd_main(S6BwdArgs p) {
         const int64_t t0 = k * kTile;
         const float hprev0 = id.ok ? hck : 0.0f;
         TileScalars<HAS_Z, SOFTPLUS, true> s;
-        s.template from<T>(raw, p, id, t0, bias);
+        if constexpr (!VEC) s.template from<T>(raw, p, id, t0, bias);
         lds_barrier();                   // previous tile's LDS reads done
         bct[0][(threadIdx.x % 16) * kPitch + threadIdx.x / 16] = Bits<T>::f32(bpre);
         bct[1][(threadIdx.x % 16) * kPitch + threadIdx.x / 16] = Bits<T>::f32(cpre);
+        if constexpr (VEC) {
+            if (act_lane) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) actst[wu][4 * (id.l & 3) + q][id.l >> 2] = apre.elem(q);
+            }
+        }
         lds_barrier();
+        if constexpr (VEC) {
+            raw.delta = elem_bits<T>(actst[0][cl][id.n]);
+            raw.u = elem_bits<T>(actst[1][cl][id.n]);
+            raw.dy = elem_bits<T>(actst[2][cl][id.n]);
+            raw.z = HAS_Z ? elem_bits<T>(actst[kNT - 1][cl][id.n]) : 0u;
+            s.template from<T>(raw, p, id, t0, bias);
+        }
         // The previous tile's inputs travel during this one.  The loads are
         // unconditional (for k = 0 the buffer loads fall before the row and
         // read zeros, the checkpoint load repeats tile 0): a branch around
         // them would join the loaded and the old values, and the compiler
         // waits for the loads at that join, in the tile that issues them.
-        raw.load(p, id, rr, t0 - kTile);
+        if constexpr (VEC) load_act(t0 - kTile);
+        else raw.load(p, id, rr, t0 - kTile);
         bpre = load_bc_bits<T>(p, t0 - kTile, rB);
         cpre = load_bc_bits<T>(p, t0 - kTile, rC);
         hck = ck[(k > 0 ? k - 1 : 0) * p.N];
@@ -372,7 +488,6 @@ void s6_bwd_main(S6BwdArgs p) {
         // per-channel results of token t0 + j in lane j, staged in LDS
         {
             const int64_t t = t0 + id.n;
-            const int cl = 4 * id.w + id.row;                  // channel in the workgroup
             const float r = r_y + dsk * s.u;
             const float dd = r_ddt * s.sig;
             Elem<T>::store(&outst[0][id.n][0], cl, fmaf(s.g, dsk, s.dt * r_su));
@@ -467,17 +582,24 @@ __global__ __launch_bounds__(256) void s6_bwd_reduce(S6BwdArgs p) {
     }
 }
 
-template <typename T>
-hipError_t launch_t(const S6BwdArgs& a, hipStream_t stream) {
+template <typename T, bool VEC>
+void launch_sweeps(const S6BwdArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)((a.D + kChans - 1) / kChans), (unsigned)a.B);
     const bool sp = (a.flags & SSM_FLAG_DELTA_SOFTPLUS) != 0;
-    if (sp) s6_bwd_ckpt<T, true><<<grid, kThreads, 0, stream>>>(a);
-    else s6_bwd_ckpt<T, false><<<grid, kThreads, 0, stream>>>(a);
+    if (sp) s6_bwd_ckpt<T, true, VEC><<<grid, kThreads, 0, stream>>>(a);
+    else s6_bwd_ckpt<T, false, VEC><<<grid, kThreads, 0, stream>>>(a);
     const bool hz = a.z != nullptr;
-    if (hz && sp) s6_bwd_main<T, true, true><<<grid, kThreads, 0, stream>>>(a);
-    else if (hz) s6_bwd_main<T, true, false><<<grid, kThreads, 0, stream>>>(a);
-    else if (sp) s6_bwd_main<T, false, true><<<grid, kThreads, 0, stream>>>(a);
-    else s6_bwd_main<T, false, false><<<grid, kThreads, 0, stream>>>(a);
+    if (hz && sp) s6_bwd_main<T, true, true, VEC><<<grid, kThreads, 0, stream>>>(a);
+    else if (hz) s6_bwd_main<T, true, false, VEC><<<grid, kThreads, 0, stream>>>(a);
+    else if (sp) s6_bwd_main<T, false, true, VEC><<<grid, kThreads, 0, stream>>>(a);
+    else s6_bwd_main<T, false, false, VEC><<<grid, kThreads, 0, stream>>>(a);
+}
+
+template <typename T>
+hipError_t launch_t(const S6BwdArgs& a, hipStream_t stream) {
+    // 16-byte activation pieces need every token's channel run 16-byte aligned
+    if ((a.D * (int64_t)sizeof(T)) % 16 == 0) launch_sweeps<T, true>(a, stream);
+    else launch_sweeps<T, false>(a, stream);
     const int64_t total = 2 * a.B * a.L * a.N + a.D * a.N + a.D;
     s6_bwd_reduce<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(a);
     return hipGetLastError();

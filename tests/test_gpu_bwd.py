@@ -73,6 +73,17 @@ def test_bwd_parity_lengths(L, dtype):
     _check(_gpu(inp), _ref(inp), dtype, f"L={L}")
 
 
+@pytest.mark.parametrize("L", [1, 17, 128, 129, 300])
+@pytest.mark.parametrize("Dm", [48, 24, 44])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_parity_channel_runs(L, Dm, dtype):
+    # D * elem size a multiple of 16 (D = 48, 24; D = 44 in fp32): activations
+    # arrive as 16-byte / 4-channel pieces of each token's channel run, including
+    # a partial last group (D = 24); otherwise (D = 44 in bf16) lane by lane
+    inp = _case(2, L, Dm, 16, dtype, seed=L + Dm)
+    _check(_gpu(inp), _ref(inp), dtype, f"L={L} D={Dm}")
+
+
 @pytest.mark.parametrize("N", [1, 4, 7, 16])
 @pytest.mark.parametrize("Dm", [5, 32, 70])
 def test_bwd_parity_shapes(N, Dm):
