@@ -94,8 +94,8 @@ const char* ssm_status_string(int status);
  *     scanned in parallel, and the segments' (decay, offset) pairs are carried
  *     by a wavefront-level scan in which each lane composes the pairs of one
  *     (b, d, n) chain in segment order.  The workspace holds those pairs.
- * The workspace query returns the split path's size (calls with a fused
- * convolution or SSM_FLAG_ZOH take that path at any size).  It depends on
+ * The workspace query returns the split path's size (calls with
+ * SSM_FLAG_ZOH take that path at any size).  It depends on
  * the sizes and on the CU count of the current device (the segment count and
  * the path balance wavefronts over its SIMDs): query and call on the same
  * device.
@@ -108,9 +108,9 @@ size_t ssm_selective_scan_workspace_bytes(int64_t B, int64_t L, int64_t D, int64
  * (1..256) overrides the choice, for both this query and the call. */
 int ssm_selective_scan_segments(int64_t B, int64_t L, int64_t D, int64_t N);
 
-/* 1 if a forward call at these sizes without a fused convolution and without
- * SSM_FLAG_ZOH runs the state-per-lane kernel (unsplit: the segment count
- * above then applies only to the other calls), else 0 (also for invalid
+/* 1 if a forward call at these sizes without SSM_FLAG_ZOH (with or without
+ * the fused convolution) runs the state-per-lane kernel (unsplit: the segment
+ * count above then applies only to ZOH calls), else 0 (also for invalid
  * sizes).  The environment variable SSM_S6_LANES=0 turns that kernel off,
  * SSM_S6_LANES=1 takes it whenever N = 16, D is a multiple of 16 and the
  * offsets fit, for both this query and the call. */

@@ -54,8 +54,8 @@ def selective_scan_segments(B: int, L: int, D: int, N: int) -> int:
 
 
 def selective_scan_lanes(B: int, L: int, D: int, N: int) -> bool:
-    """True if a forward call at these sizes (no fused conv, no ZOH) runs the
-    state-per-lane kernel, unsplit."""
+    """True if a forward call at these sizes (without ZOH; with or without the
+    fused convolution) runs the state-per-lane kernel, unsplit."""
     return bool(_native.load().ssm_selective_scan_lanes(B, L, D, N))
 
 

@@ -451,7 +451,7 @@ void s6_fast(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
 }
 
 // -------------------------------------------------------- state-per-lane path
-// N = 16, first-order input term, D a multiple of 16, no fused convolution.
+// N = 16, first-order input term, D a multiple of 16.
 // One lane per (channel, state): each 16-lane row of a wavefront is one
 // channel and lane n holds its state n, so a workgroup of four wavefronts
 // covers 16 channels of one batch row.  With B*D/4 wavefronts the chip is
@@ -474,6 +474,10 @@ void s6_fast(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
 // which adds skip and gate and stages y in LDS; y leaves as 16-byte pieces of
 // the workgroup's channel run when the next super-tile starts.
 // The next super-tile's pieces are loaded while this one is computed.
+// CONV: the causal conv1d + SiLU runs in front (u_ holds its input x): lane j
+// convolves token j's window x_{t-3..t} from the staged row; the three inputs
+// before a super-tile come from the previous one (or the carried conv state),
+// kept in fp32 in a double-buffered LDS halo.
 namespace lanes {
 constexpr int kTile = 16;                 // tokens per tile (one per lane of a row)
 constexpr int kSuper = 8;                 // tiles per super-tile
@@ -494,7 +498,7 @@ struct Pieces {
 };
 }  // namespace lanes
 
-template <typename T, bool HAS_Z, bool SOFTPLUS>
+template <typename T, bool HAS_Z, bool SOFTPLUS, bool CONV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
 void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
               const T* __restrict__ z_, const T* __restrict__ Bm_, const T* __restrict__ Cm_,
@@ -509,6 +513,10 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
     __shared__ __attribute__((aligned(16))) float bct[2][kSuper][16 * kPitch];
     __shared__ __attribute__((aligned(16))) T act[HAS_Z ? 3 : 2][kChans][kActPitch];
     __shared__ __attribute__((aligned(16))) T yst[kSpan][kChans];
+    // CONV: inputs x_{t0-3 .. t0-1} before the super-tile (fp32), by parity;
+    // the convolution's output u when the caller asks for it
+    __shared__ float xh[CONV ? 2 : 1][kChans][4];
+    __shared__ __attribute__((aligned(16))) T ust[CONV ? kSpan : 1][kChans];
     const int tid = threadIdx.x;
     const int w = tid >> 6, row = (tid >> 4) & 3, n = tid & 15;
     // Workgroups are dealt to the 8 XCDs round robin (i -> XCD i % 8); the id
@@ -541,6 +549,27 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
     const auto rC = make_rsrc(Cm_ + b * p.L * 16, bc_bytes);
     const uint32_t row_bytes = (uint32_t)(D * E);
     const uint32_t grp_bytes = (uint32_t)(grp * kChans * E);
+    // CONV: four taps (a width K < 4 padded with leading zero weights)
+    float cw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, cb = 0.0f;
+    const bool want_u = CONV && p.u_out != nullptr;
+    const auto ruo = make_rsrc(want_u ? static_cast<T*>(p.u_out) + rowoff : nullptr,
+                               want_u ? act_bytes : 0u);
+    if constexpr (CONV) {
+        const int K = (int)p.conv_K;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int kk = k - (4 - K);
+            cw[k] = kk >= 0 ? p.conv_w[d * K + kk] : 0.0f;
+        }
+        cb = p.conv_b ? p.conv_b[d] : 0.0f;
+        if (tid < 3 * kChans) {
+            // the inputs before token 0: the carried state (its last K-1 slots
+            // are x_{-K+1 .. -1}) or zeros
+            const int ch = tid / 3, i = tid % 3, slot = i + K - 4;
+            xh[0][ch][i] = (p.conv_state_in && slot >= 0)
+                               ? p.conv_state_in[(b * D + grp * kChans + ch) * (K - 1) + slot] : 0.0f;
+        }
+    }
 
     // thread -> (token idx / kPerToken, piece idx % kPerToken) of the super-tile
     auto load = [&](Raw& r, int64_t st0) {
@@ -588,6 +617,12 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
                 reinterpret_cast<const char*>(&yst[t][0]) + 16 * pc);
             __builtin_amdgcn_raw_buffer_store_b128(v, ry, (int)(t * row_bytes + grp_bytes + 16 * pc),
                                                    (int)((uint32_t)st0 * row_bytes), 0);
+            if (want_u) {
+                const u32x4 w = *reinterpret_cast<const u32x4*>(
+                    reinterpret_cast<const char*>(&ust[t][0]) + 16 * pc);
+                __builtin_amdgcn_raw_buffer_store_b128(w, ruo, (int)(t * row_bytes + grp_bytes + 16 * pc),
+                                                       (int)((uint32_t)st0 * row_bytes), 0);
+            }
         }
     };
 
@@ -612,7 +647,33 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
             const uint32_t keep = st0 + tl < Lb ? 0xffffffffu : 0u;
             const float xr = widen<T>(elem_bits<T>(act[1][chan][tl])) + bias;
             const float dt = __uint_as_float(__float_as_uint(SOFTPLUS ? softplus_f(xr) : xr) & keep);
-            const float ut = widen<T>(elem_bits<T>(act[0][chan][tl]));
+            float ut;
+            if constexpr (CONV) {
+                // window x_{t-3..t}: the staged row, before the super-tile the halo
+                float xw[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int m = tl - 3 + k;
+                    if (i == 0 && k < 3) {
+                        const float xa = widen<T>(elem_bits<T>(act[0][chan][m < 0 ? 0 : m]));
+                        const float xb = xh[sg & 1][chan][m < 0 ? m + 3 : 0];
+                        xw[k] = m < 0 ? xb : xa;
+                    } else {
+                        xw[k] = widen<T>(elem_bits<T>(act[0][chan][m]));
+                    }
+                }
+                // the same product order as the split path's fused convolution
+                const float sc = fmaf(cw[3], xw[3], fmaf(cw[2], xw[2], fmaf(cw[1], xw[1], fmaf(cw[0], xw[0], cb))));
+                ut = silu_f(sc);
+                if (want_u) {
+                    if constexpr (sizeof(T) == 2) ust[tl][chan] = f32_to_bf16_bits(ut);
+                    else ust[tl][chan] = ut;
+                }
+                // the next super-tile's halo: this one's last three inputs
+                if (i == kSuper - 1 && n >= kTile - 3) xh[(sg + 1) & 1][chan][n - (kTile - 3)] = xw[3];
+            } else {
+                ut = widen<T>(elem_bits<T>(act[0][chan][tl]));
+            }
             const float dtu = dt * ut;
             float bv[kTile], cv[kTile], dA[kTile], pr[kTile];
 #pragma unroll
@@ -645,6 +706,20 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
     lds_barrier();
     if (nsup > 0) store_y((nsup - 1) * kSpan);
     if (p.h_last) p.h_last[(b * D + d) * 16 + n] = h;
+    if constexpr (CONV) {
+        // the last K-1 inputs of the row, oldest first (from the carried state
+        // when the row is shorter than that)
+        const int K = (int)p.conv_K;
+        if (p.conv_state_out && tid < (K - 1) * kChans) {
+            const int ch = tid / (K - 1), i = tid % (K - 1);
+            const int64_t dd = grp * kChans + ch;
+            const int64_t t = Lb - (K - 1) + i;
+            float v = 0.0f;
+            if (t >= 0) v = widen<T>(elem_bits<T>(u_[(b * p.L + t) * D + dd]));
+            else if (p.conv_state_in) v = p.conv_state_in[(b * D + dd) * (K - 1) + (t + K - 1)];
+            p.conv_state_out[(b * D + dd) * (K - 1) + i] = v;
+        }
+    }
 }
 
 // --------------------------------------------------------------- generic path
@@ -836,20 +911,24 @@ hipError_t launch_lanes(const S6Args& a, hipStream_t stream) {
     T* Y = static_cast<T*>(a.y);
     const dim3 grid((unsigned)(a.D / lanes::kChans), (unsigned)a.B), block(256);
     for (int i = 0; i < 3; ++i) mark(a, i, stream);     // no reduce or carry phase
-    if (a.z) {
-        if (sp) hipLaunchKernelGGL((s6_lanes<T, true, true>), grid, block, 0, stream, a, U, Dl, Z, Bp, Cp, Y);
-        else hipLaunchKernelGGL((s6_lanes<T, true, false>), grid, block, 0, stream, a, U, Dl, Z, Bp, Cp, Y);
+    const bool cv = a.conv_w != nullptr;
+#define SSM_LANES(Z_, SP_, CV_) \
+    hipLaunchKernelGGL((s6_lanes<T, Z_, SP_, CV_>), grid, block, 0, stream, a, U, Dl, Z, Bp, Cp, Y)
+    if (cv) {
+        if (a.z) { if (sp) SSM_LANES(true, true, true); else SSM_LANES(true, false, true); }
+        else { if (sp) SSM_LANES(false, true, true); else SSM_LANES(false, false, true); }
     } else {
-        if (sp) hipLaunchKernelGGL((s6_lanes<T, false, true>), grid, block, 0, stream, a, U, Dl, Z, Bp, Cp, Y);
-        else hipLaunchKernelGGL((s6_lanes<T, false, false>), grid, block, 0, stream, a, U, Dl, Z, Bp, Cp, Y);
+        if (a.z) { if (sp) SSM_LANES(true, true, false); else SSM_LANES(true, false, false); }
+        else { if (sp) SSM_LANES(false, true, false); else SSM_LANES(false, false, false); }
     }
+#undef SSM_LANES
     mark(a, 3, stream);
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_fast(const S6Args& a, hipStream_t stream) {
-    if (a.lanes && !a.conv_w) return launch_lanes<T>(a, stream);
+    if (a.lanes) return launch_lanes<T>(a, stream);
     const bool sp = (a.flags & SSM_FLAG_DELTA_SOFTPLUS) != 0;
     if (a.conv_w)
         return sp ? launch_fast_sp<T, true, true>(a, stream) : launch_fast_sp<T, false, true>(a, stream);

@@ -39,14 +39,14 @@ struct S6Args {
     void* u_out;                // [B, L, D] or NULL: the convolution's output u
     int64_t conv_K;
     const int32_t* seq_lens;    // [B] tokens per batch row (device), or NULL: all L
-    bool lanes;                 // state-per-lane kernel (unsplit) when no convolution is fused
+    bool lanes;                 // state-per-lane kernel (unsplit) for N = 16 without ZOH
 };
 
 struct S6Plan {
     int S;                  // segments of the split path
     int64_t seg_len;
     size_t workspace_bytes; // of the split path (also required when lanes is set)
-    bool lanes;             // a call without fused convolution or ZOH takes the state-per-lane kernel
+    bool lanes;             // an N = 16 call without ZOH takes the state-per-lane kernel
 };
 
 // Deterministic in the sizes (plus the SSM_S6_SEGMENTS / SSM_S6_LANES overrides).

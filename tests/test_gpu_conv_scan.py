@@ -18,6 +18,14 @@ from _parity import TOL, normwise_err, to_dev
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(params=["split", "lanes"], autouse=True)
+def s6_path(request, monkeypatch):
+    """Every test runs on both S6 paths: the split path (SSM_S6_LANES=0) and the
+    state-per-lane kernel (SSM_S6_LANES=1, taken where D is a multiple of 16)."""
+    monkeypatch.setenv("SSM_S6_LANES", "0" if request.param == "split" else "1")
+    return request.param
+
+
 def _case(Bt, L, Dm, K, dtype, seed, gate=True, skip=True, bias=True):
     w = W.S6_MAMBA130M.scaled(B=Bt, L=L, D=Dm, dtype=dtype, gate=gate,
                               skip="normal" if skip else None,
@@ -48,9 +56,10 @@ def _oracle(inp, conv_state=None, h0=None):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", [(2, 300, 128, 4), (1, 1000, 100, 4), (2, 77, 64, 3),
-                                   (1, 2, 64, 4), (3, 129, 70, 2), (1, 64, 64, 1)])
-def test_fused_parity(dtype, shape):
+                                   (1, 2, 64, 4), (3, 129, 70, 2), (1, 64, 64, 1), (2, 260, 48, 4)])
+def test_fused_parity(dtype, shape, s6_path):
     Bt, L, Dm, K = shape
+    assert ssm.selective_scan_lanes(Bt, L, Dm, 16) == (s6_path == "lanes" and Dm % 16 == 0)
     inp = _case(Bt, L, Dm, K, dtype, seed=L + K)
     g = torch.Generator().manual_seed(L)
     cs0 = torch.randn(Bt, Dm, K - 1, generator=g) if K > 1 else None
