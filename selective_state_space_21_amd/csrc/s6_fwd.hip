@@ -462,8 +462,8 @@ void s6_fast(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
 // The sequence is walked in super-tiles of 128 tokens.  Per super-tile the
 // workgroup loads u, delta, z (the 16 channels' 32-byte run of each token)
 // and the B and C rows as 16-byte pieces, one of each per thread, and stages
-// them in LDS: the activations as [channel][token], B and C as fp32
-// [tile][state][token].  A lane loading its own 2-byte element instead
+// them in LDS: the activations as loaded ([token][channel], 16-byte writes),
+// B and C as fp32 [tile][state][token].  A lane loading its own 2-byte element instead
 // touches 16 cache lines per instruction, which ran 1.7x slower.
 // Per 16-token tile, lane j of a row forms the per-channel scalars of token j
 // (step size, dt*u, skip, gate); the decay exp(dt*A) and input term dt*u*B of
@@ -508,10 +508,9 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
     constexpr uint32_t E = sizeof(T);
     constexpr int kPerToken = Raw::kPerToken, kPer = Raw::kPer;
     constexpr int kVals = 16 / (int)E;                  // elements per piece
-    // activation rows padded so the four rows a wavefront reads start 8 banks apart
-    constexpr int kActPitch = kSpan + 2 * kVals;
+    constexpr int kActPitch = kChans + 8;   // [tensor][token][channel], 48-byte token rows
     __shared__ __attribute__((aligned(16))) float bct[2][kSuper][16 * kPitch];
-    __shared__ __attribute__((aligned(16))) T act[HAS_Z ? 3 : 2][kChans][kActPitch];
+    __shared__ __attribute__((aligned(16))) T act[HAS_Z ? 3 : 2][kSpan][kActPitch];
     __shared__ __attribute__((aligned(16))) T yst[kSpan][kChans];
     // CONV: inputs x_{t0-3 .. t0-1} before the super-tile (fp32), by parity;
     // the convolution's output u when the caller asks for it
@@ -592,17 +591,14 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
             const int idx = tid + 256 * k, t = idx / kPerToken, pc = idx % kPerToken;
-            const T* vu = reinterpret_cast<const T*>(&r.u[k]);
-            const T* vd = reinterpret_cast<const T*>(&r.d[k]);
-            const T* vz = reinterpret_cast<const T*>(&r.z[k]);
             const T* vb = reinterpret_cast<const T*>(&r.b[k]);
             const T* vc = reinterpret_cast<const T*>(&r.c[k]);
+            *reinterpret_cast<u32x4*>(&act[0][t][kVals * pc]) = r.u[k];
+            *reinterpret_cast<u32x4*>(&act[1][t][kVals * pc]) = r.d[k];
+            if constexpr (HAS_Z) *reinterpret_cast<u32x4*>(&act[2][t][kVals * pc]) = r.z[k];
 #pragma unroll
             for (int e = 0; e < kVals; ++e) {
-                const int ch = kVals * pc + e;           // channel, or state for B/C
-                act[0][ch][t] = vu[e];
-                act[1][ch][t] = vd[e];
-                if constexpr (HAS_Z) act[2][ch][t] = vz[e];
+                const int ch = kVals * pc + e;           // state for B/C
                 bct[0][t / kTile][ch * kPitch + t % kTile] = widen<T>(elem_bits<T>(vb[e]));
                 bct[1][t / kTile][ch * kPitch + t % kTile] = widen<T>(elem_bits<T>(vc[e]));
             }
@@ -645,7 +641,7 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
             // into one basic block per tile (which kept the scheduler from
             // overlapping a tile's exponentials with the previous tile's chain)
             const uint32_t keep = st0 + tl < Lb ? 0xffffffffu : 0u;
-            const float xr = widen<T>(elem_bits<T>(act[1][chan][tl])) + bias;
+            const float xr = widen<T>(elem_bits<T>(act[1][tl][chan])) + bias;
             const float dt = __uint_as_float(__float_as_uint(SOFTPLUS ? softplus_f(xr) : xr) & keep);
             float ut;
             if constexpr (CONV) {
@@ -655,11 +651,11 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
                 for (int k = 0; k < 4; ++k) {
                     const int m = tl - 3 + k;
                     if (i == 0 && k < 3) {
-                        const float xa = widen<T>(elem_bits<T>(act[0][chan][m < 0 ? 0 : m]));
+                        const float xa = widen<T>(elem_bits<T>(act[0][m < 0 ? 0 : m][chan]));
                         const float xb = xh[sg & 1][chan][m < 0 ? m + 3 : 0];
                         xw[k] = m < 0 ? xb : xa;
                     } else {
-                        xw[k] = widen<T>(elem_bits<T>(act[0][chan][m]));
+                        xw[k] = widen<T>(elem_bits<T>(act[0][m][chan]));
                     }
                 }
                 // the same product order as the split path's fused convolution
@@ -672,7 +668,7 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
                 // the next super-tile's halo: this one's last three inputs
                 if (i == kSuper - 1 && n >= kTile - 3) xh[(sg + 1) & 1][chan][n - (kTile - 3)] = xw[3];
             } else {
-                ut = widen<T>(elem_bits<T>(act[0][chan][tl]));
+                ut = widen<T>(elem_bits<T>(act[0][tl][chan]));
             }
             const float dtu = dt * ut;
             float bv[kTile], cv[kTile], dA[kTile], pr[kTile];
@@ -698,7 +694,7 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
             }
             float yv = row_reduce_scatter16(pr, n);
             yv = fmaf(dsk, ut, yv);
-            if constexpr (HAS_Z) yv *= silu_f(widen<T>(elem_bits<T>(act[2][chan][tl])));
+            if constexpr (HAS_Z) yv *= silu_f(widen<T>(elem_bits<T>(act[2][tl][chan])));
             if constexpr (sizeof(T) == 2) yst[tl][chan] = f32_to_bf16_bits(yv);
             else yst[tl][chan] = yv;
         }
