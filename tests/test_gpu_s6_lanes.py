@@ -180,3 +180,24 @@ def test_full_lengths_equal_plain_call(lanes):
                                     seq_lens=torch.full((3,), 512, dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(h1, h2)
+
+
+def test_long_fp32_sequence_sampled(lanes):
+    """The long fp32 shape (131072 tokens, 1024 super-tiles per row) forced onto
+    the state-per-lane kernel; sampled channels against the oracle at the fp32
+    bar."""
+    from _parity import s6_oracle_sampled
+    w = W.S6_LONG_FP32
+    assert ssm.selective_scan_lanes(w.B, w.L, w.D, w.N)
+    inp = W.make_s6_inputs(w, seed=0)
+    y, h = s6_gpu(inp)
+    y = y.float().cpu().numpy()
+    h = h.cpu().numpy()
+    ds = [0, 1, 15, 16, 511, 1024, 2047]
+    ys, yr, hs, hr = [], [], [], []
+    for b, dl, yo, ho in s6_oracle_sampled(inp, [(0, ds)]):
+        ys.append(y[b][:, dl]); yr.append(yo)
+        hs.append(h[b][dl]); hr.append(ho)
+    ey = normwise_err(np.concatenate(ys, 1), np.concatenate(yr, 1))
+    eh = normwise_err(np.concatenate(hs, 0), np.concatenate(hr, 0))
+    assert ey <= TOL[w.dtype] and eh <= 1e-5, (ey, eh)
