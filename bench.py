@@ -109,6 +109,7 @@ def bench_s6(args, torch, ssm, W, native, hip):
     torch.cuda.synchronize()
     # the call as a whole, between two events on its stream
     total = 0.0
+    per_step = []
     wall0 = time.perf_counter()
     for i in range(args.steps):
         flush.fill_(float(i))                      # evict the Infinity Cache (untimed)
@@ -116,7 +117,8 @@ def bench_s6(args, torch, ssm, W, native, hip):
         step(None)
         hip.hipEventRecord(evs[1], stream.cuda_stream)
         torch.cuda.synchronize()
-        total += _elapsed(hip, evs[0], evs[1])
+        per_step.append(_elapsed(hip, evs[0], evs[1]))
+        total += per_step[-1]
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     # the split path's phases (the library records an event at each boundary;
@@ -146,6 +148,7 @@ def bench_s6(args, torch, ssm, W, native, hip):
     scan_gbs = nbytes / (scan_ms * 1e-3) / 1e9
     flops = 6.0 * elems                            # mul, mul, fma, fma per state update
     return dict(
+        ms_median=sorted(per_step)[len(per_step) // 2], ms_min=min(per_step),
         w=w, t=t, ms=ms, gbs=gbs, nbytes=nbytes, segments=segments, lanes=lanes, wall=wall,
         hot_ms=hot_ms,
         phases_ms=(dict(state_per_lane=scan_ms) if lanes else
@@ -406,6 +409,7 @@ def main():
             "gtoken_channels_per_s": round(r["gtokch"], 3),
             "algorithmic_bytes": r["nbytes"],
             "phases_ms": {k: round(v, 5) for k, v in r["phases_ms"].items()},
+            "ms_median": round(r["ms_median"], 5), "ms_min": round(r["ms_min"], 5),
             "ms_per_step_without_cache_flush": round(r["hot_ms"], 5),
         },
         "roofline": {
