@@ -64,7 +64,7 @@ __device__ __forceinline__ float f32(__bf16 x) { return static_cast<float>(x); }
 
 template <int Q, int N>
 struct SsdLds {
-    static constexpr int kBStride = N + 8;       // bf16 per B row (16-byte pad)
+    static constexpr int kBStride = N + 16;      // bf16 per B row (32-byte pad: ~1% faster than 16)
     static constexpr int kXStride = Q + 8;       // bf16 per X^T row
     // X^T rows are swizzled by 32-token blocks: element (p, s) sits in column
     // s ^ 32 * ((p / 16) % KX).  The staging writes put eight rows 8 apart in
