@@ -143,7 +143,8 @@ int ssm_selective_scan_fwd_varlen(const void* u, const void* delta, const float*
  * Same operation, for measurement: `events` is NULL or points to 4 hipEvent_t
  * created by the caller; they are recorded on `stream` at the phase
  * boundaries -- before the segment reduce, before the carry scan, before the
- * segment scan, and after it (with one segment the first three coincide).
+ * segment scan, and after it (with one segment, or on the state-per-lane
+ * path, the first three coincide).
  * Recording is asynchronous; the caller reads the intervals after it has
  * synchronised.  The arguments and results are otherwise those of
  * ssm_selective_scan_fwd.
