@@ -22,6 +22,9 @@
 // is computed; barriers wait on LDS only, so those loads stay in flight.  Per
 // chunk, B rows and X^T are staged in LDS and each wavefront keeps the C rows
 // of its output columns in registers (the B operand of both S C^T and B C^T).
+// The state update scales its B operand (8 consecutive tokens of one state
+// column) by the tokens' weights w_s in registers, so no scaled copy of X^T
+// is staged.
 // Output tiles are paired first-with-last so every wavefront does the same
 // share of the causal work.  Products use v_mfma_f32_16x16x32_bf16 (bf16
 // operands, fp32 accumulation); masks, decays, skip and gate are fp32.
@@ -81,7 +84,7 @@ struct SsdLds {
     alignas(16) int wide[kWaves];                 // per-wavefront: a 32-token block spans > 2^64
     alignas(16) __bf16 B[Q * kBStride];           // B rows of the chunk
     alignas(16) __bf16 Xt[kP * kXStride];         // X^T of the chunk
-    alignas(16) __bf16 XWt[kP * kXStride];        // X^T with column s scaled by exp(cum_Q - cum_s) dt_s
+    alignas(16) float wst[Q];                     // exp(cum_Q - cum_s) dt_s: token s's weight in the final state
     alignas(16) __bf16 H[kP * kHStride];          // state (bf16) for Y_off
 };
 
@@ -312,23 +315,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
             far = fabsf(rel) > 64.0f;
             sm.fblk[tid] = fast_exp2(rel) * ds;
         }
-        if (tid < TL::XGROUP) {
-            // X^T scaled per token by its weight in the chunk's final state
-            const int sg = tid / (kP / 8), p8 = tid % (kP / 8);
-            const f32x4 cs = *reinterpret_cast<const f32x4*>(&sm.cum[4 * sg]);
-            const f32x4 ds = *reinterpret_cast<const f32x4*>(&sm.dt[4 * sg]);
-            uint32_t xs[4][4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float wq = fast_exp2(cumQ - cs[q]) * ds[q];
-                const uint32_t v[4] = {xpre[q].x, xpre[q].y, xpre[q].z, xpre[q].w};
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    xs[q][m] = pack_bf16x2(__uint_as_float(v[m] << 16) * wq,
-                                           __uint_as_float(v[m] & 0xffff0000u) * wq);
-            }
-            stage_xt(sm.XWt, sg, p8, xs);
-        }
+        if (tid < Q) sm.wst[tid] = fast_exp2(cumQ - sm.cum[tid]) * sm.dt[tid];
         far = __any(far);
         if (l == 0) sm.wide[w] = far;
         lds_barrier();
@@ -484,11 +471,21 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
                 const int s8 = 32 * ks + 8 * g;
                 const bf16x4 lo = lds_read_tr16(bsrc + 32 * ks * Lds::kBStride);
                 const bf16x4 hi = lds_read_tr16(bsrc + (32 * ks + 4) * Lds::kBStride);
-                const bf16x8 bcol = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                const bf16x8 braw = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                // the column scaled by w_s (rounded once to bf16, as the product
+                // X^T (w o B) needs one of its operands scaled)
+                const f32x4 w0 = *reinterpret_cast<const f32x4*>(&sm.wst[s8]);
+                const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sm.wst[s8 + 4]);
+                bf16x8 bcol;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    bcol[e] = bf(f32(braw[e]) * w0[e]);
+                    bcol[4 + e] = bf(f32(braw[4 + e]) * w1[e]);
+                }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const bf16x8 xa = *reinterpret_cast<const bf16x8*>(
-                        &sm.XWt[(16 * j + c) * Lds::kXStride + Lds::xcol(16 * j + c, s8)]);
+                        &sm.Xt[(16 * j + c) * Lds::kXStride + Lds::xcol(16 * j + c, s8)]);
                     hacc[j] = mfma(xa, bcol, hacc[j]);
                 }
             }
