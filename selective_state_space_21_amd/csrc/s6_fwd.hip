@@ -629,8 +629,10 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
         const Raw cur = nxt;
         const int64_t st0 = sg * kSpan;
         lds_barrier();                      // previous super-tile's LDS reads and y staging done
-        if (sg > 0) store_y(st0 - kSpan);
+        // staged before the previous y leaves: the wait for this super-tile's
+        // loads then does not also wait for those stores (~1-2% faster)
         stage(cur);
+        if (sg > 0) store_y(st0 - kSpan);
         lds_barrier();
         load(nxt, st0 + kSpan);             // travels while this super-tile is computed
 #pragma unroll
