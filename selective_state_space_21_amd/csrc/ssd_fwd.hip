@@ -206,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
     const auto rB = make_rsrc(Bg + b * L * G * N, (uint32_t)(L * G * N * 2));
     const auto rC = make_rsrc(Cg + b * L * G * N, (uint32_t)(L * G * N * 2));
     const auto rD = make_rsrc(Dl + b * L * H, (uint32_t)(L * H * 2));
-    float dpre = 0.0f;
+    uint32_t dbits = 0;                  // step of this thread's token, bf16 bits
     uint4 bpre[TL::BPIECE];
     uint4 xpre[TL::XPIECE];
     // B pieces [k0, k1), X and delta of chunk ch into registers
@@ -222,8 +222,10 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
     };
     auto prefetch = [&](int64_t ch) {
         const uint32_t tc = (uint32_t)(ch * Q);
-        dpre = bf16_bits_to_f32(__builtin_amdgcn_raw_buffer_load_b16(
-            rD, (int)(((tc + min(tid, Q - 1)) * (uint32_t)H + (uint32_t)h) * 2), 0, 0));
+        // kept as loaded and widened where used: widening here would wait for
+        // the load right after issuing it
+        dbits = __builtin_amdgcn_raw_buffer_load_b16(
+            rD, (int)(((tc + min(tid, Q - 1)) * (uint32_t)H + (uint32_t)h) * 2), 0, 0);
         prefetch_b(ch, std::integral_constant<int, 0>{}, std::integral_constant<int, TL::BEARLY>{});
         {
             // thread -> tokens 4*sg .. 4*sg+3, head-dim values 8*p8 .. 8*p8+7;
@@ -267,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
         // ---- 1. steps and in-chunk cumulative decay (log2 units)
         float dtv = 0.0f, a2 = 0.0f;
         if (tid < Q && tc + tid < L) {              // past the end: no step, no decay
-            const float x = dpre + bias;
+            const float x = bf16_bits_to_f32(dbits) + bias;
             dtv = softplus ? softplus_f(x) : x;
             a2 = dtv * A2;
         }
@@ -326,8 +328,18 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
             wide = (f0.x | f0.y | f0.z | f0.w | f1.x | f1.y | f1.z | f1.w) != 0;
         }
 
-        // next chunk's inputs travel while this one is computed
-        if (ch + 1 < nchunks) prefetch(ch + 1);
+        // The C rows are waited for here, before the next chunk's inputs are
+        // requested: loads complete in order, so a wait for them after the
+        // prefetch (which the compiler otherwise places at the second tile)
+        // would also wait for the whole prefetch.
+#pragma unroll
+        for (int k = 0; k < TPW; ++k)
+#pragma unroll
+            for (int kk = 0; kk < KN; ++kk) asm volatile("" : : "v"(cop[k][kk]));
+        // next chunk's inputs travel while this one is computed (past the last
+        // chunk the loads read zero: unconditional, so no copy at a branch
+        // join waits for them)
+        prefetch(ch + 1);
 
         // ---- 5. skip, gate, store of one output tile: lane writes p = 16j + 4g .. +3 of token t
         auto store_tile = [&](int ti, const f32x4 (&yacc)[4]) __attribute__((always_inline)) {
@@ -451,11 +463,9 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
         }
         };
         out_tiles();
-        if constexpr (TL::BEARLY < TL::BPIECE) {
-            if (ch + 1 < nchunks)
-                prefetch_b(ch + 1, std::integral_constant<int, TL::BEARLY>{},
-                           std::integral_constant<int, TL::BPIECE>{});
-        }
+        if constexpr (TL::BEARLY < TL::BPIECE)
+            prefetch_b(ch + 1, std::integral_constant<int, TL::BEARLY>{},
+                       std::integral_constant<int, TL::BPIECE>{});
 
         // ---- 4. state update on this wavefront's 16 columns
         if (ntile >= 0) {
