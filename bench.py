@@ -48,9 +48,9 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3
 # (fetch x2.000, write x1.000); profiles/s6_scan_mamba130m_layer_bf16.md and
 # profiles/s6_split_mamba130m_layer_bf16.md, profiles/ssd_chunk_mamba2_bf16.md.  Valid for the kernels as profiled: to be
 # re-taken (or set to None) when those kernels change.
-S6_LANES_TRAFFIC_BYTES = int((75649.0 * 2.0 + 51620.0) * 1024)
+S6_LANES_TRAFFIC_BYTES = int((75527.0 * 2.0 + 50814.0) * 1024)
 S6_SCAN_TRAFFIC_BYTES = int((83273.4 * 2.0 + 49920.0) * 1024)
-SSD_CHUNK_TRAFFIC_BYTES = int((151680.0 * 2.0 + 270336.0) * 1024)
+SSD_CHUNK_TRAFFIC_BYTES = int((151675.0 * 2.0 + 270336.0) * 1024)
 
 
 def _hip():
