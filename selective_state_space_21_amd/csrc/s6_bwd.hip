@@ -242,6 +242,20 @@ __device__ __forceinline__ uint32_t load_bc_bits(const S6BwdArgs& p, int64_t t0,
     return Bits<T>::load(r, off);
 }
 
+// The same element for the super-tile fetch of the checkpoint sweep.  States
+// n >= N read zero through an offset with bit 31 set (past the resource,
+// which spans less than 2 GiB), formed without a select: of eight selects the
+// compiler built branches whose joins waited for every outstanding load (the
+// rest of the prefetch included) before the next offset was written.
+template <typename T>
+__device__ __forceinline__ uint32_t load_bc_bits_ahead(const S6BwdArgs& p, int64_t t0,
+                                                       __amdgpu_buffer_rsrc_t r) {
+    const int j = threadIdx.x / 16, n = threadIdx.x % 16;
+    const uint32_t o = (((uint32_t)t0 + (uint32_t)j) * (uint32_t)p.N + (uint32_t)n) * (uint32_t)sizeof(T);
+    const uint32_t past = ((uint32_t)((int)p.N - 1 - n) >> 31) << 31;   // n >= N
+    return Bits<T>::load(r, o | past);
+}
+
 // Inputs of kSuper consecutive tiles, fetched together so that one memory
 // round trip covers 128 tokens of the sequential sweep.
 constexpr int kSuper = 8;
@@ -274,7 +288,7 @@ struct SuperRaw {
                 delta[i] = r.delta;
                 u[i] = r.u;
             }
-            b[i] = load_bc_bits<T>(p, t0 + i * kTile, rB);
+            b[i] = load_bc_bits_ahead<T>(p, t0 + i * kTile, rB);
         }
     }
 };
