@@ -54,8 +54,9 @@ int ssd_check_sizes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64
     if (chunk != 64 && chunk != 128 && chunk != 256) return SSM_ERR_UNSUPPORTED;
     if (B * H > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;
     // one batch row of X (and of B/C) is addressed with 32-bit byte offsets,
-    // including the reads past a ragged last chunk
-    if ((L + 256) * H * P * 2 > (int64_t)0xFFFFFFFF || (L + 256) * G * N * 2 > (int64_t)0xFFFFFFFF)
+    // including the reads past a ragged last chunk and the prefetch of the
+    // chunk after the last (up to two chunks of 256 past L)
+    if ((L + 512) * H * P * 2 > (int64_t)0xFFFFFFFF || (L + 512) * G * N * 2 > (int64_t)0xFFFFFFFF)
         return SSM_ERR_UNSUPPORTED;
     return SSM_OK;
 }

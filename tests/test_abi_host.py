@@ -142,6 +142,13 @@ def test_ssd_validation_errors(lib):
     assert lib.ssm_ssd_chunk_workspace_bytes(4, 8192, 64, 64, 1, 128, 256, 1) == 0
 
 
+def test_ssd_offset_limit(lib):
+    # a batch row of X with two chunks of 256 tokens to spare must fit 32-bit
+    # byte offsets: H=64, P=64 is 8192 bytes per token, so L + 512 <= 524287
+    assert ssd(lib, L=524288 - 512, H=64) == 4
+    assert ssd(lib, L=2**20, H=64) == 4
+
+
 def step(lib, **kw):
     a = dict(state=FAKE, u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None,
              flags=1, y=FAKE, Bt=4, Dm=256, N=16, dtype=1, stream=None)
