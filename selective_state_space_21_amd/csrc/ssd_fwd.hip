@@ -98,9 +98,11 @@ struct Tiles {
     static constexpr int BPIECE = (Q * N / 8 + kThreads - 1) / kThreads;   // 16-B pieces / thread
     static constexpr int XGROUP = (Q / 4) * (kP / 8);          // (4 tokens x 8 p) groups
     static constexpr int XPIECE = 4;                           // 16-B rows per group
-    // B pieces fetched ahead of the output tiles; the rest after them, which
-    // keeps the largest tile shape inside the register file
-    static constexpr int BEARLY = (Q == 256 && N == 128) ? BPIECE / 2 : BPIECE;
+    // B pieces fetched ahead of the output tiles; the rest after them.  At the
+    // largest tile shape all of B is fetched after the tiles (it is mostly an
+    // L2 hit, shared by the heads of a batch row): the tiles then have 16 more
+    // registers, 338 -> 325 us at Q = 256, N = 128 (all early: 368)
+    static constexpr int BEARLY = (Q == 256 && N == 128) ? 0 : BPIECE;
     // k-th output tile of wavefront w (-1: none); pairs first with last
     static __device__ __forceinline__ int tile(int w, int k) {
         if constexpr (T >= 2 * kWaves) return k == 0 ? w : T - 1 - w;
