@@ -464,7 +464,128 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
             store_tile(ti, yacc);
         }
         };
-        out_tiles();
+        // Both output tiles of the wavefront at once (two tiles per wavefront:
+        // t0 = w and t1 = T - 1 - w).  The state rows of Y_off, and the B rows
+        // and X^T blocks of the score blocks below t0's diagonal, are read from
+        // LDS once for both tiles.
+        auto make_mop = [&](const f32x4 (&st)[2], int sb, int ti, float cum_t, auto wide_tag)
+            __attribute__((always_inline)) {
+            constexpr bool kWide = decltype(wide_tag)::value;
+            const int tl = 16 * ti + c;
+            const bool diag = 32 * sb + 31 > 16 * ti;
+            f32x4 fac[2];
+            if constexpr (!kWide) {
+                const float et = fast_exp2(cum_t - sm.cum[32 * sb]);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    fac[hh] = *reinterpret_cast<const f32x4*>(&sm.fblk[32 * sb + 16 * hh + 4 * g]) * et;
+            } else {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int sq = 32 * sb + 16 * hh + 4 * g;
+                    const f32x4 cs = *reinterpret_cast<const f32x4*>(&sm.cum[sq]);
+                    const f32x4 ds = *reinterpret_cast<const f32x4*>(&sm.dt[sq]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) fac[hh][r] = fast_exp2(cum_t - cs[r]) * ds[r];
+                }
+            }
+            bf16x8 mop;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int sq = 32 * sb + 16 * hh + 4 * g;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float m = st[hh][r] * fac[hh][r];
+                    if (diag && sq + r > tl) m = 0.0f;
+                    mop[4 * hh + r] = bf(m);
+                }
+            }
+            return mop;
+        };
+        auto xop_at = [&](int j, int sb) __attribute__((always_inline)) {
+            const __bf16* xr = &sm.Xt[(16 * j + c) * Lds::kXStride + Lds::xcol(16 * j + c, 32 * sb + 4 * g)];
+            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(xr);
+            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(xr + 16);
+            return (bf16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        auto out_pair = [&]() __attribute__((always_inline)) {
+            const int t0 = w, t1 = TL::T - 1 - w;
+            f32x4 y0[4], y1[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                y0[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                y1[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+#pragma unroll
+            for (int kk = 0; kk < KN; ++kk)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bf16x8 hop = *reinterpret_cast<const bf16x8*>(
+                        &sm.H[(16 * j + c) * Lds::kHStride + 32 * kk + 8 * g]);
+                    y0[j] = mfma(hop, cop[0][kk], y0[j]);
+                    y1[j] = mfma(hop, cop[1][kk], y1[j]);
+                }
+            const float cum0 = sm.cum[16 * t0 + c], cum1 = sm.cum[16 * t1 + c];
+            const float e0 = fast_exp2(cum0), e1 = fast_exp2(cum1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                y0[j] *= e0;
+                y1[j] *= e1;
+            }
+            const int nsb0 = (16 * t0 + 15) / 32 + 1, nsb1 = (16 * t1 + 15) / 32 + 1;
+            auto scores = [&](int sb, int k, f32x4 (&st)[2]) __attribute__((always_inline)) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    st[hh] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int kk = 0; kk < KN; ++kk) {
+                        const bf16x8 bop = *reinterpret_cast<const bf16x8*>(
+                            &sm.B[(32 * sb + 16 * hh + c) * Lds::kBStride + 32 * kk + 8 * g]);
+                        st[hh] = mfma(bop, cop[k][kk], st[hh]);
+                    }
+                }
+            };
+            auto blocks = [&](auto wide_tag) __attribute__((always_inline)) {
+                for (int sb = 0; sb < nsb0; ++sb) {
+                    f32x4 s0[2], s1[2];
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        s0[hh] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                        s1[hh] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                        for (int kk = 0; kk < KN; ++kk) {
+                            const bf16x8 bop = *reinterpret_cast<const bf16x8*>(
+                                &sm.B[(32 * sb + 16 * hh + c) * Lds::kBStride + 32 * kk + 8 * g]);
+                            s0[hh] = mfma(bop, cop[0][kk], s0[hh]);
+                            s1[hh] = mfma(bop, cop[1][kk], s1[hh]);
+                        }
+                    }
+                    const bf16x8 m0 = make_mop(s0, sb, t0, cum0, wide_tag);
+                    const bf16x8 m1 = make_mop(s1, sb, t1, cum1, wide_tag);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const bf16x8 xop = xop_at(j, sb);
+                        y0[j] = mfma(xop, m0, y0[j]);
+                        y1[j] = mfma(xop, m1, y1[j]);
+                    }
+                }
+                store_tile(t0, y0);
+                for (int sb = nsb0; sb < nsb1; ++sb) {
+                    f32x4 s1[2];
+                    scores(sb, 1, s1);
+                    const bf16x8 m1 = make_mop(s1, sb, t1, cum1, wide_tag);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) y1[j] = mfma(xop_at(j, sb), m1, y1[j]);
+                }
+                store_tile(t1, y1);
+            };
+            if (wide) blocks(std::true_type{});
+            else blocks(std::false_type{});
+        };
+        // measured at N = 128 (326 against 337 us); the paired form spills a
+        // few registers there, which are reloaded only around the tile stores
+        if constexpr (TPW == 2 && N == 128) out_pair();
+        else out_tiles();
         if constexpr (TL::BEARLY < TL::BPIECE)
             prefetch_b(ch + 1, std::integral_constant<int, TL::BEARLY>{},
                        std::integral_constant<int, TL::BPIECE>{});
