@@ -50,7 +50,7 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3
 # re-taken (or set to None) when those kernels change.
 S6_LANES_TRAFFIC_BYTES = int((75527.0 * 2.0 + 50814.0) * 1024)
 S6_SCAN_TRAFFIC_BYTES = int((83273.4 * 2.0 + 49920.0) * 1024)
-SSD_CHUNK_TRAFFIC_BYTES = int((151676.0 * 2.0 + 270336.0) * 1024)
+SSD_CHUNK_TRAFFIC_BYTES = int((153721.0 * 2.0 + 275968.0) * 1024)
 
 
 def _hip():
