@@ -95,10 +95,9 @@ const char* ssm_status_string(int status);
  *     by a wavefront-level scan in which each lane composes the pairs of one
  *     (b, d, n) chain in segment order.  The workspace holds those pairs.
  * The workspace query returns the split path's size (calls with
- * SSM_FLAG_ZOH take that path at any size).  It depends on
- * the sizes and on the CU count of the current device (the segment count and
- * the path balance wavefronts over its SIMDs): query and call on the same
- * device.
+ * SSM_FLAG_ZOH take that path at any size).  The plan (path, segment count,
+ * workspace size) is a pure function of the sizes: it balances wavefronts over
+ * the 1024 SIMDs of an MI355X and makes no HIP call.
  */
 size_t ssm_selective_scan_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
                                           int dtype);

@@ -191,10 +191,11 @@ def s6_step(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
 def causal_conv1d_silu(x, weight, bias=None, state=None, silu=True):
     """Causal depthwise convolution over tokens, then SiLU, in fp64.
 
-    The Mamba block passes one branch through a short causal depthwise
-    convolution and a SiLU before the selective SSM (temporalbook "Selective
-    State-Space Models (Mamba)", section 4; width d_conv = 4 in the block
-    constructor of section 5).  Reading: per channel d,
+    In the Mamba block the input of the selective SSM is first mixed over a
+    few neighbouring tokens, channel by channel and looking only backwards,
+    then put through SiLU (temporalbook "Selective State-Space Models
+    (Mamba)", section 4; width d_conv = 4 in the block constructor of
+    section 5).  Reading: per channel d,
         s[b,t,d] = bias[d] + sum_{k<K} weight[d,k] * x[b, t-(K-1)+k, d]
     (the last tap multiplies the current token), with x at negative times taken
     from `state` [B, D, K-1] (oldest first) or zero; u = s * sigmoid(s).

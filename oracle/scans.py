@@ -105,7 +105,9 @@ def scan_chunked(a, b, chunk, h0=None):
     """Split the sequence into chunks: reduce each chunk to one affine pair
     (product of a, end state from zero), scan those pairs to obtain each
     chunk's incoming state, then rerun each chunk from its incoming state.
-    This is the "scan within a block, carry the block's state forward" form.
+    This is the chunked prefill of the Transformer-math article ("What it
+    costs at inference, and on a CPU"): each block is scanned on its own and
+    its end state is handed on to the next.
     """
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)

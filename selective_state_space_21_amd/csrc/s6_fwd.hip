@@ -28,9 +28,10 @@
 //   s6_generic -- any N <= 64 and the ZOH variant: plain token loop with
 //                 wavefront-uniform scalar loads of B/C.
 //
-// Long sequences: the token axis is cut into S segments ("scan within a
-// block, carry the block's state forward", Transformer-math article, "What it
-// costs at inference").  Three launches:
+// Long sequences: the token axis is cut into S segments, each scanned on its
+// own and its end state handed to the next (the chunked prefill of the
+// Transformer-math article, section "What it costs at inference, and on a
+// CPU").  Three launches:
 //   1. s6_segment_reduce: each segment but the last reduces to the affine pair
 //      (decay = exp(A * sum dt), offset = its end state from h = 0);
 //   2. s6_carry_scan:    folds those pairs in segment order with the
@@ -45,7 +46,6 @@
 #include <stdint.h>
 #include <stdlib.h>
 
-#include <atomic>
 #include <type_traits>
 
 #include "device_math.h"
@@ -960,21 +960,10 @@ hipError_t launch_n(const S6Args& a, hipStream_t stream) {
     return launch_generic<T, 64, ZOH>(a, stream);
 }
 
-// SIMDs of the current device (four per CU), read once per device.
-int64_t simd_count() {
-    static std::atomic<int> cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-    const int slot = dev < 64 ? dev : 63;
-    int cus = cached[slot].load(std::memory_order_relaxed);
-    if (cus <= 0) {
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
-            cus = 256;
-        cached[slot].store(cus, std::memory_order_relaxed);
-    }
-    return 4 * (int64_t)cus;
-}
+// SIMDs the planner balances wavefronts over: MI355X has 256 CUs of four
+// SIMDs.  A constant, so that the plan (and the workspace size it implies) is a
+// pure function of the sizes and no HIP call is needed before validation ends.
+constexpr int64_t kSimds = 4 * 256;
 
 }  // namespace
 S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N) {
@@ -987,7 +976,7 @@ S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N) {
     {
         const bool shape_ok = N == 16 && D % lanes::kChans == 0 &&
                               (L + 2 * lanes::kSpan) * D * 4 <= (int64_t)0xFFFFFFFF;
-        pl.lanes = shape_ok && B * D / 4 >= 2 * simd_count();
+        pl.lanes = shape_ok && B * D / 4 >= 2 * kSimds;
         const char* env = getenv("SSM_S6_LANES");
         if (env && env[0] == '0') pl.lanes = false;
         if (env && env[0] == '1') pl.lanes = shape_ok;
@@ -998,7 +987,7 @@ S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N) {
     // wavefronts and all SIMDs the same number (a whole multiple of the SIMD
     // count), else the one nearest three per SIMD.
     const int64_t waves = B * ((D + kWave - 1) / kWave);
-    const int64_t simds = simd_count();
+    const int64_t simds = kSimds;
     const int64_t min_seg = 32;
     int64_t maxS = (L + min_seg - 1) / min_seg;
     if (maxS > kMaxSegments) maxS = kMaxSegments;

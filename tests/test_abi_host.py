@@ -96,7 +96,7 @@ def test_s6_plan_env_override(lib, monkeypatch):
 
 
 def test_s6_lanes_plan(lib, monkeypatch):
-    # Without a GPU the planner assumes 256 CUs (1024 SIMDs): the state-per-lane
+    # The planner balances over 1024 SIMDs (256 CUs), device or not: the state-per-lane
     # kernel needs N = 16, D % 16 == 0 and B*D/4 >= 2048 wavefronts
     monkeypatch.delenv("SSM_S6_LANES", raising=False)
     assert lib.ssm_selective_scan_lanes(8, 2048, 1536, 16) == 1
@@ -262,3 +262,54 @@ def test_python_wrapper_rejects_host_tensors():
     u = torch.zeros(1, 4, 64)
     with pytest.raises(ValueError):
         ssm.selective_scan_fwd(u, u, torch.zeros(64, 16), torch.zeros(1, 4, 16), torch.zeros(1, 4, 16))
+
+
+def test_python_wrappers_check_out_shapes_before_devices():
+    """A caller-supplied output buffer of the wrong shape (or dtype) is
+    rejected, by every wrapper, before any device check, so these host tensors
+    never get near the library."""
+    import torch
+    import selective_state_space_21_amd as ssm
+    bf = torch.bfloat16
+    u = torch.zeros(2, 8, 64, dtype=bf)
+    A = torch.zeros(64, 16)
+    Bm = torch.zeros(2, 8, 16, dtype=bf)
+    with pytest.raises(ValueError, match="out has shape"):
+        ssm.selective_scan_fwd(u, u, A, Bm, Bm, out=torch.zeros(2, 7, 64, dtype=bf))
+    with pytest.raises(TypeError, match="out must be"):
+        ssm.selective_scan_fwd(u, u, A, Bm, Bm, out=torch.zeros(2, 8, 64))
+    with pytest.raises(ValueError, match="out has shape"):
+        ssm.selective_scan_conv_fwd(u, torch.zeros(64, 4), None, u, A, Bm, Bm,
+                                    out=torch.zeros(1, 8, 64, dtype=bf))
+    X = torch.zeros(1, 8, 2, 64, dtype=bf)
+    Bg = torch.zeros(1, 8, 1, 128, dtype=bf)
+    with pytest.raises(ValueError, match="out has shape"):
+        ssm.ssd_chunk_fwd(X, torch.zeros(1, 8, 2, dtype=bf), torch.zeros(2), Bg, Bg,
+                          out=torch.zeros(1, 8, 2, 32, dtype=bf))
+    st = torch.zeros(2, 64, 16)
+    v = torch.zeros(2, 64, dtype=bf)
+    with pytest.raises(ValueError, match="out has shape"):
+        ssm.selective_state_update(st, v, v, A, torch.zeros(2, 16, dtype=bf),
+                                   torch.zeros(2, 16, dtype=bf), out=torch.zeros(2, 63, dtype=bf))
+    with pytest.raises(ValueError, match="out has shape"):
+        ssm.causal_conv1d_silu(u, torch.zeros(64, 4), out=torch.zeros(2, 8, 32, dtype=bf))
+    # an input of the wrong shape is caught the same way
+    with pytest.raises(ValueError, match="C has shape"):
+        ssm.selective_scan_fwd(u, u, A, Bm, torch.zeros(2, 8, 8, dtype=bf))
+
+
+def test_python_workspace_checks():
+    """A workspace must be a contiguous uint8 tensor on the call's device, at
+    least as large as the query."""
+    import torch
+    from selective_state_space_21_amd import _check_workspace
+    dev = torch.device("cuda:0")
+    assert _check_workspace(None, 100, dev) is None
+    with pytest.raises(ValueError, match="expected cuda:0"):
+        _check_workspace(torch.empty(128, dtype=torch.uint8), 100, dev)
+    with pytest.raises(TypeError, match="uint8"):
+        _check_workspace(torch.empty(128, dtype=torch.float32), 100, dev)
+    with pytest.raises(ValueError, match="needs 100"):
+        _check_workspace(torch.empty(64, dtype=torch.uint8), 100, dev)
+    with pytest.raises(TypeError):
+        _check_workspace(12345, 100, dev)

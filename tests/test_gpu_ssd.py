@@ -38,6 +38,13 @@ def test_state_sizes(N):
     _cmp(W.make_ssd_inputs(w, seed=N))
 
 
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_state64_every_chunk(chunk):
+    """N = 64 at each chunk length, ragged L, with skip, gate, bias and h0."""
+    w = W.SSD_MAMBA2.scaled(B=2, L=517, H=3, N=64, chunk=chunk)
+    _cmp(_with_extras(W.make_ssd_inputs(w, seed=chunk + 64), chunk), chunk=chunk)
+
+
 def test_groups():
     w = W.SSD_MAMBA2.scaled(B=2, L=333, H=8, G=2, chunk=64)
     _cmp(W.make_ssd_inputs(w, seed=3))
@@ -154,3 +161,59 @@ def test_full_size_sampled():
     print(f"{w.name}: sampled Y err {ey:.3e}, h_last err {eh:.3e}")
     assert ey <= 2e-2 and eh <= 2e-2
     assert np.all(np.isfinite(Y))
+
+
+def _block_decay_log2(inp, chunk):
+    """For each (b, h, chunk): the largest decay, in log2 units, from the first
+    token of a 32-token block to a later token of the same block (the cumulative
+    sum of dt * A * log2(e) inside the chunk, differenced against the block's
+    first token).  Plain numpy on the CPU from the inputs."""
+    raw = inp["delta"].float().numpy().astype(np.float64)
+    bias = inp["delta_bias"].numpy().astype(np.float64)
+    A = inp["A"].numpy().astype(np.float64)
+    x = raw + bias
+    dt = np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+    a = dt * A * np.log2(np.e)                       # [B, L, H]
+    Bt, L, H = a.shape
+    nch = -(-L // chunk)
+    pad = np.zeros((Bt, nch * chunk, H))
+    pad[:, :L] = a
+    cum = np.cumsum(pad.reshape(Bt, nch, chunk, H), axis=2)
+    first = cum.reshape(Bt, nch, chunk // 32, 32, H)[:, :, :, :1, :]
+    rel = first - cum.reshape(Bt, nch, chunk // 32, 32, H)
+    return np.abs(rel).max(axis=(2, 3))              # [B, nch, H]
+
+
+def _spiked_case(L, H, N, chunk, seed):
+    """Random X, B and C; steps softplus(N(-2, 0.5) + bias) with strong decays
+    |A_h| in [2, 5]; in about one 32-token block in twelve, 40% of the tokens
+    have their raw step raised to +2.5 (a write/flush spike), so those blocks
+    decay by far more than 2^64 while the others stay well below.  Skip, gate,
+    bias and h0 are on."""
+    w = W.SSD_MAMBA2.scaled(B=2, L=L, H=H, N=N, chunk=chunk)
+    inp = _with_extras(W.make_ssd_inputs(w, seed=seed), seed)
+    rng = np.random.default_rng(seed + 1000)
+    raw = inp["delta"].float().numpy().copy()
+    nblk = -(-L // 32)
+    hot = rng.random((2, nblk)) < 1.0 / 12.0
+    for b in range(2):
+        for k in np.nonzero(hot[b])[0]:
+            toks = 32 * k + np.nonzero(rng.random(32) < 0.4)[0]
+            raw[b, toks[toks < L], :] = 2.5
+    inp["delta"] = torch.from_numpy(raw).to(torch.bfloat16)
+    inp["delta_bias"] = torch.from_numpy(rng.uniform(-0.5, 0.0, size=H).astype(np.float32))
+    inp["A"] = -torch.from_numpy(rng.uniform(2.0, 5.0, size=H).astype(np.float32))
+    return inp
+
+
+@pytest.mark.parametrize("chunk,N", [(64, 128), (256, 128), (64, 64), (128, 64), (256, 64)])
+def test_wide_block_decay(chunk, N):
+    """Chunks where a 32-token block decays by more than 2^64 (which the kernel
+    handles with a per-element mask) next to chunks where none does, in one
+    call, against the oracle at the bf16 bar."""
+    inp = _spiked_case(L=1000, H=4, N=N, chunk=chunk, seed=chunk + N)
+    span = _block_decay_log2(inp, chunk)
+    assert np.any(span > 64.0), "no chunk reaches the wide case"
+    assert np.any(span <= 64.0), "every chunk is wide"
+    ey, eh = _cmp(inp, chunk=chunk)
+    print(f"wide chunks {np.mean(span > 64.0):.2f}; Y err {ey:.2e}, h_last err {eh:.2e}")
