@@ -7,22 +7,30 @@ A step is one S6 selective-scan forward (softplus step, per-token
 discretisation, state update, readout, skip, silu gate, segment carry) over the
 Mamba-130M-shaped layer workload B=8 L=2048 D=1536 N=16 with bf16 activations
 and fp32 state; inputs are seeded synthetic tensors resident in HBM before the
-timed region.  Before every step a 512 MiB buffer is rewritten (outside the
-timed interval) so that the 203 MB working set is not served from the 256 MB
-Infinity Cache.  Each step is bracketed by HIP events recorded by the library
-itself on the stream it launches on, at its phase boundaries (segment reduce,
-carry scan, segment scan); `value` is the algorithmic bytes of the step
-divided by the mean step time.  The default 60 untimed warm-up steps bring the
-GPU to its steady clock first (the first ~40 calls of a cold process run up to
-~10% slower).
+timed region.  `value` is the algorithmic bytes of the step (every input read
+once, y and the final state written once) divided by the mean step time
+between two HIP events on the stream the library launches on.
 
-The same run also measures, under "paths", the other calls of the library on
-their own workloads (each flushed and timed the same way): the SSD chunked
-forward (Mamba-2, B=4 L=8192 H=64 P=64 N=128, chunk 256), the decode step
-(64 sequences, D=5120 N=16), the backward pass with recomputation, the
-causal conv1d + SiLU, and the conv1d fused in front of the scan (all three on
-the Mamba-130M layer shape), and it times the
-fp64 CPU oracle on the host cores over the whole S6 workload.
+Cache: the 203 MB working set fits the 256 MB Infinity Cache, so before every
+timed call a 512 MiB buffer is read (outside the timed interval).  A read pass
+leaves clean lines behind; the previous protocol rewrote the buffer instead,
+which left the cache full of dirty lines whose write-back then landed inside
+the timed call.  Both are reported for the headline workload
+(`ms_per_step_dirty_flush`), as is the time of back-to-back calls without any
+flush.
+
+The same run measures, under "paths", the other workloads and calls of the
+library, each flushed and timed the same way: the Mamba-2.8B-shaped layer
+scan, the long fp32 sequence (131072 tokens, split over the sequence with a
+segment carry), the SSD chunked forward (Mamba-2), the decode step, the
+backward pass with recomputation, the causal conv1d + SiLU and the conv1d
+fused in front of the scan.  It also times a plain device copy of the same
+byte count as the practical bandwidth ceiling.
+
+The CPU leg (`cpu_baseline`) times the fp64 oracle on the host, on one thread
+and on all cores, and checks sampled outputs of every timed S6 and SSD call
+against it before the line is printed (the line carries `verified`; a failed
+check exits with status 1 after printing).
 
 `--only PART` runs one part alone and prints its result (for profiling).
 Prints one JSON line.  Only one GPU is used; --gpus above 1 exits.
@@ -31,26 +39,61 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+CSRC = os.path.join(ROOT, "selective_state_space_21_amd", "csrc")
 
-HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
+HBM_PEAK_GBS = 8000.0           # MI355X published HBM3E bandwidth
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+# MI355X published fp32 vector peak: 256 CUs x 2.4 GHz x 256 flop/clk.  On
+# gfx950 this is the rate of plain (non-packed) v_fma_f32: the issue-rate probe
+# runs only v_fmaak_f32 and reaches 52.25 T lane-FMA/s (66% of 78.6 T), above
+# what 64 lanes per CU per clock would allow (profiles/issue_rates_gfx950.md).
 FP32_VECTOR_PEAK_TFLOPS = 157.3
+# The bare per-element pattern of the scan (dt*A, exp2, dt*u*B, state FMA,
+# readout FMA) measured on its own at 8 waves per SIMD: the rate a scan kernel
+# cannot exceed while it evaluates one v_exp_f32 per state update
+# (profiles/issue_rates_gfx950.md).
+ISSUE_PEAK_ELEMS_PER_S = 6.41e12
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per
-# dispatch), scaled by what the same counters read for a 256 MiB copy
-# (fetch x2.000, write x1.000); profiles/s6_scan_mamba130m_layer_bf16.md and
-# profiles/s6_split_mamba130m_layer_bf16.md, profiles/ssd_chunk_mamba2_bf16.md.  Valid for the kernels as profiled: to be
-# re-taken (or set to None) when those kernels change.
-S6_LANES_TRAFFIC_BYTES = int((75527.0 * 2.0 + 50814.0) * 1024)
-S6_SCAN_TRAFFIC_BYTES = int((83273.4 * 2.0 + 49920.0) * 1024)
-SSD_CHUNK_TRAFFIC_BYTES = int((153721.0 * 2.0 + 275968.0) * 1024)
+# dispatch), scaled by what the same counters read for a 256 MiB copy (fetch
+# x2.000, write x1.000), with the hash of the sources the kernel was built from
+# when the counters were taken.  A kernel whose sources changed since then
+# reports traffic null until its counters are taken again.
+COUNTER_TRAFFIC = {
+    # kernel@workload: (bytes, sources, sha1 of the sources)
+}
+KERNEL_SOURCES = {
+    "s6": ["s6_fwd.hip", "device_math.h", "lane_ops.h", "ssm_internal.h"],
+    "ssd": ["ssd_fwd.hip", "device_math.h", "lane_ops.h", "ssm_internal.h"],
+}
+
+
+def sources_sha1(files) -> str:
+    h = hashlib.sha1()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:12]
+
+
+def counter_traffic(key: str):
+    """(bytes or None, note) for a kernel@workload key."""
+    ent = COUNTER_TRAFFIC.get(key)
+    if ent is None:
+        return None, "no counter run for this kernel"
+    nbytes, srcs, sha = ent
+    if sources_sha1(srcs) != sha:
+        return None, "kernel sources changed since the counters were taken"
+    return nbytes, "rocprofv3 FETCH_SIZE/WRITE_SIZE scaled by a 256 MiB copy"
 
 
 def _hip():
@@ -78,158 +121,207 @@ def _elapsed(hip, a, b):
     return ms.value
 
 
-def bench_s6(args, torch, ssm, W, native, hip):
-    w = W.S6_MAMBA130M
+class Flusher:
+    """Evicts the 256 MB Infinity Cache before a timed call (untimed): `clean`
+    reads a 512 MiB buffer (the lines it leaves are clean), `dirty` rewrites it
+    (the old protocol: the dirty lines are written back during the next call)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.buf = torch.zeros(512 * 2**20 // 4, dtype=torch.float32, device="cuda:0")
+        self.i = 0
+
+    def clean(self):
+        self.torch.sum(self.buf)
+
+    def dirty(self):
+        self.i += 1
+        self.buf.fill_(float(self.i))
+
+
+class Timer:
+    """Mean/median/min ms of a call between two HIP events recorded on the
+    stream the call launches on, each call preceded by `flush` (untimed)."""
+
+    def __init__(self, torch, hip):
+        self.torch, self.hip = torch, hip
+        self.ev = _events(hip, 2)
+
+    def run(self, fn, steps, warmup, flush=None):
+        torch, hip = self.torch, self.hip
+        stream = torch.cuda.current_stream().cuda_stream
+        for _ in range(warmup):
+            if flush:
+                flush()
+            fn()
+        torch.cuda.synchronize()
+        per = []
+        for _ in range(steps):
+            if flush:
+                flush()
+            hip.hipEventRecord(self.ev[0], stream)
+            fn()
+            hip.hipEventRecord(self.ev[1], stream)
+            torch.cuda.synchronize()
+            per.append(_elapsed(hip, self.ev[0], self.ev[1]))
+        per.sort()
+        return dict(mean=sum(per) / len(per), median=per[len(per) // 2], min=per[0])
+
+
+def roofline(kind, achieved, peak, unit, traffic=None, note=None, **extra):
+    r = {"bound": kind, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4), "traffic": traffic}
+    if note:
+        r["traffic_note"] = note
+    r.update(extra)
+    return r
+
+
+# ------------------------------------------------------------------ S6
+def bench_s6(args, ctx, w, headline=False):
+    torch, ssm, W, native, hip = ctx["torch"], ctx["ssm"], ctx["W"], ctx["native"], ctx["hip"]
     t = W.make_s6_inputs(w, seed=0)
     dev = torch.device("cuda:0")
     d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
     y = torch.empty_like(d["u"])
     h_last = torch.empty((w.B, w.D, w.N), dtype=torch.float32, device=dev)
-    ws_bytes = ssm.selective_scan_workspace_bytes(w.B, w.L, w.D, w.N, torch.bfloat16)
+    dtc = native.SSM_BF16 if w.dtype == "bf16" else native.SSM_F32
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    ws_bytes = ssm.selective_scan_workspace_bytes(w.B, w.L, w.D, w.N, tdt)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     lanes = ssm.selective_scan_lanes(w.B, w.L, w.D, w.N)
     segments = 1 if lanes else ssm.selective_scan_segments(w.B, w.L, w.D, w.N)
-    flush = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
     lib = native.load()
     stream = torch.cuda.current_stream(dev)
     evs = _events(hip, 4)
+    ptr = lambda k: None if d[k] is None else d[k].data_ptr()
 
-    def step(events):
+    def step(events=None):
         rc = lib.ssm_selective_scan_fwd_timed(
-            d["u"].data_ptr(), d["delta"].data_ptr(), d["A"].data_ptr(), d["B"].data_ptr(),
-            d["C"].data_ptr(), d["D"].data_ptr(), d["z"].data_ptr(), d["delta_bias"].data_ptr(),
-            native.FLAG_DELTA_SOFTPLUS, None, y.data_ptr(), h_last.data_ptr(),
-            w.B, w.L, w.D, w.N, native.SSM_BF16, ws.data_ptr(), ws_bytes, stream.cuda_stream,
-            events)
+            ptr("u"), ptr("delta"), ptr("A"), ptr("B"), ptr("C"), ptr("D"), ptr("z"),
+            ptr("delta_bias"), native.FLAG_DELTA_SOFTPLUS, None, y.data_ptr(), h_last.data_ptr(),
+            w.B, w.L, w.D, w.N, dtc, ws.data_ptr(), ws_bytes, stream.cuda_stream, events)
         native.check(rc, "ssm_selective_scan_fwd_timed")
 
-    for i in range(args.warmup):
-        flush.fill_(float(i))
-        step(None)
-    torch.cuda.synchronize()
-    # the call as a whole, between two events on its stream
-    total = 0.0
-    per_step = []
+    fl = ctx["flusher"]
+    tm = ctx["timer"]
     wall0 = time.perf_counter()
-    for i in range(args.steps):
-        flush.fill_(float(i))                      # evict the Infinity Cache (untimed)
-        hip.hipEventRecord(evs[0], stream.cuda_stream)
-        step(None)
-        hip.hipEventRecord(evs[1], stream.cuda_stream)
-        torch.cuda.synchronize()
-        per_step.append(_elapsed(hip, evs[0], evs[1]))
-        total += per_step[-1]
-    torch.cuda.synchronize()
+    res = tm.run(step, args.steps, args.warmup, fl.clean)
     wall = time.perf_counter() - wall0
-    # the split path's phases (the library records an event at each boundary;
-    # a recorded event costs a few microseconds, so this loop is kept apart)
+    # phases (the library records an event at each boundary; recording costs a
+    # few microseconds, so this loop is kept apart from the timed one)
     phases = [0.0, 0.0, 0.0]
-    for i in range(args.steps):
-        flush.fill_(float(i))
+    n_ph = max(3, args.steps // 4)
+    for _ in range(n_ph):
+        fl.clean()
         step(evs)
         torch.cuda.synchronize()
         for k in range(3):
             phases[k] += _elapsed(hip, evs[k], evs[k + 1])
-    # back-to-back steps without the flush (working set may sit in the MALL)
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(None)
+    phases = [p / n_ph for p in phases]
+    extra = {}
+    if headline:
+        extra["dirty"] = tm.run(step, args.steps, 0, fl.dirty)
+        extra["hot"] = tm.run(step, args.steps, 0, None)
     torch.cuda.synchronize()
-    hot_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-
-    ms = total / args.steps
+    ms = res["mean"]
     nbytes = W.s6_algorithmic_bytes(w)
-    gbs = nbytes / (ms * 1e-3) / 1e9
     elems = w.B * w.L * w.D * w.N
-    # the state-per-lane call is one kernel: its time is the call's
-    scan_ms = ms if lanes else phases[2] / args.steps
-    reduce_ms = phases[0] / args.steps
-    carry_ms = phases[1] / args.steps
-    scan_gbs = nbytes / (scan_ms * 1e-3) / 1e9
-    flops = 6.0 * elems                            # mul, mul, fma, fma per state update
-    return dict(
-        ms_median=sorted(per_step)[len(per_step) // 2], ms_min=min(per_step),
-        w=w, t=t, ms=ms, gbs=gbs, nbytes=nbytes, segments=segments, lanes=lanes, wall=wall,
-        hot_ms=hot_ms,
-        phases_ms=(dict(state_per_lane=scan_ms) if lanes else
-                   dict(segment_reduce=reduce_ms, carry_scan=carry_ms, segment_scan=scan_ms)),
-        scan_gbs=scan_gbs, scan_tflops=flops / (scan_ms * 1e-3) / 1e12,
-        gtokch=w.tok_ch / (ms * 1e-3) / 1e9, elems=elems)
+    if lanes:
+        ph = {"state_per_lane": phases[2]}
+        dom_name, dom_ms = "s6_lanes", phases[2]
+    else:
+        ph = {"segment_pass": phases[0], "carry": phases[1], "final_pass": phases[2]}
+        dom_name, dom_ms = ("s6 final pass", phases[2]) if phases[2] >= phases[0] else \
+            ("s6 segment pass", phases[0])
+    key = f"{'s6_lanes' if lanes else 's6_split'}@{w.name}"
+    traffic, note = counter_traffic(key)
+    # the dominant kernel's share of the algorithmic bytes: on the
+    # state-per-lane path it is the whole call
+    dom_gbs = nbytes / (dom_ms * 1e-3) / 1e9 if lanes else nbytes / (ms * 1e-3) / 1e9
+    out = dict(
+        status="ok", workload=w.name, B=w.B, L=w.L, D=w.D, N=w.N, io_dtype=w.dtype,
+        path="state_per_lane" if lanes else "split", segments=segments,
+        ms=round(ms, 5), ms_median=round(res["median"], 5), ms_min=round(res["min"], 5),
+        gbs=round(nbytes / (ms * 1e-3) / 1e9, 2),
+        pct_hbm_peak=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS * 100, 2),
+        gtokch=round(w.tok_ch / (ms * 1e-3) / 1e9, 3), algorithmic_bytes=nbytes,
+        phases_ms={k: round(v, 5) for k, v in ph.items()},
+        roofline=roofline("hbm", dom_gbs, HBM_PEAK_GBS, "GB/s", traffic, note,
+                          kernel=dom_name),
+        issue=roofline("issue", elems / (ms * 1e-3) / 1e9, ISSUE_PEAK_ELEMS_PER_S / 1e9,
+                       "G state updates/s",
+                       peak_source="the bare per-element pattern (4 VALU + 1 v_exp_f32) "
+                                   "measured alone at 8 waves per SIMD"),
+        alu_view={"achieved_tflops": round(6.0 * elems / (ms * 1e-3) / 1e12, 3),
+                  "peak_tflops": FP32_VECTOR_PEAK_TFLOPS, "flops_per_state_update": 6,
+                  "transcendentals_per_state_update": 1},
+        wall_s=round(wall, 3))
+    if headline:
+        out["ms_dirty_flush"] = round(extra["dirty"]["mean"], 5)
+        out["ms_no_flush"] = round(extra["hot"]["mean"], 5)
+    import numpy as np
+    samples = _sample_channels(w, np.random.default_rng(123))
+    ctx["verify"].append(("s6", w, t, samples,
+                          [y[b][:, ds].float().cpu() for b, ds in samples],
+                          [h_last[b][ds].cpu() for b, ds in samples]))
+    return out
 
 
-def bench_ssd(args, torch, ssm, W):
+# ------------------------------------------------------------------ SSD
+def bench_ssd(args, ctx):
+    torch, ssm, W = ctx["torch"], ctx["ssm"], ctx["W"]
     s = W.SSD_MAMBA2
     t = W.make_ssd_inputs(s, seed=0)
     dev = torch.device("cuda:0")
     d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
     Y = torch.empty_like(d["X"])
-    flush = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
 
     def step():
         ssm.ssd_chunk_fwd(d["X"], d["delta"], d["A"], d["B"], d["C"], chunk=s.chunk, out=Y)
 
     try:
-        step()
+        ssm.ssd_chunk_fwd(d["X"], d["delta"], d["A"], d["B"], d["C"], chunk=s.chunk, out=Y)
     except ssm.SSMError as e:
         return dict(status=f"unavailable: {e}")
-    for _ in range(max(1, args.warmup)):
-        step()
+    res = ctx["timer"].run(step, args.steps, args.warmup, ctx["flusher"].clean)
+    _, h_last = ssm.ssd_chunk_fwd(d["X"], d["delta"], d["A"], d["B"], d["C"], chunk=s.chunk,
+                                  out=Y)
     torch.cuda.synchronize()
-    total = 0.0
-    for i in range(args.steps):
-        flush.fill_(float(i))
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        step()
-        b.record()
-        torch.cuda.synchronize()
-        total += a.elapsed_time(b)
-    ms = total / args.steps
+    ms = res["mean"]
     nbytes = W.ssd_algorithmic_bytes(s)
     Q = s.chunk
     nchunks = -(-s.L // Q)
     # causal chunked-SSD MACs: the scores C B^T (lower triangle, Q(Q+1)/2 * N)
     # once per (b, group, chunk), as they depend on the group only; per (b, h,
     # chunk) the masked Y_diag (Q(Q+1)/2 * P), chunk state (P*N*Q) and Y_off
-    # (Q*P*N).  The kernel forms the scores per head, so it executes more.
+    # (Q*P*N).
     tri = Q * (Q + 1) / 2
     per_head = tri * s.P + 2 * s.P * s.N * Q
     macs = s.B * nchunks * (s.G * tri * s.N + s.H * per_head)
     macs_exec = s.B * nchunks * s.H * (tri * s.N + per_head)
-    return dict(status="ok", workload=s.name, ms=round(ms, 5),
-                gbs=round(nbytes / (ms * 1e-3) / 1e9, 2),
-                pct_hbm_peak=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS * 100, 2),
+    traffic, note = counter_traffic(f"ssd@{s.name}")
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    pairs = [(0, 0), (s.B - 1, s.H - 1)]
+    ctx["verify"].append(("ssd", s, t, pairs, [Y[b, :, hh].float().cpu() for b, hh in pairs],
+                          [h_last[b, hh].cpu() for b, hh in pairs]))
+    return dict(status="ok", workload=s.name, ms=round(ms, 5), ms_median=round(res["median"], 5),
+                ms_min=round(res["min"], 5), gbs=round(gbs, 2),
+                pct_hbm_peak=round(gbs / HBM_PEAK_GBS * 100, 2),
                 tflops=round(2 * macs / (ms * 1e-3) / 1e12, 2),
                 mfma_util=round(2 * macs / (ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                 gtokch=round(s.tok_ch / (ms * 1e-3) / 1e9, 3), algorithmic_bytes=nbytes,
                 causal_gflop=round(2 * macs / 1e9, 3),
                 executed_gflop=round(2 * macs_exec / 1e9, 3),
                 executed_tflops=round(2 * macs_exec / (ms * 1e-3) / 1e12, 2),
-                hbm_traffic_bytes=SSD_CHUNK_TRAFFIC_BYTES)
+                roofline=roofline("hbm", gbs, HBM_PEAK_GBS, "GB/s", traffic, note,
+                                  kernel="ssd_chunk_kernel (the only kernel of the call)"),
+                mfma_view=roofline("mfma", 2 * macs / (ms * 1e-3) / 1e12, BF16_MFMA_PEAK_TFLOPS,
+                                   "TFLOP/s"))
 
 
-def _time_flushed(torch, fn, steps, warmup):
-    """Mean ms of fn() over `steps` calls, each after rewriting a 512 MiB
-    buffer (untimed), bracketed by events on the current stream."""
-    flush = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device="cuda:0")
-    for _ in range(max(1, warmup)):
-        fn()
-    torch.cuda.synchronize()
-    total = 0.0
-    for i in range(steps):
-        flush.fill_(float(i))
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        fn()
-        b.record()
-        torch.cuda.synchronize()
-        total += a.elapsed_time(b)
-    return total / steps
-
-
-def bench_decode(args, torch, ssm, W):
+def bench_decode(args, ctx):
+    torch, ssm, W = ctx["torch"], ctx["ssm"], ctx["W"]
     w = W.S6_DECODE_2P8B
     t = W.make_step_inputs(w, seed=0)
     d = {k: (v.to("cuda:0") if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
@@ -239,7 +331,7 @@ def bench_decode(args, torch, ssm, W):
         ssm.selective_state_update(d["state"], d["u"], d["delta"], d["A"], d["B"], d["C"],
                                    D=d["D"], z=d["z"], delta_bias=d["delta_bias"], out=y)
 
-    ms = _time_flushed(torch, step, args.steps, args.warmup)
+    ms = ctx["timer"].run(step, args.steps, args.warmup, ctx["flusher"].clean)["mean"]
     nbytes = W.step_algorithmic_bytes(w)
     return dict(status="ok", workload=w.name, ms=round(ms, 5), algorithmic_bytes=nbytes,
                 gbs=round(nbytes / (ms * 1e-3) / 1e9, 2),
@@ -247,7 +339,8 @@ def bench_decode(args, torch, ssm, W):
                 state_updates_per_s=round(w.B * w.D * w.N / (ms * 1e-3), 1))
 
 
-def bench_bwd(args, torch, ssm, W):
+def bench_bwd(args, ctx):
+    torch, ssm, W = ctx["torch"], ctx["ssm"], ctx["W"]
     w = W.S6_MAMBA130M
     t = W.make_s6_inputs(w, seed=0)
     d = {k: (v.to("cuda:0") if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
@@ -260,7 +353,7 @@ def bench_bwd(args, torch, ssm, W):
         ssm.selective_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], dy, D=d["D"],
                                z=d["z"], delta_bias=d["delta_bias"], workspace=ws)
 
-    ms = _time_flushed(torch, step, args.steps, args.warmup)
+    ms = ctx["timer"].run(step, args.steps, args.warmup, ctx["flusher"].clean)["mean"]
     e = 2
     # inputs u, delta, z, dy, B, C read and du, ddelta, dz written once (bf16);
     # dB, dC fp32; A, dA and the per-channel vectors are negligible
@@ -270,7 +363,8 @@ def bench_bwd(args, torch, ssm, W):
                 gtokch=round(w.tok_ch / (ms * 1e-3) / 1e9, 3), workspace_bytes=need)
 
 
-def bench_conv(args, torch, ssm, W):
+def bench_conv(args, ctx):
+    torch, ssm, W = ctx["torch"], ctx["ssm"], ctx["W"]
     w = W.CONV_MAMBA130M
     t = W.make_conv_inputs(w, seed=0)
     d = {k: v.to("cuda:0") for k, v in t.items()}
@@ -279,17 +373,18 @@ def bench_conv(args, torch, ssm, W):
     def step():
         ssm.causal_conv1d_silu(d["x"], d["weight"], d["bias"], out=u)
 
-    ms = _time_flushed(torch, step, args.steps, args.warmup)
+    ms = ctx["timer"].run(step, args.steps, args.warmup, ctx["flusher"].clean)["mean"]
     nbytes = W.conv_algorithmic_bytes(w)
     return dict(status="ok", workload=w.name, ms=round(ms, 5), algorithmic_bytes=nbytes,
                 gbs=round(nbytes / (ms * 1e-3) / 1e9, 2),
                 pct_hbm_peak=round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS * 100, 2))
 
 
-def bench_conv_scan(args, torch, ssm, W):
+def bench_conv_scan(args, ctx):
     """The conv1d + SiLU fused in front of the S6 scan, on the Mamba-130M layer
     shape with a K = 4 convolution: x replaces u as the input, so the
     algorithmic bytes are those of the scan plus the convolution weights."""
+    torch, ssm, W = ctx["torch"], ctx["ssm"], ctx["W"]
     w = W.S6_MAMBA130M
     t = W.make_s6_inputs(w, seed=0)
     cv = W.make_conv_inputs(W.CONV_MAMBA130M, seed=1)
@@ -303,51 +398,144 @@ def bench_conv_scan(args, torch, ssm, W):
         ssm.selective_scan_conv_fwd(x, cw, cb, d["delta"], d["A"], d["B"], d["C"], D=d["D"],
                                     z=d["z"], delta_bias=d["delta_bias"], out=y, workspace=ws)
 
-    ms = _time_flushed(torch, step, args.steps, args.warmup)
+    ms = ctx["timer"].run(step, args.steps, args.warmup, ctx["flusher"].clean)["mean"]
     nbytes = W.s6_algorithmic_bytes(w) + W.CONV_MAMBA130M.D * (W.CONV_MAMBA130M.K + 1) * 4
     return dict(status="ok", workload=w.name + "+conv1d_k4", ms=round(ms, 5),
                 algorithmic_bytes=nbytes, gbs=round(nbytes / (ms * 1e-3) / 1e9, 2),
                 gtokch=round(w.tok_ch / (ms * 1e-3) / 1e9, 3))
 
 
-def cpu_baseline(r, torch, min_seconds=10.0):
-    """The fp64 oracle over the whole S6 workload on the host cores, repeated
-    until at least `min_seconds` of wall time (the workload alone takes well
-    under a second); value = algorithmic bytes per workload / mean seconds."""
+def bench_copy(args, ctx, nbytes):
+    """A plain device copy moving `nbytes` in total (nbytes/2 read, nbytes/2
+    written), flushed and timed like the scan: the practical ceiling."""
+    torch = ctx["torch"]
+    n = nbytes // 8
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    res = ctx["timer"].run(lambda: dst.copy_(src), args.steps, max(3, args.warmup // 4),
+                           ctx["flusher"].clean)
+    del src, dst
+    return dict(bytes_moved=8 * n, ms=round(res["mean"], 5),
+                gbs=round(8 * n / (res["mean"] * 1e-3) / 1e9, 2))
+
+
+# ------------------------------------------------------------------ CPU leg
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def _sample_channels(w, rng, per_b=16):
+    bs = sorted(set([0, w.B - 1]))
+    return [(b, sorted(set([0, w.D - 1] + list(rng.choice(w.D, size=per_b, replace=False)))))
+            for b in bs]
+
+
+def verify_outputs(ctx):
+    """Sampled channels (S6) or (batch, head) pairs (SSD) of each timed call's
+    output against the fp64 oracle, normwise max relative error."""
+    import numpy as np
     import oracle
+    out = {}
+    for kind, w, t, samples, ys, hs in ctx["verify"]:
+        yr, hr = [], []
+        if kind == "s6":
+            for b, ds in samples:
+                yo, ho = oracle.s6_fwd(
+                    t["u"][b:b + 1, :, ds], t["delta"][b:b + 1, :, ds], t["A"][ds],
+                    t["B"][b:b + 1], t["C"][b:b + 1],
+                    D=None if t["D"] is None else t["D"][ds],
+                    z=None if t["z"] is None else t["z"][b:b + 1, :, ds],
+                    delta_bias=None if t["delta_bias"] is None else t["delta_bias"][ds])
+                yr.append(yo[0]); hr.append(ho[0])
+            g, r = np.concatenate([v.numpy() for v in ys], 1), np.concatenate(yr, 1)
+            gh, rh = np.concatenate([v.numpy() for v in hs], 0), np.concatenate(hr, 0)
+            what = f"{sum(len(ds) for _, ds in samples)} sampled channels"
+        else:
+            for b, hh in samples:
+                gg = hh // (w.H // w.G)
+                Yo, ho = oracle.ssd_fwd(t["X"][b:b + 1, :, hh:hh + 1],
+                                        t["delta"][b:b + 1, :, hh:hh + 1], t["A"][hh:hh + 1],
+                                        t["B"][b:b + 1, :, gg:gg + 1],
+                                        t["C"][b:b + 1, :, gg:gg + 1])
+                yr.append(Yo[0, :, 0]); hr.append(ho[0, 0])
+            g, r = np.stack([v.numpy() for v in ys]), np.stack(yr)
+            gh, rh = np.stack([v.numpy() for v in hs]), np.stack(hr)
+            what = f"{len(samples)} sampled (batch, head) pairs"
+        err_y = float(np.max(np.abs(g - r)) / np.max(np.abs(r)))
+        err_h = float(np.max(np.abs(gh - rh)) / np.max(np.abs(rh)))
+        tol = 1e-5 if w.dtype == "f32" else 2e-2
+        out[w.name] = {"sample": what, "err_y": float(f"{err_y:.3e}"),
+                       "err_h_last": float(f"{err_h:.3e}"), "tol": tol,
+                       "ok": bool(err_y <= tol and err_h <= max(tol, 1e-5))}
+    return out
+
+
+def cpu_baseline(r, ctx, seconds=8.0):
+    """The fp64 oracle (as it stands, untuned) on the host: on all cores over
+    the whole headline workload, and on one thread over a slice of it, each
+    repeated until `seconds` of wall time; value = algorithmic bytes per
+    workload / mean seconds per workload (the slice scaled to the whole)."""
+    import oracle
+    torch = ctx["torch"]
+    W = ctx["W"]
     w, t = r["w"], r["t"]
     f64 = {k: (oracle._f64(v) if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
     threads = oracle.default_threads()
-    runs = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.s6_fwd(f64["u"], f64["delta"], f64["A"], f64["B"], f64["C"], D=f64["D"],
-                      z=f64["z"], delta_bias=f64["delta_bias"], threads=threads)
-        runs += 1
-        total = time.perf_counter() - t0
-        if total >= min_seconds:
-            break
-    sec = total / runs
-    return {"value": round(r["nbytes"] / sec / 1e9, 4), "unit": "GB/s", "cores": threads,
+
+    def run(sub, th):
+        runs, t0 = 0, time.perf_counter()
+        while True:
+            oracle.s6_fwd(sub["u"], sub["delta"], sub["A"], sub["B"], sub["C"], D=sub["D"],
+                          z=sub["z"], delta_bias=sub["delta_bias"], threads=th)
+            runs += 1
+            if time.perf_counter() - t0 >= seconds:
+                return runs, time.perf_counter() - t0
+
+    runs, total = run(f64, threads)
+    sec_all = total / runs
+    nd = 256
+    sl = {"u": f64["u"][:1, :, :nd], "delta": f64["delta"][:1, :, :nd], "A": f64["A"][:nd],
+          "B": f64["B"][:1], "C": f64["C"][:1], "D": f64["D"][:nd], "z": f64["z"][:1, :, :nd],
+          "delta_bias": f64["delta_bias"][:nd]}
+    sl = {k: (v.copy() if hasattr(v, "copy") else v) for k, v in sl.items()}
+    runs1, total1 = run(sl, 1)
+    frac = (1 * w.L * nd) / w.tok_ch
+    sec_one = total1 / runs1 / frac
+    nbytes = r["nbytes"]
+    return {"value": round(nbytes / sec_all / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"the whole {w.name} workload (B={w.B} L={w.L} D={w.D} N={w.N}), run "
                       f"{runs} times ({total:.1f} s wall); fp64 sequential loop per channel, "
-                      f"channels over {threads} OpenMP threads; algorithmic bytes of the "
-                      f"workload / mean seconds per run",
-            "seconds_per_run": round(sec, 4),
-            "gtokch_per_s": round(w.tok_ch / sec / 1e9, 6)}
+                      f"channels over {threads} OpenMP threads",
+            "cpu_model": _cpu_model(), "os_cpu_count": os.cpu_count(),
+            "seconds_per_workload": round(sec_all, 4),
+            "gtokch_per_s": round(w.tok_ch / sec_all / 1e9, 6),
+            "single_thread": {"value": round(nbytes / sec_one / 1e9, 4), "unit": "GB/s",
+                              "cores": 1,
+                              "sample": f"batch row 0, channels 0..{nd - 1} (1/{round(1 / frac)} "
+                                        f"of the workload), run {runs1} times "
+                                        f"({total1:.1f} s); scaled to the whole workload",
+                              "seconds_per_workload": round(sec_one, 3)}}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # the GPU reaches its steady clock after ~30-40 back-to-back calls
-    # (~15 ms): the first calls of a cold process run ~10% slower
+    # the GPU reaches its steady clock after ~30-40 back-to-back calls: the
+    # first calls of a cold process run ~10% slower
     ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-ssd", action="store_true", help="skip every path but the S6 scan")
-    ap.add_argument("--only", choices=["s6", "ssd", "decode", "bwd", "conv", "conv_scan"],
+    ap.add_argument("--no-paths", action="store_true", help="the headline S6 workload only")
+    ap.add_argument("--only", choices=["s6", "s6_2p8b", "s6_long", "ssd", "decode", "bwd",
+                                       "conv", "conv_scan", "copy"],
                     help="run one part alone and print its result")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 256 MiB device copy three times, the "
@@ -366,6 +554,9 @@ def main():
     from selective_state_space_21_amd import workloads as W
 
     hip = _hip()
+    ctx = dict(torch=torch, ssm=ssm, W=W, native=native, hip=hip, verify=[])
+    ctx["flusher"] = Flusher(torch)
+    ctx["timer"] = Timer(torch, hip)
     if args.calibration_copy:
         src = torch.ones(64 * 2**20, dtype=torch.float32, device="cuda:0")   # 256 MiB
         dst = torch.empty_like(src)
@@ -373,29 +564,37 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    if args.only and args.only != "s6":
-        fn = {"ssd": bench_ssd, "decode": bench_decode, "bwd": bench_bwd, "conv": bench_conv,
-              "conv_scan": bench_conv_scan}
-        res = fn[args.only](args, torch, ssm, W)
-        print(json.dumps({"part": args.only, **{k: v for k, v in res.items()}}), flush=True)
+    parts = {"s6": lambda: bench_s6(args, ctx, W.S6_MAMBA130M, headline=True),
+             "s6_2p8b": lambda: bench_s6(args, ctx, W.S6_MAMBA2P8B),
+             "s6_long": lambda: bench_s6(args, ctx, W.S6_LONG_FP32),
+             "ssd": lambda: bench_ssd(args, ctx), "decode": lambda: bench_decode(args, ctx),
+             "bwd": lambda: bench_bwd(args, ctx), "conv": lambda: bench_conv(args, ctx),
+             "conv_scan": lambda: bench_conv_scan(args, ctx),
+             "copy": lambda: bench_copy(args, ctx, W.s6_algorithmic_bytes(W.S6_MAMBA130M))}
+    if args.only:
+        res = parts[args.only]()
+        print(json.dumps({"part": args.only, **res}), flush=True)
         return
-    r = bench_s6(args, torch, ssm, W, native, hip)
+    w = W.S6_MAMBA130M
+    r = bench_s6(args, ctx, w, headline=True)
+    copy_same = bench_copy(args, ctx, r["algorithmic_bytes"])
+    copy_big = bench_copy(args, ctx, 2 * 2**30)
     paths = {}
-    if not args.no_ssd and not args.only:
-        paths["ssd_chunk_fwd"] = bench_ssd(args, torch, ssm, W)
-        paths["selective_state_update"] = bench_decode(args, torch, ssm, W)
-        paths["selective_scan_bwd"] = bench_bwd(args, torch, ssm, W)
-        paths["causal_conv1d_silu"] = bench_conv(args, torch, ssm, W)
-        paths["selective_scan_conv_fwd"] = bench_conv_scan(args, torch, ssm, W)
-    w = r["w"]
+    if not args.no_paths:
+        for name, key in [("s6_mamba2.8b_layer", "s6_2p8b"), ("s6_long_fp32", "s6_long"),
+                          ("ssd_chunk_fwd", "ssd"), ("selective_state_update", "decode"),
+                          ("selective_scan_bwd", "bwd"), ("causal_conv1d_silu", "conv"),
+                          ("selective_scan_conv_fwd", "conv_scan")]:
+            paths[name] = parts[key]()
+            torch.cuda.empty_cache()
     line = {
         "metric": "selective-scan fwd achieved HBM GB/s (% of peak) + Gtoken·channels/s",
-        "value": round(r["gbs"], 2),
+        "value": r["gbs"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(r["ms"], 5),
+        "ms_per_step": r["ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -403,34 +602,29 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": w.name, "B": w.B, "L": w.L, "D": w.D, "N": w.N,
-            "io_dtype": "bf16", "state_dtype": "f32",
-            "path": "state_per_lane" if r["lanes"] else "split", "segments": r["segments"],
-            "pct_of_hbm_peak": round(r["gbs"] / HBM_PEAK_GBS * 100, 2),
-            "gtoken_channels_per_s": round(r["gtokch"], 3),
-            "algorithmic_bytes": r["nbytes"],
-            "phases_ms": {k: round(v, 5) for k, v in r["phases_ms"].items()},
-            "ms_median": round(r["ms_median"], 5), "ms_min": round(r["ms_min"], 5),
-            "ms_per_step_without_cache_flush": round(r["hot_ms"], 5),
+            "io_dtype": "bf16", "state_dtype": "f32", "path": r["path"],
+            "segments": r["segments"], "pct_of_hbm_peak": r["pct_hbm_peak"],
+            "gtoken_channels_per_s": r["gtokch"], "algorithmic_bytes": r["algorithmic_bytes"],
+            "phases_ms": r["phases_ms"], "ms_median": r["ms_median"], "ms_min": r["ms_min"],
+            "cache_flush": "read of a 512 MiB buffer before every timed call (clean lines)",
+            "ms_per_step_dirty_flush": r["ms_dirty_flush"],
+            "ms_per_step_without_cache_flush": r["ms_no_flush"],
+            "copy_ceiling": {"same_bytes": copy_same, "2_GiB": copy_big,
+                             "pct_of_copy_same_bytes": round(r["gbs"] / copy_same["gbs"] * 100, 2)},
         },
-        "roofline": {
-            "kernel": ("s6_lanes (state per lane, the only kernel of the call)" if r["lanes"]
-                       else "s6_fast segment scan (dominant phase)"),
-            "bound": "hbm",
-            "achieved": round(r["scan_gbs"], 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(r["scan_gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": S6_LANES_TRAFFIC_BYTES if r["lanes"] else S6_SCAN_TRAFFIC_BYTES,
-            "alu_view": {"achieved_tflops": round(r["scan_tflops"], 3),
-                         "peak_tflops": FP32_VECTOR_PEAK_TFLOPS,
-                         "flops_per_state_update": 6, "transcendentals_per_state_update": 1},
-        },
+        "roofline": {**r["roofline"], "issue_view": r["issue"], "alu_view": r["alu_view"]},
     }
     if paths:
         line["paths"] = paths
-    if not args.no_cpu_baseline and not args.only:
-        line["cpu_baseline"] = cpu_baseline(r, torch)
+    ok = True
+    if not args.no_cpu_baseline:
+        rr = dict(w=w, t=W.make_s6_inputs(w, seed=0), nbytes=r["algorithmic_bytes"])
+        line["verified"] = verify_outputs(ctx)
+        ok = all(v["ok"] for v in line["verified"].values())
+        line["cpu_baseline"] = cpu_baseline(rr, ctx)
     print(json.dumps(line), flush=True)
+    if not ok:
+        sys.exit(1)
 
 
 if __name__ == "__main__":
