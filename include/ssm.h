@@ -123,6 +123,31 @@ int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * operation of ssm_selective_scan_fwd with no workspace argument.  Where the
+ * plan needs scratch (the split path's segment pairs), it comes from a static
+ * device array inside the library, SSM_NOALLOC_SCRATCH_BYTES on each GPU,
+ * which the runtime sets up when it loads the library's code on that device
+ * and holds until the process ends; the call itself allocates nothing (no
+ * hipMalloc, no allocating library routine).  Sizes whose workspace query
+ * exceeds SSM_NOALLOC_SCRATCH_BYTES return SSM_ERR_WORKSPACE before any HIP
+ * call.  All calls on one GPU share that array and leave their contents in
+ * it: calls that overlap on one GPU (other streams, other host threads) race
+ * and must be serialised by the caller.  The first call on a device looks up
+ * the array's device address (hipGetSymbolAddress, after validation).
+ * Arguments, results and errors are otherwise those of ssm_selective_scan_fwd.
+ */
+#define SSM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+int ssm_selective_scan_fwd_noalloc(const void* u, const void* delta, const float* A,
+                                   const void* Bm, const void* Cm, const float* Dskip,
+                                   const void* z, const float* delta_bias, unsigned flags,
+                                   const float* h0, void* y, float* h_last,
+                                   int64_t B, int64_t L, int64_t D, int64_t N, int dtype,
+                                   void* stream);
+
+/*
  * Variable-length batch: row b runs only its first seq_lens[b] tokens
  * (seq_lens: device int32 [B], values clamped to [0, L]); y at positions
  * t >= seq_lens[b] is left untouched and h_last is the state after the row's

@@ -18,7 +18,7 @@ import torch
 from . import _native
 from ._native import SSMError
 
-__all__ = ["selective_scan_fwd", "selective_scan_conv_fwd",
+__all__ = ["selective_scan_fwd", "selective_scan_fwd_noalloc", "selective_scan_conv_fwd",
            "selective_scan_bwd", "ssd_chunk_fwd", "selective_state_update",
            "causal_conv1d_silu", "selective_scan_workspace_bytes",
            "selective_scan_segments", "selective_scan_lanes", "ssd_chunk_workspace_bytes",
@@ -175,6 +175,28 @@ def selective_scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
         _ptr(workspace), ws_bytes, _stream_handle(dev))
     _native.check(rc, "ssm_selective_scan_fwd")
     return y, h_last
+
+
+def selective_scan_fwd_noalloc(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
+                               B: torch.Tensor, C: torch.Tensor, y: torch.Tensor,
+                               h_last: Optional[torch.Tensor] = None,
+                               D: Optional[torch.Tensor] = None,
+                               z: Optional[torch.Tensor] = None,
+                               delta_bias: Optional[torch.Tensor] = None,
+                               delta_softplus: bool = True, zoh: bool = False,
+                               h0: Optional[torch.Tensor] = None) -> None:
+    """The S6 forward through ssm_selective_scan_fwd_noalloc, for callers that
+    cannot allocate: the caller passes y (and h_last), the library takes its
+    scratch from a static device array, and nothing is allocated here or there.
+    Calls that overlap on one GPU share that scratch and race."""
+    dt, dev, Bt, L, Dm, N = _s6_prepare(u, delta, A, B, C, D, z, delta_bias, h0, y)
+    _check_args(dev, ("h_last", h_last, (Bt, Dm, N), _F32))
+    lib = _native.load()
+    flags = (_native.FLAG_DELTA_SOFTPLUS if delta_softplus else 0) | (_native.FLAG_ZOH if zoh else 0)
+    rc = lib.ssm_selective_scan_fwd_noalloc(
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+        flags, _ptr(h0), _ptr(y), _ptr(h_last), Bt, L, Dm, N, _DT[dt], _stream_handle(dev))
+    _native.check(rc, "ssm_selective_scan_fwd_noalloc")
 
 
 def ssd_chunk_fwd(X: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,

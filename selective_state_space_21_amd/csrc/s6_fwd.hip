@@ -46,6 +46,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include <type_traits>
 
 #include "device_math.h"
@@ -1031,6 +1033,38 @@ hipError_t launch_s6(const S6Args& a, hipStream_t stream) {
     if (a.N == 16 && !zoh) return a.bf16 ? launch_fast<uint16_t>(a, stream) : launch_fast<float>(a, stream);
     if (a.bf16) return zoh ? launch_n<uint16_t, true>(a, stream) : launch_n<uint16_t, false>(a, stream);
     return zoh ? launch_n<float, true>(a, stream) : launch_n<float, false>(a, stream);
+}
+
+// ------------------------------------------------- static scratch (no allocation)
+// Device scratch for callers that cannot allocate: the split path's segment
+// pairs live here instead of in a caller workspace.  One copy per GPU, held
+// until the process ends; every call on a GPU shares it, so calls that overlap
+// on one GPU (different streams, or host threads) race.  Nothing in it has to
+// start at zero: the segment pass writes every pair before the carry reads it.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        // the array's name is a host-side stand-in: its device address (this
+        // device's copy) comes from the runtime, once per device
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace ssm

@@ -29,7 +29,8 @@ int s6_fwd_impl(const void* u, const void* delta, const float* A, const void* Bm
                 const float* Dskip, const void* z, const float* delta_bias, unsigned flags,
                 const float* h0, void* y, float* h_last, const int32_t* seq_lens,
                 int64_t B, int64_t L, int64_t D, int64_t N, int dtype,
-                void* workspace, size_t workspace_bytes, void* stream, void* const* events);
+                void* workspace, size_t workspace_bytes, void* stream, void* const* events,
+                bool static_scratch = false);
 
 int s6_check_sizes(int64_t B, int64_t L, int64_t D, int64_t N, int dtype) {
     if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_BAD_DTYPE;
@@ -135,6 +136,16 @@ int ssm_selective_scan_fwd_varlen(const void* u, const void* delta, const float*
                        B, L, D, N, dtype, workspace, workspace_bytes, stream, nullptr);
 }
 
+int ssm_selective_scan_fwd_noalloc(const void* u, const void* delta, const float* A,
+                                   const void* Bm, const void* Cm, const float* Dskip,
+                                   const void* z, const float* delta_bias, unsigned flags,
+                                   const float* h0, void* y, float* h_last,
+                                   int64_t B, int64_t L, int64_t D, int64_t N, int dtype,
+                                   void* stream) {
+    return s6_fwd_impl(u, delta, A, Bm, Cm, Dskip, z, delta_bias, flags, h0, y, h_last, nullptr,
+                       B, L, D, N, dtype, nullptr, 0, stream, nullptr, true);
+}
+
 int ssm_selective_scan_fwd_timed(const void* u, const void* delta, const float* A,
                                  const void* Bm, const void* Cm, const float* Dskip,
                                  const void* z, const float* delta_bias, unsigned flags,
@@ -154,7 +165,8 @@ int s6_fwd_impl(const void* u, const void* delta, const float* A, const void* Bm
                 const float* Dskip, const void* z, const float* delta_bias, unsigned flags,
                 const float* h0, void* y, float* h_last, const int32_t* seq_lens,
                 int64_t B, int64_t L, int64_t D, int64_t N, int dtype,
-                void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+                void* workspace, size_t workspace_bytes, void* stream, void* const* events,
+                bool static_scratch) {
     int rc = s6_check_sizes(B, L, D, N, dtype);
     if (rc != SSM_OK) return rc;
     if (flags & ~(unsigned)(SSM_FLAG_DELTA_SOFTPLUS | SSM_FLAG_ZOH)) return SSM_ERR_UNSUPPORTED;
@@ -167,7 +179,14 @@ int s6_fwd_impl(const void* u, const void* delta, const float* A, const void* Bm
     for (const void* p : vec)
         if (p && !aligned(p, 4)) return SSM_ERR_MISALIGNED;
     const ssm::S6Plan plan = ssm::plan_s6(B, L, D, N);
-    if (plan.workspace_bytes > 0) {
+    if (static_scratch) {
+        // validation is complete once the plan fits the static scratch; only
+        // then is the HIP runtime asked for this device's copy of it
+        if (plan.workspace_bytes > ssm::kNoAllocScratchBytes) return SSM_ERR_WORKSPACE;
+        workspace = nullptr;
+        if (plan.workspace_bytes > 0 && ssm::noalloc_scratch(&workspace) != hipSuccess)
+            return SSM_ERR_HIP;
+    } else if (plan.workspace_bytes > 0) {
         if (!workspace || workspace_bytes < plan.workspace_bytes) return SSM_ERR_WORKSPACE;
         if (!aligned(workspace, 16)) return SSM_ERR_MISALIGNED;
     }

@@ -54,6 +54,12 @@ S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N);
 
 hipError_t launch_s6(const S6Args& a, hipStream_t stream);
 
+// Size of the static device scratch of ssm_selective_scan_fwd_noalloc.
+constexpr size_t kNoAllocScratchBytes = SSM_NOALLOC_SCRATCH_BYTES;
+// Device address of the current device's copy of that scratch (looked up once
+// per device with hipGetSymbolAddress, then cached).
+hipError_t noalloc_scratch(void** out);
+
 struct SSDArgs {
     const void* X;
     const void* delta;
