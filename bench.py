@@ -190,7 +190,7 @@ def bench_s6(args, ctx, w, headline=False):
     ws_bytes = ssm.selective_scan_workspace_bytes(w.B, w.L, w.D, w.N, tdt)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     lanes = ssm.selective_scan_lanes(w.B, w.L, w.D, w.N)
-    segments = 1 if lanes else ssm.selective_scan_segments(w.B, w.L, w.D, w.N)
+    segments = ssm.selective_scan_segments(w.B, w.L, w.D, w.N)
     lib = native.load()
     stream = torch.cuda.current_stream(dev)
     evs = _events(hip, 4)
@@ -227,18 +227,21 @@ def bench_s6(args, ctx, w, headline=False):
     ms = res["mean"]
     nbytes = W.s6_algorithmic_bytes(w)
     elems = w.B * w.L * w.D * w.N
+    # library events: state-per-lane path [scan of every segment | carry |
+    # fix-up of the later segments]; split path [segment reduce | carry |
+    # segment rescan]
     if lanes:
-        ph = {"state_per_lane": phases[2]}
-        dom_name, dom_ms = "s6_lanes", phases[2]
+        ph = {"scan": phases[0]}
+        if segments > 1:
+            ph.update(carry=phases[1], fixup=phases[2])
+        dom_name, dom_ms = "s6_lanes (scan of every segment)", phases[0]
     else:
-        ph = {"segment_pass": phases[0], "carry": phases[1], "final_pass": phases[2]}
-        dom_name, dom_ms = ("s6 final pass", phases[2]) if phases[2] >= phases[0] else \
-            ("s6 segment pass", phases[0])
+        ph = {"segment_reduce": phases[0], "carry": phases[1], "segment_rescan": phases[2]}
+        dom_name, dom_ms = "s6_fast segment rescan", phases[2]
+    # the dominant kernel reads every input and writes y
+    dom_gbs = nbytes / (dom_ms * 1e-3) / 1e9
     key = f"{'s6_lanes' if lanes else 's6_split'}@{w.name}"
     traffic, note = counter_traffic(key)
-    # the dominant kernel's share of the algorithmic bytes: on the
-    # state-per-lane path it is the whole call
-    dom_gbs = nbytes / (dom_ms * 1e-3) / 1e9 if lanes else nbytes / (ms * 1e-3) / 1e9
     out = dict(
         status="ok", workload=w.name, B=w.B, L=w.L, D=w.D, N=w.N, io_dtype=w.dtype,
         path="state_per_lane" if lanes else "split", segments=segments,

@@ -87,32 +87,41 @@ const char* ssm_status_string(int status);
  *   h_last         : [B, D, N]  fp32 or NULL; receives the state after t = L-1
  *   1 <= N <= 64; B, D >= 1; L >= 0.
  * Two execution paths, chosen from the sizes:
- *   - state per lane (N = 16, D a multiple of 16, B*D/4 wavefronts at least
- *     two per SIMD; see ssm_selective_scan_lanes): one lane per (channel,
- *     state), the whole sequence in one pass, no workspace used;
- *   - split: one lane per channel; long sequences are split into segments
- *     scanned in parallel, and the segments' (decay, offset) pairs are carried
- *     by a wavefront-level scan in which each lane composes the pairs of one
- *     (b, d, n) chain in segment order.  The workspace holds those pairs.
- * The workspace query returns the split path's size (calls with
- * SSM_FLAG_ZOH take that path at any size).  The plan (path, segment count,
- * workspace size) is a pure function of the sizes: it balances wavefronts over
- * the 1024 SIMDs of an MI355X and makes no HIP call.
+ *   - state per lane (N = 16, D a multiple of 16, no ZOH; see
+ *     ssm_selective_scan_lanes): one lane per (channel, state).  With at least
+ *     two of its B*D/4 wavefronts per SIMD the whole sequence is one pass.
+ *     With fewer the sequence is cut into segments of whole 128-token tiles,
+ *     scanned in parallel (each after the first from a zero state); their
+ *     (decay, end state) pairs are folded in segment order into each
+ *     segment's incoming state and h_last, and a third launch adds to y the
+ *     part of the incoming state that survives to each token,
+ *     exp(A * cumsum dt) * h_in, stopping once that is exactly zero in fp32
+ *     (with softplus, where dt >= 0).  No exponential is evaluated twice
+ *     except in that fix-up's reach.
+ *   - split: one lane per channel (other N, ZOH, D not a multiple of 16, or
+ *     the state-per-lane kernel turned off); long sequences are split into
+ *     short segments whose (decay, offset) pairs are carried the same way,
+ *     then every segment is rescanned from its incoming state.
+ * The workspace holds the segment pairs; the query returns the larger of the
+ * two paths' needs (it takes no flags, and ZOH calls take the split path).
+ * The plan (path, segment count, workspace size) is a pure function of the
+ * sizes: it balances wavefronts over the 1024 SIMDs of an MI355X and makes no
+ * HIP call.
  */
 size_t ssm_selective_scan_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
                                           int dtype);
 
-/* Number of sequence segments the planner uses for these sizes (1 = one pass,
- * no carry); 0 for invalid sizes.  The environment variable SSM_S6_SEGMENTS
- * (1..256) overrides the choice, for both this query and the call. */
+/* Number of sequence segments a forward call without SSM_FLAG_ZOH uses at
+ * these sizes, on the path it takes (1 = one pass, no carry); 0 for invalid
+ * sizes.  The environment variable SSM_S6_SEGMENTS (1..256) overrides the
+ * choice, for both this query and the call (on the state-per-lane path
+ * capped at one segment per 128 tokens). */
 int ssm_selective_scan_segments(int64_t B, int64_t L, int64_t D, int64_t N);
 
 /* 1 if a forward call at these sizes without SSM_FLAG_ZOH (with or without
- * the fused convolution) runs the state-per-lane kernel (unsplit: the segment
- * count above then applies only to ZOH calls), else 0 (also for invalid
- * sizes).  The environment variable SSM_S6_LANES=0 turns that kernel off,
- * SSM_S6_LANES=1 takes it whenever N = 16, D is a multiple of 16 and the
- * offsets fit, for both this query and the call. */
+ * the fused convolution) runs the state-per-lane kernel, else 0 (also for
+ * invalid sizes).  The environment variable SSM_S6_LANES=0 turns that kernel
+ * off, for both this query and the call. */
 int ssm_selective_scan_lanes(int64_t B, int64_t L, int64_t D, int64_t N);
 
 int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A,
@@ -166,9 +175,10 @@ int ssm_selective_scan_fwd_varlen(const void* u, const void* delta, const float*
 /*
  * Same operation, for measurement: `events` is NULL or points to 4 hipEvent_t
  * created by the caller; they are recorded on `stream` at the phase
- * boundaries -- before the segment reduce, before the carry scan, before the
- * segment scan, and after it (with one segment, or on the state-per-lane
- * path, the first three coincide).
+ * boundaries.  State-per-lane path: before the scan of the segments, before
+ * the carry, before the fix-up, after it (with one segment the last three
+ * coincide).  Split path: before the segment reduce, before the carry, before
+ * the segment rescan, after it (with one segment the first three coincide).
  * Recording is asynchronous; the caller reads the intervals after it has
  * synchronised.  The arguments and results are otherwise those of
  * ssm_selective_scan_fwd.

@@ -29,6 +29,15 @@ __device__ __forceinline__ float row_bcast(float v, int k) {
     }
 }
 
+// Value of lane j - K of the same 16-lane row (DPP row_shr:K); lanes j < K
+// read 0.
+template <int K>
+__device__ __forceinline__ float dpp_shr(float v) {
+    static_assert(K > 0 && K < 16, "row shift");
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, v), 0x110 + K, 0xf, 0xf, true));
+}
+
 // Value of lane (lane ^ M) for M < 32 (ds_swizzle bit-mask mode: the xor
 // mask in bits 10-14, and-mask 0x1f).
 template <int M>

@@ -533,10 +533,17 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
     const int64_t D = p.D;
     const int64_t d = grp * kChans + chan;
     const int64_t Lb = row_len(p, b);
+    // segment s of the row (one segment: the whole row): tokens [t0, t1)
+    const int s = (int)blockIdx.z;
+    const int64_t t0 = (int64_t)s * p.seg_len;
+    const int64_t t1 = t0 + p.seg_len < Lb ? t0 + p.seg_len : Lb;
     const float a2 = p.A[d * 16 + n] * kLog2e;
     const float bias = p.delta_bias ? p.delta_bias[d] : 0.0f;
     const float dsk = p.Dskip ? p.Dskip[d] : 0.0f;
-    float h = p.h0 ? p.h0[(b * D + d) * 16 + n] : 0.0f;
+    // the first segment starts from h0, the others from zero (their incoming
+    // state is added to y afterwards, by the fix-up pass)
+    float h = (s == 0 && p.h0) ? p.h0[(b * D + d) * 16 + n] : 0.0f;
+    float dt_sum = 0.0f;                  // this lane's share of the segment's sum of dt
     // buffer resources over this row's tokens: loads past the row's end read
     // zero, stores there are dropped (the planner keeps offsets in 32 bits)
     const int64_t rowoff = b * p.L * D;
@@ -564,11 +571,17 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
         }
         cb = p.conv_b ? p.conv_b[d] : 0.0f;
         if (tid < 3 * kChans) {
-            // the inputs before token 0: the carried state (its last K-1 slots
-            // are x_{-K+1 .. -1}) or zeros
+            // the inputs before the segment's first token: inside the row the
+            // previous tokens; before token 0 the carried state (its last K-1
+            // slots are x_{-K+1 .. -1}) or zeros
             const int ch = tid / 3, i = tid % 3, slot = i + K - 4;
-            xh[0][ch][i] = (p.conv_state_in && slot >= 0)
-                               ? p.conv_state_in[(b * D + grp * kChans + ch) * (K - 1) + slot] : 0.0f;
+            const int64_t tt = t0 - 3 + i;
+            const int64_t dd = grp * kChans + ch;
+            float v = 0.0f;
+            if (tt >= 0 && tt < Lb) v = widen<T>(elem_bits<T>(u_[(b * p.L + tt) * D + dd]));
+            else if (tt < 0 && p.conv_state_in && slot >= 0)
+                v = p.conv_state_in[(b * D + dd) * (K - 1) + slot];
+            xh[0][ch][i] = v;
         }
     }
 
@@ -624,29 +637,25 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
         }
     };
 
-    const int64_t nsup = (Lb + kSpan - 1) / kSpan;
-    Raw nxt;
-    if (nsup > 0) load(nxt, 0);
-    for (int64_t sg = 0; sg < nsup; ++sg) {
-        const Raw cur = nxt;
-        const int64_t st0 = sg * kSpan;
-        lds_barrier();                      // previous super-tile's LDS reads and y staging done
-        // staged before the previous y leaves: the wait for this super-tile's
-        // loads then does not also wait for those stores (~1-2% faster)
-        stage(cur);
-        if (sg > 0) store_y(st0 - kSpan);
-        lds_barrier();
-        load(nxt, st0 + kSpan);             // travels while this super-tile is computed
+    // The 8 tiles of one super-tile (TAIL: the super-tile reaches past the
+    // row's end, so tokens there are masked to dt = 0).
+    auto tiles = [&](int64_t st0, int64_t sg, auto tail_tag) __attribute__((always_inline)) {
+        constexpr bool kTail = decltype(tail_tag)::value;
 #pragma unroll
         for (int i = 0; i < kSuper; ++i) {
             const int tl = kTile * i + n;   // this lane's token within the super-tile
-            // past the row's end dt = 0 leaves h unchanged; the step is formed
-            // unconditionally and masked, so no branch splits the super-tile
-            // into one basic block per tile (which kept the scheduler from
-            // overlapping a tile's exponentials with the previous tile's chain)
-            const uint32_t keep = st0 + tl < Lb ? 0xffffffffu : 0u;
+            // past the row's end (TAIL) dt = 0 leaves h unchanged; the step is
+            // masked rather than branched on, so no branch splits the
+            // super-tile into one basic block per tile (which kept the
+            // scheduler from overlapping a tile's exponentials with the
+            // previous tile's chain)
             const float xr = widen<T>(elem_bits<T>(act[1][tl][chan])) + bias;
-            const float dt = __uint_as_float(__float_as_uint(SOFTPLUS ? softplus_f(xr) : xr) & keep);
+            float dt = SOFTPLUS ? softplus_f(xr) : xr;
+            if constexpr (kTail) {
+                const uint32_t keep = st0 + tl < t1 ? 0xffffffffu : 0u;
+                dt = __uint_as_float(__float_as_uint(dt) & keep);
+            }
+            dt_sum += dt;
             float ut;
             if constexpr (CONV) {
                 // window x_{t-3..t}: the staged row, before the super-tile the halo
@@ -702,15 +711,46 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
             if constexpr (sizeof(T) == 2) yst[tl][chan] = f32_to_bf16_bits(yv);
             else yst[tl][chan] = yv;
         }
+    };
+
+    const int64_t nsup = t1 > t0 ? (t1 - t0 + kSpan - 1) / kSpan : 0;
+    Raw nxt;
+    if (nsup > 0) load(nxt, t0);
+    for (int64_t sg = 0; sg < nsup; ++sg) {
+        const Raw cur = nxt;
+        const int64_t st0 = t0 + sg * kSpan;
+        lds_barrier();                      // previous super-tile's LDS reads and y staging done
+        // staged before the previous y leaves: the wait for this super-tile's
+        // loads then does not also wait for those stores (~1-2% faster)
+        stage(cur);
+        if (sg > 0) store_y(st0 - kSpan);
+        lds_barrier();
+        load(nxt, st0 + kSpan);             // travels while this super-tile is computed
+        if (st0 + kSpan <= t1) tiles(st0, sg, std::false_type{});
+        else tiles(st0, sg, std::true_type{});
     }
     lds_barrier();
-    if (nsup > 0) store_y((nsup - 1) * kSpan);
-    if (p.h_last) p.h_last[(b * D + d) * 16 + n] = h;
+    if (nsup > 0) store_y(t0 + (nsup - 1) * kSpan);
+    if (p.S == 1) {
+        if (p.h_last) p.h_last[(b * D + d) * 16 + n] = h;
+    } else {
+        // the segment as an affine map of its incoming state: decay
+        // exp(A * sum dt) (the row's sum over its 16 lanes) and the end state
+        // from the segment's own start
+        float tot = dt_sum;
+        tot += dpp_mov<0x128>(tot);            // row_ror:8
+        tot += dpp_mov<0x124>(tot);            // row_ror:4
+        tot += dpp_mov<0x122>(tot);            // row_ror:2
+        tot += dpp_mov<0x121>(tot);            // row_ror:1
+        const int64_t pi = (int64_t)s * (p.B * D * 16) + (b * D + d) * 16 + n;   // segment-major
+        p.seg_a[pi] = fast_exp2(a2 * tot);
+        p.seg_b[pi] = h;
+    }
     if constexpr (CONV) {
         // the last K-1 inputs of the row, oldest first (from the carried state
         // when the row is shorter than that)
         const int K = (int)p.conv_K;
-        if (p.conv_state_out && tid < (K - 1) * kChans) {
+        if (p.conv_state_out && s == p.S - 1 && tid < (K - 1) * kChans) {
             const int ch = tid / (K - 1), i = tid % (K - 1);
             const int64_t dd = grp * kChans + ch;
             const int64_t t = Lb - (K - 1) + i;
@@ -844,6 +884,228 @@ __global__ __launch_bounds__(256) void s6_carry_scan(const float* __restrict__ s
     seg_b[(int64_t)(S - 1) * chains + i] = h;      // entering the last segment
 }
 
+// Carry of the segmented state-per-lane path.  Segment 0 ran from h0, so its
+// offset is the true state after it; every later segment ran from zero and is
+// the affine map h -> decay * h + offset of its incoming state.  Each lane
+// folds one (b, d, n) chain in segment order, overwrites each later offset
+// with the state entering that segment (the composition of the temporalbook
+// chapter's section 3), and writes the state after the last segment to
+// h_last.
+__global__ __launch_bounds__(256) void s6_carry_lanes(const float* __restrict__ seg_a,
+                                                      float* __restrict__ seg_b,
+                                                      float* __restrict__ h_last,
+                                                      int64_t chains, int S) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= chains) return;
+    float h = seg_b[i];
+    constexpr int kBatch = 8;
+    for (int s0 = 1; s0 < S; s0 += kBatch) {
+        float a[kBatch], c[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const bool in = s0 + k < S;
+            a[k] = in ? seg_a[(int64_t)(s0 + k) * chains + i] : 1.0f;
+            c[k] = in ? seg_b[(int64_t)(s0 + k) * chains + i] : 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            if (s0 + k < S) seg_b[(int64_t)(s0 + k) * chains + i] = h;
+            h = fmaf(a[k], h, c[k]);
+        }
+    }
+    if (h_last) h_last[i] = h;
+}
+
+// Fix-up of the segmented state-per-lane path: segment s >= 1
+// was scanned from a zero state, so its y lacks the part of the incoming state
+// h_in that survives to each token, which is exp(A * cum_t) * h_in with cum_t
+// the sum of dt over the segment up to and including t (each token multiplies
+// the state by exp(dt * A)).  So
+//   y_t += silu(z_t) * sum_n C_t[n] * exp(A[d,n] * cum_t) * h_in[n].
+// The correction of a token needs only cum_t, so the tokens are handled in
+// parallel (a prefix sum of dt gives cum).  With softplus every dt >= 0, so
+// cum never decreases; once exp(A * cum) is exactly 0 in fp32 for every
+// state of every channel of the workgroup (A <= 0), every later correction is
+// exactly zero and the walk stops there; a state whose decay is already 0 is
+// skipped before that.  Without softplus it runs to the segment's end.
+// Workgroup: 16 channels (D a multiple of 16); it walks the segment in blocks
+// of 64 tokens.  Each block's delta, z, y and C rows are loaded as 16-byte
+// pieces of the group's 16-channel run (one memory round trip per block),
+// staged in LDS and read per (channel, token): lane j of 16-lane row c handles
+// token 16k + j of the block for channel c.  The new y leaves through LDS as
+// 16-byte pieces again.
+namespace fixup {
+constexpr int kBlock = 64;                 // tokens per block
+constexpr int kPad = 4;                    // LDS row padding (floats)
+}  // namespace fixup
+
+template <typename T, bool HAS_Z, bool SOFTPLUS>
+__global__ __launch_bounds__(256) void s6_fixup(S6Args p, const T* __restrict__ delta_,
+                                                const T* __restrict__ z_,
+                                                const T* __restrict__ Cm_, T* __restrict__ y_) {
+    using namespace fixup;
+    constexpr int kChans = lanes::kChans;
+    constexpr uint32_t E = sizeof(T);
+    constexpr int kPerTok = kChans * (int)E / 16;     // 16-byte pieces per token (2 bf16, 4 fp32)
+    constexpr int kPieces = kBlock * kPerTok;         // per tensor and block
+    constexpr int kVals = 16 / (int)E;
+    constexpr int kW = kChans + kPad;
+    __shared__ __attribute__((aligned(16))) float sd[kBlock][kW];    // dt (raw), then y
+    __shared__ __attribute__((aligned(16))) float sz[HAS_Z ? kBlock : 1][kW];
+    __shared__ __attribute__((aligned(16))) float sy[kBlock][kW];
+    __shared__ __attribute__((aligned(16))) float sc[kBlock][kW];    // C rows [token][state]
+    const int tid = threadIdx.x;
+    const int j = tid & 15;                      // token within a 16-token tile
+    const int c = tid >> 4;                      // channel within the group
+    const int64_t b = blockIdx.y;
+    const int s = (int)blockIdx.z + 1;
+    const int64_t D = p.D;
+    const int64_t grp = blockIdx.x;
+    const int64_t d = grp * kChans + c;
+    const int64_t Lb = row_len(p, b);
+    const int64_t t0 = (int64_t)s * p.seg_len;
+    const int64_t t1 = t0 + p.seg_len < Lb ? t0 + p.seg_len : Lb;
+    if (t0 >= t1) return;
+    float a2[16], hin[16];
+    float a2max = -INFINITY;
+    const int64_t hb = (int64_t)s * (p.B * D * 16) + (b * D + d) * 16;
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+        a2[n] = p.A[d * 16 + n] * kLog2e;
+        hin[n] = p.seg_b[hb + n];
+        a2max = fmaxf(a2max, a2[n]);
+    }
+    const float bias = p.delta_bias ? p.delta_bias[d] : 0.0f;
+    // buffer resources over the row's tokens (32-bit offsets as in the scan)
+    const int64_t rowoff = b * p.L * D;
+    const uint32_t act_bytes = (uint32_t)(Lb * D * E);
+    const auto rd = make_rsrc(delta_ + rowoff, act_bytes);
+    const auto rz = make_rsrc(HAS_Z ? z_ + rowoff : nullptr, HAS_Z ? act_bytes : 0u);
+    const auto ry = make_rsrc(y_ + rowoff, act_bytes);
+    const auto rC = make_rsrc(Cm_ + b * p.L * 16, (uint32_t)(Lb * 16 * E));
+    const uint32_t row_bytes = (uint32_t)(D * E);
+    const uint32_t grp_bytes = (uint32_t)(grp * kChans * E);
+    // piece of this thread (threads >= kPieces idle in the staging)
+    const int pt = tid / kPerTok, pc = tid % kPerTok;
+    const bool loader = tid < kPieces;
+    auto widen4 = [&](const u32x4& v, float* out) __attribute__((always_inline)) {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if constexpr (E == 2) {
+                out[2 * q] = __uint_as_float(w[q] << 16);
+                out[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+            } else {
+                out[q] = __uint_as_float(w[q]);
+            }
+        }
+    };
+    float carry = 0.0f;                          // cum at the previous tile's last token
+    uint32_t live = 0xf;                         // groups of four states still contributing
+    for (int64_t tt = t0; tt < t1; tt += kBlock) {
+        // stage the block: one 16-byte piece of each tensor per loader thread
+        if (loader) {
+            const uint32_t soff = (uint32_t)tt * row_bytes;
+            const uint32_t voff = (uint32_t)pt * row_bytes + grp_bytes + 16 * pc;
+            const u32x4 vd = __builtin_amdgcn_raw_buffer_load_b128(rd, (int)voff, (int)soff, 0);
+            const u32x4 vy = __builtin_amdgcn_raw_buffer_load_b128(ry, (int)voff, (int)soff, 0);
+            u32x4 vz{};
+            if constexpr (HAS_Z) vz = __builtin_amdgcn_raw_buffer_load_b128(rz, (int)voff, (int)soff, 0);
+            const u32x4 vc = __builtin_amdgcn_raw_buffer_load_b128(
+                rC, (int)((uint32_t)pt * 16 * E + 16 * pc), (int)((uint32_t)tt * 16 * E), 0);
+            float f[kVals];
+            widen4(vd, f);
+#pragma unroll
+            for (int e = 0; e < kVals; ++e) sd[pt][kVals * pc + e] = f[e];
+            widen4(vy, f);
+#pragma unroll
+            for (int e = 0; e < kVals; ++e) sy[pt][kVals * pc + e] = f[e];
+            if constexpr (HAS_Z) {
+                widen4(vz, f);
+#pragma unroll
+                for (int e = 0; e < kVals; ++e) sz[pt][kVals * pc + e] = f[e];
+            }
+            widen4(vc, f);
+#pragma unroll
+            for (int e = 0; e < kVals; ++e) sc[pt][kVals * pc + e] = f[e];
+        }
+        lds_barrier();
+        if constexpr (SOFTPLUS) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bool any = false;
+#pragma unroll
+                for (int n = 4 * g; n < 4 * g + 4; ++n) any |= fast_exp2(a2[n] * carry) != 0.0f;
+                if (__any(any)) m |= 1u << g;
+            }
+            live &= __builtin_amdgcn_readfirstlane(m);
+        }
+        constexpr int kT = kBlock / 16;
+        float cum[kT], corr[kT];
+#pragma unroll
+        for (int k = 0; k < kT; ++k) {
+            const int tl = 16 * k + j;
+            const bool in = tt + tl < t1;
+            float x = in ? step_dt(sd[tl][c], bias, SOFTPLUS ? SSM_FLAG_DELTA_SOFTPLUS : 0u) : 0.0f;
+            // inclusive prefix sum of dt over the 16 tokens of the row (DPP
+            // row shifts; lanes shifted in from outside the row read 0)
+            x += dpp_shr<1>(x);
+            x += dpp_shr<2>(x);
+            x += dpp_shr<4>(x);
+            x += dpp_shr<8>(x);
+            cum[k] = x + carry;
+            carry = row_bcast_c<15>(cum[k]);
+            corr[k] = 0.0f;
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            if (live & (1u << g)) {
+#pragma unroll
+                for (int k = 0; k < kT; ++k) {
+                    const f32x4 cq = *reinterpret_cast<const f32x4*>(&sc[16 * k + j][4 * g]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        corr[k] = fmaf(cq[r], fast_exp2(a2[4 * g + r] * cum[k]) * hin[4 * g + r], corr[k]);
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kT; ++k) {
+            const int tl = 16 * k + j;
+            float g = 1.0f;
+            if constexpr (HAS_Z) g = silu_f(sz[tl][c]);
+            sy[tl][c] = fmaf(corr[k], g, sy[tl][c]);
+        }
+        lds_barrier();
+        // the block's y back as 16-byte pieces, none past the segment's end
+        if (loader && tt + pt < t1) {
+            float f[kVals];
+#pragma unroll
+            for (int e = 0; e < kVals; ++e) f[e] = sy[pt][kVals * pc + e];
+            u32x4 v;
+            if constexpr (E == 2) {
+                uint32_t w[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    w[q] = (uint32_t)f32_to_bf16_bits(f[2 * q]) | ((uint32_t)f32_to_bf16_bits(f[2 * q + 1]) << 16);
+                v = u32x4{w[0], w[1], w[2], w[3]};
+            } else {
+                v = u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                          __float_as_uint(f[3])};
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(v, ry, (int)((uint32_t)pt * row_bytes + grp_bytes + 16 * pc),
+                                                   (int)((uint32_t)tt * row_bytes), 0);
+        }
+        if constexpr (SOFTPLUS) {
+            // exact stop: exp(A * cum) is 0 for every state from here on
+            if (__syncthreads_and(fast_exp2(a2max * carry) == 0.0f)) break;
+        } else {
+            __syncthreads();                     // the staging of the next block waits for these reads
+        }
+    }
+}
+
 // h_last = h0 (or zeros) for an empty sequence.
 __global__ void s6_copy_state(const float* h0, float* h_last, int64_t count) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -859,6 +1121,27 @@ void launch_carry(const S6Args& a, hipStream_t stream) {
     const int64_t chains = a.B * a.D * a.N;
     hipLaunchKernelGGL(s6_carry_scan, dim3((unsigned)((chains + 255) / 256)), dim3(256), 0,
                        stream, a.seg_a, a.seg_b, a.h0, chains, (int)a.S);
+}
+
+// The carry of the state-per-lane segments and the fix-up of segments 1..
+// (marks the two phase boundaries in between).
+template <typename T, bool SP>
+void launch_carry_fixup(const S6Args& a, hipStream_t stream) {
+    const int64_t chains = a.B * a.D * 16;
+    hipLaunchKernelGGL(s6_carry_lanes, dim3((unsigned)((chains + 255) / 256)), dim3(256), 0,
+                       stream, a.seg_a, a.seg_b, a.h_last, chains, (int)a.S);
+    mark(a, 2, stream);
+    const dim3 fgrid((unsigned)((a.D + lanes::kChans - 1) / lanes::kChans), (unsigned)a.B,
+                     (unsigned)(a.S - 1));
+    const T* Dl = static_cast<const T*>(a.delta);
+    const T* Z = static_cast<const T*>(a.z);
+    const T* Cp = static_cast<const T*>(a.Cm);
+    T* Y = static_cast<T*>(a.y);
+    if (a.z)
+        hipLaunchKernelGGL((s6_fixup<T, true, SP>), fgrid, dim3(256), 0, stream, a, Dl, Z, Cp, Y);
+    else
+        hipLaunchKernelGGL((s6_fixup<T, false, SP>), fgrid, dim3(256), 0, stream, a, Dl, Z, Cp, Y);
+    mark(a, 3, stream);
 }
 
 template <typename T, bool SP, bool CV>
@@ -909,8 +1192,9 @@ hipError_t launch_lanes(const S6Args& a, hipStream_t stream) {
     const T* Bp = static_cast<const T*>(a.Bm);
     const T* Cp = static_cast<const T*>(a.Cm);
     T* Y = static_cast<T*>(a.y);
-    const dim3 grid((unsigned)(a.D / lanes::kChans), (unsigned)a.B), block(256);
-    for (int i = 0; i < 3; ++i) mark(a, i, stream);     // no reduce or carry phase
+    const unsigned groups = (unsigned)(a.D / lanes::kChans);
+    const dim3 grid(groups, (unsigned)a.B, (unsigned)a.S), block(256);
+    mark(a, 0, stream);
     const bool cv = a.conv_w != nullptr;
 #define SSM_LANES(Z_, SP_, CV_) \
     hipLaunchKernelGGL((s6_lanes<T, Z_, SP_, CV_>), grid, block, 0, stream, a, U, Dl, Z, Bp, Cp, Y)
@@ -922,7 +1206,14 @@ hipError_t launch_lanes(const S6Args& a, hipStream_t stream) {
         else { if (sp) SSM_LANES(false, true, false); else SSM_LANES(false, false, false); }
     }
 #undef SSM_LANES
-    mark(a, 3, stream);
+    mark(a, 1, stream);
+    if (a.S > 1) {
+        if (sp) launch_carry_fixup<T, true>(a, stream);
+        else launch_carry_fixup<T, false>(a, stream);
+    } else {
+        mark(a, 2, stream);
+        mark(a, 3, stream);
+    }
     return hipGetLastError();
 }
 
@@ -969,25 +1260,44 @@ constexpr int64_t kSimds = 4 * 256;
 
 }  // namespace
 S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N) {
-    S6Plan pl{1, L > 0 ? L : 1, 0, false};
+    S6Plan pl{};
+    pl.S = 1;
+    pl.seg_len = L > 0 ? L : 1;
+    pl.S_lanes = 1;
+    pl.seg_len_lanes = pl.seg_len;
     if (L <= 0) return pl;
-    // State-per-lane kernel: N = 16, D a multiple of 16, a batch row's
-    // activations (plus one super-tile) within 32-bit buffer offsets at 4
-    // bytes per element, and its B*D/4 wavefronts at least two per SIMD.
-    // SSM_S6_LANES=0 turns it off, =1 takes it whenever the shape allows.
+    const char* env_seg = getenv("SSM_S6_SEGMENTS");
+    const int64_t forced = (env_seg && atoi(env_seg) > 0) ? atoi(env_seg) : 0;
+    // State-per-lane kernel: N = 16, D a multiple of 16 and a batch row's
+    // activations (plus two super-tiles) within 32-bit buffer offsets at 4
+    // bytes per element.  SSM_S6_LANES=0 turns it off.  It runs B*D/4
+    // wavefronts per segment: unsplit with at least two per SIMD, else cut
+    // into the fewest segments (whole super-tiles) that give three per SIMD;
+    // the segments after the first are fixed up afterwards.
     {
         const bool shape_ok = N == 16 && D % lanes::kChans == 0 &&
                               (L + 2 * lanes::kSpan) * D * 4 <= (int64_t)0xFFFFFFFF;
-        pl.lanes = shape_ok && B * D / 4 >= 2 * kSimds;
+        pl.lanes = shape_ok;
         const char* env = getenv("SSM_S6_LANES");
         if (env && env[0] == '0') pl.lanes = false;
-        if (env && env[0] == '1') pl.lanes = shape_ok;
+        const int64_t waves = B * D / 4;
+        int64_t S = waves >= 2 * kSimds ? 1 : (3 * kSimds + waves - 1) / (waves > 0 ? waves : 1);
+        if (forced) S = forced;
+        int64_t maxS = (L + lanes::kSpan - 1) / lanes::kSpan;
+        if (maxS > kMaxSegments) maxS = kMaxSegments;
+        if (S > maxS) S = maxS;
+        if (S < 1) S = 1;
+        int64_t seg_len = (L + S - 1) / S;
+        seg_len = (seg_len + lanes::kSpan - 1) / lanes::kSpan * lanes::kSpan;
+        pl.S_lanes = (int)((L + seg_len - 1) / seg_len);
+        pl.seg_len_lanes = seg_len;
     }
-    // Wavefronts per segment.  With at least one per SIMD the sequence is not
-    // split (a split adds a second pass over the tokens); otherwise the
-    // segment count is the smallest that gives every SIMD at least three
-    // wavefronts and all SIMDs the same number (a whole multiple of the SIMD
-    // count), else the one nearest three per SIMD.
+    // Split path (one lane per channel; ZOH calls, other N, or the
+    // state-per-lane kernel turned off).  With at least one wavefront per SIMD
+    // the sequence is not split; otherwise the segment count is the smallest
+    // that gives every SIMD at least three wavefronts and all SIMDs the same
+    // number (a whole multiple of the SIMD count), else the one nearest three
+    // per SIMD.
     const int64_t waves = B * ((D + kWave - 1) / kWave);
     const int64_t simds = kSimds;
     const int64_t min_seg = 32;
@@ -997,8 +1307,7 @@ S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N) {
     for (int64_t c = 1; c <= maxS && S == 0; ++c)
         if (waves * c >= 3 * simds && (waves * c) % simds == 0) S = c;
     if (S == 0) S = (3 * simds + waves - 1) / waves;
-    const char* env = getenv("SSM_S6_SEGMENTS");
-    if (env && atoi(env) > 0) S = atoi(env);
+    if (forced) S = forced;
     if (S > maxS) S = maxS;
     if (S < 1) S = 1;
     int64_t seg_len = (L + S - 1) / S;
@@ -1010,7 +1319,11 @@ S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N) {
     S = (L + seg_len - 1) / seg_len;   // no empty trailing segment
     pl.S = (int)S;
     pl.seg_len = seg_len;
-    if (S > 1) pl.workspace_bytes = (size_t)2 * (size_t)(B * D * S * N) * sizeof(float);
+    // one workspace serves both paths: (decay, offset) pairs per segment
+    int64_t S_ws = 0;
+    if (pl.S > 1) S_ws = pl.S;
+    if (pl.lanes && pl.S_lanes > S_ws) S_ws = pl.S_lanes;
+    if (S_ws > 1) pl.workspace_bytes = (size_t)2 * (size_t)(B * D * S_ws * N) * sizeof(float);
     return pl;
 }
 

@@ -98,7 +98,8 @@ const char* ssm_status_string(int status) {
 
 int ssm_selective_scan_segments(int64_t B, int64_t L, int64_t D, int64_t N) {
     if (s6_check_sizes(B, L, D, N, SSM_F32) != SSM_OK) return 0;
-    return ssm::plan_s6(B, L, D, N).S;
+    const ssm::S6Plan pl = ssm::plan_s6(B, L, D, N);
+    return pl.lanes ? pl.S_lanes : pl.S;
 }
 
 int ssm_selective_scan_lanes(int64_t B, int64_t L, int64_t D, int64_t N) {
@@ -194,13 +195,15 @@ int s6_fwd_impl(const void* u, const void* delta, const float* A, const void* Bm
     a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.z = z;
     a.delta_bias = delta_bias; a.h0 = h0; a.y = y; a.h_last = h_last;
     a.B = B; a.L = L; a.D = D; a.N = N;
-    a.S = plan.S; a.seg_len = plan.seg_len; a.flags = flags; a.bf16 = dtype == SSM_BF16;
-    a.lanes = plan.lanes;
+    a.lanes = plan.lanes && !(flags & SSM_FLAG_ZOH);
+    a.S = a.lanes ? plan.S_lanes : plan.S;
+    a.seg_len = a.lanes ? plan.seg_len_lanes : plan.seg_len;
+    a.flags = flags; a.bf16 = dtype == SSM_BF16;
     a.events = reinterpret_cast<hipEvent_t const*>(events);
     a.seq_lens = seq_lens;
-    if (plan.S > 1) {
+    if (a.S > 1) {
         a.seg_a = static_cast<float*>(workspace);
-        a.seg_b = a.seg_a + B * D * (int64_t)plan.S * N;
+        a.seg_b = a.seg_a + B * D * (int64_t)a.S * N;
     }
     const hipError_t e = ssm::launch_s6(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
@@ -241,13 +244,15 @@ int ssm_selective_scan_conv_fwd(const void* x, const float* conv_weight, const f
     a.u = x; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.z = z;
     a.delta_bias = delta_bias; a.h0 = h0; a.y = y; a.h_last = h_last;
     a.B = B; a.L = L; a.D = D; a.N = N;
-    a.S = plan.S; a.seg_len = plan.seg_len; a.flags = flags; a.bf16 = dtype == SSM_BF16;
     a.lanes = plan.lanes;
+    a.S = a.lanes ? plan.S_lanes : plan.S;
+    a.seg_len = a.lanes ? plan.seg_len_lanes : plan.seg_len;
+    a.flags = flags; a.bf16 = dtype == SSM_BF16;
     a.conv_w = conv_weight; a.conv_b = conv_bias; a.conv_state_in = conv_state_in;
     a.conv_state_out = conv_state_out; a.u_out = u_out; a.conv_K = K;
-    if (plan.S > 1) {
+    if (a.S > 1) {
         a.seg_a = static_cast<float*>(workspace);
-        a.seg_b = a.seg_a + B * D * (int64_t)plan.S * N;
+        a.seg_b = a.seg_a + B * D * (int64_t)a.S * N;
     }
     const hipError_t e = ssm::launch_s6(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;

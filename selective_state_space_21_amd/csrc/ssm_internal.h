@@ -39,13 +39,15 @@ struct S6Args {
     void* u_out;                // [B, L, D] or NULL: the convolution's output u
     int64_t conv_K;
     const int32_t* seq_lens;    // [B] tokens per batch row (device), or NULL: all L
-    bool lanes;                 // state-per-lane kernel (unsplit) for N = 16 without ZOH
+    bool lanes;                 // state-per-lane kernel for N = 16 without ZOH
 };
 
 struct S6Plan {
-    int S;                  // segments of the split path
+    int S;                  // segments of the split path (ZOH calls, or lanes off)
     int64_t seg_len;
-    size_t workspace_bytes; // of the split path (also required when lanes is set)
+    int S_lanes;            // segments of the state-per-lane path
+    int64_t seg_len_lanes;
+    size_t workspace_bytes; // pairs of either path
     bool lanes;             // an N = 16 call without ZOH takes the state-per-lane kernel
 };
 

@@ -78,10 +78,24 @@ def test_s6_workspace_and_plan(lib):
     # one segment when there are plenty of channels
     assert lib.ssm_selective_scan_segments(64, 2048, 4096, 16) == 1
     assert lib.ssm_selective_scan_workspace_bytes(64, 2048, 4096, 16, 1) == 0
-    # few channels, long sequence: split into up to 256 segments
+    # few channels, long sequence: split into up to 256 segments; the
+    # workspace holds the pairs of whichever path is larger (the query has
+    # no flags, and ZOH calls take the split path)
     S = lib.ssm_selective_scan_segments(1, 131072, 2048, 16)
     assert 2 <= S <= 256
-    assert lib.ssm_selective_scan_workspace_bytes(1, 131072, 2048, 16, 0) == 2 * 4 * 2048 * 16 * S
+    import os
+    old = os.environ.get("SSM_S6_LANES")
+    os.environ["SSM_S6_LANES"] = "0"
+    try:
+        S_split = lib.ssm_selective_scan_segments(1, 131072, 2048, 16)
+    finally:
+        if old is None:
+            del os.environ["SSM_S6_LANES"]
+        else:
+            os.environ["SSM_S6_LANES"] = old
+    assert 2 <= S_split <= 256
+    assert (lib.ssm_selective_scan_workspace_bytes(1, 131072, 2048, 16, 0)
+            == 2 * 4 * 2048 * 16 * max(S, S_split))
     # never more segments than ceil(L / 32)
     assert lib.ssm_selective_scan_segments(1, 40, 64, 16) <= 2
     assert lib.ssm_selective_scan_segments(1, 0, 64, 16) == 1
@@ -89,29 +103,42 @@ def test_s6_workspace_and_plan(lib):
 
 
 def test_s6_plan_env_override(lib, monkeypatch):
+    # split path: any count up to 256, segments of at least 32 tokens
+    monkeypatch.setenv("SSM_S6_LANES", "0")
     monkeypatch.setenv("SSM_S6_SEGMENTS", "7")
     assert lib.ssm_selective_scan_segments(1, 7000, 64, 16) == 7
     monkeypatch.setenv("SSM_S6_SEGMENTS", "500")
     assert lib.ssm_selective_scan_segments(1, 70000, 64, 16) == 256
+    # state-per-lane path: segments are whole 128-token super-tiles
+    monkeypatch.delenv("SSM_S6_LANES")
+    monkeypatch.setenv("SSM_S6_SEGMENTS", "7")
+    assert lib.ssm_selective_scan_segments(1, 7000, 64, 16) == 7
+    monkeypatch.setenv("SSM_S6_SEGMENTS", "500")
+    seg = -(-(-(-70000 // 256)) // 128) * 128
+    assert lib.ssm_selective_scan_segments(1, 70000, 64, 16) == -(-70000 // seg)
 
 
 def test_s6_lanes_plan(lib, monkeypatch):
     # The planner balances over 1024 SIMDs (256 CUs), device or not: the state-per-lane
-    # kernel needs N = 16, D % 16 == 0 and B*D/4 >= 2048 wavefronts
+    # kernel needs N = 16 and D % 16 == 0; below 2048 wavefronts (B*D/4) it cuts the
+    # sequence into segments of whole super-tiles for three wavefronts per SIMD
     monkeypatch.delenv("SSM_S6_LANES", raising=False)
+    monkeypatch.delenv("SSM_S6_SEGMENTS", raising=False)
     assert lib.ssm_selective_scan_lanes(8, 2048, 1536, 16) == 1
+    assert lib.ssm_selective_scan_segments(8, 2048, 1536, 16) == 1
     assert lib.ssm_selective_scan_lanes(4, 4096, 5120, 16) == 1
-    assert lib.ssm_selective_scan_lanes(1, 131072, 2048, 16) == 0      # too few channels
+    assert lib.ssm_selective_scan_lanes(1, 131072, 2048, 16) == 1      # few channels: segments
+    assert lib.ssm_selective_scan_segments(1, 131072, 2048, 16) == 6
     assert lib.ssm_selective_scan_lanes(8, 2048, 1544, 16) == 0        # D % 16 != 0
     assert lib.ssm_selective_scan_lanes(8, 2048, 1536, 32) == 0        # N != 16
     assert lib.ssm_selective_scan_lanes(0, 2048, 1536, 16) == 0        # invalid sizes
     # offsets of one batch row (plus a super-tile) must fit 32 bits at 4 B per element
     assert lib.ssm_selective_scan_lanes(2, 2**20, 1024, 16) == 0
-    # the split plan (segments, workspace) is unchanged: other calls still use it
-    assert lib.ssm_selective_scan_segments(8, 2048, 1536, 16) > 1
+    # the split plan (segments, workspace) is unchanged: ZOH calls still use it
     monkeypatch.setenv("SSM_S6_LANES", "0")
     assert lib.ssm_selective_scan_lanes(8, 2048, 1536, 16) == 0
-    monkeypatch.setenv("SSM_S6_LANES", "1")
+    assert lib.ssm_selective_scan_segments(8, 2048, 1536, 16) > 1
+    monkeypatch.delenv("SSM_S6_LANES")
     assert lib.ssm_selective_scan_lanes(1, 40, 64, 16) == 1
     assert lib.ssm_selective_scan_lanes(1, 40, 72, 16) == 0
     assert lib.ssm_selective_scan_lanes(1, 40, 64, 8) == 0

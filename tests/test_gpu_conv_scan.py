@@ -21,8 +21,12 @@ pytestmark = pytest.mark.gpu
 @pytest.fixture(params=["split", "lanes"], autouse=True)
 def s6_path(request, monkeypatch):
     """Every test runs on both S6 paths: the split path (SSM_S6_LANES=0) and the
-    state-per-lane kernel (SSM_S6_LANES=1, taken where D is a multiple of 16)."""
-    monkeypatch.setenv("SSM_S6_LANES", "0" if request.param == "split" else "1")
+    state-per-lane kernel (the default where D is a multiple of 16; small
+    shapes are cut into segments of whole super-tiles and fixed up)."""
+    if request.param == "split":
+        monkeypatch.setenv("SSM_S6_LANES", "0")
+    else:
+        monkeypatch.delenv("SSM_S6_LANES", raising=False)
     return request.param
 
 
@@ -74,7 +78,7 @@ def test_fused_parity(dtype, shape, s6_path):
 
 
 @pytest.mark.parametrize("segments", [1, 3, 16])
-def test_fused_equals_separate_calls_fp32(monkeypatch, segments):
+def test_fused_equals_separate_calls_fp32(monkeypatch, segments, s6_path):
     monkeypatch.setenv("SSM_S6_SEGMENTS", str(segments))
     inp = _case(2, 600, 96, 4, "f32", seed=segments)
     d = to_dev(inp)
@@ -83,7 +87,9 @@ def test_fused_equals_separate_calls_fp32(monkeypatch, segments):
     y, h = ssm.selective_scan_fwd(u, d["delta"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
                                   delta_bias=d["delta_bias"])
     torch.cuda.synchronize()
-    assert ssm.selective_scan_segments(2, 600, 96, 16) == segments
+    from test_gpu_s6 import lanes_segments
+    want = segments if s6_path == "split" else lanes_segments(600, segments)
+    assert ssm.selective_scan_segments(2, 600, 96, 16) == want
     assert torch.equal(r["u"], u)
     assert torch.equal(r["y"], y)
     assert torch.equal(r["h_last"], h)

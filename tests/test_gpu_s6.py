@@ -43,18 +43,32 @@ def test_workload_parity_small(w):
     _cmp(W.make_s6_inputs(w, seed=0))
 
 
+def lanes_segments(L, S):
+    """Segments of the state-per-lane path for a forced count S: whole
+    128-token super-tiles, at most ceil(L / 128) and 256."""
+    S = max(1, min(S, math.ceil(L / 128), 256))
+    seg = math.ceil(math.ceil(L / S) / 128) * 128
+    return math.ceil(L / seg)
+
+
+@pytest.mark.parametrize("path", ["split", "lanes"])
 @pytest.mark.parametrize("S", [1, 2, 3, 5, 16, 64])
-def test_every_segment_count(S, monkeypatch):
+def test_every_segment_count(S, path, monkeypatch):
     monkeypatch.setenv("SSM_S6_SEGMENTS", str(S))
+    if path == "split":
+        monkeypatch.setenv("SSM_S6_LANES", "0")
     w = W.S6_MAMBA130M.scaled(B=2, L=2100, D=64)
     inp = W.make_s6_inputs(w, seed=1)
-    assert ssm.selective_scan_segments(w.B, w.L, w.D, w.N) == min(S, math.ceil(2100 / 32))
+    assert ssm.selective_scan_lanes(w.B, w.L, w.D, w.N) == (path == "lanes")
+    want = min(S, math.ceil(2100 / 32)) if path == "split" else lanes_segments(2100, S)
+    assert ssm.selective_scan_segments(w.B, w.L, w.D, w.N) == want
     _cmp(inp)
 
 
 @pytest.mark.parametrize("S", [96, 200, 256])
 def test_more_than_64_segments(S, monkeypatch):
-    # the segment carry folds up to 256 (decay, offset) pairs per chain
+    # the split path's segment carry folds up to 256 (decay, offset) pairs per chain
+    monkeypatch.setenv("SSM_S6_LANES", "0")
     monkeypatch.setenv("SSM_S6_SEGMENTS", str(S))
     w = W.S6_LONG_FP32.scaled(L=9000, D=64)
     inp = W.make_s6_inputs(w, seed=3)
@@ -136,6 +150,25 @@ def _exact_case(L, Dm, N, dtype, mode, seed):
     td = W.torch_dtype(dtype)
     return dict(u=u.to(td), delta=dt.to(td), A=A, B=Bm.to(td), C=Cm.to(td), D=Dsk, z=None,
                 delta_bias=None, h0=h0, delta_softplus=False)
+
+
+@pytest.mark.parametrize("mode", ["prefix", "reset", "mixed"])
+@pytest.mark.parametrize("L", [1, 127, 128, 129, 255, 256, 257, 1000, 4099])
+@pytest.mark.parametrize("S", [1, 2, 3, 8, 33])
+def test_bit_exact_segments_lanes(mode, L, S, monkeypatch):
+    """The state-per-lane path cut into segments of whole super-tiles, each
+    later segment scanned from zero and fixed up with its incoming state:
+    exact integers at every length around the segment boundaries."""
+    monkeypatch.setenv("SSM_S6_SEGMENTS", str(S))
+    for dtype in ("f32", "bf16"):
+        inp = _exact_case(L, 96, 16, dtype, mode, seed=L * 11 + S)
+        assert ssm.selective_scan_lanes(2, L, 96, 16)
+        assert ssm.selective_scan_segments(2, L, 96, 16) == lanes_segments(L, S)
+        y, h = s6_gpu(inp)
+        yr, hr = s6_oracle(inp)
+        assert np.all(np.abs(yr) < 256) and np.all(yr == np.round(yr))
+        np.testing.assert_array_equal(y.float().cpu().numpy(), yr)
+        np.testing.assert_array_equal(h.cpu().numpy(), hr)
 
 
 @pytest.mark.parametrize("mode", ["prefix", "reset", "mixed"])

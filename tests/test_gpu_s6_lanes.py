@@ -1,6 +1,6 @@
 """GPU parity of the state-per-lane S6 forward (one lane per channel x state,
-the whole sequence in one pass) against the fp64 oracle.  SSM_S6_LANES=1
-forces that kernel at sizes the planner would give to the split path.  Bars
+the whole sequence in one pass) against the fp64 oracle.  SSM_S6_SEGMENTS=1
+keeps it in one pass at sizes the planner would cut into segments.  Bars
 as for the split path: normwise 1e-5 (fp32), 2e-2 (bf16); bit-exact on the
 integer-valued boundary cases."""
 import numpy as np
@@ -19,7 +19,10 @@ pytestmark = pytest.mark.gpu
 
 @pytest.fixture
 def lanes(monkeypatch):
-    monkeypatch.setenv("SSM_S6_LANES", "1")
+    # the state-per-lane kernel in one pass over the sequence (small shapes
+    # would otherwise be cut into segments)
+    monkeypatch.delenv("SSM_S6_LANES", raising=False)
+    monkeypatch.setenv("SSM_S6_SEGMENTS", "1")
 
 
 def _cmp(inp, tol=None):
@@ -33,11 +36,15 @@ def _cmp(inp, tol=None):
     return ey, eh
 
 
-def test_planner_takes_lanes_at_the_layer_shapes():
+def test_planner_takes_lanes_at_the_layer_shapes(monkeypatch):
+    monkeypatch.delenv("SSM_S6_SEGMENTS", raising=False)
     for w in (W.S6_MAMBA130M, W.S6_MAMBA2P8B):
         assert ssm.selective_scan_lanes(w.B, w.L, w.D, w.N)
-    # too few channels to fill the chip, D not a multiple of 16, N != 16
-    assert not ssm.selective_scan_lanes(1, 131072, 2048, 16)
+        assert ssm.selective_scan_segments(w.B, w.L, w.D, w.N) == 1
+    # too few channels to fill the chip: segments of whole super-tiles
+    assert ssm.selective_scan_lanes(1, 131072, 2048, 16)
+    assert ssm.selective_scan_segments(1, 131072, 2048, 16) == 6
+    # D not a multiple of 16, N != 16: the split path
     assert not ssm.selective_scan_lanes(8, 2048, 1544, 16)
     assert not ssm.selective_scan_lanes(8, 2048, 1536, 8)
 
@@ -122,6 +129,7 @@ def test_agrees_with_split_path(monkeypatch):
     w = W.S6_MAMBA130M.scaled(B=2, L=2048, D=256)
     d = to_dev(W.make_s6_inputs(w, seed=4))
     outs = []
+    monkeypatch.setenv("SSM_S6_SEGMENTS", "1")
     for env in ("1", "0"):
         monkeypatch.setenv("SSM_S6_LANES", env)
         assert ssm.selective_scan_lanes(w.B, w.L, w.D, w.N) == (env == "1")

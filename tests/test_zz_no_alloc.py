@@ -1,7 +1,7 @@
 """The allocation-free S6 entry point (ssm_selective_scan_fwd_noalloc) against
 the ordinary one, through the C ABI: same kernels, so bit-identical results,
-on two calls in a row (the second smaller) that take the split path and so
-use the library's static scratch.  Both calls run in one process, the second
+on two calls in a row (the second smaller) whose plans cut the sequence into
+segments and so use the library's static scratch.  Both calls run in one process, the second
 after the first left its pairs in the scratch."""
 import ctypes
 
@@ -15,12 +15,14 @@ from selective_state_space_21_amd import workloads as W
 pytestmark = pytest.mark.gpu
 
 
-def _both(w, seed, monkeypatch, segments=None):
+def _both(w, seed, monkeypatch, segments=None, split=False):
     if segments:
         monkeypatch.setenv("SSM_S6_SEGMENTS", str(segments))
+    if split:
+        monkeypatch.setenv("SSM_S6_LANES", "0")
     t = W.make_s6_inputs(w, seed=seed)
     d = {k: (v.to("cuda") if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
-    assert not ssm.selective_scan_lanes(w.B, w.L, w.D, w.N)
+    assert ssm.selective_scan_lanes(w.B, w.L, w.D, w.N) == (not split)
     S = ssm.selective_scan_segments(w.B, w.L, w.D, w.N)
     assert S > 1, "the case must use the scratch (split path)"
     need = ssm.selective_scan_workspace_bytes(w.B, w.L, w.D, w.N, d["u"].dtype)
@@ -38,9 +40,11 @@ def _both(w, seed, monkeypatch, segments=None):
 
 
 def test_noalloc_matches_workspace_call_twice(monkeypatch):
+    # first the state-per-lane path cut into segments (pairs, carry, fix-up),
+    # then a smaller call on the split path, over what the first left behind
     s1 = _both(W.S6_LONG_FP32.scaled(L=30000, D=256), seed=1, monkeypatch=monkeypatch)
     s2 = _both(W.S6_MAMBA130M.scaled(B=1, L=3000, D=64), seed=2, monkeypatch=monkeypatch,
-               segments=7)
+               segments=7, split=True)
     assert s1 > 1 and s2 > 1
 
 
