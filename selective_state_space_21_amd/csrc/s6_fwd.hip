@@ -482,8 +482,9 @@ void s6_fast(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
 // kept in fp32 in a double-buffered LDS halo.
 namespace lanes {
 constexpr int kTile = 16;                 // tokens per tile (one per lane of a row)
-constexpr int kSuper = 8;                 // tiles per super-tile
-constexpr int kSpan = kTile * kSuper;     // tokens per super-tile
+constexpr int kSuper = 8;                 // tiles per super-tile, one pass over the sequence
+constexpr int kSuperSeg = 4;              // tiles per super-tile, segments (half the LDS)
+constexpr int kSpan = kTile * kSuper;     // segments are whole multiples of this
 constexpr int kChans = 16;                // channels per workgroup
 constexpr int kPitch = kTile + 4;         // staged B/C row of one state (floats)
 
@@ -491,22 +492,26 @@ template <typename T> __device__ __forceinline__ uint32_t elem_bits(T v);
 template <> __device__ __forceinline__ uint32_t elem_bits<uint16_t>(uint16_t v) { return v; }
 template <> __device__ __forceinline__ uint32_t elem_bits<float>(float v) { return __float_as_uint(v); }
 
-// One super-tile's inputs as loaded: 16-byte pieces, kPer per thread and tensor.
-template <typename T, bool HAS_Z>
+// One super-tile's inputs as loaded: 16-byte pieces, kPer per thread and
+// tensor (kPieces in all; with fewer than 256 some threads load none).
+template <typename T, bool HAS_Z, int SPAN>
 struct Pieces {
     static constexpr int kPerToken = kChans * (int)sizeof(T) / 16;   // channels' run of a token
-    static constexpr int kPer = kSpan * kPerToken / 256;
+    static constexpr int kPieces = SPAN * kPerToken;
+    static constexpr int kPer = (kPieces + 255) / 256;
     u32x4 u[kPer], d[kPer], z[HAS_Z ? kPer : 1], b[kPer], c[kPer];
 };
 }  // namespace lanes
 
-template <typename T, bool HAS_Z, bool SOFTPLUS, bool CONV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+template <typename T, bool HAS_Z, bool SOFTPLUS, bool CONV, int SUP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SUP == lanes::kSuper ? 3 : 4)))
 void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
               const T* __restrict__ z_, const T* __restrict__ Bm_, const T* __restrict__ Cm_,
               T* __restrict__ y_) {
     using namespace lanes;
-    using Raw = Pieces<T, HAS_Z>;
+    constexpr int kSuper = SUP;               // tiles per super-tile
+    constexpr int kSpan = kTile * SUP;        // tokens per super-tile
+    using Raw = Pieces<T, HAS_Z, kSpan>;
     constexpr uint32_t E = sizeof(T);
     constexpr int kPerToken = Raw::kPerToken, kPer = Raw::kPer;
     constexpr int kVals = 16 / (int)E;                  // elements per piece
@@ -592,6 +597,7 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
             const uint32_t idx = tid + 256 * k, t = idx / kPerToken, pc = idx % kPerToken;
+            if (Raw::kPieces % 256 != 0 && idx >= (uint32_t)Raw::kPieces) break;
             const uint32_t voff = t * row_bytes + grp_bytes + 16 * pc;
             r.u[k] = __builtin_amdgcn_raw_buffer_load_b128(ru, (int)voff, (int)soff, 0);
             r.d[k] = __builtin_amdgcn_raw_buffer_load_b128(rd, (int)voff, (int)soff, 0);
@@ -606,6 +612,7 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
             const int idx = tid + 256 * k, t = idx / kPerToken, pc = idx % kPerToken;
+            if (Raw::kPieces % 256 != 0 && idx >= Raw::kPieces) break;
             const T* vb = reinterpret_cast<const T*>(&r.b[k]);
             const T* vc = reinterpret_cast<const T*>(&r.c[k]);
             *reinterpret_cast<u32x4*>(&act[0][t][kVals * pc]) = r.u[k];
@@ -619,11 +626,11 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
             }
         }
     };
-    constexpr int kPerY = kSpan * kPerToken / 256;
     auto store_y = [&](int64_t st0) {
 #pragma unroll
-        for (int k = 0; k < kPerY; ++k) {
+        for (int k = 0; k < kPer; ++k) {
             const uint32_t idx = tid + 256 * k, t = idx / kPerToken, pc = idx % kPerToken;
+            if (Raw::kPieces % 256 != 0 && idx >= (uint32_t)Raw::kPieces) break;
             const u32x4 v = *reinterpret_cast<const u32x4*>(
                 reinterpret_cast<const char*>(&yst[t][0]) + 16 * pc);
             __builtin_amdgcn_raw_buffer_store_b128(v, ry, (int)(t * row_bytes + grp_bytes + 16 * pc),
@@ -1196,8 +1203,17 @@ hipError_t launch_lanes(const S6Args& a, hipStream_t stream) {
     const dim3 grid(groups, (unsigned)a.B, (unsigned)a.S), block(256);
     mark(a, 0, stream);
     const bool cv = a.conv_w != nullptr;
-#define SSM_LANES(Z_, SP_, CV_) \
-    hipLaunchKernelGGL((s6_lanes<T, Z_, SP_, CV_>), grid, block, 0, stream, a, U, Dl, Z, Bp, Cp, Y)
+    // one pass: 128-token super-tiles (3 workgroups per CU by LDS);
+    // segments: 64-token super-tiles (half the LDS, 4 wavefronts per SIMD)
+#define SSM_LANES(Z_, SP_, CV_)                                                                   \
+    do {                                                                                          \
+        if (a.S > 1)                                                                              \
+            hipLaunchKernelGGL((s6_lanes<T, Z_, SP_, CV_, lanes::kSuperSeg>), grid, block, 0,     \
+                               stream, a, U, Dl, Z, Bp, Cp, Y);                                   \
+        else                                                                                      \
+            hipLaunchKernelGGL((s6_lanes<T, Z_, SP_, CV_, lanes::kSuper>), grid, block, 0,        \
+                               stream, a, U, Dl, Z, Bp, Cp, Y);                                   \
+    } while (0)
     if (cv) {
         if (a.z) { if (sp) SSM_LANES(true, true, true); else SSM_LANES(true, false, true); }
         else { if (sp) SSM_LANES(false, true, true); else SSM_LANES(false, false, true); }
@@ -1272,8 +1288,9 @@ S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N) {
     // activations (plus two super-tiles) within 32-bit buffer offsets at 4
     // bytes per element.  SSM_S6_LANES=0 turns it off.  It runs B*D/4
     // wavefronts per segment: unsplit with at least two per SIMD, else cut
-    // into the fewest segments (whole super-tiles) that give three per SIMD;
-    // the segments after the first are fixed up afterwards.
+    // into the fewest segments (whole 128-token multiples) that give four per
+    // SIMD (the segmented kernel stages half as much and fits four); the
+    // segments after the first are fixed up afterwards.
     {
         const bool shape_ok = N == 16 && D % lanes::kChans == 0 &&
                               (L + 2 * lanes::kSpan) * D * 4 <= (int64_t)0xFFFFFFFF;
@@ -1281,7 +1298,7 @@ S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N) {
         const char* env = getenv("SSM_S6_LANES");
         if (env && env[0] == '0') pl.lanes = false;
         const int64_t waves = B * D / 4;
-        int64_t S = waves >= 2 * kSimds ? 1 : (3 * kSimds + waves - 1) / (waves > 0 ? waves : 1);
+        int64_t S = waves >= 2 * kSimds ? 1 : (4 * kSimds + waves - 1) / (waves > 0 ? waves : 1);
         if (forced) S = forced;
         int64_t maxS = (L + lanes::kSpan - 1) / lanes::kSpan;
         if (maxS > kMaxSegments) maxS = kMaxSegments;
