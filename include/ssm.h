@@ -232,7 +232,9 @@ int ssm_selective_scan_conv_fwd(const void* x, const float* conv_weight, const f
  *   A       : [H] fp32 (negative);  Dskip, delta_bias : [H] fp32 or NULL
  *   Bm, Cm  : [B, L, G, N] dtype;  H % G == 0
  *   h0, h_last : [B, H, P, N] fp32 or NULL
- *   supported: dtype SSM_BF16, P = 64, N in {64, 128}, chunk in {64, 128, 256},
+ *   supported: dtype SSM_BF16, P a multiple of 32, N in {32, 64, 96, 128},
+ *   chunk in {64, 128, 256}, B * H * (P / 64, or P / 32 when P % 64 != 0)
+ *   below 2^31,
  *   and one batch row within 32-bit byte offsets with two chunks to spare:
  *   (L + 512) * H * P * 2 and (L + 512) * G * N * 2 at most 2^32 - 1
  *   (else SSM_ERR_UNSUPPORTED).

@@ -14,10 +14,12 @@
 //   S_new[p][n]    = exp(cum_Q) S[p][n] + sum_s X[s][p] w_s B[s][n],
 //       w_s        = exp(cum_Q - cum_s) dt_s                         (K = Q)
 //
-// Work mapping: one workgroup of eight wavefronts owns one (b, h) for the
-// whole sequence and walks its chunks in order, so the P x N state never
-// leaves the chip: it sits in fp32 MFMA accumulators (each wavefront owns 16
-// state columns) with a bf16 copy in LDS for the next chunk's Y_off.  The next
+// Work mapping: one workgroup of eight wavefronts owns one (b, h) -- or, for a
+// head dimension P above 64, one slice of PT = 64 (or 32) head-dim rows of it
+// -- for the whole sequence and walks its chunks in order, so its PT x N part
+// of the state never leaves the chip: it sits in fp32 MFMA accumulators (each
+// wavefront owns 16 state columns) with a bf16 copy in LDS for the next
+// chunk's Y_off.  Slices of one head repeat the head's score products.  The next
 // chunk's B, X, C and delta are fetched into registers while the current one
 // is computed; barriers wait on LDS only, so those loads stay in flight.  Per
 // chunk, B rows and X^T are staged in LDS and each wavefront keeps the C rows
@@ -51,7 +53,6 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kP = 64;          // head dimension
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 
@@ -65,7 +66,7 @@ __device__ __forceinline__ float f32(__bf16 x) { return static_cast<float>(x); }
 // lds_barrier() (lane_ops.h) waits for this wavefront's LDS traffic only:
 // global loads issued before it (the next chunk's prefetch) stay in flight.
 
-template <int Q, int N>
+template <int Q, int N, int PT>
 struct SsdLds {
     static constexpr int kBStride = N + 16;      // bf16 per B row (32-byte pad: ~1% faster than 16)
     static constexpr int kXStride = Q + 8;       // bf16 per X^T row
@@ -83,20 +84,22 @@ struct SsdLds {
     alignas(16) float part[kWaves];               // per-wavefront scan totals
     alignas(16) int wide[kWaves];                 // per-wavefront: a 32-token block spans > 2^64
     alignas(16) __bf16 B[Q * kBStride];           // B rows of the chunk
-    alignas(16) __bf16 Xt[kP * kXStride];         // X^T of the chunk
+    alignas(16) __bf16 Xt[PT * kXStride];         // X^T of the chunk (this workgroup's rows)
     alignas(16) float wst[Q];                     // exp(cum_Q - cum_s) dt_s: token s's weight in the final state
-    alignas(16) __bf16 H[kP * kHStride];          // state (bf16) for Y_off
+    alignas(16) __bf16 H[PT * kHStride];          // state (bf16) for Y_off
 };
 
-template <int Q, int N>
+template <int Q, int N, int PT>
 struct Tiles {
     static constexpr int T = Q / 16;                           // output column tiles
     static constexpr int TPW = T >= 2 * kWaves ? 2 : 1;        // tiles per wavefront
     static constexpr int NTILE = N / 16;                       // state column tiles
     static constexpr int KN = N / 32;
     static constexpr int KQ = Q / 32;
-    static constexpr int BPIECE = (Q * N / 8 + kThreads - 1) / kThreads;   // 16-B pieces / thread
-    static constexpr int XGROUP = (Q / 4) * (kP / 8);          // (4 tokens x 8 p) groups
+    static constexpr int JP = PT / 16;                         // head-dim row tiles
+    static constexpr int BPIECES = Q * N / 8;                  // 16-B pieces of a chunk's B rows
+    static constexpr int BPIECE = (BPIECES + kThreads - 1) / kThreads;   // per thread
+    static constexpr int XGROUP = (Q / 4) * (PT / 8);          // (4 tokens x 8 p) groups
     static constexpr int XPIECE = 4;                           // 16-B rows per group
     // B pieces fetched ahead of the output tiles; the rest after them.  At the
     // largest tile shape all of B is fetched after the tiles (it is mostly an
@@ -145,11 +148,11 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
     return __builtin_bit_cast(bf16x4, v);
 }
 
-template <int Q, int N, bool HAS_Z>
+template <int Q, int N, int PT, bool HAS_Z>
 __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
-    using TL = Tiles<Q, N>;
-    constexpr int TPW = TL::TPW, KN = TL::KN, KQ = TL::KQ;
-    using Lds = SsdLds<Q, N>;
+    using TL = Tiles<Q, N, PT>;
+    constexpr int TPW = TL::TPW, KN = TL::KN, KQ = TL::KQ, JP = TL::JP;
+    using Lds = SsdLds<Q, N, PT>;
     __shared__ Lds sm;
     auto stage_xt = [](__bf16* xt, int sg, int p8, const uint32_t (&xs)[4][4]) {
         stage_xt_rows<Lds>(xt, sg, p8, xs);
@@ -161,13 +164,20 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
     const int g = l / 16;
     const int c = l % 16;
     // Workgroups are dealt to the 8 XCDs round robin (i -> XCD i % 8); renumber
-    // them so that each XCD receives a contiguous range of (batch, head) pairs.
-    // Heads of one batch row share B and C, so those rows are then fetched
-    // into about two of the eight L2 caches instead of all eight.
-    const int64_t bh = [] {
+    // them so that each XCD receives a contiguous range of (batch, head, slice)
+    // triples.  Heads of one batch row share B and C, so those rows are then
+    // fetched into about two of the eight L2 caches instead of all eight.
+    const int64_t wg = [] {
         const uint32_t n = gridDim.x, i = blockIdx.x, x = i % 8, q = n / 8, r = n % 8;
         return (int64_t)(x * q + min(x, r) + i / 8);
     }();
+    // A head of P > PT values is split over P / PT workgroups, each owning PT
+    // consecutive rows of the state (rows of S evolve independently: the
+    // decay is one scalar per head and the input term is an outer product).
+    const int64_t P = p.P;
+    const int64_t nslice = P / PT;
+    const int64_t bh = wg / nslice;
+    const int64_t pbase = (wg % nslice) * PT;     // first head-dim row of this workgroup
     const int64_t b = bh / p.H;
     const int64_t h = bh % p.H;
     const int64_t grp = h / (p.H / p.G);
@@ -188,23 +198,23 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
     const bool softplus = (p.flags & SSM_FLAG_DELTA_SOFTPLUS) != 0;
     const int ntile = w < TL::NTILE ? w : -1;      // this wavefront's state columns
 
-    // ---- state: hacc[j] = S[p = 16j + 4g + r][n = 16 * ntile + c]
-    f32x4 hacc[4];
+    // ---- state: hacc[j] = S[p = pbase + 16j + 4g + r][n = 16 * ntile + c]
+    f32x4 hacc[JP];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < JP; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             hacc[j][r] = (p.h0 && ntile >= 0)
-                             ? p.h0[(bh * kP + 16 * j + 4 * g + r) * N + 16 * ntile + c] : 0.0f;
-    for (int i = tid; i < kP * N; i += kThreads) {
+                             ? p.h0[(bh * P + pbase + 16 * j + 4 * g + r) * N + 16 * ntile + c] : 0.0f;
+    for (int i = tid; i < PT * N; i += kThreads) {
         const int pp = i / N, nn = i % N;
-        sm.H[pp * Lds::kHStride + nn] = bf(p.h0 ? p.h0[(bh * kP + pp) * N + nn] : 0.0f);
+        sm.H[pp * Lds::kHStride + nn] = bf(p.h0 ? p.h0[(bh * P + pbase + pp) * N + nn] : 0.0f);
     }
 
     // ---- inputs through buffer resources based at batch row b: a read past
     // the end of the sequence (chunk tail) returns zero, so no load is guarded
-    static_assert((Q * N / 8) % kThreads == 0 && TL::XGROUP <= kThreads, "piece split");
-    const auto rX = make_rsrc(X + b * L * H * kP, (uint32_t)(L * H * kP * 2));
+    static_assert(TL::XGROUP <= kThreads, "one X group per thread at most");
+    const auto rX = make_rsrc(X + b * L * H * P, (uint32_t)(L * H * P * 2));
     const auto rB = make_rsrc(Bg + b * L * G * N, (uint32_t)(L * G * N * 2));
     const auto rC = make_rsrc(Cg + b * L * G * N, (uint32_t)(L * G * N * 2));
     const auto rD = make_rsrc(Dl + b * L * H, (uint32_t)(L * H * 2));
@@ -217,6 +227,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
 #pragma unroll
         for (int k = decltype(k0)::value; k < decltype(k1)::value; ++k) {
             const uint32_t i = tid + k * kThreads;
+            if (TL::BPIECES % kThreads != 0 && i >= (uint32_t)TL::BPIECES) break;
             const uint32_t s = i / (N / 8), k8 = i % (N / 8);
             bpre[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                 rB, (int)((((tc + s) * (uint32_t)G + (uint32_t)grp) * N + 8 * k8) * 2), 0, 0));
@@ -235,11 +246,12 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
             // The Y stores stay cached: each 128-byte row of a token is
             // written in four 32-byte pieces, which the L2 merges; as
             // nontemporal stores they doubled the bytes written to HBM.
-            const uint32_t sg = min(tid, TL::XGROUP - 1) / (kP / 8), p8 = tid % (kP / 8);
+            const uint32_t sg = min(tid, TL::XGROUP - 1) / (PT / 8), p8 = tid % (PT / 8);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 xpre[q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                    rX, (int)((((tc + 4 * sg + q) * (uint32_t)H + (uint32_t)h) * kP + 8 * p8) * 2),
+                    rX, (int)((((tc + 4 * sg + q) * (uint32_t)H + (uint32_t)h) * (uint32_t)P
+                               + (uint32_t)pbase + 8 * p8) * 2),
                     0, 2));
         }
     };
@@ -286,11 +298,12 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
 #pragma unroll
         for (int k = 0; k < TL::BPIECE; ++k) {
             const int i = tid + k * kThreads;
+            if (TL::BPIECES % kThreads != 0 && i >= TL::BPIECES) break;
             const int s = i / (N / 8), k8 = i % (N / 8);
             *reinterpret_cast<uint4*>(&sm.B[s * Lds::kBStride + 8 * k8]) = bpre[k];
         }
         if (tid < TL::XGROUP) {
-            const int sg = tid / (kP / 8), p8 = tid % (kP / 8);
+            const int sg = tid / (PT / 8), p8 = tid % (PT / 8);
             uint32_t xs[4][4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -343,15 +356,16 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
         // join waits for them)
         prefetch(ch + 1);
 
-        // ---- 5. skip, gate, store of one output tile: lane writes p = 16j + 4g .. +3 of token t
-        auto store_tile = [&](int ti, const f32x4 (&yacc)[4]) __attribute__((always_inline)) {
+        // ---- 5. skip, gate, store of one output tile: lane writes rows
+        // p = 16j + 4g .. +3 (of this workgroup's PT) of token t
+        auto store_tile = [&](int ti, const f32x4 (&yacc)[JP]) __attribute__((always_inline)) {
             const int tl = 16 * ti + c;
             const int64_t t = tc + tl;
             if (t >= L) return;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < JP; ++j) {
                 const int p0 = 16 * j + 4 * g;
-                const int64_t o = ((b * L + t) * H + h) * kP + p0;
+                const int64_t o = ((b * L + t) * H + h) * P + pbase + p0;
                 float yv[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) yv[r] = yacc[j][r];
@@ -385,14 +399,14 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
         for (int k = 0; k < TPW; ++k) {
             const int ti = TL::tile(w, k);
             if (ti < 0) continue;
-            f32x4 yacc[4];
+            f32x4 yacc[JP];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) yacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int j = 0; j < JP; ++j) yacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             // Y_off^T = S C^T, scaled per column by exp(cum_t)
 #pragma unroll
             for (int kk = 0; kk < KN; ++kk)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < JP; ++j) {
                     const bf16x8 hop = *reinterpret_cast<const bf16x8*>(
                         &sm.H[(16 * j + c) * Lds::kHStride + 32 * kk + 8 * g]);
                     yacc[j] = mfma(hop, cop[k][kk], yacc[j]);
@@ -401,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
             const float cum_t = sm.cum[tl];
             const float eoff = fast_exp2(cum_t);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) yacc[j] *= eoff;
+            for (int j = 0; j < JP; ++j) yacc[j] *= eoff;
             auto diag_blocks = [&](auto wide_tag) __attribute__((always_inline)) {
             constexpr bool kWide = decltype(wide_tag)::value;
             // Y_diag^T over the causal s-blocks of 32 tokens
@@ -450,7 +464,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
                     }
                 }
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < JP; ++j) {
                     const __bf16* xr = &sm.Xt[(16 * j + c) * Lds::kXStride + Lds::xcol(16 * j + c, 32 * sb + 4 * g)];
                     const bf16x4 lo = *reinterpret_cast<const bf16x4*>(xr);
                     const bf16x4 hi = *reinterpret_cast<const bf16x4*>(xr + 16);
@@ -510,16 +524,16 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
         };
         auto out_pair = [&]() __attribute__((always_inline)) {
             const int t0 = w, t1 = TL::T - 1 - w;
-            f32x4 y0[4], y1[4];
+            f32x4 y0[JP], y1[JP];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < JP; ++j) {
                 y0[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
                 y1[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             }
 #pragma unroll
             for (int kk = 0; kk < KN; ++kk)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < JP; ++j) {
                     const bf16x8 hop = *reinterpret_cast<const bf16x8*>(
                         &sm.H[(16 * j + c) * Lds::kHStride + 32 * kk + 8 * g]);
                     y0[j] = mfma(hop, cop[0][kk], y0[j]);
@@ -528,7 +542,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
             const float cum0 = sm.cum[16 * t0 + c], cum1 = sm.cum[16 * t1 + c];
             const float e0 = fast_exp2(cum0), e1 = fast_exp2(cum1);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < JP; ++j) {
                 y0[j] *= e0;
                 y1[j] *= e1;
             }
@@ -563,7 +577,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
                     const bf16x8 m0 = make_mop(s0, sb, t0, cum0, wide_tag);
                     const bf16x8 m1 = make_mop(s1, sb, t1, cum1, wide_tag);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
+                    for (int j = 0; j < JP; ++j) {
                         const bf16x8 xop = xop_at(j, sb);
                         y0[j] = mfma(xop, m0, y0[j]);
                         y1[j] = mfma(xop, m1, y1[j]);
@@ -575,7 +589,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
                     scores(sb, 1, s1);
                     const bf16x8 m1 = make_mop(s1, sb, t1, cum1, wide_tag);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) y1[j] = mfma(xop_at(j, sb), m1, y1[j]);
+                    for (int j = 0; j < JP; ++j) y1[j] = mfma(xop_at(j, sb), m1, y1[j]);
                 }
                 store_tile(t1, y1);
             };
@@ -594,7 +608,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
         if (ntile >= 0) {
             const float decay = fast_exp2(cumQ);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) hacc[j] *= decay;
+            for (int j = 0; j < JP; ++j) hacc[j] *= decay;
             // B operand B[s][n = 16 ntile + c] for 8 consecutive s through two
             // transposed reads; as supplier this lane addresses row 8g + c/4 (+4),
             // columns 16 ntile + 4 (c % 4) .. +3
@@ -616,7 +630,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
                     bcol[4 + e] = bf(f32(braw[4 + e]) * w1[e]);
                 }
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < JP; ++j) {
                     const bf16x8 xa = *reinterpret_cast<const bf16x8*>(
                         &sm.Xt[(16 * j + c) * Lds::kXStride + Lds::xcol(16 * j + c, s8)]);
                     hacc[j] = mfma(xa, bcol, hacc[j]);
@@ -626,7 +640,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
         lds_barrier();                                   // all reads of the old state copy done
         if (ntile >= 0) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < JP; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     sm.H[(16 * j + 4 * g + r) * Lds::kHStride + 16 * ntile + c] = bf(hacc[j][r]);
@@ -635,21 +649,29 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
     }
     if (p.h_last && ntile >= 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < JP; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                p.h_last[(bh * kP + 16 * j + 4 * g + r) * N + 16 * ntile + c] = hacc[j][r];
+                p.h_last[(bh * P + pbase + 16 * j + 4 * g + r) * N + 16 * ntile + c] = hacc[j][r];
     }
 }
 
+template <int Q, int N, int PT>
+hipError_t launch_qnp(const SSDArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)(a.B * a.H * (a.P / PT)));
+    if (a.z)
+        hipLaunchKernelGGL((ssd_chunk_kernel<Q, N, PT, true>), grid, dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((ssd_chunk_kernel<Q, N, PT, false>), grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+// P tile: 64 head-dim rows per workgroup where P allows, else 32
 template <int Q, int N>
 hipError_t launch_qn(const SSDArgs& a, hipStream_t stream) {
-    const dim3 grid((unsigned)(a.B * a.H));
-    if (a.z)
-        hipLaunchKernelGGL((ssd_chunk_kernel<Q, N, true>), grid, dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL((ssd_chunk_kernel<Q, N, false>), grid, dim3(kThreads), 0, stream, a);
-    return hipGetLastError();
+    if (a.P % 64 == 0) return launch_qnp<Q, N, 64>(a, stream);
+    if (a.P % 32 == 0) return launch_qnp<Q, N, 32>(a, stream);
+    return hipErrorNotSupported;
 }
 
 template <int N>
@@ -665,10 +687,13 @@ hipError_t launch_n(const SSDArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_ssd(const SSDArgs& a, hipStream_t stream) {
-    if (a.P != kP) return hipErrorNotSupported;
-    if (a.N == 128) return launch_n<128>(a, stream);
-    if (a.N == 64) return launch_n<64>(a, stream);
-    return hipErrorNotSupported;
+    switch (a.N) {
+        case 32: return launch_n<32>(a, stream);
+        case 64: return launch_n<64>(a, stream);
+        case 96: return launch_n<96>(a, stream);
+        case 128: return launch_n<128>(a, stream);
+        default: return hipErrorNotSupported;
+    }
 }
 
 }  // namespace ssm

@@ -51,9 +51,11 @@ int ssd_check_sizes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64
     if (H % G != 0) return SSM_ERR_BAD_SHAPE;
     if (mul3(B, L, H) < 0 || mul3(B * H, L, P) < 0 || mul3(B * G, L, N) < 0) return SSM_ERR_BAD_SHAPE;
     if (mul3(B * H, L, P) > kMaxElems / esize(dtype)) return SSM_ERR_BAD_SHAPE;
-    if (dtype != SSM_BF16 || P != 64 || (N != 64 && N != 128)) return SSM_ERR_UNSUPPORTED;
+    if (dtype != SSM_BF16 || P % 32 != 0 || N % 32 != 0 || N > 128) return SSM_ERR_UNSUPPORTED;
     if (chunk != 64 && chunk != 128 && chunk != 256) return SSM_ERR_UNSUPPORTED;
-    if (B * H > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;
+    // one workgroup per (b, h, slice of 64 head-dim rows, or 32 when P is not a multiple of 64)
+    const int64_t slices = P % 64 == 0 ? P / 64 : P / 32;
+    if (B * H > 0x7fffffffLL / slices) return SSM_ERR_UNSUPPORTED;
     // one batch row of X (and of B/C) is addressed with 32-bit byte offsets,
     // including the reads past a ragged last chunk and the prefetch of the
     // chunk after the last (up to two chunks of 256 past L)

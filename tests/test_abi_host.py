@@ -163,10 +163,22 @@ def test_ssd_validation_errors(lib):
     assert ssd(lib, dtype=5) == 3
     assert ssd(lib, chunk=100) == 4
     assert ssd(lib, P=48) == 4
+    assert ssd(lib, P=16) == 4
+    assert ssd(lib, N=48) == 4
+    assert ssd(lib, N=160) == 4
+    assert ssd(lib, N=16) == 4
     assert ssd(lib, dtype=0) == 4
     assert ssd(lib, flags=2) == 4
     assert ssd(lib, Y=FAKE_MIS) == 5
     assert lib.ssm_ssd_chunk_workspace_bytes(4, 8192, 64, 64, 1, 128, 256, 1) == 0
+
+
+def test_ssd_grid_limit(lib):
+    # one workgroup per (b, h, slice of 64 head-dim rows; 32 when P % 64 != 0):
+    # the count must stay below 2^31
+    # (row offsets stay small here, so only the grid count can refuse these)
+    assert ssd(lib, Bt=2**20, L=0, H=2**10, P=128) == 4
+    assert ssd(lib, Bt=2**20, L=0, H=700, P=96) == 4
 
 
 def test_ssd_offset_limit(lib):

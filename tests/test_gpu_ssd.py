@@ -99,13 +99,13 @@ def test_empty_sequence_copies_h0():
     assert Y.shape == (2, 0, 3, 64) and torch.equal(h, h0)
 
 
-def _exact_case(L, mode, seed, H=3, N=128, G=1):
+def _exact_case(L, mode, seed, H=3, N=128, G=1, P=64):
     """Integer inputs, softplus off, dt = 1.  mode 'ones': A = 0 (every decay 1,
     the mask is causal all-ones); 'eye': A = -1e4 (every decay underflows to 0,
     the mask is the identity).  Sparse X and C keep every partial sum a small
     integer, exact in bf16 and fp32."""
     g = torch.Generator().manual_seed(seed)
-    Bt, P = 2, 64
+    Bt = 2
     X = torch.randint(-1, 2, (Bt, L, H, P), generator=g).float()
     X = X * (torch.rand(Bt, L, H, 1, generator=g) < 3.0 / max(L, 3)).float()
     Bm = (torch.rand(Bt, L, G, N, generator=g) < 0.5).float()
@@ -184,13 +184,13 @@ def _block_decay_log2(inp, chunk):
     return np.abs(rel).max(axis=(2, 3))              # [B, nch, H]
 
 
-def _spiked_case(L, H, N, chunk, seed):
+def _spiked_case(L, H, N, chunk, seed, P=64):
     """Random X, B and C; steps softplus(N(-2, 0.5) + bias) with strong decays
     |A_h| in [2, 5]; in about one 32-token block in twelve, 40% of the tokens
     have their raw step raised to +2.5 (a write/flush spike), so those blocks
     decay by far more than 2^64 while the others stay well below.  Skip, gate,
     bias and h0 are on."""
-    w = W.SSD_MAMBA2.scaled(B=2, L=L, H=H, N=N, chunk=chunk)
+    w = W.SSD_MAMBA2.scaled(B=2, L=L, H=H, N=N, P=P, chunk=chunk)
     inp = _with_extras(W.make_ssd_inputs(w, seed=seed), seed)
     rng = np.random.default_rng(seed + 1000)
     raw = inp["delta"].float().numpy().copy()
@@ -217,3 +217,50 @@ def test_wide_block_decay(chunk, N):
     assert np.any(span <= 64.0), "every chunk is wide"
     ey, eh = _cmp(inp, chunk=chunk)
     print(f"wide chunks {np.mean(span > 64.0):.2f}; Y err {ey:.2e}, h_last err {eh:.2e}")
+
+
+@pytest.mark.parametrize("P", [32, 96, 128])
+@pytest.mark.parametrize("chunk", [64, 256])
+def test_head_dims(P, chunk):
+    """Head dimensions other than 64: P = 32 (one 32-row slice per head), 96
+    (three 32-row slices) and 128 (two 64-row slices), ragged L, with skip,
+    gate, bias and h0 (whose rows each slice reads at its own offset)."""
+    w = W.SSD_MAMBA2.scaled(B=2, L=419, H=3, P=P, chunk=chunk)
+    _cmp(_with_extras(W.make_ssd_inputs(w, seed=P + chunk), P), chunk=chunk)
+
+
+@pytest.mark.parametrize("N", [32, 96])
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_state_dims(N, chunk):
+    """State sizes 32 and 96 (one and three 32-wide k steps of the score and
+    Y_off products; two and six wavefronts own state columns)."""
+    w = W.SSD_MAMBA2.scaled(B=2, L=517, H=3, N=N, chunk=chunk)
+    _cmp(_with_extras(W.make_ssd_inputs(w, seed=N + chunk), N), chunk=chunk)
+
+
+@pytest.mark.parametrize("P,N", [(32, 32), (128, 96), (96, 128)])
+def test_head_and_state_dims_groups(P, N):
+    """Mixed sizes with two groups of heads (each group's B and C rows)."""
+    w = W.SSD_MAMBA2.scaled(B=2, L=300, H=4, G=2, P=P, N=N, chunk=128)
+    _cmp(_with_extras(W.make_ssd_inputs(w, seed=P * N), 3), chunk=128)
+
+
+@pytest.mark.parametrize("P,N,chunk", [(128, 128, 64), (32, 96, 256)])
+def test_wide_block_decay_sizes(P, N, chunk):
+    """The per-element mask of strongly decaying blocks at other head and state
+    sizes, with h0 rows read per slice."""
+    inp = _spiked_case(L=700, H=3, N=N, chunk=chunk, seed=P + N + chunk, P=P)
+    span = _block_decay_log2(inp, chunk)
+    assert np.any(span > 64.0) and np.any(span <= 64.0)
+    _cmp(inp, chunk=chunk)
+
+
+@pytest.mark.parametrize("P", [32, 128])
+def test_bit_exact_masks_head_dims(P):
+    """The exact integer cases at other head dimensions (every slice's rows)."""
+    for mode in ("ones", "eye"):
+        inp = _exact_case(257, mode, seed=P, P=P)
+        Y, h = ssd_gpu(inp, chunk=64)
+        Yr, hr = ssd_oracle(inp)
+        np.testing.assert_array_equal(Y.float().cpu().numpy(), Yr)
+        np.testing.assert_array_equal(h.cpu().numpy(), hr)
