@@ -45,6 +45,8 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kChans = 4 * kWaves;     // channels per workgroup
 constexpr int kTile = 16;              // tokens per tile = per checkpoint
+static_assert(kTile == plan::kBwdTile && kChans == plan::kBwdChans,
+              "the host workspace layout's tiling constants");
 
 struct LaneId {
     int w, l, row, n;
@@ -620,30 +622,6 @@ hipError_t launch_t(const S6BwdArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
-
-size_t s6_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N) {
-    const int64_t nblk = (L + kTile - 1) / kTile;
-    const int64_t G = (D + kChans - 1) / kChans;
-    auto al = [](int64_t bytes) { return (bytes + 255) / 256 * 256; };
-    return (size_t)(al(B * D * nblk * N * 4) + al(2 * G * B * L * N * 4) + al(B * D * N * 4) +
-                    2 * al(B * D * 4));
-}
-
-void s6_bwd_carve(S6BwdArgs& a, void* ws) {
-    const int64_t nblk = (a.L + kTile - 1) / kTile;
-    const int64_t G = (a.D + kChans - 1) / kChans;
-    auto al = [](int64_t bytes) { return (bytes + 255) / 256 * 256; };
-    char* p = static_cast<char*>(ws);
-    a.ckpt = reinterpret_cast<float*>(p);
-    p += al(a.B * a.D * nblk * a.N * 4);
-    a.part_bc = reinterpret_cast<float*>(p);
-    p += al(2 * G * a.B * a.L * a.N * 4);
-    a.part_dA = reinterpret_cast<float*>(p);
-    p += al(a.B * a.D * a.N * 4);
-    a.part_dD = reinterpret_cast<float*>(p);
-    p += al(a.B * a.D * 4);
-    a.part_db = reinterpret_cast<float*>(p);
-}
 
 hipError_t launch_s6_bwd(const S6BwdArgs& a, hipStream_t stream) {
     return a.bf16 ? launch_t<uint16_t>(a, stream) : launch_t<float>(a, stream);

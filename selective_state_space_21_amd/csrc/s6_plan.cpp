@@ -1,0 +1,109 @@
+// Host-side planning of the library's calls: the S6 segment plan (which
+// kernel, how many sequence segments, the workspace they need) and the layout
+// of the backward call's workspace.  Plain host code: pure functions of the
+// sizes (and two environment overrides), no HIP call, so the C-ABI layer can
+// run them while validating its arguments.
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "ssm_internal.h"
+
+namespace ssm {
+
+using namespace plan;
+
+S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N) {
+    S6Plan pl{};
+    pl.S = 1;
+    pl.seg_len = L > 0 ? L : 1;
+    pl.S_lanes = 1;
+    pl.seg_len_lanes = pl.seg_len;
+    if (L <= 0) return pl;
+    const char* env_seg = getenv("SSM_S6_SEGMENTS");
+    const int64_t forced = (env_seg && atoi(env_seg) > 0) ? atoi(env_seg) : 0;
+    // State-per-lane kernel: N = 16, D a multiple of 16 and a batch row's
+    // activations (plus two super-tiles) within 32-bit buffer offsets at 4
+    // bytes per element.  SSM_S6_LANES=0 turns it off.  It runs B*D/4
+    // wavefronts per segment: unsplit with at least two per SIMD, else cut
+    // into the fewest segments (whole 128-token multiples) that give four per
+    // SIMD (the segmented kernel stages half as much and fits four); the
+    // segments after the first are fixed up afterwards.
+    {
+        const bool shape_ok = N == 16 && D % kLanesChans == 0 &&
+                              (L + 2 * kLanesSpan) * D * 4 <= (int64_t)0xFFFFFFFF;
+        pl.lanes = shape_ok;
+        const char* env = getenv("SSM_S6_LANES");
+        if (env && env[0] == '0') pl.lanes = false;
+        const int64_t waves = B * D / 4;
+        int64_t S = waves >= 2 * kSimds ? 1 : (4 * kSimds + waves - 1) / (waves > 0 ? waves : 1);
+        if (forced) S = forced;
+        int64_t maxS = (L + kLanesSpan - 1) / kLanesSpan;
+        if (maxS > kMaxSegments) maxS = kMaxSegments;
+        if (S > maxS) S = maxS;
+        if (S < 1) S = 1;
+        int64_t seg_len = (L + S - 1) / S;
+        seg_len = (seg_len + kLanesSpan - 1) / kLanesSpan * kLanesSpan;
+        pl.S_lanes = (int)((L + seg_len - 1) / seg_len);
+        pl.seg_len_lanes = seg_len;
+    }
+    // Split path (one lane per channel; ZOH calls, other N, or the
+    // state-per-lane kernel turned off).  With at least one wavefront per SIMD
+    // the sequence is not split; otherwise the segment count is the smallest
+    // that gives every SIMD at least three wavefronts and all SIMDs the same
+    // number (a whole multiple of the SIMD count), else the one nearest three
+    // per SIMD.
+    const int64_t waves = B * ((D + kWave - 1) / kWave);
+    const int64_t simds = kSimds;
+    const int64_t min_seg = 32;
+    int64_t maxS = (L + min_seg - 1) / min_seg;
+    if (maxS > kMaxSegments) maxS = kMaxSegments;
+    int64_t S = waves >= simds ? 1 : 0;
+    for (int64_t c = 1; c <= maxS && S == 0; ++c)
+        if (waves * c >= 3 * simds && (waves * c) % simds == 0) S = c;
+    if (S == 0) S = (3 * simds + waves - 1) / waves;
+    if (forced) S = forced;
+    if (S > maxS) S = maxS;
+    if (S < 1) S = 1;
+    int64_t seg_len = (L + S - 1) / S;
+    // the kernels address one segment through 32-bit buffer offsets
+    while (seg_len * D * 4 > (int64_t)0xFFFFFFFF && S < kMaxSegments) {
+        ++S;
+        seg_len = (L + S - 1) / S;
+    }
+    S = (L + seg_len - 1) / seg_len;   // no empty trailing segment
+    pl.S = (int)S;
+    pl.seg_len = seg_len;
+    // one workspace serves both paths: (decay, offset) pairs per segment
+    int64_t S_ws = 0;
+    if (pl.S > 1) S_ws = pl.S;
+    if (pl.lanes && pl.S_lanes > S_ws) S_ws = pl.S_lanes;
+    if (S_ws > 1) pl.workspace_bytes = (size_t)2 * (size_t)(B * D * S_ws * N) * sizeof(float);
+    return pl;
+}
+
+
+size_t s6_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N) {
+    const int64_t nblk = (L + kBwdTile - 1) / kBwdTile;
+    const int64_t G = (D + kBwdChans - 1) / kBwdChans;
+    auto al = [](int64_t bytes) { return (bytes + 255) / 256 * 256; };
+    return (size_t)(al(B * D * nblk * N * 4) + al(2 * G * B * L * N * 4) + al(B * D * N * 4) +
+                    2 * al(B * D * 4));
+}
+
+void s6_bwd_carve(S6BwdArgs& a, void* ws) {
+    const int64_t nblk = (a.L + kBwdTile - 1) / kBwdTile;
+    const int64_t G = (a.D + kBwdChans - 1) / kBwdChans;
+    auto al = [](int64_t bytes) { return (bytes + 255) / 256 * 256; };
+    char* p = static_cast<char*>(ws);
+    a.ckpt = reinterpret_cast<float*>(p);
+    p += al(a.B * a.D * nblk * a.N * 4);
+    a.part_bc = reinterpret_cast<float*>(p);
+    p += al(2 * G * a.B * a.L * a.N * 4);
+    a.part_dA = reinterpret_cast<float*>(p);
+    p += al(a.B * a.D * a.N * 4);
+    a.part_dD = reinterpret_cast<float*>(p);
+    p += al(a.B * a.D * 4);
+    a.part_db = reinterpret_cast<float*>(p);
+}
+
+}  // namespace ssm

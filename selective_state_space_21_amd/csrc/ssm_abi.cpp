@@ -39,6 +39,8 @@ int s6_check_sizes(int64_t B, int64_t L, int64_t D, int64_t N, int dtype) {
     if (mul3(B, L, D) > kMaxElems / esize(dtype)) return SSM_ERR_BAD_SHAPE;
     if (N > 64) return SSM_ERR_UNSUPPORTED;
     if (B > 65535) return SSM_ERR_UNSUPPORTED;                 // grid y
+    // state copies (L = 0) and conv-state copies run B*D*N (or B*D*3) threads
+    if ((B * D * N * 4 + 255) / 256 > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;
     if ((D + 63) / 64 > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;
     if (((L + 63) / 64) * D * 4 > (int64_t)0xFFFFFFFF) return SSM_ERR_UNSUPPORTED;  // 32-bit segment offsets
     return SSM_OK;
@@ -49,7 +51,10 @@ int ssd_check_sizes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64
     if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_BAD_DTYPE;
     if (B < 1 || H < 1 || P < 1 || G < 1 || N < 1 || L < 0 || chunk < 1) return SSM_ERR_BAD_SHAPE;
     if (H % G != 0) return SSM_ERR_BAD_SHAPE;
+    // bound the products B*H*P and B*G*N first, then every tensor's element count
+    if (mul3(B, H, P) < 0 || mul3(B, G, N) < 0) return SSM_ERR_BAD_SHAPE;
     if (mul3(B, L, H) < 0 || mul3(B * H, L, P) < 0 || mul3(B * G, L, N) < 0) return SSM_ERR_BAD_SHAPE;
+    if (mul3(B * H, P, N) < 0) return SSM_ERR_BAD_SHAPE;          // h0, h_last
     if (mul3(B * H, L, P) > kMaxElems / esize(dtype)) return SSM_ERR_BAD_SHAPE;
     if (dtype != SSM_BF16 || P % 32 != 0 || N % 32 != 0 || N > 128) return SSM_ERR_UNSUPPORTED;
     if (chunk != 64 && chunk != 128 && chunk != 256) return SSM_ERR_UNSUPPORTED;
@@ -59,7 +64,7 @@ int ssd_check_sizes(int64_t B, int64_t L, int64_t H, int64_t P, int64_t G, int64
     // one batch row of X (and of B/C) is addressed with 32-bit byte offsets,
     // including the reads past a ragged last chunk and the prefetch of the
     // chunk after the last (up to two chunks of 256 past L)
-    if ((L + 512) * H * P * 2 > (int64_t)0xFFFFFFFF || (L + 512) * G * N * 2 > (int64_t)0xFFFFFFFF)
+    if (H * P * 2 > (int64_t)0xFFFFFFFF / (L + 512) || G * N * 2 > (int64_t)0xFFFFFFFF / (L + 512))
         return SSM_ERR_UNSUPPORTED;
     return SSM_OK;
 }
@@ -368,7 +373,10 @@ int ssm_causal_conv1d_silu(const void* x, const float* weight, const float* bias
     if (B < 1 || D < 1 || L < 0 || K < 1) return SSM_ERR_BAD_SHAPE;
     if (mul3(B, L, D) < 0 || mul3(B, L, D) > kMaxElems / esize(dtype)) return SSM_ERR_BAD_SHAPE;
     if (K > 4) return SSM_ERR_UNSUPPORTED;
-    if (D * B * ((L + 31) / 32) / 256 > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;   // grid x
+    if (mul3(B, D, K) < 0) return SSM_ERR_BAD_SHAPE;                // states [B, D, K-1]
+    if ((B * D * K + 255) / 256 > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;   // state-pass grid
+    const int64_t tiles = mul3(B, D, (L + 31) / 32);
+    if (tiles < 0 || tiles / 256 > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;  // grid x
     if (!weight) return SSM_ERR_NULL_ARG;
     if (L > 0 && (!x || !u)) return SSM_ERR_NULL_ARG;
     const void* big[] = {x, u};

@@ -52,7 +52,23 @@ struct S6Plan {
 };
 
 // Deterministic in the sizes (plus the SSM_S6_SEGMENTS / SSM_S6_LANES overrides).
+// Host code only (s6_plan.cpp): no HIP call.
 S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N);
+
+// Tiling the planners share with the kernels (the kernel sources assert that
+// their own constants agree).
+namespace plan {
+constexpr int kWave = 64;                 // lanes per wavefront
+constexpr int64_t kMaxSegments = 256;     // sequence segments per call at most
+constexpr int kLanesSpan = 128;           // state-per-lane segments: whole multiples of this
+constexpr int kLanesChans = 16;           // state-per-lane kernel: channels per workgroup
+constexpr int kBwdTile = 16;              // backward: tokens per state checkpoint
+constexpr int kBwdChans = 16;             // backward: channels per workgroup
+// SIMDs the S6 planner balances wavefronts over: MI355X has 256 CUs of four
+// SIMDs.  A constant, so that the plan (and the workspace size it implies) is
+// a pure function of the sizes and no HIP call is needed before validation.
+constexpr int64_t kSimds = 4 * 256;
+}  // namespace plan
 
 hipError_t launch_s6(const S6Args& a, hipStream_t stream);
 
