@@ -43,12 +43,15 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 
 // log1p(e) for e in [0, 1]: with w = 1 + e rounded to fp32, the rounding
 // error c = e - (w - 1) is exact (Fast2Sum), and log1p(e) = log(w) + c / w to
-// first order in c.  v_log_f32 gives log2(w) to about one ulp, so the result
-// keeps full relative precision even for tiny e (then w = 1, c = e).
+// first order in c.  The correction is taken as c rather than c / w: |c| is at
+// most half an ulp of w, so the difference, c e / w, stays below 2^-25 e,
+// about a quarter ulp of the result (which is at least e / 2).  v_log_f32
+// gives log2(w) to about one ulp, so the result keeps full relative precision
+// even for tiny e (then w = 1, c = e).
 __device__ __forceinline__ float log1p_unit(float e) {
     const float w = 1.0f + e;
     const float c = e - (w - 1.0f);
-    return fmaf(fast_log2(w), kLn2, c * fast_rcp(w));
+    return fmaf(fast_log2(w), kLn2, c);
 }
 
 // log(1 + e^x) = max(x, 0) + log1p(e^-|x|).

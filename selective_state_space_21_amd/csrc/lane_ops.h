@@ -55,20 +55,12 @@ __device__ __forceinline__ float dpp_mov(float x) {
         0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
 }
 
-// Reduce-scatter over the 16 lanes of each row: v[i] is this lane's term for
-// token i; the result in lane j is the row's sum over all lanes for token j.
-// Four halving exchanges, each between lanes that differ in one bit of j:
-// lane j keeps the half of its tokens whose index bit equals its own bit and
-// adds the partner's copy of that half.  Partners: j ^ 8 (DPP row_ror:8),
-// j ^ 7 (row_half_mirror, which flips bit 2 and keeps bit 3), j ^ 2 and j ^ 1
-// (quad permutes).  In the first two exchanges the kept half is fixed per
-// group of four lanes (a DPP "bank"), so each result is two bank-masked DPP
-// adds (lanes of disabled banks are not written) instead of two selects and
-// an add.  DPP reads a VGPR two wait states after a VALU write at the
-// earliest: the blocks open with s_nop 1 for their inputs and the second ends
-// with one for its outputs, which the compiler does not see being written.
-__device__ __forceinline__ float row_reduce_scatter16(const float (&v)[16], int j) {
-    float a[8], c[4], e[2];
+// The first halving exchange of row_reduce_scatter16 below, on its own: lane
+// j < 8 ends with a[k] = v[k] + (v[k] of lane j + 8), the partial sum of token
+// k; lane j >= 8 with a[k] = v[k + 8] + (v[k + 8] of lane j - 8), token k + 8.
+// Two bank-masked DPP adds per result; the block opens with s_nop 1 because
+// DPP reads its inputs two wait states after a VALU write at the earliest.
+__device__ __forceinline__ void row_fold_halves16(const float (&v)[16], float (&a)[8]) {
     asm("s_nop 1\n\t"
         "v_add_f32_dpp %0, %8, %8 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
         "v_add_f32_dpp %0, %16, %16 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
@@ -91,6 +83,23 @@ __device__ __forceinline__ float row_reduce_scatter16(const float (&v)[16], int 
         : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]),
           "v"(v[8]), "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]),
           "v"(v[15]));
+}
+
+// Reduce-scatter over the 16 lanes of each row: v[i] is this lane's term for
+// token i; the result in lane j is the row's sum over all lanes for token j.
+// Four halving exchanges, each between lanes that differ in one bit of j:
+// lane j keeps the half of its tokens whose index bit equals its own bit and
+// adds the partner's copy of that half.  Partners: j ^ 8 (DPP row_ror:8),
+// j ^ 7 (row_half_mirror, which flips bit 2 and keeps bit 3), j ^ 2 and j ^ 1
+// (quad permutes).  In the first two exchanges the kept half is fixed per
+// group of four lanes (a DPP "bank"), so each result is two bank-masked DPP
+// adds (lanes of disabled banks are not written) instead of two selects and
+// an add.  DPP reads a VGPR two wait states after a VALU write at the
+// earliest: the blocks open with s_nop 1 for their inputs and the second ends
+// with one for its outputs, which the compiler does not see being written.
+__device__ __forceinline__ float row_reduce_scatter16(const float (&v)[16], int j) {
+    float a[8], c[4], e[2];
+    row_fold_halves16(v, a);
     asm("s_nop 1\n\t"
         "v_add_f32_dpp %0, %4, %4 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
         "v_add_f32_dpp %0, %8, %8 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
@@ -108,6 +117,15 @@ __device__ __forceinline__ float row_reduce_scatter16(const float (&v)[16], int 
     for (int i = 0; i < 2; ++i)
         e[i] = (b1 ? c[i + 2] : c[i]) + dpp_mov<0x4E>(b1 ? c[i] : c[i + 2]);   // quad xor 2
     return (b0 ? e[1] : e[0]) + dpp_mov<0xB1>(b0 ? e[0] : e[1]);               // quad xor 1
+}
+
+// Compiler-level ordering of one wavefront's LDS accesses at a point: LDS
+// performs a wavefront's accesses in issue order, so lanes of the wavefront
+// read what other lanes of it wrote before the fence with no wait.
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // Workgroup barrier that first waits for this wavefront's own LDS accesses.

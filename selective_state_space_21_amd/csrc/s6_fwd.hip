@@ -482,11 +482,23 @@ void s6_fast(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
 // kept in fp32 in a double-buffered LDS halo.
 namespace lanes {
 constexpr int kTile = 16;                 // tokens per tile (one per lane of a row)
-constexpr int kSuper = 8;                 // tiles per super-tile, one pass over the sequence
-constexpr int kSuperSeg = 4;              // tiles per super-tile, segments (half the LDS)
-constexpr int kSpan = kTile * kSuper;     // segments are whole multiples of this
+constexpr int kSpan = 128;                // segments are whole multiples of this many tokens
 constexpr int kChans = 16;                // channels per workgroup
 constexpr int kPitch = kTile + 4;         // staged B/C row of one state (floats)
+// Tiles per super-tile: 64-token super-tiles keep the LDS of a workgroup small
+// enough for four to share a CU.
+constexpr int kSuper = 4;
+// Readout of y: bf16 one-pass calls fold the row's 16 partial products with
+// one DPP exchange and finish through LDS (fewer VALU instructions, measured
+// faster there); the others reduce entirely with DPP (row_reduce_scatter16).
+template <typename T, bool SEG>
+constexpr bool lds_readout() { return sizeof(T) == 2 && !SEG; }
+// Readout buffer of one wavefront: after the first halving exchange each lane
+// holds 8 partial sums (token k + 8 * (lane / 8), states lane % 8 and + 8);
+// the 8 lanes that share a token write them next to each other and the
+// token's lane reads them back.  Token k + 8h, partial j sits at 16k + 8h + j
+// (the 16 lanes' writes of one k hit 16 banks); rows sit 16 banks apart.
+constexpr int kRedRow = 8 * kTile + 16;   // floats per row (channel)
 
 template <typename T> __device__ __forceinline__ uint32_t elem_bits(T v);
 template <> __device__ __forceinline__ uint32_t elem_bits<uint16_t>(uint16_t v) { return v; }
@@ -503,18 +515,19 @@ struct Pieces {
 };
 }  // namespace lanes
 
+static_assert(lanes::kSpan % (lanes::kTile * lanes::kSuper) == 0, "segments are whole super-tiles");
 static_assert(kWave == plan::kWave && kMaxSegments == plan::kMaxSegments &&
                   lanes::kSpan == plan::kLanesSpan && lanes::kChans == plan::kLanesChans,
               "the host planner's tiling constants");
 
-template <typename T, bool HAS_Z, bool SOFTPLUS, bool CONV, int SUP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SUP == lanes::kSuper ? 3 : 4)))
+template <typename T, bool HAS_Z, bool SOFTPLUS, bool CONV, bool SEG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
               const T* __restrict__ z_, const T* __restrict__ Bm_, const T* __restrict__ Cm_,
               T* __restrict__ y_) {
     using namespace lanes;
-    constexpr int kSuper = SUP;               // tiles per super-tile
-    constexpr int kSpan = kTile * SUP;        // tokens per super-tile
+    constexpr int kSpan = kTile * kSuper;                 // tokens per super-tile
+    constexpr bool kLdsReadout = lds_readout<T, SEG>();
     using Raw = Pieces<T, HAS_Z, kSpan>;
     constexpr uint32_t E = sizeof(T);
     constexpr int kPerToken = Raw::kPerToken, kPer = Raw::kPer;
@@ -523,6 +536,7 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
     __shared__ __attribute__((aligned(16))) float bct[2][kSuper][16 * kPitch];
     __shared__ __attribute__((aligned(16))) T act[HAS_Z ? 3 : 2][kSpan][kActPitch];
     __shared__ __attribute__((aligned(16))) T yst[kSpan][kChans];
+    __shared__ __attribute__((aligned(16))) float red[kLdsReadout ? 4 : 1][kLdsReadout ? 4 * kRedRow : 1];
     // CONV: inputs x_{t0-3 .. t0-1} before the super-tile (fp32), by parity;
     // the convolution's output u when the caller asks for it
     __shared__ float xh[CONV ? 2 : 1][kChans][4];
@@ -552,7 +566,7 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
     // the first segment starts from h0, the others from zero (their incoming
     // state is added to y afterwards, by the fix-up pass)
     float h = (s == 0 && p.h0) ? p.h0[(b * D + d) * 16 + n] : 0.0f;
-    float dt_sum = 0.0f;                  // this lane's share of the segment's sum of dt
+    float dt_sum = 0.0f;                  // segments: this lane's share of the segment's sum of dt
     // buffer resources over this row's tokens: loads past the row's end read
     // zero, stores there are dropped (the planner keeps offsets in 32 bits)
     const int64_t rowoff = b * p.L * D;
@@ -666,7 +680,7 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
                 const uint32_t keep = st0 + tl < t1 ? 0xffffffffu : 0u;
                 dt = __uint_as_float(__float_as_uint(dt) & keep);
             }
-            dt_sum += dt;
+            if constexpr (SEG) dt_sum += dt;
             float ut;
             if constexpr (CONV) {
                 // window x_{t-3..t}: the staged row, before the super-tile the halo
@@ -716,7 +730,29 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
                 h = fmaf(dA[j], h, bv[j]);
                 pr[j] = cv[j] * h;
             }
-            float yv = row_reduce_scatter16(pr, n);
+            float yv;
+            if constexpr (kLdsReadout) {
+                // fold the row's two halves of states with DPP, then the
+                // remaining 8 partial sums of each token through this
+                // wavefront's LDS buffer (LDS performs a wavefront's accesses
+                // in order)
+                float a8[8];
+                row_fold_halves16(pr, a8);
+                float* const rb = &red[w][row * kRedRow];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) rb[16 * k + 8 * (n >> 3) + (n & 7)] = a8[k];
+                wave_lds_fence();
+                // token n's block: its first half read first for n % 8 < 4,
+                // else its second, so the row's 16 first reads cover all 64
+                // banks (the sum is the same: the half sums are added last)
+                const int blk = 16 * (n & 7) + 8 * (n >> 3);
+                const int sw = 4 * ((n >> 2) & 1);
+                const f32x4 q0 = *reinterpret_cast<const f32x4*>(&rb[blk + sw]);
+                const f32x4 q1 = *reinterpret_cast<const f32x4*>(&rb[blk + 4 - sw]);
+                yv = ((q0[0] + q0[1]) + (q0[2] + q0[3])) + ((q1[0] + q1[1]) + (q1[2] + q1[3]));
+            } else {
+                yv = row_reduce_scatter16(pr, n);
+            }
             yv = fmaf(dsk, ut, yv);
             if constexpr (HAS_Z) yv *= silu_f(widen<T>(elem_bits<T>(act[2][tl][chan])));
             if constexpr (sizeof(T) == 2) yst[tl][chan] = f32_to_bf16_bits(yv);
@@ -742,7 +778,7 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
     }
     lds_barrier();
     if (nsup > 0) store_y(t0 + (nsup - 1) * kSpan);
-    if (p.S == 1) {
+    if (!SEG) {
         if (p.h_last) p.h_last[(b * D + d) * 16 + n] = h;
     } else {
         // the segment as an affine map of its incoming state: decay
@@ -1212,10 +1248,10 @@ hipError_t launch_lanes(const S6Args& a, hipStream_t stream) {
 #define SSM_LANES(Z_, SP_, CV_)                                                                   \
     do {                                                                                          \
         if (a.S > 1)                                                                              \
-            hipLaunchKernelGGL((s6_lanes<T, Z_, SP_, CV_, lanes::kSuperSeg>), grid, block, 0,     \
+            hipLaunchKernelGGL((s6_lanes<T, Z_, SP_, CV_, true>), grid, block, 0,                 \
                                stream, a, U, Dl, Z, Bp, Cp, Y);                                   \
         else                                                                                      \
-            hipLaunchKernelGGL((s6_lanes<T, Z_, SP_, CV_, lanes::kSuper>), grid, block, 0,        \
+            hipLaunchKernelGGL((s6_lanes<T, Z_, SP_, CV_, false>), grid, block, 0,                \
                                stream, a, U, Dl, Z, Bp, Cp, Y);                                   \
     } while (0)
     if (cv) {
