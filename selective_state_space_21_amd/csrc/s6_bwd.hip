@@ -16,17 +16,18 @@
 //   du_t  = g_t D + dt_t sum_n m_t B_t;  dz_t = dy_t r_t silu'(z_t)
 //   dA   += m_t h_{t-1} dt_t a_t;  dD += g_t u_t;  dbias += ddelta_t;  dh0 = a_0 m_0
 //
-// Mapping: a workgroup of 4 wavefronts covers 16 channels of one batch row;
-// each 16-lane row of a wavefront is one channel and lane n holds state n
-// (N <= 16), so a lane carries one state and one adjoint.  Per-channel,
-// per-token scalars (dt, u, g, ...) of a 16-token tile are computed by lane j
-// for token j and broadcast along the row with DPP.
-//   1. s6_bwd_ckpt: forward sweep storing the state before every tile.
-//   2. s6_bwd_main: tiles in reverse; each tile recomputes its 16 states
-//      from the checkpoint into registers, then runs the adjoint backwards.
-//      Sums over n are row all-reduces (4 DPP adds); dB and dC are summed
-//      over the wavefront's 4 rows (xor swizzles) and the workgroup's 4
-//      wavefronts (LDS), giving one partial per (channel group, b, t, n).
+// Mapping: each 16-lane row of a wavefront is one channel of one batch row
+// and lane n holds state n (N <= 16), so a lane carries one state and one
+// adjoint.  Per-channel, per-token scalars (dt, u, g, ...) of a 16-token tile
+// are computed by lane j for token j and broadcast along the row with DPP.
+//   1. s6_bwd_ckpt (4 wavefronts, 16 channels per workgroup): forward sweep
+//      storing the state before every tile.
+//   2. s6_bwd_main (12 wavefronts, 48 channels per workgroup): tiles in
+//      reverse; each tile recomputes its 16 states from the checkpoint into
+//      registers, then runs the adjoint backwards.  Sums over n are row
+//      all-reduces (4 DPP adds); dB and dC are summed over the wavefront's 4
+//      rows (xor swizzles) and the workgroup's 12 wavefronts (LDS), giving
+//      one partial per (48-channel group, b, t, n).
 //   3. s6_bwd_reduce: sums the channel-group partials of dB and dC and the
 //      batch partials of dA, D and bias.  No atomics: results are
 //      deterministic.
@@ -41,11 +42,18 @@
 namespace ssm {
 namespace {
 
+constexpr int kTile = 16;              // tokens per tile = per checkpoint
+// Checkpoint sweep: 4 wavefronts, 16 channels per workgroup.
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kChans = 4 * kWaves;     // channels per workgroup
-constexpr int kTile = 16;              // tokens per tile = per checkpoint
-static_assert(kTile == plan::kBwdTile && kChans == plan::kBwdChans,
+constexpr int kChans = 4 * kWaves;
+// Adjoint sweep: 12 wavefronts (three per SIMD, its register budget), 48
+// channels per workgroup, so dB and dC are summed over 48 channels before
+// their partials leave the chip (one partial per 48 channels).
+constexpr int kMainWaves = 12;
+constexpr int kMainThreads = 64 * kMainWaves;
+constexpr int kMainChans = 4 * kMainWaves;
+static_assert(kTile == plan::kBwdTile && kMainChans == plan::kBwdChans,
               "the host workspace layout's tiling constants");
 
 struct LaneId {
@@ -54,6 +62,7 @@ struct LaneId {
     bool chan_ok, ok;      // channel exists; channel and state exist
 };
 
+template <int CH>
 __device__ __forceinline__ LaneId lane_id(const S6BwdArgs& p) {
     LaneId id;
     const int tid = threadIdx.x;
@@ -61,17 +70,16 @@ __device__ __forceinline__ LaneId lane_id(const S6BwdArgs& p) {
     id.l = tid % 64;
     id.row = id.l / 16;
     id.n = id.l % 16;
-    // Workgroups are dealt to the 8 XCDs round robin (i -> XCD i % 8).  A
-    // workgroup's 16 channels are a quarter of a 128-byte row of u, delta, z
-    // and dy (bf16), so the id is renumbered to give each XCD a contiguous
-    // range of channel groups: the four that share a row then fetch it into
-    // one L2 instead of four.
+    // Workgroups are dealt to the 8 XCDs round robin (i -> XCD i % 8).  The
+    // id is renumbered to give each XCD a contiguous range of channel groups,
+    // so groups that share 128-byte rows of u, delta, z and dy fetch them
+    // into one L2.
     const uint32_t n = gridDim.x * gridDim.y, i = blockIdx.x + gridDim.x * blockIdx.y;
     const uint32_t x = i % 8, q = n / 8, r = n % 8;
     const uint32_t lid = x * q + min(x, r) + i / 8;
     id.b = lid / gridDim.x;
     id.grp = lid % gridDim.x;
-    id.d = (int64_t)id.grp * kChans + 4 * id.w + id.row;
+    id.d = (int64_t)id.grp * CH + 4 * id.w + id.row;
     id.chan_ok = id.d < p.D;
     id.dc = id.chan_ok ? id.d : p.D - 1;
     id.ok = id.chan_ok && id.n < p.N;
@@ -184,11 +192,12 @@ __device__ __forceinline__ uint32_t piece_off(const S6BwdArgs& p, int64_t grp, i
                                : (uint32_t)((t * p.D + grp * kChans) * (int64_t)sizeof(T) + 16 * pc);
 }
 
-// Four consecutive channels of one token (8 bytes in bf16, 16 in fp32).
-template <typename T>
+// Four consecutive channels of one token (8 bytes in bf16, 16 in fp32), for a
+// workgroup of CH channels.
+template <typename T, int CH>
 __device__ __forceinline__ uint32_t quad_off(const S6BwdArgs& p, int64_t grp, int64_t t, int q) {
     return (t < 0 || t >= p.L) ? 0xFFFFFFF0u
-                               : (uint32_t)((t * p.D + grp * kChans + 4 * q) * (int64_t)sizeof(T));
+                               : (uint32_t)((t * p.D + grp * CH + 4 * q) * (int64_t)sizeof(T));
 }
 template <typename T> struct Quad;
 template <> struct Quad<uint16_t> {
@@ -236,11 +245,14 @@ __device__ __forceinline__ void tile_row(const float* tile, int n, float (&v)[kT
     }
 }
 
+// Threads past the tile's 256 elements load nothing (an offset past the
+// resource reads zero without a memory access).
 template <typename T>
 __device__ __forceinline__ uint32_t load_bc_bits(const S6BwdArgs& p, int64_t t0,
                                                  __amdgpu_buffer_rsrc_t r) {
     const int j = threadIdx.x / 16, n = threadIdx.x % 16;
-    const uint32_t off = n < p.N ? (uint32_t)(((t0 + j) * p.N + n) * sizeof(T)) : 0x80000000u;
+    const uint32_t off = (n < p.N && j < kTile) ? (uint32_t)(((t0 + j) * p.N + n) * sizeof(T))
+                                                 : 0x80000000u;
     return Bits<T>::load(r, off);
 }
 
@@ -301,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void s6_bwd_ckpt(S6BwdArgs p) {
     constexpr int kSpan = kSuper * kTile;
     __shared__ __attribute__((aligned(16))) float bt[kSuper][16 * kPitch];
     __shared__ __attribute__((aligned(16))) T actc[VEC ? 2 : 1][kChans][kSpan + 8];
-    const LaneId id = lane_id(p);
+    const LaneId id = lane_id<kChans>(p);
     const int cl = 4 * id.w + id.row;                    // channel in the workgroup
     const float a2 = id.ok ? p.A[id.dc * p.N + id.n] * kLog2e : 0.0f;
     const float bias = p.delta_bias ? p.delta_bias[id.dc] : 0.0f;
@@ -366,8 +378,9 @@ __global__ __launch_bounds__(kThreads) void s6_bwd_ckpt(S6BwdArgs p) {
 }
 
 template <typename T, bool HAS_Z, bool SOFTPLUS, bool VEC>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(kMainThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void s6_bwd_main(S6BwdArgs p) {
+    constexpr int kWaves = kMainWaves, kThreads = kMainThreads, kChans = kMainChans;
     __shared__ float red[2][kWaves][kTile][16];     // [dB|dC][wave][token][n]
     // du, ddelta, dz of the tile as stored ([output][token][channel]): written
     // per lane, then stored as 16-byte rows pieces, so that one store covers
@@ -375,11 +388,15 @@ void s6_bwd_main(S6BwdArgs p) {
     constexpr int kOut = HAS_Z ? 3 : 2;
     __shared__ __attribute__((aligned(16))) T outst[kOut][kTile][kChans];
     __shared__ __attribute__((aligned(16))) float bct[2][16 * kPitch];   // B, C: [n][token]
-    // VEC: delta, u, dy (, z) of the tile as [tensor][channel][token]; wave w
-    // loads tensor w: lane l loads channels 4 (l % 4) .. +3 of token l / 4
+    // VEC: delta, u, dy (, z) of the tile as [tensor][channel][token].  Each
+    // tensor's tile is 16 tokens x 12 runs of 4 channels, loaded by three
+    // wavefronts: wave w loads tensor w / 3, lane l the run (64 (w % 3) + l)
+    // % 12 of token (64 (w % 3) + l) / 12
     constexpr int kNT = HAS_Z ? 4 : 3;
+    constexpr int kQuads = kChans / 4;                   // 4-channel runs per token
+    static_assert(kTile * kQuads == 3 * 64, "three wavefronts per tensor");
     __shared__ __attribute__((aligned(16))) T actst[VEC ? kNT : 1][kChans][kTile + 8];
-    const LaneId id = lane_id(p);
+    const LaneId id = lane_id<kChans>(p);
     const int cl = 4 * id.w + id.row;                    // channel in the workgroup
     const float an = id.ok ? p.A[id.dc * p.N + id.n] : 0.0f;
     const float a2 = an * kLog2e;
@@ -403,14 +420,17 @@ void s6_bwd_main(S6BwdArgs p) {
     uint32_t bpre = 0, cpre = 0;
     float hck = 0.0f;
     const int wu = __builtin_amdgcn_readfirstlane(id.w);
-    const __amdgpu_buffer_rsrc_t rs_act = wu == 0 ? rr.delta : wu == 1 ? rr.u : wu == 2 ? rr.dy : rr.z;
-    const bool act_lane = wu < kNT;
+    const int wt = wu / 3;                               // tensor this wavefront loads
+    const __amdgpu_buffer_rsrc_t rs_act = wt == 0 ? rr.delta : wt == 1 ? rr.u : wt == 2 ? rr.dy : rr.z;
+    const bool act_lane = wt < kNT;
+    const int qi = 64 * (wu % 3) + id.l;                 // run index within the tensor's tile
+    const int aq = qi % kQuads, at = qi / kQuads;        // channel run, token
     Quad<T> apre;
     // every lane loads (a wavefront without a tensor at an offset past the
     // resource), so no branch separates the prefetch from the work it overlaps
     auto load_act = [&](int64_t t0) {
-        const int64_t t = act_lane ? t0 + (id.l >> 2) : -1;
-        apre.load(rs_act, quad_off<T>(p, id.grp, t, id.l & 3));
+        const int64_t t = act_lane ? t0 + at : -1;
+        apre.load(rs_act, quad_off<T, kChans>(p, id.grp, t, aq));
     };
     if (nblk > 0) {
         if constexpr (VEC) load_act((nblk - 1) * kTile);
@@ -425,12 +445,14 @@ void s6_bwd_main(S6BwdArgs p) {
         TileScalars<HAS_Z, SOFTPLUS, true> s;
         if constexpr (!VEC) s.template from<T>(raw, p, id, t0, bias);
         lds_barrier();                   // previous tile's LDS reads done
-        bct[0][(threadIdx.x % 16) * kPitch + threadIdx.x / 16] = Bits<T>::f32(bpre);
-        bct[1][(threadIdx.x % 16) * kPitch + threadIdx.x / 16] = Bits<T>::f32(cpre);
+        if (threadIdx.x < kTile * 16) {
+            bct[0][(threadIdx.x % 16) * kPitch + threadIdx.x / 16] = Bits<T>::f32(bpre);
+            bct[1][(threadIdx.x % 16) * kPitch + threadIdx.x / 16] = Bits<T>::f32(cpre);
+        }
         if constexpr (VEC) {
             if (act_lane) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) actst[wu][4 * (id.l & 3) + q][id.l >> 2] = apre.elem(q);
+                for (int q = 0; q < 4; ++q) actst[wt][4 * aq + q][at] = apre.elem(q);
             }
         }
         lds_barrier();
@@ -570,7 +592,7 @@ void s6_bwd_main(S6BwdArgs p) {
 // sums over the batch rows.  One thread per output element.
 __global__ __launch_bounds__(256) void s6_bwd_reduce(S6BwdArgs p) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t G = (p.D + kChans - 1) / kChans;
+    const int64_t G = (p.D + kMainChans - 1) / kMainChans;
     const int64_t nbc = p.B * p.L * p.N;
     if (i < 2 * nbc) {
         const int64_t q = i / nbc, e = i % nbc;
@@ -604,11 +626,12 @@ void launch_sweeps(const S6BwdArgs& a, hipStream_t stream) {
     const bool sp = (a.flags & SSM_FLAG_DELTA_SOFTPLUS) != 0;
     if (sp) s6_bwd_ckpt<T, true, VEC><<<grid, kThreads, 0, stream>>>(a);
     else s6_bwd_ckpt<T, false, VEC><<<grid, kThreads, 0, stream>>>(a);
+    const dim3 mgrid((unsigned)((a.D + kMainChans - 1) / kMainChans), (unsigned)a.B);
     const bool hz = a.z != nullptr;
-    if (hz && sp) s6_bwd_main<T, true, true, VEC><<<grid, kThreads, 0, stream>>>(a);
-    else if (hz) s6_bwd_main<T, true, false, VEC><<<grid, kThreads, 0, stream>>>(a);
-    else if (sp) s6_bwd_main<T, false, true, VEC><<<grid, kThreads, 0, stream>>>(a);
-    else s6_bwd_main<T, false, false, VEC><<<grid, kThreads, 0, stream>>>(a);
+    if (hz && sp) s6_bwd_main<T, true, true, VEC><<<mgrid, kMainThreads, 0, stream>>>(a);
+    else if (hz) s6_bwd_main<T, true, false, VEC><<<mgrid, kMainThreads, 0, stream>>>(a);
+    else if (sp) s6_bwd_main<T, false, true, VEC><<<mgrid, kMainThreads, 0, stream>>>(a);
+    else s6_bwd_main<T, false, false, VEC><<<mgrid, kMainThreads, 0, stream>>>(a);
 }
 
 template <typename T>

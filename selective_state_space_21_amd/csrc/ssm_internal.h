@@ -63,7 +63,7 @@ constexpr int64_t kMaxSegments = 256;     // sequence segments per call at most
 constexpr int kLanesSpan = 128;           // state-per-lane segments: whole multiples of this
 constexpr int kLanesChans = 16;           // state-per-lane kernel: channels per workgroup
 constexpr int kBwdTile = 16;              // backward: tokens per state checkpoint
-constexpr int kBwdChans = 16;             // backward: channels per workgroup
+constexpr int kBwdChans = 48;             // backward: channels per adjoint-sweep workgroup
 // SIMDs the S6 planner balances wavefronts over: MI355X has 256 CUs of four
 // SIMDs.  A constant, so that the plan (and the workspace size it implies) is
 // a pure function of the sizes and no HIP call is needed before validation.
