@@ -2,13 +2,13 @@
 against the fp64 oracle (reverse-mode differentiation of the per-token
 definition), through the C ABI.
 
-Bar: normwise max relative error per gradient.  fp32 storage: 1e-4 -- the
-gradients are sums over up to B*L*N products accumulated in fp32 along the
-adjoint recurrence, about an order of magnitude more terms than the forward
-readout, so the forward's 1e-5 is scaled by that factor.  bf16 storage: 2e-2
-for the bf16 outputs (du, ddelta, dz), 1e-4 for the fp32 ones (dA, dB, dC,
-dD, ddelta_bias, dh0), whose inputs are the exact bf16 values.  Integer
-cases (A = 0, dt = 1) are compared bit for bit."""
+Bar: normwise max relative error per gradient.  Every fp32 gradient (all
+gradients of fp32 calls; dA, dB, dC, dD, ddelta_bias and dh0 of bf16 calls,
+whose inputs are the exact bf16 values) meets the forward's fp32 bar, 1e-5:
+the adjoint runs the same fp32 recurrences as the forward, and the largest
+error measured over these cases is 7.4e-7, so a regression by an order of
+magnitude or more fails.  bf16 outputs (du, ddelta, dz): 2e-2.  Integer cases
+(A = 0, dt = 1) are compared bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -22,6 +22,7 @@ from _parity import normwise_err, to_dev
 pytestmark = pytest.mark.gpu
 
 FP32_OUT = ("dA", "dB", "dC", "dD", "ddelta_bias", "dh0")
+FP32_TOL = 1e-5
 
 
 def _case(Bt, L, Dm, N, dtype, seed, skip=True, gate=True, bias=True, h0=True, dh=True,
@@ -61,7 +62,7 @@ def _ref(inp):
 def _check(got, ref, dtype, label=""):
     assert set(got) == set(ref), (set(got), set(ref))
     for k in ref:
-        tol = 1e-4 if (k in FP32_OUT or dtype == "f32") else 2e-2
+        tol = FP32_TOL if (k in FP32_OUT or dtype == "f32") else 2e-2
         e = normwise_err(got[k].numpy(), ref[k].numpy())
         assert e <= tol, f"{label} {k}: err {e:.3e} > {tol}"
 
@@ -137,7 +138,7 @@ def test_bwd_full_size_sampled():
     one = {k: (v[:1] if isinstance(v, torch.Tensor) and v.dim() == 3 else v) for k, v in inp.items()}
     ref = _ref(one)
     for k in ("du", "ddelta", "dz", "dB", "dC"):
-        tol = 1e-4 if k in FP32_OUT else 2e-2
+        tol = FP32_TOL if k in FP32_OUT else 2e-2
         e = normwise_err(got[k][:1].numpy(), ref[k].numpy())
         print(f"{k}: err {e:.3e}")
         assert e <= tol, k
@@ -145,4 +146,4 @@ def test_bwd_full_size_sampled():
     for k in ("dA", "dD", "ddelta_bias"):
         e = normwise_err(got1[k].numpy(), ref[k].numpy())
         print(f"{k} (B=1): err {e:.3e}")
-        assert e <= 1e-4, k
+        assert e <= FP32_TOL, k
