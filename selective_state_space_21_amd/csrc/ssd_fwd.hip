@@ -81,8 +81,8 @@ struct SsdLds {
     alignas(16) float dt[Q];                      // step per token
     alignas(16) float cum[Q];                     // inclusive sum of dt*A*log2(e)
     alignas(16) float fblk[Q];                    // exp(cum_{32 floor(s/32)} - cum_s) * dt_s
-    alignas(16) float part[kWaves];               // per-wavefront scan totals
-    alignas(16) int wide[kWaves];                 // per-wavefront: a 32-token block spans > 2^64
+    alignas(16) float part[Q / 64];               // scan totals of the wavefronts holding tokens
+    alignas(16) int wide[Q / 64];                 // per such wavefront: a 32-token block spans > 2^64
     alignas(16) __bf16 B[Q * kBStride];           // B rows of the chunk
     alignas(16) __bf16 Xt[PT * kXStride];         // X^T of the chunk (this workgroup's rows)
     alignas(16) float wst[Q];                     // exp(cum_Q - cum_s) dt_s: token s's weight in the final state
@@ -99,6 +99,10 @@ struct Tiles {
     static constexpr int JP = PT / 16;                         // head-dim row tiles
     static constexpr int BPIECES = Q * N / 8;                  // 16-B pieces of a chunk's B rows
     static constexpr int BPIECE = (BPIECES + kThreads - 1) / kThreads;   // per thread
+    // state update: wavefront w owns state column tile w % NTILE and JW of
+    // the JP head-dim row tiles (group w / NTILE); waves past NTILE * WPN idle
+    static constexpr int WPN = (kWaves / NTILE < JP) ? kWaves / NTILE : JP;   // wavefronts per column tile
+    static constexpr int JW = JP / WPN;
     static constexpr int XGROUP = (Q / 4) * (PT / 8);          // (4 tokens x 8 p) groups
     static constexpr int XPIECE = 4;                           // 16-B rows per group
     // B pieces fetched ahead of the output tiles; the rest after them.  At the
@@ -151,7 +155,7 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p) {
 template <int Q, int N, int PT, bool HAS_Z>
 __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
     using TL = Tiles<Q, N, PT>;
-    constexpr int TPW = TL::TPW, KN = TL::KN, KQ = TL::KQ, JP = TL::JP;
+    constexpr int TPW = TL::TPW, KN = TL::KN, KQ = TL::KQ, JP = TL::JP, JW = TL::JW;
     using Lds = SsdLds<Q, N, PT>;
     __shared__ Lds sm;
     auto stage_xt = [](__bf16* xt, int sg, int p8, const uint32_t (&xs)[4][4]) {
@@ -196,16 +200,19 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
     const float bias = p.delta_bias ? p.delta_bias[h] : 0.0f;
     const float dsk = p.Dskip ? p.Dskip[h] : 0.0f;
     const bool softplus = (p.flags & SSM_FLAG_DELTA_SOFTPLUS) != 0;
-    const int ntile = w < TL::NTILE ? w : -1;      // this wavefront's state columns
+    // this wavefront's state columns (-1: none) and first head-dim row tile
+    const int ntile = w < TL::NTILE * TL::WPN ? (TL::WPN == 1 ? w : w % TL::NTILE) : -1;
+    const int jbase = TL::WPN == 1 ? 0 : (w / TL::NTILE) * JW;
 
-    // ---- state: hacc[j] = S[p = pbase + 16j + 4g + r][n = 16 * ntile + c]
-    f32x4 hacc[JP];
+    // ---- state: hacc[jj] = S[p = pbase + 16 (jbase + jj) + 4g + r][n = 16 * ntile + c]
+    f32x4 hacc[JW];
 #pragma unroll
-    for (int j = 0; j < JP; ++j)
+    for (int jj = 0; jj < JW; ++jj)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            hacc[j][r] = (p.h0 && ntile >= 0)
-                             ? p.h0[(bh * P + pbase + 16 * j + 4 * g + r) * N + 16 * ntile + c] : 0.0f;
+            hacc[jj][r] = (p.h0 && ntile >= 0)
+                              ? p.h0[(bh * P + pbase + 16 * (jbase + jj) + 4 * g + r) * N + 16 * ntile + c]
+                              : 0.0f;
     for (int i = tid; i < PT * N; i += kThreads) {
         const int pp = i / N, nn = i % N;
         sm.H[pp * Lds::kHStride + nn] = bf(p.h0 ? p.h0[(bh * P + pbase + pp) * N + nn] : 0.0f);
@@ -293,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
             const float o = __shfl_up(v, off, 64);
             if (l >= off) v += o;
         }
-        if (l == 63) sm.part[w] = v;
+        if (l == 63 && w < Q / 64) sm.part[w] = v;
         // ---- 2. stage B rows and X^T; C rows to the operand registers
 #pragma unroll
         for (int k = 0; k < TL::BPIECE; ++k) {
@@ -313,11 +320,9 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
         }
         lds_barrier();
         {
-            const f32x4 p0 = *reinterpret_cast<const f32x4*>(&sm.part[0]);
-            const f32x4 p1 = *reinterpret_cast<const f32x4*>(&sm.part[4]);
             float base = 0.0f;
 #pragma unroll
-            for (int k = 0; k < kWaves; ++k) base += k < w ? (k < 4 ? p0[k] : p1[k - 4]) : 0.0f;
+            for (int k = 0; k < Q / 64 - 1; ++k) base += k < w ? sm.part[k] : 0.0f;
             if (tid < Q) {
                 sm.dt[tid] = dtv;
                 sm.cum[tid] = base + v;
@@ -334,14 +339,11 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
         }
         if (tid < Q) sm.wst[tid] = fast_exp2(cumQ - sm.cum[tid]) * sm.dt[tid];
         far = __any(far);
-        if (l == 0) sm.wide[w] = far;
+        if (l == 0 && w < Q / 64) sm.wide[w] = far;
         lds_barrier();
-        bool wide;
-        {
-            const int4 f0 = *reinterpret_cast<const int4*>(&sm.wide[0]);
-            const int4 f1 = *reinterpret_cast<const int4*>(&sm.wide[4]);
-            wide = (f0.x | f0.y | f0.z | f0.w | f1.x | f1.y | f1.z | f1.w) != 0;
-        }
+        bool wide = false;
+#pragma unroll
+        for (int k = 0; k < Q / 64; ++k) wide |= sm.wide[k] != 0;
 
         // The C rows are waited for here, before the next chunk's inputs are
         // requested: loads complete in order, so a wait for them after the
@@ -604,11 +606,11 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
             prefetch_b(ch + 1, std::integral_constant<int, TL::BEARLY>{},
                        std::integral_constant<int, TL::BPIECE>{});
 
-        // ---- 4. state update on this wavefront's 16 columns
+        // ---- 4. state update on this wavefront's 16 columns, JW row tiles
         if (ntile >= 0) {
             const float decay = fast_exp2(cumQ);
 #pragma unroll
-            for (int j = 0; j < JP; ++j) hacc[j] *= decay;
+            for (int jj = 0; jj < JW; ++jj) hacc[jj] *= decay;
             // B operand B[s][n = 16 ntile + c] for 8 consecutive s through two
             // transposed reads; as supplier this lane addresses row 8g + c/4 (+4),
             // columns 16 ntile + 4 (c % 4) .. +3
@@ -630,29 +632,31 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
                     bcol[4 + e] = bf(f32(braw[4 + e]) * w1[e]);
                 }
 #pragma unroll
-                for (int j = 0; j < JP; ++j) {
+                for (int jj = 0; jj < JW; ++jj) {
+                    const int j = jbase + jj;
                     const bf16x8 xa = *reinterpret_cast<const bf16x8*>(
                         &sm.Xt[(16 * j + c) * Lds::kXStride + Lds::xcol(16 * j + c, s8)]);
-                    hacc[j] = mfma(xa, bcol, hacc[j]);
+                    hacc[jj] = mfma(xa, bcol, hacc[jj]);
                 }
             }
         }
         lds_barrier();                                   // all reads of the old state copy done
         if (ntile >= 0) {
 #pragma unroll
-            for (int j = 0; j < JP; ++j)
+            for (int jj = 0; jj < JW; ++jj)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    sm.H[(16 * j + 4 * g + r) * Lds::kHStride + 16 * ntile + c] = bf(hacc[j][r]);
+                    sm.H[(16 * (jbase + jj) + 4 * g + r) * Lds::kHStride + 16 * ntile + c] = bf(hacc[jj][r]);
         }
 
     }
     if (p.h_last && ntile >= 0) {
 #pragma unroll
-        for (int j = 0; j < JP; ++j)
+        for (int jj = 0; jj < JW; ++jj)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                p.h_last[(bh * P + pbase + 16 * j + 4 * g + r) * N + 16 * ntile + c] = hacc[j][r];
+                p.h_last[(bh * P + pbase + 16 * (jbase + jj) + 4 * g + r) * N + 16 * ntile + c] =
+                    hacc[jj][r];
     }
 }
 
