@@ -52,16 +52,18 @@ CSRC = os.path.join(ROOT, "selective_state_space_21_amd", "csrc")
 
 HBM_PEAK_GBS = 8000.0           # MI355X published HBM3E bandwidth
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
-# MI355X published fp32 vector peak: 256 CUs x 2.4 GHz x 256 flop/clk.  On
-# gfx950 this is the rate of plain (non-packed) v_fma_f32: the issue-rate probe
-# runs only v_fmaak_f32 and reaches 52.25 T lane-FMA/s (66% of 78.6 T), above
-# what 64 lanes per CU per clock would allow (profiles/issue_rates_gfx950.md).
+# MI355X published fp32 vector peak: 256 CUs x 2.4 GHz x 256 flop/clk, i.e. a
+# wave64 FMA every 2 cycles per SIMD.  Plain (non-packed) v_fma_f32 is priced
+# against it: instruction counters on the issue-rate probe show one
+# non-packed FMA per lane and instruction retiring at 24.6 lanes per
+# SIMD-cycle, above the 16 a 78.6 TFLOP/s reading would allow
+# (profiles/issue_rates_gfx950.md).
 FP32_VECTOR_PEAK_TFLOPS = 157.3
 # The bare per-element pattern of the scan (dt*A, exp2, dt*u*B, state FMA,
 # readout FMA) measured on its own at 8 waves per SIMD: the rate a scan kernel
 # cannot exceed while it evaluates one v_exp_f32 per state update
 # (profiles/issue_rates_gfx950.md).
-ISSUE_PEAK_ELEMS_PER_S = 6.41e12
+ISSUE_PEAK_ELEMS_PER_S = 6.52e12
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per
 # dispatch), scaled by what the same counters read for a 256 MiB copy (fetch
@@ -70,6 +72,10 @@ ISSUE_PEAK_ELEMS_PER_S = 6.41e12
 # reports traffic null until its counters are taken again.
 COUNTER_TRAFFIC = {
     # kernel@workload: (bytes, sources, sha1 of the sources)
+    "s6_lanes@s6_mamba130m_layer_bf16": (205368162, ['s6_fwd.hip', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "21dbdf92d8db"),
+    "s6_lanes@s6_mamba2.8b_layer_bf16": (686899070, ['s6_fwd.hip', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "21dbdf92d8db"),
+    "s6_lanes@s6_long_fp32": (3536628854, ['s6_fwd.hip', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "21dbdf92d8db"),
+    "ssd@ssd_mamba2_bf16": (597920238, ['ssd_fwd.hip', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "65164f749a40"),
 }
 KERNEL_SOURCES = {
     "s6": ["s6_fwd.hip", "device_math.h", "lane_ops.h", "ssm_internal.h"],
