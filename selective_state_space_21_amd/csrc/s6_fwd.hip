@@ -1001,27 +1001,38 @@ __global__ __launch_bounds__(256) void s6_fixup(S6Args p, const T* __restrict__ 
     __shared__ __attribute__((aligned(16))) float sz[HAS_Z ? kBlock : 1][kW];
     __shared__ __attribute__((aligned(16))) float sy[kBlock][kW];
     __shared__ __attribute__((aligned(16))) float sc[kBlock][kW];    // C rows [token][state]
+    __shared__ int sdone[2][4];                                      // per wavefront, by block parity
     const int tid = threadIdx.x;
     const int j = tid & 15;                      // token within a 16-token tile
     const int c = tid >> 4;                      // channel within the group
-    const int64_t b = blockIdx.y;
-    const int s = (int)blockIdx.z + 1;
+    // Workgroups are dealt to the 8 XCDs round robin (i -> XCD i % 8): the id
+    // is renumbered so each XCD runs a contiguous range of channel groups, and
+    // the groups that share 128-byte rows of delta, y and z share one L2
+    // (dealt round robin, each fetched whole rows for its half: twice the bytes).
+    const uint32_t gx = gridDim.x, gy = gridDim.y;
+    const uint32_t total = gx * gy * gridDim.z;
+    const uint32_t bi = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+    const uint32_t xcd = bi % 8, per = total / 8, extra = total % 8;
+    const uint32_t lid = xcd * per + min(xcd, extra) + bi / 8;
+    const int64_t grp = lid % gx;
+    const int64_t b = (lid / gx) % gy;
+    const int s = (int)(lid / (gx * gy)) + 1;
     const int64_t D = p.D;
-    const int64_t grp = blockIdx.x;
     const int64_t d = grp * kChans + c;
     const int64_t Lb = row_len(p, b);
     const int64_t t0 = (int64_t)s * p.seg_len;
     const int64_t t1 = t0 + p.seg_len < Lb ? t0 + p.seg_len : Lb;
     if (t0 >= t1) return;
     float a2[16], hin[16];
-    float a2max = -INFINITY;
+    float gmax[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // per group of four states
     const int64_t hb = (int64_t)s * (p.B * D * 16) + (b * D + d) * 16;
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
         a2[n] = p.A[d * 16 + n] * kLog2e;
         hin[n] = p.seg_b[hb + n];
-        a2max = fmaxf(a2max, a2[n]);
+        gmax[n / 4] = fmaxf(gmax[n / 4], a2[n]);
     }
+    const float a2max = fmaxf(fmaxf(gmax[0], gmax[1]), fmaxf(gmax[2], gmax[3]));
     const float bias = p.delta_bias ? p.delta_bias[d] : 0.0f;
     // buffer resources over the row's tokens (32-bit offsets as in the scan)
     const int64_t rowoff = b * p.L * D;
@@ -1049,17 +1060,26 @@ __global__ __launch_bounds__(256) void s6_fixup(S6Args p, const T* __restrict__ 
     };
     float carry = 0.0f;                          // cum at the previous tile's last token
     uint32_t live = 0xf;                         // groups of four states still contributing
-    for (int64_t tt = t0; tt < t1; tt += kBlock) {
-        // stage the block: one 16-byte piece of each tensor per loader thread
+    // one 16-byte piece of each tensor per loader thread, a block ahead: the
+    // next block's loads are issued before this block's y stores, so the
+    // wait for them (loads and stores complete in order) waits for no store
+    u32x4 nd{}, ny{}, nz{}, nc{};
+    auto load_block = [&](int64_t tb) {
         if (loader) {
-            const uint32_t soff = (uint32_t)tt * row_bytes;
+            const uint32_t soff = (uint32_t)tb * row_bytes;
             const uint32_t voff = (uint32_t)pt * row_bytes + grp_bytes + 16 * pc;
-            const u32x4 vd = __builtin_amdgcn_raw_buffer_load_b128(rd, (int)voff, (int)soff, 0);
-            const u32x4 vy = __builtin_amdgcn_raw_buffer_load_b128(ry, (int)voff, (int)soff, 0);
-            u32x4 vz{};
-            if constexpr (HAS_Z) vz = __builtin_amdgcn_raw_buffer_load_b128(rz, (int)voff, (int)soff, 0);
-            const u32x4 vc = __builtin_amdgcn_raw_buffer_load_b128(
-                rC, (int)((uint32_t)pt * 16 * E + 16 * pc), (int)((uint32_t)tt * 16 * E), 0);
+            nd = __builtin_amdgcn_raw_buffer_load_b128(rd, (int)voff, (int)soff, 0);
+            ny = __builtin_amdgcn_raw_buffer_load_b128(ry, (int)voff, (int)soff, 0);
+            if constexpr (HAS_Z) nz = __builtin_amdgcn_raw_buffer_load_b128(rz, (int)voff, (int)soff, 0);
+            nc = __builtin_amdgcn_raw_buffer_load_b128(
+                rC, (int)((uint32_t)pt * 16 * E + 16 * pc), (int)((uint32_t)tb * 16 * E), 0);
+        }
+    };
+    load_block(t0);
+    for (int64_t tt = t0; tt < t1; tt += kBlock) {
+        // stage the block
+        if (loader) {
+            const u32x4 vd = nd, vy = ny, vz = nz, vc = nc;
             float f[kVals];
             widen4(vd, f);
 #pragma unroll
@@ -1076,16 +1096,18 @@ __global__ __launch_bounds__(256) void s6_fixup(S6Args p, const T* __restrict__ 
 #pragma unroll
             for (int e = 0; e < kVals; ++e) sc[pt][kVals * pc + e] = f[e];
         }
+        // the next block travels while this one is computed (past the row's
+        // end the loads read zero; within it, tokens past the segment are
+        // read and not used)
+        load_block(tt + kBlock);
         lds_barrier();
         if constexpr (SOFTPLUS) {
+            // a group is spent once the decay of its slowest state is exactly
+            // 0 (exp2 is monotone, so the others' are too) in every channel
             uint32_t m = 0;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                bool any = false;
-#pragma unroll
-                for (int n = 4 * g; n < 4 * g + 4; ++n) any |= fast_exp2(a2[n] * carry) != 0.0f;
-                if (__any(any)) m |= 1u << g;
-            }
+            for (int g = 0; g < 4; ++g)
+                if (__any(fast_exp2(gmax[g] * carry) != 0.0f)) m |= 1u << g;
             live &= __builtin_amdgcn_readfirstlane(m);
         }
         constexpr int kT = kBlock / 16;
@@ -1144,11 +1166,18 @@ __global__ __launch_bounds__(256) void s6_fixup(S6Args p, const T* __restrict__ 
             __builtin_amdgcn_raw_buffer_store_b128(v, ry, (int)((uint32_t)pt * row_bytes + grp_bytes + 16 * pc),
                                                    (int)((uint32_t)tt * row_bytes), 0);
         }
+        // The next block's staging waits for these reads.  The barriers wait
+        // for LDS only: a workgroup barrier with a memory fence would also
+        // wait for the y stores and the next block's loads.
         if constexpr (SOFTPLUS) {
             // exact stop: exp(A * cum) is 0 for every state from here on
-            if (__syncthreads_and(fast_exp2(a2max * carry) == 0.0f)) break;
+            const int par = (int)(((tt - t0) / kBlock) & 1);
+            const bool spent = __all(fast_exp2(a2max * carry) == 0.0f);
+            if ((tid & 63) == 0) sdone[par][tid >> 6] = spent;
+            lds_barrier();
+            if (sdone[par][0] && sdone[par][1] && sdone[par][2] && sdone[par][3]) break;
         } else {
-            __syncthreads();                     // the staging of the next block waits for these reads
+            lds_barrier();
         }
     }
 }
