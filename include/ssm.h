@@ -95,15 +95,19 @@ const char* ssm_status_string(int status);
  *     (decay, end state) pairs are folded in segment order into each
  *     segment's incoming state and h_last, and a third launch adds to y the
  *     part of the incoming state that survives to each token,
- *     exp(A * cumsum dt) * h_in, stopping once that is exactly zero in fp32
- *     (with softplus, where dt >= 0).  No exponential is evaluated twice
- *     except in that fix-up's reach.
+ *     exp(A * cumsum dt) * h_in, in parallel over 1024-token chunks that
+ *     start from the running sums of dt the scan stored, each stopping once
+ *     that part is exactly zero in fp32 (with softplus, where dt >= 0).  No
+ *     exponential is evaluated twice except in that fix-up's reach.  (Shapes
+ *     whose fix-up would need 2^24 workgroups or more take the split path.)
  *   - split: one lane per channel (other N, ZOH, D not a multiple of 16, or
  *     the state-per-lane kernel turned off); long sequences are split into
  *     short segments whose (decay, offset) pairs are carried the same way,
  *     then every segment is rescanned from its incoming state.
- * The workspace holds the segment pairs; the query returns the larger of the
- * two paths' needs (it takes no flags, and ZOH calls take the split path).
+ * The workspace holds the segment pairs, and on the state-per-lane path one
+ * fp32 sum of dt per (segment, 1024-token chunk, batch row, channel); the
+ * query returns the larger of the two paths' needs (it takes no flags, and
+ * ZOH calls take the split path).
  * The plan (path, segment count, workspace size) is a pure function of the
  * sizes: it balances wavefronts over the 1024 SIMDs of an MI355X and makes no
  * HIP call.

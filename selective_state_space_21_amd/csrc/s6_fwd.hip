@@ -519,6 +519,8 @@ static_assert(lanes::kSpan % (lanes::kTile * lanes::kSuper) == 0, "segments are 
 static_assert(kWave == plan::kWave && kMaxSegments == plan::kMaxSegments &&
                   lanes::kSpan == plan::kLanesSpan && lanes::kChans == plan::kLanesChans,
               "the host planner's tiling constants");
+static_assert(plan::kFixChunk % (lanes::kTile * lanes::kSuper) == 0,
+              "fix-up chunks are whole super-tiles of the segmented scan");
 
 template <typename T, bool HAS_Z, bool SOFTPLUS, bool CONV, bool SEG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
@@ -775,6 +777,20 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
         load(nxt, st0 + kSpan);             // travels while this super-tile is computed
         if (st0 + kSpan <= t1) tiles(st0, sg, std::false_type{});
         else tiles(st0, sg, std::true_type{});
+        if constexpr (SEG) {
+            // where the fix-up's chunks start: the segment's sum of dt up to
+            // the end of each whole chunk (the row's 16 shares added up)
+            constexpr int64_t kSupChunk = plan::kFixChunk / kSpan;
+            if (s > 0 && (sg + 1) % kSupChunk == 0) {
+                float cum = dt_sum;
+                cum += dpp_mov<0x128>(cum);            // row_ror:8
+                cum += dpp_mov<0x124>(cum);            // row_ror:4
+                cum += dpp_mov<0x122>(cum);            // row_ror:2
+                cum += dpp_mov<0x121>(cum);            // row_ror:1
+                if (n == 0)
+                    p.seg_cum[(((int64_t)s * p.fix_chunks + (sg + 1) / kSupChunk - 1) * p.B + b) * D + d] = cum;
+            }
+        }
     }
     lds_barrier();
     if (nsup > 0) store_y(t0 + (nsup - 1) * kSpan);
@@ -969,14 +985,18 @@ __global__ __launch_bounds__(256) void s6_carry_lanes(const float* __restrict__ 
 // the sum of dt over the segment up to and including t (each token multiplies
 // the state by exp(dt * A)).  So
 //   y_t += silu(z_t) * sum_n C_t[n] * exp(A[d,n] * cum_t) * h_in[n].
-// The correction of a token needs only cum_t, so the tokens are handled in
-// parallel (a prefix sum of dt gives cum).  With softplus every dt >= 0, so
-// cum never decreases; once exp(A * cum) is exactly 0 in fp32 for every
-// state of every channel of the workgroup (A <= 0), every later correction is
-// exactly zero and the walk stops there; a state whose decay is already 0 is
-// skipped before that.  Without softplus it runs to the segment's end.
-// Workgroup: 16 channels (D a multiple of 16); it walks the segment in blocks
-// of 64 tokens.  Each block's delta, z, y and C rows are loaded as 16-byte
+// The correction of a token needs only cum_t, so the tokens are independent
+// given a running sum of dt: the segment is cut into chunks of kFixChunk
+// tokens, one workgroup each, which start from the sum up to the chunk's
+// start that the scan stored (seg_cum) and extend it over the chunk.  With
+// softplus every dt >= 0, so cum never decreases within a chunk; once
+// exp(A * cum) is exactly 0 in fp32 for every state of every channel of the
+// workgroup (A <= 0), every later correction of the chunk is exactly zero and
+// the walk stops there (a chunk that starts there returns before loading
+// anything); a state whose decay is already 0 is skipped before that.
+// Without softplus every chunk runs to its end.
+// Workgroup: 16 channels (D a multiple of 16); it walks its chunk in blocks of
+// 64 tokens.  Each block's delta, z, y and C rows are loaded as 16-byte
 // pieces of the group's 16-channel run (one memory round trip per block),
 // staged in LDS and read per (channel, token): lane j of 16-lane row c handles
 // token 16k + j of the block for channel c.  The new y leaves through LDS as
@@ -985,6 +1005,7 @@ namespace fixup {
 constexpr int kBlock = 64;                 // tokens per block
 constexpr int kPad = 4;                    // LDS row padding (floats)
 }  // namespace fixup
+static_assert(plan::kFixChunk % fixup::kBlock == 0, "fix-up chunks are whole blocks");
 
 template <typename T, bool HAS_Z, bool SOFTPLUS>
 __global__ __launch_bounds__(256) void s6_fixup(S6Args p, const T* __restrict__ delta_,
@@ -995,44 +1016,74 @@ __global__ __launch_bounds__(256) void s6_fixup(S6Args p, const T* __restrict__ 
     constexpr uint32_t E = sizeof(T);
     constexpr int kPerTok = kChans * (int)E / 16;     // 16-byte pieces per token (2 bf16, 4 fp32)
     constexpr int kPieces = kBlock * kPerTok;         // per tensor and block
+    constexpr int kPer = (kPieces + 255) / 256;       // per thread
+    static_assert(kPieces % 256 == 0 || kPer == 1, "whole pieces per thread");
     constexpr int kVals = 16 / (int)E;
     constexpr int kW = kChans + kPad;
+    constexpr uint32_t kLine = 128 / (kChans * E);    // channel groups per 128-byte row (2 fp32, 4 bf16)
     __shared__ __attribute__((aligned(16))) float sd[kBlock][kW];    // dt (raw), then y
     __shared__ __attribute__((aligned(16))) float sz[HAS_Z ? kBlock : 1][kW];
     __shared__ __attribute__((aligned(16))) float sy[kBlock][kW];
     __shared__ __attribute__((aligned(16))) float sc[kBlock][kW];    // C rows [token][state]
-    __shared__ int sdone[2][4];                                      // per wavefront, by block parity
+    __shared__ int sdone[3][4];         // exit votes per wavefront: by block parity, and at the start
     const int tid = threadIdx.x;
     const int j = tid & 15;                      // token within a 16-token tile
     const int c = tid >> 4;                      // channel within the group
-    // Workgroups are dealt to the 8 XCDs round robin (i -> XCD i % 8): the id
-    // is renumbered so each XCD runs a contiguous range of channel groups, and
-    // the groups that share 128-byte rows of delta, y and z share one L2
-    // (dealt round robin, each fetched whole rows for its half: twice the bytes).
-    const uint32_t gx = gridDim.x, gy = gridDim.y;
-    const uint32_t total = gx * gy * gridDim.z;
-    const uint32_t bi = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+    // One workgroup per (channel group, batch row, segment >= 1, chunk), in
+    // the order: group within its 128-byte row fastest, then chunk, segment,
+    // batch row, row of groups.  Workgroups are dealt to the 8 XCDs round
+    // robin (i -> XCD i % 8): the id is renumbered so each XCD runs a
+    // contiguous range of that order, so the groups that share 128-byte rows
+    // of delta, y and z run side by side on one XCD and share its L2, and the
+    // chunks of a segment (the first ones carry the work, later ones stop at
+    // once) are spread evenly.
+    const uint32_t total = gridDim.x;
+    const uint32_t bi = blockIdx.x;
     const uint32_t xcd = bi % 8, per = total / 8, extra = total % 8;
-    const uint32_t lid = xcd * per + min(xcd, extra) + bi / 8;
-    const int64_t grp = lid % gx;
-    const int64_t b = (lid / gx) % gy;
-    const int s = (int)(lid / (gx * gy)) + 1;
+    uint32_t q = xcd * per + min(xcd, extra) + bi / 8;
+    const uint32_t r = q % kLine;
+    q /= kLine;
+    const int64_t k = q % (uint32_t)p.fix_chunks;
+    q /= (uint32_t)p.fix_chunks;
+    const int s = (int)(q % (uint32_t)(p.S - 1)) + 1;
+    q /= (uint32_t)(p.S - 1);
+    const int64_t b = q % (uint32_t)p.B;
+    const int64_t grp = (int64_t)(q / (uint32_t)p.B) * kLine + r;
     const int64_t D = p.D;
+    if (grp * kChans >= D) return;
     const int64_t d = grp * kChans + c;
     const int64_t Lb = row_len(p, b);
-    const int64_t t0 = (int64_t)s * p.seg_len;
-    const int64_t t1 = t0 + p.seg_len < Lb ? t0 + p.seg_len : Lb;
+    const int64_t s0 = (int64_t)s * p.seg_len;
+    const int64_t s1 = s0 + p.seg_len < Lb ? s0 + p.seg_len : Lb;
+    const int64_t t0 = s0 + k * plan::kFixChunk;
+    const int64_t t1 = t0 + plan::kFixChunk < s1 ? t0 + plan::kFixChunk : s1;
     if (t0 >= t1) return;
-    float a2[16], hin[16];
+    float a2[16];
     float gmax[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // per group of four states
-    const int64_t hb = (int64_t)s * (p.B * D * 16) + (b * D + d) * 16;
 #pragma unroll
     for (int n = 0; n < 16; ++n) {
         a2[n] = p.A[d * 16 + n] * kLog2e;
-        hin[n] = p.seg_b[hb + n];
         gmax[n / 4] = fmaxf(gmax[n / 4], a2[n]);
     }
     const float a2max = fmaxf(fmaxf(gmax[0], gmax[1]), fmaxf(gmax[2], gmax[3]));
+    // cum at the last token before the chunk
+    float carry = k == 0 ? 0.0f : p.seg_cum[(((int64_t)s * p.fix_chunks + k - 1) * p.B + b) * D + d];
+    // every wavefront's vote through LDS; the barriers wait for LDS only (a
+    // workgroup barrier with a memory fence would also wait for the y stores
+    // and the next block's loads)
+    auto all_spent = [&](int slot) {
+        const bool spent = __all(fast_exp2(a2max * carry) == 0.0f);
+        if ((tid & 63) == 0) sdone[slot][tid >> 6] = spent;
+        lds_barrier();
+        return sdone[slot][0] && sdone[slot][1] && sdone[slot][2] && sdone[slot][3];
+    };
+    if constexpr (SOFTPLUS) {
+        if (all_spent(2)) return;
+    }
+    float hin[16];
+    const int64_t hb = (int64_t)s * (p.B * D * 16) + (b * D + d) * 16;
+#pragma unroll
+    for (int n = 0; n < 16; ++n) hin[n] = p.seg_b[hb + n];
     const float bias = p.delta_bias ? p.delta_bias[d] : 0.0f;
     // buffer resources over the row's tokens (32-bit offsets as in the scan)
     const int64_t rowoff = b * p.L * D;
@@ -1043,9 +1094,10 @@ __global__ __launch_bounds__(256) void s6_fixup(S6Args p, const T* __restrict__ 
     const auto rC = make_rsrc(Cm_ + b * p.L * 16, (uint32_t)(Lb * 16 * E));
     const uint32_t row_bytes = (uint32_t)(D * E);
     const uint32_t grp_bytes = (uint32_t)(grp * kChans * E);
-    // piece of this thread (threads >= kPieces idle in the staging)
-    const int pt = tid / kPerTok, pc = tid % kPerTok;
+    // pieces of this thread: tid + 256 i (threads >= kPieces idle in the staging)
+    const int pc = tid % kPerTok;
     const bool loader = tid < kPieces;
+    auto ptok = [&](int i) { return (tid + 256 * i) / kPerTok; };
     auto widen4 = [&](const u32x4& v, float* out) __attribute__((always_inline)) {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -1058,48 +1110,54 @@ __global__ __launch_bounds__(256) void s6_fixup(S6Args p, const T* __restrict__ 
             }
         }
     };
-    float carry = 0.0f;                          // cum at the previous tile's last token
     uint32_t live = 0xf;                         // groups of four states still contributing
     // one 16-byte piece of each tensor per loader thread, a block ahead: the
     // next block's loads are issued before this block's y stores, so the
     // wait for them (loads and stores complete in order) waits for no store
-    u32x4 nd{}, ny{}, nz{}, nc{};
+    u32x4 nd[kPer], ny[kPer], nz[HAS_Z ? kPer : 1], nc[kPer];
     auto load_block = [&](int64_t tb) {
         if (loader) {
             const uint32_t soff = (uint32_t)tb * row_bytes;
-            const uint32_t voff = (uint32_t)pt * row_bytes + grp_bytes + 16 * pc;
-            nd = __builtin_amdgcn_raw_buffer_load_b128(rd, (int)voff, (int)soff, 0);
-            ny = __builtin_amdgcn_raw_buffer_load_b128(ry, (int)voff, (int)soff, 0);
-            if constexpr (HAS_Z) nz = __builtin_amdgcn_raw_buffer_load_b128(rz, (int)voff, (int)soff, 0);
-            nc = __builtin_amdgcn_raw_buffer_load_b128(
-                rC, (int)((uint32_t)pt * 16 * E + 16 * pc), (int)((uint32_t)tb * 16 * E), 0);
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const uint32_t pt = (uint32_t)ptok(i);
+                const uint32_t voff = pt * row_bytes + grp_bytes + 16 * pc;
+                nd[i] = __builtin_amdgcn_raw_buffer_load_b128(rd, (int)voff, (int)soff, 0);
+                ny[i] = __builtin_amdgcn_raw_buffer_load_b128(ry, (int)voff, (int)soff, 0);
+                if constexpr (HAS_Z) nz[i] = __builtin_amdgcn_raw_buffer_load_b128(rz, (int)voff, (int)soff, 0);
+                nc[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rC, (int)(pt * 16 * E + 16 * pc), (int)((uint32_t)tb * 16 * E), 0);
+            }
         }
     };
     load_block(t0);
     for (int64_t tt = t0; tt < t1; tt += kBlock) {
         // stage the block
         if (loader) {
-            const u32x4 vd = nd, vy = ny, vz = nz, vc = nc;
-            float f[kVals];
-            widen4(vd, f);
 #pragma unroll
-            for (int e = 0; e < kVals; ++e) sd[pt][kVals * pc + e] = f[e];
-            widen4(vy, f);
+            for (int i = 0; i < kPer; ++i) {
+                const int pt = ptok(i);
+                float f[kVals];
+                widen4(nd[i], f);
 #pragma unroll
-            for (int e = 0; e < kVals; ++e) sy[pt][kVals * pc + e] = f[e];
-            if constexpr (HAS_Z) {
-                widen4(vz, f);
+                for (int e = 0; e < kVals; ++e) sd[pt][kVals * pc + e] = f[e];
+                widen4(ny[i], f);
 #pragma unroll
-                for (int e = 0; e < kVals; ++e) sz[pt][kVals * pc + e] = f[e];
+                for (int e = 0; e < kVals; ++e) sy[pt][kVals * pc + e] = f[e];
+                if constexpr (HAS_Z) {
+                    widen4(nz[i], f);
+#pragma unroll
+                    for (int e = 0; e < kVals; ++e) sz[pt][kVals * pc + e] = f[e];
+                }
+                widen4(nc[i], f);
+#pragma unroll
+                for (int e = 0; e < kVals; ++e) sc[pt][kVals * pc + e] = f[e];
             }
-            widen4(vc, f);
-#pragma unroll
-            for (int e = 0; e < kVals; ++e) sc[pt][kVals * pc + e] = f[e];
         }
-        // the next block travels while this one is computed (past the row's
-        // end the loads read zero; within it, tokens past the segment are
-        // read and not used)
-        load_block(tt + kBlock);
+        // the next block of the chunk travels while this one is computed
+        // (past the row's end the loads read zero; tokens past the chunk's
+        // end in its last block are read and not used)
+        if (tt + kBlock < t1) load_block(tt + kBlock);
         lds_barrier();
         if constexpr (SOFTPLUS) {
             // a group is spent once the decay of its slowest state is exactly
@@ -1113,8 +1171,8 @@ __global__ __launch_bounds__(256) void s6_fixup(S6Args p, const T* __restrict__ 
         constexpr int kT = kBlock / 16;
         float cum[kT], corr[kT];
 #pragma unroll
-        for (int k = 0; k < kT; ++k) {
-            const int tl = 16 * k + j;
+        for (int i = 0; i < kT; ++i) {
+            const int tl = 16 * i + j;
             const bool in = tt + tl < t1;
             float x = in ? step_dt(sd[tl][c], bias, SOFTPLUS ? SSM_FLAG_DELTA_SOFTPLUS : 0u) : 0.0f;
             // inclusive prefix sum of dt over the 16 tokens of the row (DPP
@@ -1123,59 +1181,58 @@ __global__ __launch_bounds__(256) void s6_fixup(S6Args p, const T* __restrict__ 
             x += dpp_shr<2>(x);
             x += dpp_shr<4>(x);
             x += dpp_shr<8>(x);
-            cum[k] = x + carry;
-            carry = row_bcast_c<15>(cum[k]);
-            corr[k] = 0.0f;
+            cum[i] = x + carry;
+            carry = row_bcast_c<15>(cum[i]);
+            corr[i] = 0.0f;
         }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             if (live & (1u << g)) {
 #pragma unroll
-                for (int k = 0; k < kT; ++k) {
-                    const f32x4 cq = *reinterpret_cast<const f32x4*>(&sc[16 * k + j][4 * g]);
+                for (int i = 0; i < kT; ++i) {
+                    const f32x4 cq = *reinterpret_cast<const f32x4*>(&sc[16 * i + j][4 * g]);
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        corr[k] = fmaf(cq[r], fast_exp2(a2[4 * g + r] * cum[k]) * hin[4 * g + r], corr[k]);
+                        corr[i] = fmaf(cq[r], fast_exp2(a2[4 * g + r] * cum[i]) * hin[4 * g + r], corr[i]);
                 }
             }
         }
 #pragma unroll
-        for (int k = 0; k < kT; ++k) {
-            const int tl = 16 * k + j;
+        for (int i = 0; i < kT; ++i) {
+            const int tl = 16 * i + j;
             float g = 1.0f;
             if constexpr (HAS_Z) g = silu_f(sz[tl][c]);
-            sy[tl][c] = fmaf(corr[k], g, sy[tl][c]);
+            sy[tl][c] = fmaf(corr[i], g, sy[tl][c]);
         }
         lds_barrier();
-        // the block's y back as 16-byte pieces, none past the segment's end
-        if (loader && tt + pt < t1) {
-            float f[kVals];
+        // the block's y back as 16-byte pieces, none past the chunk's end
 #pragma unroll
-            for (int e = 0; e < kVals; ++e) f[e] = sy[pt][kVals * pc + e];
-            u32x4 v;
-            if constexpr (E == 2) {
-                uint32_t w[4];
+        for (int i = 0; i < kPer; ++i) {
+            const int pt = ptok(i);
+            if (loader && tt + pt < t1) {
+                float f[kVals];
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    w[q] = (uint32_t)f32_to_bf16_bits(f[2 * q]) | ((uint32_t)f32_to_bf16_bits(f[2 * q + 1]) << 16);
-                v = u32x4{w[0], w[1], w[2], w[3]};
-            } else {
-                v = u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
-                          __float_as_uint(f[3])};
+                for (int e = 0; e < kVals; ++e) f[e] = sy[pt][kVals * pc + e];
+                u32x4 v;
+                if constexpr (E == 2) {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        w[q] = (uint32_t)f32_to_bf16_bits(f[2 * q]) | ((uint32_t)f32_to_bf16_bits(f[2 * q + 1]) << 16);
+                    v = u32x4{w[0], w[1], w[2], w[3]};
+                } else {
+                    v = u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                              __float_as_uint(f[3])};
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(v, ry, (int)((uint32_t)pt * row_bytes + grp_bytes + 16 * pc),
+                                                       (int)((uint32_t)tt * row_bytes), 0);
             }
-            __builtin_amdgcn_raw_buffer_store_b128(v, ry, (int)((uint32_t)pt * row_bytes + grp_bytes + 16 * pc),
-                                                   (int)((uint32_t)tt * row_bytes), 0);
         }
-        // The next block's staging waits for these reads.  The barriers wait
-        // for LDS only: a workgroup barrier with a memory fence would also
-        // wait for the y stores and the next block's loads.
+        // the next block's staging waits for these reads
         if constexpr (SOFTPLUS) {
-            // exact stop: exp(A * cum) is 0 for every state from here on
-            const int par = (int)(((tt - t0) / kBlock) & 1);
-            const bool spent = __all(fast_exp2(a2max * carry) == 0.0f);
-            if ((tid & 63) == 0) sdone[par][tid >> 6] = spent;
-            lds_barrier();
-            if (sdone[par][0] && sdone[par][1] && sdone[par][2] && sdone[par][3]) break;
+            // exact stop: exp(A * cum) is 0 for every state from here to the
+            // chunk's end
+            if (all_spent((int)(((tt - t0) / kBlock) & 1))) break;
         } else {
             lds_barrier();
         }
@@ -1207,8 +1264,12 @@ void launch_carry_fixup(const S6Args& a, hipStream_t stream) {
     hipLaunchKernelGGL(s6_carry_lanes, dim3((unsigned)((chains + 255) / 256)), dim3(256), 0,
                        stream, a.seg_a, a.seg_b, a.h_last, chains, (int)a.S);
     mark(a, 2, stream);
-    const dim3 fgrid((unsigned)((a.D + lanes::kChans - 1) / lanes::kChans), (unsigned)a.B,
-                     (unsigned)(a.S - 1));
+    // one workgroup per (channel group, batch row, segment after the first,
+    // chunk), the groups padded to whole 128-byte rows (the planner keeps the
+    // count within 32 bits)
+    const int64_t line = 128 / (lanes::kChans * (int64_t)sizeof(T));
+    const int64_t rows = (a.D / lanes::kChans + line - 1) / line;
+    const dim3 fgrid((unsigned)(rows * line * a.B * (a.S - 1) * a.fix_chunks));
     const T* Dl = static_cast<const T*>(a.delta);
     const T* Z = static_cast<const T*>(a.z);
     const T* Cp = static_cast<const T*>(a.Cm);

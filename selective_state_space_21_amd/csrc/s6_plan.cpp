@@ -45,6 +45,15 @@ S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N) {
         seg_len = (seg_len + kLanesSpan - 1) / kLanesSpan * kLanesSpan;
         pl.S_lanes = (int)((L + seg_len - 1) / seg_len);
         pl.seg_len_lanes = seg_len;
+        // the fix-up runs one 256-thread workgroup per (16 channels, batch
+        // row, later segment, chunk), the groups padded to four per row: a
+        // one-dimensional grid of fewer than 2^24 workgroups (else the split
+        // path takes the call)
+        if (pl.lanes && pl.S_lanes > 1) {
+            const int64_t K = (seg_len + kFixChunk - 1) / kFixChunk;
+            const int64_t rows = (D / kLanesChans + 3) / 4 * 4;
+            if (rows * B * (pl.S_lanes - 1) * K >= ((int64_t)1 << 24)) pl.lanes = false;
+        }
     }
     // Split path (one lane per channel; ZOH calls, other N, or the
     // state-per-lane kernel turned off).  With at least one wavefront per SIMD
@@ -73,12 +82,30 @@ S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N) {
     S = (L + seg_len - 1) / seg_len;   // no empty trailing segment
     pl.S = (int)S;
     pl.seg_len = seg_len;
-    // one workspace serves both paths: (decay, offset) pairs per segment
-    int64_t S_ws = 0;
-    if (pl.S > 1) S_ws = pl.S;
-    if (pl.lanes && pl.S_lanes > S_ws) S_ws = pl.S_lanes;
-    if (S_ws > 1) pl.workspace_bytes = (size_t)2 * (size_t)(B * D * S_ws * N) * sizeof(float);
+    // one workspace serves both paths (the size query has no flags, and ZOH
+    // calls take the split path): (decay, offset) pairs per segment, and on
+    // the state-per-lane path a dt checkpoint per fix-up chunk
+    size_t split = 0, lanes = 0;
+    if (pl.S > 1) split = (size_t)2 * (size_t)(B * D * pl.S * N) * sizeof(float);
+    if (pl.lanes && pl.S_lanes > 1) {
+        const int64_t K = (pl.seg_len_lanes + kFixChunk - 1) / kFixChunk;
+        lanes = ((size_t)2 * (size_t)(B * D * pl.S_lanes * N) + (size_t)(pl.S_lanes * K * B * D)) *
+                sizeof(float);
+    }
+    pl.workspace_bytes = split > lanes ? split : lanes;
     return pl;
+}
+
+void s6_carve(S6Args& a, void* ws) {
+    a.seg_a = a.seg_b = a.seg_cum = nullptr;
+    a.fix_chunks = 0;
+    if (a.S <= 1) return;
+    a.seg_a = static_cast<float*>(ws);
+    a.seg_b = a.seg_a + a.B * a.D * (int64_t)a.S * a.N;
+    if (a.lanes) {
+        a.seg_cum = a.seg_b + a.B * a.D * (int64_t)a.S * a.N;
+        a.fix_chunks = (a.seg_len + kFixChunk - 1) / kFixChunk;
+    }
 }
 
 

@@ -208,10 +208,7 @@ int s6_fwd_impl(const void* u, const void* delta, const float* A, const void* Bm
     a.flags = flags; a.bf16 = dtype == SSM_BF16;
     a.events = reinterpret_cast<hipEvent_t const*>(events);
     a.seq_lens = seq_lens;
-    if (a.S > 1) {
-        a.seg_a = static_cast<float*>(workspace);
-        a.seg_b = a.seg_a + B * D * (int64_t)a.S * N;
-    }
+    ssm::s6_carve(a, workspace);
     const hipError_t e = ssm::launch_s6(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
@@ -257,10 +254,7 @@ int ssm_selective_scan_conv_fwd(const void* x, const float* conv_weight, const f
     a.flags = flags; a.bf16 = dtype == SSM_BF16;
     a.conv_w = conv_weight; a.conv_b = conv_bias; a.conv_state_in = conv_state_in;
     a.conv_state_out = conv_state_out; a.u_out = u_out; a.conv_K = K;
-    if (a.S > 1) {
-        a.seg_a = static_cast<float*>(workspace);
-        a.seg_b = a.seg_a + B * D * (int64_t)a.S * N;
-    }
+    ssm::s6_carve(a, workspace);
     const hipError_t e = ssm::launch_s6(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

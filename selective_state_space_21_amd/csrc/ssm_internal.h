@@ -25,6 +25,10 @@ struct S6Args {
     // workspace: per (b, d, segment, n) decay and offset, fp32 each
     float* seg_a;
     float* seg_b;
+    // state-per-lane segments: per (segment, chunk, b, d) the sum of dt over
+    // the segment up to the end of that chunk of plan::kFixChunk tokens
+    float* seg_cum;
+    int64_t fix_chunks;   // chunks per segment
     int64_t B, L, D, N;
     int64_t seg_len;   // tokens per segment (last one may be shorter)
     int S;             // number of segments along L (1 = no carry)
@@ -55,6 +59,10 @@ struct S6Plan {
 // Host code only (s6_plan.cpp): no HIP call.
 S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N);
 
+// Points a call's segment buffers (pairs, and on the state-per-lane path the
+// dt checkpoints) into its workspace, after a.S, a.seg_len and a.lanes are set.
+void s6_carve(S6Args& a, void* ws);
+
 // Tiling the planners share with the kernels (the kernel sources assert that
 // their own constants agree).
 namespace plan {
@@ -62,6 +70,7 @@ constexpr int kWave = 64;                 // lanes per wavefront
 constexpr int64_t kMaxSegments = 256;     // sequence segments per call at most
 constexpr int kLanesSpan = 128;           // state-per-lane segments: whole multiples of this
 constexpr int kLanesChans = 16;           // state-per-lane kernel: channels per workgroup
+constexpr int kFixChunk = 1024;           // state-per-lane fix-up: tokens per workgroup
 constexpr int kBwdTile = 16;              // backward: tokens per state checkpoint
 constexpr int kBwdChans = 48;             // backward: channels per adjoint-sweep workgroup
 // SIMDs the S6 planner balances wavefronts over: MI355X has 256 CUs of four

@@ -2,6 +2,7 @@
 every function include/ssm.h declares, and rejects bad arguments before any
 HIP call (only invalid calls are made here; nothing is launched)."""
 import ctypes
+import math
 import os
 import re
 
@@ -94,8 +95,24 @@ def test_s6_workspace_and_plan(lib):
         else:
             os.environ["SSM_S6_LANES"] = old
     assert 2 <= S_split <= 256
+    # lanes: pairs plus one dt checkpoint per (segment, 1024-token chunk, channel)
+    seg = math.ceil(math.ceil(131072 / S) / 128) * 128
+    lanes_bytes = 2 * 4 * 2048 * 16 * S + 4 * S * math.ceil(seg / 1024) * 2048
     assert (lib.ssm_selective_scan_workspace_bytes(1, 131072, 2048, 16, 0)
-            == 2 * 4 * 2048 * 16 * max(S, S_split))
+            == max(2 * 4 * 2048 * 16 * S_split, lanes_bytes))
+    # the same forced segment count on both paths: the checkpoints make the
+    # lanes workspace the larger (3 chunks per segment of 2176 tokens here)
+    old_seg = os.environ.get("SSM_S6_SEGMENTS")
+    os.environ["SSM_S6_SEGMENTS"] = "4"
+    try:
+        assert lib.ssm_selective_scan_segments(2, 8700, 64, 16) == 4
+        assert (lib.ssm_selective_scan_workspace_bytes(2, 8700, 64, 16, 0)
+                == 2 * 4 * 2 * 64 * 16 * 4 + 4 * 4 * 3 * 2 * 64)
+    finally:
+        if old_seg is None:
+            del os.environ["SSM_S6_SEGMENTS"]
+        else:
+            os.environ["SSM_S6_SEGMENTS"] = old_seg
     # never more segments than ceil(L / 32)
     assert lib.ssm_selective_scan_segments(1, 40, 64, 16) <= 2
     assert lib.ssm_selective_scan_segments(1, 0, 64, 16) == 1
@@ -116,6 +133,13 @@ def test_s6_plan_env_override(lib, monkeypatch):
     monkeypatch.setenv("SSM_S6_SEGMENTS", "500")
     seg = -(-(-(-70000 // 256)) // 128) * 128
     assert lib.ssm_selective_scan_segments(1, 70000, 64, 16) == -(-70000 // seg)
+    # the fix-up's one-dimensional grid stays under 2^24 workgroups: 128 groups
+    # x 512 rows x 244 later segments x 2 chunks is 32M, so the split path
+    # takes that call; 64 rows (4M workgroups) stay on the state-per-lane path
+    monkeypatch.setenv("SSM_S6_SEGMENTS", "256")
+    assert lib.ssm_selective_scan_lanes(512, 500000, 2048, 16) == 0
+    assert lib.ssm_selective_scan_lanes(64, 500000, 2048, 16) == 1
+    assert lib.ssm_selective_scan_segments(64, 500000, 2048, 16) == 245
 
 
 def test_s6_lanes_plan(lib, monkeypatch):

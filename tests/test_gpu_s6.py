@@ -76,6 +76,65 @@ def test_more_than_64_segments(S, monkeypatch):
     _cmp(inp)
 
 
+def _chunk_case(decay, softplus, seed):
+    w = W.S6_LONG_FP32.scaled(B=2, L=6000, D=64)
+    inp = W.make_s6_inputs(w, seed=seed)
+    inp["A"] = inp["A"] * {"slow": 0.01, "page": 1.0, "fast": 10.0}[decay]
+    if not softplus:
+        inp["delta"] = inp["delta"].abs() * 0.05
+        inp["delta_bias"] = None
+        inp["delta_softplus"] = False
+    inp["h0"] = 0.5 * torch.randn(2, 64, 16, generator=torch.Generator().manual_seed(seed))
+    return w, inp
+
+
+@pytest.mark.parametrize("decay", ["slow", "page", "fast"])
+@pytest.mark.parametrize("softplus", [True, False])
+@pytest.mark.parametrize("S", [2, 3])
+def test_fixup_chunks(decay, softplus, S, monkeypatch):
+    """The state-per-lane fix-up runs one workgroup per 1024-token chunk of a
+    segment, each starting from the running sum of dt the scan stored at the
+    chunk's start: segments of 3072 (S = 2) or 2048 (S = 3) tokens give three
+    or two chunks.  Slow decay (A / 100) keeps the incoming state alive
+    through every chunk; with the workload's A it dies within a few chunks;
+    fast decay (10 A) ends it in the first, so the later chunks stop before
+    loading anything (with softplus)."""
+    monkeypatch.delenv("SSM_S6_LANES", raising=False)
+    monkeypatch.setenv("SSM_S6_SEGMENTS", str(S))
+    w, inp = _chunk_case(decay, softplus, seed=11 + S)
+    assert ssm.selective_scan_lanes(w.B, w.L, w.D, w.N)
+    assert ssm.selective_scan_segments(w.B, w.L, w.D, w.N) == S
+    _cmp(inp)
+
+
+@pytest.mark.parametrize("decay", ["slow", "page"])
+def test_fixup_chunks_ragged_rows(decay, monkeypatch):
+    """Rows that end inside a segment's chunks (seq_lens): row 1's second
+    segment holds 1028 tokens, a whole chunk and 4 tokens of the next, which
+    starts from a stored sum; its third chunk is empty."""
+    monkeypatch.delenv("SSM_S6_LANES", raising=False)
+    monkeypatch.setenv("SSM_S6_SEGMENTS", "2")
+    w, inp = _chunk_case(decay, True, seed=5)
+    lens = [6000, 4100]
+    sentinel = 7.0
+    d = to_dev(inp)
+    y = torch.full((w.B, w.L, w.D), sentinel, device="cuda")
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    _, h = ssm.selective_scan_fwd(d["u"], d["delta"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
+                                  delta_bias=d["delta_bias"], h0=d["h0"], out=y, seq_lens=sl)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    h = h.cpu().numpy()
+    for b, n in enumerate(lens):
+        cut = lambda t: None if t is None else t[b:b + 1, :n]
+        yr, hr = oracle.s6_fwd(cut(inp["u"]), cut(inp["delta"]), inp["A"], cut(inp["B"]),
+                               cut(inp["C"]), D=inp["D"], z=cut(inp["z"]),
+                               delta_bias=inp["delta_bias"], h0=inp["h0"][b:b + 1])
+        assert normwise_err(y[b:b + 1, :n], yr) <= TOL["f32"]
+        assert normwise_err(h[b:b + 1], hr) <= TOL["f32"]
+        assert np.all(y[b, n:] == sentinel)
+
+
 @pytest.mark.parametrize("N", [1, 3, 4, 5, 8, 15, 16, 17, 32, 33, 64])
 def test_state_sizes(N):
     w = W.S6_SMALL_FP32.scaled(B=2, L=300, D=70, N=N)
