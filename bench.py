@@ -72,14 +72,10 @@ ISSUE_PEAK_ELEMS_PER_S = 6.52e12
 # reports traffic null until its counters are taken again.
 COUNTER_TRAFFIC = {
     # kernel@workload: (bytes, sources, sha1 of the sources)
-    "s6_lanes@s6_mamba130m_layer_bf16": (205368162, ['s6_fwd.hip', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "21dbdf92d8db"),
-    "s6_lanes@s6_mamba2.8b_layer_bf16": (686899070, ['s6_fwd.hip', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "21dbdf92d8db"),
-    "s6_lanes@s6_long_fp32": (3536628854, ['s6_fwd.hip', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "21dbdf92d8db"),
+    "s6_lanes@s6_mamba130m_layer_bf16": (205407959, ['s6_fwd.hip', 's6_plan.cpp', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "37c5422abc2d"),
+    "s6_lanes@s6_mamba2.8b_layer_bf16": (686213377, ['s6_fwd.hip', 's6_plan.cpp', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "37c5422abc2d"),
+    "s6_lanes@s6_long_fp32": (3540503219, ['s6_fwd.hip', 's6_plan.cpp', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "37c5422abc2d"),
     "ssd@ssd_mamba2_bf16": (597920238, ['ssd_fwd.hip', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "65164f749a40"),
-}
-KERNEL_SOURCES = {
-    "s6": ["s6_fwd.hip", "device_math.h", "lane_ops.h", "ssm_internal.h"],
-    "ssd": ["ssd_fwd.hip", "device_math.h", "lane_ops.h", "ssm_internal.h"],
 }
 
 

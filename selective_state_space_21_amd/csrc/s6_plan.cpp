@@ -25,9 +25,12 @@ S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N) {
     // activations (plus two super-tiles) within 32-bit buffer offsets at 4
     // bytes per element.  SSM_S6_LANES=0 turns it off.  It runs B*D/4
     // wavefronts per segment: unsplit with at least two per SIMD, else cut
-    // into the fewest segments (whole 128-token multiples) that give four per
-    // SIMD (the segmented kernel stages half as much and fits four); the
-    // segments after the first are fixed up afterwards.
+    // into the fewest segments (whole 128-token multiples) that give six per
+    // SIMD; the segments after the first are fixed up afterwards.  (Six is
+    // more than fit at once, five by registers, but the scan's gain from the
+    // extra wavefronts outweighs the tail and the longer fix-up: at B=1
+    // L=131072 D=2048 fp32, 12 segments ran 1.25-1.27 ms, 8 segments
+    // (four per SIMD, one round) 1.27-1.30 ms, 16 segments 1.33 ms.)
     {
         const bool shape_ok = N == 16 && D % kLanesChans == 0 &&
                               (L + 2 * kLanesSpan) * D * 4 <= (int64_t)0xFFFFFFFF;
@@ -35,7 +38,7 @@ S6Plan plan_s6(int64_t B, int64_t L, int64_t D, int64_t N) {
         const char* env = getenv("SSM_S6_LANES");
         if (env && env[0] == '0') pl.lanes = false;
         const int64_t waves = B * D / 4;
-        int64_t S = waves >= 2 * kSimds ? 1 : (4 * kSimds + waves - 1) / (waves > 0 ? waves : 1);
+        int64_t S = waves >= 2 * kSimds ? 1 : (6 * kSimds + waves - 1) / (waves > 0 ? waves : 1);
         if (forced) S = forced;
         int64_t maxS = (L + kLanesSpan - 1) / kLanesSpan;
         if (maxS > kMaxSegments) maxS = kMaxSegments;

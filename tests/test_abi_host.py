@@ -145,14 +145,14 @@ def test_s6_plan_env_override(lib, monkeypatch):
 def test_s6_lanes_plan(lib, monkeypatch):
     # The planner balances over 1024 SIMDs (256 CUs), device or not: the state-per-lane
     # kernel needs N = 16 and D % 16 == 0; below 2048 wavefronts (B*D/4) it cuts the
-    # sequence into segments of whole super-tiles for four wavefronts per SIMD
+    # sequence into segments of whole super-tiles for six wavefronts per SIMD
     monkeypatch.delenv("SSM_S6_LANES", raising=False)
     monkeypatch.delenv("SSM_S6_SEGMENTS", raising=False)
     assert lib.ssm_selective_scan_lanes(8, 2048, 1536, 16) == 1
     assert lib.ssm_selective_scan_segments(8, 2048, 1536, 16) == 1
     assert lib.ssm_selective_scan_lanes(4, 4096, 5120, 16) == 1
     assert lib.ssm_selective_scan_lanes(1, 131072, 2048, 16) == 1      # few channels: segments
-    assert lib.ssm_selective_scan_segments(1, 131072, 2048, 16) == 8
+    assert lib.ssm_selective_scan_segments(1, 131072, 2048, 16) == 12
     assert lib.ssm_selective_scan_lanes(8, 2048, 1544, 16) == 0        # D % 16 != 0
     assert lib.ssm_selective_scan_lanes(8, 2048, 1536, 32) == 0        # N != 16
     assert lib.ssm_selective_scan_lanes(0, 2048, 1536, 16) == 0        # invalid sizes

@@ -43,7 +43,7 @@ def test_planner_takes_lanes_at_the_layer_shapes(monkeypatch):
         assert ssm.selective_scan_segments(w.B, w.L, w.D, w.N) == 1
     # too few channels to fill the chip: segments of whole super-tiles
     assert ssm.selective_scan_lanes(1, 131072, 2048, 16)
-    assert ssm.selective_scan_segments(1, 131072, 2048, 16) == 8
+    assert ssm.selective_scan_segments(1, 131072, 2048, 16) == 12
     # D not a multiple of 16, N != 16: the split path
     assert not ssm.selective_scan_lanes(8, 2048, 1544, 16)
     assert not ssm.selective_scan_lanes(8, 2048, 1536, 8)
