@@ -25,9 +25,9 @@
 //   2. s6_bwd_main (12 wavefronts, 48 channels per workgroup): tiles in
 //      reverse; each tile recomputes its 16 states from the checkpoint into
 //      registers, then runs the adjoint backwards.  Sums over n are row
-//      all-reduces (4 DPP adds); dB and dC are summed over the wavefront's 4
-//      rows (xor swizzles) and the workgroup's 12 wavefronts (LDS), giving
-//      one partial per (48-channel group, b, t, n).
+//      reduce-scatters (DPP); each lane writes its dB and dC terms to LDS and
+//      they are summed over the workgroup's 48 channels after the tile,
+//      giving one partial per (48-channel group, b, t, n).
 //   3. s6_bwd_reduce: sums the channel-group partials of dB and dC and the
 //      batch partials of dA, D and bias.  No atomics: results are
 //      deterministic.
@@ -41,6 +41,8 @@
 
 namespace ssm {
 namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 16;              // tokens per tile = per checkpoint
 // Checkpoint sweep: 4 wavefronts, 16 channels per workgroup.
@@ -381,7 +383,14 @@ template <typename T, bool HAS_Z, bool SOFTPLUS, bool VEC>
 __global__ __launch_bounds__(kMainThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void s6_bwd_main(S6BwdArgs p) {
     constexpr int kWaves = kMainWaves, kThreads = kMainThreads, kChans = kMainChans;
-    __shared__ float red[2][kWaves][kTile][16];     // [dB|dC][wave][token][n]
+    // dB and dC terms of the tile per channel, [dB|dC][token][state][channel]:
+    // each lane writes its own two terms per token, and the sums over the
+    // workgroup's 48 channels are taken after the tile as 16-byte reads.  A
+    // channel run holds kRedPitch floats, so the 64 lanes of one write (4
+    // channels x 16 states; runs 52 floats apart) hit 64 distinct banks.
+    constexpr int kRedPitch = kChans + 4;
+    static_assert(kRedPitch % 4 == 0, "16-byte reads of a channel run");
+    __shared__ __attribute__((aligned(16))) float red[2][kTile][16][kRedPitch];
     // du, ddelta, dz of the tile as stored ([output][token][channel]): written
     // per lane, then stored as 16-byte rows pieces, so that one store covers
     // a run of the workgroup's channels instead of one 2-byte element
@@ -412,7 +421,6 @@ void s6_bwd_main(S6BwdArgs p) {
     T* dz_out = static_cast<T*>(p.dz);
     const auto rB = bc_rsrc<T>(p, id.b, p.Bm);
     const auto rC = bc_rsrc<T>(p, id.b, p.Cm);
-    const bool lowhalf = id.row < 2;               // rows 0-1 gather dB, rows 2-3 dC
 
     float mu = (id.ok && p.dh_last) ? p.dh_last[(id.b * p.D + id.d) * p.N + id.n] : 0.0f;
     float dA_acc = 0.0f, dD_acc = 0.0f, db_acc = 0.0f;
@@ -498,9 +506,9 @@ void s6_bwd_main(S6BwdArgs p) {
         asm volatile("" ::: "memory");
         asm volatile("" : "+v"(s.dt), "+v"(s.dtu), "+v"(s.u), "+v"(s.g));
         // adjoint, token by token backwards.  Per-lane terms of the sums over n
-        // (pt: ddt, pu: sum m B, py: readout) are reduced after the loop;
-        // wbc[j]: dB (rows 0-1) or dC (rows 2-3) of token j summed over the wavefront
-        float pt[kTile], pu[kTile], py[kTile], wbc[kTile];
+        // (pt: ddt, pu: sum m B, py: readout) are reduced after the loop; the
+        // dB and dC terms of each token go to LDS as they are formed
+        float pt[kTile], pu[kTile], py[kTile];
         float bv[kTile], cv[kTile];
         tile_row(bct[0], id.n, bv);
         tile_row(bct[1], id.n, cv);
@@ -517,8 +525,8 @@ void s6_bwd_main(S6BwdArgs p) {
             py[j] = cj * hs[j];
             dA_acc = fmaf(m * hp, row_bcast(s.dt, j) * da[j], dA_acc);
             mu = da[j] * m;
-            const float v = (lowhalf ? pb : pc) + __shfl_xor(lowhalf ? pc : pb, 32, 64);
-            wbc[j] = v + lane_xor<16>(v);
+            red[0][j][id.n][cl] = pb;
+            red[1][j][id.n][cl] = pc;
         }
         const float r_ddt = row_reduce_scatter16(pt, id.n);
         const float r_su = row_reduce_scatter16(pu, id.n);
@@ -538,11 +546,6 @@ void s6_bwd_main(S6BwdArgs p) {
                 db_acc += dd;
                 dD_acc = fmaf(s.g, s.u, dD_acc);
             }
-        }
-        if (id.row == 0 || id.row == 2) {
-            const int q = id.row / 2;
-#pragma unroll
-            for (int j = 0; j < kTile; ++j) red[q][id.w][j][id.n] = wbc[j];
         }
         lds_barrier();
         {
@@ -564,12 +567,15 @@ void s6_bwd_main(S6BwdArgs p) {
                         if (d0 + pc * kPer + c < p.D) dst[c] = src[c];
                 }
             }
-            // thread -> (q, token, n) for half of them; sum over the wavefronts
+            // thread -> (q, token, n) for 512 of them; sum over the 48 channels
+            // (four running sums over 4-channel runs, then added pairwise)
             for (int e = threadIdx.x; e < 2 * kTile * 16; e += kThreads) {
                 const int q = e / (kTile * 16), j = (e / 16) % kTile, n = e % 16;
-                float v = 0.0f;
+                f32x4 acc = *reinterpret_cast<const f32x4*>(&red[q][j][n][0]);
 #pragma unroll
-                for (int w = 0; w < kWaves; ++w) v += red[q][w][j][n];
+                for (int c4 = 1; c4 < kChans / 4; ++c4)
+                    acc += *reinterpret_cast<const f32x4*>(&red[q][j][n][4 * c4]);
+                const float v = (acc[0] + acc[1]) + (acc[2] + acc[3]);
                 const int64_t t = t0 + j;
                 if (t < p.L && n < p.N)
                     p.part_bc[(((int64_t)q * G + id.grp) * p.B + id.b) * p.L * p.N + t * p.N + n] = v;
