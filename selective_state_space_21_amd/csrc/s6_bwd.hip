@@ -452,7 +452,10 @@ void s6_bwd_main(S6BwdArgs p) {
         const float hprev0 = id.ok ? hck : 0.0f;
         TileScalars<HAS_Z, SOFTPLUS, true> s;
         if constexpr (!VEC) s.template from<T>(raw, p, id, t0, bias);
-        lds_barrier();                   // previous tile's LDS reads done
+        // No barrier before the staging: the previous tile read bct and actst
+        // only before its last barrier, and what follows that barrier (the
+        // output stores and the dB/dC sums) reads outst and red, which this
+        // tile writes only after the barrier below.
         if (threadIdx.x < kTile * 16) {
             bct[0][(threadIdx.x % 16) * kPitch + threadIdx.x / 16] = Bits<T>::f32(bpre);
             bct[1][(threadIdx.x % 16) * kPitch + threadIdx.x / 16] = Bits<T>::f32(cpre);
@@ -520,10 +523,12 @@ void s6_bwd_main(S6BwdArgs p) {
             const float hp = j > 0 ? hs[j - 1] : hprev0;
             const float pc = gj * hs[j];
             const float pb = m * row_bcast(s.dtu, j);
-            pt[j] = m * fmaf(hp, an * da[j], bj * row_bcast(s.u, j));
+            // m_t h_{t-1} a_t serves both ddt (times A) and dA (times dt)
+            const float ya = m * hp * da[j];
             pu[j] = m * bj;
+            pt[j] = fmaf(ya, an, pu[j] * row_bcast(s.u, j));
             py[j] = cj * hs[j];
-            dA_acc = fmaf(m * hp, row_bcast(s.dt, j) * da[j], dA_acc);
+            dA_acc = fmaf(ya, row_bcast(s.dt, j), dA_acc);
             mu = da[j] * m;
             red[0][j][id.n][cl] = pb;
             red[1][j][id.n][cl] = pc;
