@@ -558,7 +558,9 @@ void s6_bwd_main(S6BwdArgs p) {
             constexpr int kPieces = kChans * (int)sizeof(T) / 16;
             const int64_t d0 = id.grp * kChans;
             const bool vec = d0 + kChans <= p.D && (p.D * (int64_t)sizeof(T)) % 16 == 0;
-            for (int e = threadIdx.x; e < kOut * kTile * kPieces; e += kThreads) {
+            // the last wavefronts (no dB/dC sums below) take the stores first
+            const int st = (int)((threadIdx.x + kThreads - 2 * kTile * 16) % kThreads);
+            for (int e = st; e < kOut * kTile * kPieces; e += kThreads) {
                 const int o = e / (kTile * kPieces), j = (e / kPieces) % kTile, pc = e % kPieces;
                 const int64_t t = t0 + j;
                 if (t >= p.L) continue;
@@ -607,15 +609,32 @@ __global__ __launch_bounds__(256) void s6_bwd_reduce(S6BwdArgs p) {
     const int64_t nbc = p.B * p.L * p.N;
     if (i < 2 * nbc) {
         const int64_t q = i / nbc, e = i % nbc;
+        // eight partials in flight at a time, added in group order
         float v = 0.0f;
-        for (int64_t g = 0; g < G; ++g) v += p.part_bc[(q * G + g) * nbc + e];
+        int64_t g = 0;
+        for (; g + 8 <= G; g += 8) {
+            float t[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) t[k] = p.part_bc[(q * G + g + k) * nbc + e];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v += t[k];
+        }
+        for (; g < G; ++g) v += p.part_bc[(q * G + g) * nbc + e];
         (q == 0 ? p.dB : p.dC)[e] = v;
         return;
     }
     const int64_t j = i - 2 * nbc;
     if (j < p.D * p.N) {
         float v = 0.0f;
-        for (int64_t b = 0; b < p.B; ++b) v += p.part_dA[b * p.D * p.N + j];
+        int64_t b = 0;
+        for (; b + 8 <= p.B; b += 8) {
+            float t[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) t[k] = p.part_dA[(b + k) * p.D * p.N + j];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v += t[k];
+        }
+        for (; b < p.B; ++b) v += p.part_dA[b * p.D * p.N + j];
         p.dA[j] = v;
         return;
     }
