@@ -75,7 +75,7 @@ COUNTER_TRAFFIC = {
     "s6_lanes@s6_mamba130m_layer_bf16": (205407959, ['s6_fwd.hip', 's6_plan.cpp', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "37c5422abc2d"),
     "s6_lanes@s6_mamba2.8b_layer_bf16": (686213377, ['s6_fwd.hip', 's6_plan.cpp', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "37c5422abc2d"),
     "s6_lanes@s6_long_fp32": (3540503219, ['s6_fwd.hip', 's6_plan.cpp', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "37c5422abc2d"),
-    "ssd@ssd_mamba2_bf16": (597920238, ['ssd_fwd.hip', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "65164f749a40"),
+    "ssd@ssd_mamba2_bf16": (597920266, ['ssd_fwd.hip', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "0bb354e1c419"),
 }
 
 
