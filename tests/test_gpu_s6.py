@@ -107,6 +107,23 @@ def test_fixup_chunks(decay, softplus, S, monkeypatch):
     _cmp(inp)
 
 
+@pytest.mark.parametrize("dtype,Dm,Bt", [("f32", 48, 3), ("bf16", 80, 2), ("bf16", 16, 5)])
+def test_fixup_partial_rows_of_groups(dtype, Dm, Bt, monkeypatch):
+    """Channel-group counts that do not fill the fix-up's 128-byte rows of
+    groups (two 16-channel groups per row in fp32, four in bf16): 3, 5 and 1
+    groups, the padding workgroups return at once; several batch rows, three
+    segments of two chunks each plus a short tail, softplus, gate and skip."""
+    monkeypatch.delenv("SSM_S6_LANES", raising=False)
+    monkeypatch.setenv("SSM_S6_SEGMENTS", "3")
+    w = W.S6_MAMBA130M.scaled(B=Bt, L=4500, D=Dm, dtype=dtype)
+    inp = W.make_s6_inputs(w, seed=Dm + Bt)
+    inp["A"] = inp["A"] * 0.05             # decay horizon longer than a chunk
+    inp["h0"] = 0.3 * torch.randn(Bt, Dm, 16, generator=torch.Generator().manual_seed(Dm))
+    assert ssm.selective_scan_lanes(w.B, w.L, w.D, w.N)
+    assert ssm.selective_scan_segments(w.B, w.L, w.D, w.N) == 3
+    _cmp(inp)
+
+
 @pytest.mark.parametrize("decay", ["slow", "page"])
 def test_fixup_chunks_ragged_rows(decay, monkeypatch):
     """Rows that end inside a segment's chunks (seq_lens): row 1's second
