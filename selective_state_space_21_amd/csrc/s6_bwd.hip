@@ -509,7 +509,7 @@ void s6_bwd_main(S6BwdArgs p) {
         asm volatile("" ::: "memory");
         asm volatile("" : "+v"(s.dt), "+v"(s.dtu), "+v"(s.u), "+v"(s.g));
         // adjoint, token by token backwards.  Per-lane terms of the sums over n
-        // (pt: ddt, pu: sum m B, py: readout) are reduced after the loop; the
+        // (pt: the A part of ddt, pu: sum m B, py: readout) are reduced after the loop; the
         // dB and dC terms of each token go to LDS as they are formed
         float pt[kTile], pu[kTile], py[kTile];
         float bv[kTile], cv[kTile];
@@ -518,23 +518,22 @@ void s6_bwd_main(S6BwdArgs p) {
 #pragma unroll
         for (int j = kTile - 1; j >= 0; --j) {
             const float bj = bv[j], cj = cv[j];
-            const float gj = row_bcast(s.g, j);
-            const float m = fmaf(gj, cj, mu);
+            const float m = fmac_bcast(mu, s.g, cj, j);          // mu + g_t C_t
             const float hp = j > 0 ? hs[j - 1] : hprev0;
-            const float pc = gj * hs[j];
+            const float pc = hs[j] * row_bcast(s.g, j);
             const float pb = m * row_bcast(s.dtu, j);
             // m_t h_{t-1} a_t serves both ddt (times A) and dA (times dt)
             const float ya = m * hp * da[j];
             pu[j] = m * bj;
-            pt[j] = fmaf(ya, an, pu[j] * row_bcast(s.u, j));
+            pt[j] = ya * an;       // ddt = sum_n ya A + u sum_n m B, the latter added below
             py[j] = cj * hs[j];
-            dA_acc = fmaf(ya, row_bcast(s.dt, j), dA_acc);
+            dA_acc = fmac_bcast(dA_acc, s.dt, ya, j);
             mu = da[j] * m;
             red[0][j][id.n][cl] = pb;
             red[1][j][id.n][cl] = pc;
         }
-        const float r_ddt = row_reduce_scatter16(pt, id.n);
         const float r_su = row_reduce_scatter16(pu, id.n);
+        const float r_ddt = fmaf(s.u, r_su, row_reduce_scatter16(pt, id.n));
         const float r_y = row_reduce_scatter16(py, id.n);
         // per-channel results of token t0 + j in lane j, staged in LDS
         {
