@@ -29,30 +29,6 @@ __device__ __forceinline__ float row_bcast(float v, int k) {
     }
 }
 
-// acc + (lane K of the row's s) * x in one v_fmac_f32_dpp: the broadcast
-// that row_bcast feeds to a multiply, for a fused multiply-add (which the
-// compiler does not fold).  DPP reads its source two wait states after a VALU
-// write at the earliest, so the statement opens with s_nop 1.
-template <int K>
-__device__ __forceinline__ float fmac_bcast_c(float acc, float s, float x) {
-    asm("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-        : "+v"(acc) : "v"(s), "v"(x), "n"(K));
-    return acc;
-}
-// k must fold to a constant after unrolling.
-__device__ __forceinline__ float fmac_bcast(float acc, float s, float x, int k) {
-    switch (k) {
-        case 0: return fmac_bcast_c<0>(acc, s, x);   case 1: return fmac_bcast_c<1>(acc, s, x);
-        case 2: return fmac_bcast_c<2>(acc, s, x);   case 3: return fmac_bcast_c<3>(acc, s, x);
-        case 4: return fmac_bcast_c<4>(acc, s, x);   case 5: return fmac_bcast_c<5>(acc, s, x);
-        case 6: return fmac_bcast_c<6>(acc, s, x);   case 7: return fmac_bcast_c<7>(acc, s, x);
-        case 8: return fmac_bcast_c<8>(acc, s, x);   case 9: return fmac_bcast_c<9>(acc, s, x);
-        case 10: return fmac_bcast_c<10>(acc, s, x); case 11: return fmac_bcast_c<11>(acc, s, x);
-        case 12: return fmac_bcast_c<12>(acc, s, x); case 13: return fmac_bcast_c<13>(acc, s, x);
-        case 14: return fmac_bcast_c<14>(acc, s, x); default: return fmac_bcast_c<15>(acc, s, x);
-    }
-}
-
 // Value of lane j - K of the same 16-lane row (DPP row_shr:K); lanes j < K
 // read 0.
 template <int K>
