@@ -368,6 +368,52 @@ def bench_bwd(args, ctx):
                 gtokch=round(w.tok_ch / (ms * 1e-3) / 1e9, 3), workspace_bytes=need)
 
 
+def bench_train(args, ctx):
+    """Forward and backward of one training step at the Mamba-130M layer, two
+    ways: the plain forward then the self-contained backward (which starts
+    with its own forward sweep), and the forward that saves the 16-token
+    checkpoints then the backward that takes them.  Each call alone and each
+    pair as one timed step."""
+    torch, ssm, W = ctx["torch"], ctx["ssm"], ctx["W"]
+    w = W.S6_MAMBA130M
+    t = W.make_s6_inputs(w, seed=0)
+    d = {k: (v.to("cuda:0") if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
+    g = torch.Generator().manual_seed(1)
+    dy = torch.randn(w.B, w.L, w.D, generator=g).to(torch.bfloat16).to("cuda:0")
+    lib = ssm._native.load()
+    y = torch.empty_like(d["u"])
+    ck = torch.empty((w.B, w.D, (w.L + 15) // 16, w.N), dtype=torch.float32, device="cuda:0")
+    ws_full = torch.empty(int(lib.ssm_selective_scan_bwd_workspace_bytes(w.B, w.L, w.D, w.N, 1)),
+                          dtype=torch.uint8, device="cuda:0")
+    ws_part = torch.empty(int(lib.ssm_selective_scan_bwd_ckpt_workspace_bytes(w.B, w.L, w.D, w.N, 1)),
+                          dtype=torch.uint8, device="cuda:0")
+    kw = dict(D=d["D"], z=d["z"], delta_bias=d["delta_bias"])
+    args_in = (d["u"], d["delta"], d["A"], d["B"], d["C"])
+
+    def fwd():
+        ssm.selective_scan_fwd(*args_in, **kw, return_last_state=False, out=y)
+
+    def fwd_ckpt():
+        ssm.selective_scan_fwd_ckpt(*args_in, **kw, return_last_state=False, out=y, ckpt=ck)
+
+    def bwd():
+        ssm.selective_scan_bwd(*args_in, dy, **kw, workspace=ws_full)
+
+    def bwd_ckpt():
+        ssm.selective_scan_bwd(*args_in, dy, **kw, workspace=ws_part, ckpt=ck)
+
+    def run(fn):
+        return round(ctx["timer"].run(fn, args.steps, args.warmup, ctx["flusher"].clean)["mean"], 5)
+
+    res = dict(status="ok", workload=w.name, ckpt_bytes=ck.numel() * 4)
+    res["ms_fwd_ckpt"] = run(fwd_ckpt)
+    res["ms_bwd_ckpt"] = run(bwd_ckpt)
+    res["ms_fwd_then_bwd_ckpt"] = run(lambda: (fwd_ckpt(), bwd_ckpt()))
+    res["ms_fwd_then_bwd"] = run(lambda: (fwd(), bwd()))
+    res["ms"] = res["ms_fwd_then_bwd_ckpt"]
+    return res
+
+
 def bench_conv(args, ctx):
     torch, ssm, W = ctx["torch"], ctx["ssm"], ctx["W"]
     w = W.CONV_MAMBA130M
@@ -540,7 +586,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-paths", action="store_true", help="the headline S6 workload only")
     ap.add_argument("--only", choices=["s6", "s6_2p8b", "s6_long", "ssd", "decode", "bwd",
-                                       "conv", "conv_scan", "copy"],
+                                       "train", "conv", "conv_scan", "copy"],
                     help="run one part alone and print its result")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 256 MiB device copy three times, the "
@@ -573,7 +619,8 @@ def main():
              "s6_2p8b": lambda: bench_s6(args, ctx, W.S6_MAMBA2P8B),
              "s6_long": lambda: bench_s6(args, ctx, W.S6_LONG_FP32),
              "ssd": lambda: bench_ssd(args, ctx), "decode": lambda: bench_decode(args, ctx),
-             "bwd": lambda: bench_bwd(args, ctx), "conv": lambda: bench_conv(args, ctx),
+             "bwd": lambda: bench_bwd(args, ctx), "train": lambda: bench_train(args, ctx),
+             "conv": lambda: bench_conv(args, ctx),
              "conv_scan": lambda: bench_conv_scan(args, ctx),
              "copy": lambda: bench_copy(args, ctx, W.s6_algorithmic_bytes(W.S6_MAMBA130M))}
     if args.only:
@@ -588,7 +635,8 @@ def main():
     if not args.no_paths:
         for name, key in [("s6_mamba2.8b_layer", "s6_2p8b"), ("s6_long_fp32", "s6_long"),
                           ("ssd_chunk_fwd", "ssd"), ("selective_state_update", "decode"),
-                          ("selective_scan_bwd", "bwd"), ("causal_conv1d_silu", "conv"),
+                          ("selective_scan_bwd", "bwd"), ("training_step_fwd_bwd", "train"),
+                          ("causal_conv1d_silu", "conv"),
                           ("selective_scan_conv_fwd", "conv_scan")]:
             paths[name] = parts[key]()
             torch.cuda.empty_cache()

@@ -275,8 +275,8 @@ int ssm_ssd_chunk_fwd(const void* X, const void* delta, const float* A,
  *   dDskip, ddelta_bias : [D]  fp32 or NULL (not computed)
  *   dh0            : [B, D, N] fp32 or NULL
  * Supported: 1 <= N <= 16; flags SSM_FLAG_DELTA_SOFTPLUS only (no ZOH).
- * The workspace (query below; 256-byte aligned) holds a state checkpoint
- * every 16 tokens and per-channel-group partial sums; results are
+ * The workspace (query below; 256-byte aligned) holds per-channel-group
+ * partial sums and a state checkpoint every 16 tokens; results are
  * deterministic (no atomics).
  */
 size_t ssm_selective_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
@@ -290,6 +290,60 @@ int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, con
                            float* ddelta_bias, float* dh0, int64_t B, int64_t L, int64_t D,
                            int64_t N, int dtype, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/*
+ * -------------------------------------------- S6 forward and backward, training
+ * A training step runs the forward and then the backward over the same
+ * inputs; the backward above starts with a forward sweep of its own that
+ * recomputes the state entering every 16-token tile.  These two calls split
+ * that work differently: the forward call saves those states as it passes
+ * them, and the backward call takes them instead of recomputing them (the
+ * chunk-boundary states of the recomputation scheme in the Transformer-math
+ * "Selective state space" article, "Why the fused kernel is the real
+ * contribution": the per-token states are still recomputed inside each tile,
+ * never stored).
+ *
+ *   ckpt : [B, D, ceil(L/16), N] fp32; ckpt[b,d,k,:] = the state before token
+ *          16k (h0, or zeros, for k = 0).  ssm_selective_scan_ckpt_bytes
+ *          returns its size (0 for sizes the backward does not take).
+ *
+ * ssm_selective_scan_fwd_ckpt: ssm_selective_scan_fwd (same arguments,
+ * results, workspace query and errors) that also writes ckpt.  Sizes, flags
+ * and dtype: those of ssm_selective_scan_bwd (1 <= N <= 16; only
+ * SSM_FLAG_DELTA_SOFTPLUS).  Where the one-pass state-per-lane scan runs, it
+ * stores each checkpoint itself (one 4-byte store per lane and tile); on
+ * every other path the call runs the backward's forward sweep after the
+ * scan.  Either way the values are those the backward's own sweep computes,
+ * bit for bit.  ckpt may be NULL only when L = 0; 16-byte aligned.
+ *
+ * ssm_selective_scan_bwd_ckpt: ssm_selective_scan_bwd (same arguments,
+ * results and errors) reading the checkpoints from ckpt, as written by
+ * ssm_selective_scan_fwd_ckpt over the same inputs (or by any forward of the
+ * same operation); its forward sweep is skipped and its workspace
+ * (ssm_selective_scan_bwd_ckpt_workspace_bytes) holds only the partial sums.
+ * With identical checkpoints the gradients equal ssm_selective_scan_bwd's bit
+ * for bit.  ckpt may be NULL only when L = 0; 16-byte aligned.
+ */
+size_t ssm_selective_scan_ckpt_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int dtype);
+
+int ssm_selective_scan_fwd_ckpt(const void* u, const void* delta, const float* A,
+                                const void* Bm, const void* Cm, const float* Dskip,
+                                const void* z, const float* delta_bias, unsigned flags,
+                                const float* h0, void* y, float* h_last, float* ckpt,
+                                int64_t B, int64_t L, int64_t D, int64_t N, int dtype,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+size_t ssm_selective_scan_bwd_ckpt_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
+                                                   int dtype);
+
+int ssm_selective_scan_bwd_ckpt(const void* u, const void* delta, const float* A, const void* Bm,
+                                const void* Cm, const float* Dskip, const void* z,
+                                const float* delta_bias, unsigned flags, const float* h0,
+                                const float* ckpt, const void* dy, const float* dh_last,
+                                void* du, void* ddelta, float* dA, float* dB, float* dC,
+                                float* dDskip, void* dz, float* ddelta_bias, float* dh0,
+                                int64_t B, int64_t L, int64_t D, int64_t N, int dtype,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * ---------------------------------------------------------------- S6 decode

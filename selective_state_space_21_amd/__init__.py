@@ -19,7 +19,8 @@ from . import _native
 from ._native import SSMError
 
 __all__ = ["selective_scan_fwd", "selective_scan_fwd_noalloc", "selective_scan_conv_fwd",
-           "selective_scan_bwd", "ssd_chunk_fwd", "selective_state_update",
+           "selective_scan_bwd", "selective_scan_fwd_ckpt", "selective_scan_ckpt_bytes",
+           "ssd_chunk_fwd", "selective_state_update",
            "causal_conv1d_silu", "selective_scan_workspace_bytes",
            "selective_scan_segments", "selective_scan_lanes", "ssd_chunk_workspace_bytes",
            "SSMError"]
@@ -177,6 +178,42 @@ def selective_scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
     return y, h_last
 
 
+def selective_scan_ckpt_bytes(B: int, L: int, D: int, N: int, dtype=torch.bfloat16) -> int:
+    return int(_native.load().ssm_selective_scan_ckpt_bytes(B, L, D, N, _DT[dtype]))
+
+
+def selective_scan_fwd_ckpt(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
+                            B: torch.Tensor, C: torch.Tensor, D: Optional[torch.Tensor] = None,
+                            z: Optional[torch.Tensor] = None,
+                            delta_bias: Optional[torch.Tensor] = None,
+                            delta_softplus: bool = True, h0: Optional[torch.Tensor] = None,
+                            return_last_state: bool = True, out: Optional[torch.Tensor] = None,
+                            ckpt: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None):
+    """S6 forward for training (ssm_selective_scan_fwd_ckpt): the forward
+    call that also saves the state entering every 16-token tile, for
+    selective_scan_bwd(..., ckpt=...).  Arguments as selective_scan_fwd (no
+    ZOH, N <= 16); ckpt: optional fp32 [Bt, Dm, ceil(L/16), N] to fill.
+    Returns (y, h_last, ckpt)."""
+    dt, dev, Bt, L, Dm, N = _s6_prepare(u, delta, A, B, C, D, z, delta_bias, h0, out)
+    nck = (L + 15) // 16
+    _check_args(dev, ("ckpt", ckpt, (Bt, Dm, nck, N), _F32))
+    lib = _native.load()
+    ws_need = int(lib.ssm_selective_scan_workspace_bytes(Bt, L, Dm, N, _DT[dt]))
+    workspace, ws_bytes = _workspace(workspace, ws_need, dev)
+    y = out if out is not None else torch.empty((Bt, L, Dm), dtype=dt, device=dev)
+    h_last = torch.empty((Bt, Dm, N), dtype=_F32, device=dev) if return_last_state else None
+    if ckpt is None:
+        ckpt = torch.empty((Bt, Dm, nck, N), dtype=_F32, device=dev)
+    flags = _native.FLAG_DELTA_SOFTPLUS if delta_softplus else 0
+    rc = lib.ssm_selective_scan_fwd_ckpt(
+        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+        flags, _ptr(h0), _ptr(y), _ptr(h_last), _ptr(ckpt), Bt, L, Dm, N, _DT[dt],
+        _ptr(workspace), ws_bytes, _stream_handle(dev))
+    _native.check(rc, "ssm_selective_scan_fwd_ckpt")
+    return y, h_last, ckpt
+
+
 def selective_scan_fwd_noalloc(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor,
                                B: torch.Tensor, C: torch.Tensor, y: torch.Tensor,
                                h_last: Optional[torch.Tensor] = None,
@@ -276,18 +313,25 @@ def selective_scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B:
                        z: Optional[torch.Tensor] = None,
                        delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = True,
                        h0: Optional[torch.Tensor] = None, dh_last: Optional[torch.Tensor] = None,
-                       workspace: Optional[torch.Tensor] = None) -> dict:
+                       workspace: Optional[torch.Tensor] = None,
+                       ckpt: Optional[torch.Tensor] = None) -> dict:
     """Gradients of the S6 scan (ssm_selective_scan_bwd), states recomputed.
 
     Inputs as selective_scan_fwd plus dy [Bt, L, Dm] (dtype of u) and
-    dh_last [Bt, Dm, N] fp32.  Returns a dict with du, ddelta (dtype of u),
-    dA [Dm, N], dB, dC [Bt, L, N] (fp32), and dD, dz, ddelta_bias, dh0 for the
-    optional inputs that were given.
+    dh_last [Bt, Dm, N] fp32.  With ckpt (fp32 [Bt, Dm, ceil(L/16), N] from
+    selective_scan_fwd_ckpt over the same inputs) the call is
+    ssm_selective_scan_bwd_ckpt, which skips its own forward sweep.  Returns a
+    dict with du, ddelta (dtype of u), dA [Dm, N], dB, dC [Bt, L, N] (fp32),
+    and dD, dz, ddelta_bias, dh0 for the optional inputs that were given.
     """
     dt, dev, Bt, L, Dm, N = _s6_prepare(u, delta, A, B, C, D, z, delta_bias, h0, None)
-    _check_args(dev, ("dy", dy, (Bt, L, Dm), dt), ("dh_last", dh_last, (Bt, Dm, N), _F32))
+    _check_args(dev, ("dy", dy, (Bt, L, Dm), dt), ("dh_last", dh_last, (Bt, Dm, N), _F32),
+                ("ckpt", ckpt, (Bt, Dm, (L + 15) // 16, N), _F32))
     lib = _native.load()
-    need = int(lib.ssm_selective_scan_bwd_workspace_bytes(Bt, L, Dm, N, _DT[dt]))
+    if ckpt is not None:
+        need = int(lib.ssm_selective_scan_bwd_ckpt_workspace_bytes(Bt, L, Dm, N, _DT[dt]))
+    else:
+        need = int(lib.ssm_selective_scan_bwd_workspace_bytes(Bt, L, Dm, N, _DT[dt]))
     workspace = _check_workspace(workspace, need, dev)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
@@ -304,13 +348,18 @@ def selective_scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B:
     if h0 is not None:
         out["dh0"] = torch.empty((Bt, Dm, N), dtype=_F32, device=dev)
     flags = _native.FLAG_DELTA_SOFTPLUS if delta_softplus else 0
-    rc = lib.ssm_selective_scan_bwd(
-        _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-        flags, _ptr(h0), _ptr(dy), _ptr(dh_last), _ptr(out["du"]), _ptr(out["ddelta"]),
-        _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out.get("dD")),
-        _ptr(out.get("dz")), _ptr(out.get("ddelta_bias")), _ptr(out.get("dh0")),
-        Bt, L, Dm, N, _DT[dt], _ptr(workspace), workspace.numel(), _stream_handle(dev))
-    _native.check(rc, "ssm_selective_scan_bwd")
+    grads = (_ptr(dy), _ptr(dh_last), _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]),
+             _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out.get("dD")), _ptr(out.get("dz")),
+             _ptr(out.get("ddelta_bias")), _ptr(out.get("dh0")))
+    tail = (Bt, L, Dm, N, _DT[dt], _ptr(workspace), workspace.numel(), _stream_handle(dev))
+    head = (_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            flags, _ptr(h0))
+    if ckpt is not None:
+        rc = lib.ssm_selective_scan_bwd_ckpt(*head, _ptr(ckpt), *grads, *tail)
+        _native.check(rc, "ssm_selective_scan_bwd_ckpt")
+    else:
+        rc = lib.ssm_selective_scan_bwd(*head, *grads, *tail)
+        _native.check(rc, "ssm_selective_scan_bwd")
     return out
 
 

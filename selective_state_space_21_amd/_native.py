@@ -51,6 +51,12 @@ SIGNATURES = {
                                _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i, _vp, _sz, _vp]),
     "ssm_selective_scan_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i]),
     "ssm_selective_scan_bwd": (_i, [_vp] * 21 + [_i64, _i64, _i64, _i64, _i, _vp, _sz, _vp]),
+    "ssm_selective_scan_ckpt_bytes": (_sz, [_i64, _i64, _i64, _i64, _i]),
+    "ssm_selective_scan_fwd_ckpt": (_i, [_vp] * 8 + [_u] + [_vp] * 4 +
+                                    [_i64, _i64, _i64, _i64, _i, _vp, _sz, _vp]),
+    "ssm_selective_scan_bwd_ckpt_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i]),
+    "ssm_selective_scan_bwd_ckpt": (_i, [_vp] * 8 + [_u] + [_vp] * 13 +
+                                    [_i64, _i64, _i64, _i64, _i, _vp, _sz, _vp]),
     "ssm_causal_conv1d_silu": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _vp, _i64, _i64, _i64, _i64,
                                     _i, _vp]),
     "ssm_selective_state_update": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _u, _vp,

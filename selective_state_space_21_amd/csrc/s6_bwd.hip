@@ -674,11 +674,16 @@ __global__ __launch_bounds__(256) void s6_bwd_reduce(S6BwdArgs p) {
 }
 
 template <typename T, bool VEC>
-void launch_sweeps(const S6BwdArgs& a, hipStream_t stream) {
+void launch_ckpt_sweep(const S6BwdArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)((a.D + kChans - 1) / kChans), (unsigned)a.B);
-    const bool sp = (a.flags & SSM_FLAG_DELTA_SOFTPLUS) != 0;
-    if (sp) s6_bwd_ckpt<T, true, VEC><<<grid, kThreads, 0, stream>>>(a);
+    if (a.flags & SSM_FLAG_DELTA_SOFTPLUS) s6_bwd_ckpt<T, true, VEC><<<grid, kThreads, 0, stream>>>(a);
     else s6_bwd_ckpt<T, false, VEC><<<grid, kThreads, 0, stream>>>(a);
+}
+
+template <typename T, bool VEC>
+void launch_sweeps(const S6BwdArgs& a, hipStream_t stream) {
+    const bool sp = (a.flags & SSM_FLAG_DELTA_SOFTPLUS) != 0;
+    if (a.own_ckpt) launch_ckpt_sweep<T, VEC>(a, stream);
     const dim3 mgrid((unsigned)((a.D + kMainChans - 1) / kMainChans), (unsigned)a.B);
     const bool hz = a.z != nullptr;
     if (hz && sp) s6_bwd_main<T, true, true, VEC><<<mgrid, kMainThreads, 0, stream>>>(a);
@@ -701,6 +706,17 @@ hipError_t launch_t(const S6BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_s6_bwd(const S6BwdArgs& a, hipStream_t stream) {
     return a.bf16 ? launch_t<uint16_t>(a, stream) : launch_t<float>(a, stream);
+}
+
+hipError_t launch_s6_bwd_ckpt(const S6BwdArgs& a, hipStream_t stream) {
+    if (a.bf16) {
+        if ((a.D * 2) % 16 == 0) launch_ckpt_sweep<uint16_t, true>(a, stream);
+        else launch_ckpt_sweep<uint16_t, false>(a, stream);
+    } else {
+        if ((a.D * 4) % 16 == 0) launch_ckpt_sweep<float, true>(a, stream);
+        else launch_ckpt_sweep<float, false>(a, stream);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace ssm

@@ -522,7 +522,7 @@ static_assert(kWave == plan::kWave && kMaxSegments == plan::kMaxSegments &&
 static_assert(plan::kFixChunk % (lanes::kTile * lanes::kSuper) == 0,
               "fix-up chunks are whole super-tiles of the segmented scan");
 
-template <typename T, bool HAS_Z, bool SOFTPLUS, bool CONV, bool SEG>
+template <typename T, bool HAS_Z, bool SOFTPLUS, bool CONV, bool SEG, bool CKPT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
               const T* __restrict__ z_, const T* __restrict__ Bm_, const T* __restrict__ Cm_,
@@ -569,6 +569,15 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
     // state is added to y afterwards, by the fix-up pass)
     float h = (s == 0 && p.h0) ? p.h0[(b * D + d) * 16 + n] : 0.0f;
     float dt_sum = 0.0f;                  // segments: this lane's share of the segment's sum of dt
+    // CKPT (one pass, no convolution): the state entering every 16-token tile
+    // for the backward pass, one 4-byte store per lane and tile, through a
+    // buffer resource over the workgroup's 16 channels; a tile past the row's
+    // end stores at an offset past the resource, which is dropped
+    static_assert(!CKPT || (!SEG && !CONV), "checkpoints are written by the one-pass scan");
+    const int64_t nck = CKPT ? p.ckpt_blocks : 0;
+    const auto rck = make_rsrc(CKPT ? p.ckpt + (b * D + grp * kChans) * nck * 16 : nullptr,
+                               CKPT ? (uint32_t)(kChans * nck * 64) : 0u);
+    const uint32_t ck_lane = CKPT ? (uint32_t)((chan * nck * 16 + n) * 4) : 0u;
     // buffer resources over this row's tokens: loads past the row's end read
     // zero, stores there are dropped (the planner keeps offsets in 32 bits)
     const int64_t rowoff = b * p.L * D;
@@ -671,6 +680,11 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
 #pragma unroll
         for (int i = 0; i < kSuper; ++i) {
             const int tl = kTile * i + n;   // this lane's token within the super-tile
+            if constexpr (CKPT) {
+                uint32_t off = ck_lane + (uint32_t)(((st0 - t0) / kTile + i) * 64);
+                if constexpr (kTail) off = st0 + kTile * i < t1 ? off : 0x80000000u;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(h), rck, (int)off, 0, 0);
+            }
             // past the row's end (TAIL) dt = 0 leaves h unchanged; the step is
             // masked rather than branched on, so no branch splits the
             // super-tile into one basic block per tile (which kept the
@@ -1337,7 +1351,10 @@ hipError_t launch_lanes(const S6Args& a, hipStream_t stream) {
     // segments: 64-token super-tiles (half the LDS, 4 wavefronts per SIMD)
 #define SSM_LANES(Z_, SP_, CV_)                                                                   \
     do {                                                                                          \
-        if (a.S > 1)                                                                              \
+        if (!(CV_) && a.ckpt && a.S == 1)                                                         \
+            hipLaunchKernelGGL((s6_lanes<T, Z_, SP_, false, false, true>), grid, block, 0,        \
+                               stream, a, U, Dl, Z, Bp, Cp, Y);                                   \
+        else if (a.S > 1)                                                                         \
             hipLaunchKernelGGL((s6_lanes<T, Z_, SP_, CV_, true>), grid, block, 0,                 \
                                stream, a, U, Dl, Z, Bp, Cp, Y);                                   \
         else                                                                                      \

@@ -112,28 +112,29 @@ void s6_carve(S6Args& a, void* ws) {
 }
 
 
-size_t s6_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N) {
+namespace {
+int64_t al256(int64_t bytes) { return (bytes + 255) / 256 * 256; }
+}  // namespace
+
+size_t s6_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, bool own_ckpt) {
     const int64_t nblk = (L + kBwdTile - 1) / kBwdTile;
     const int64_t G = (D + kBwdChans - 1) / kBwdChans;
-    auto al = [](int64_t bytes) { return (bytes + 255) / 256 * 256; };
-    return (size_t)(al(B * D * nblk * N * 4) + al(2 * G * B * L * N * 4) + al(B * D * N * 4) +
-                    2 * al(B * D * 4));
+    const int64_t parts = al256(2 * G * B * L * N * 4) + al256(B * D * N * 4) + 2 * al256(B * D * 4);
+    return (size_t)(parts + (own_ckpt ? al256(B * D * nblk * N * 4) : 0));
 }
 
 void s6_bwd_carve(S6BwdArgs& a, void* ws) {
-    const int64_t nblk = (a.L + kBwdTile - 1) / kBwdTile;
     const int64_t G = (a.D + kBwdChans - 1) / kBwdChans;
-    auto al = [](int64_t bytes) { return (bytes + 255) / 256 * 256; };
     char* p = static_cast<char*>(ws);
-    a.ckpt = reinterpret_cast<float*>(p);
-    p += al(a.B * a.D * nblk * a.N * 4);
     a.part_bc = reinterpret_cast<float*>(p);
-    p += al(2 * G * a.B * a.L * a.N * 4);
+    p += al256(2 * G * a.B * a.L * a.N * 4);
     a.part_dA = reinterpret_cast<float*>(p);
-    p += al(a.B * a.D * a.N * 4);
+    p += al256(a.B * a.D * a.N * 4);
     a.part_dD = reinterpret_cast<float*>(p);
-    p += al(a.B * a.D * 4);
+    p += al256(a.B * a.D * 4);
     a.part_db = reinterpret_cast<float*>(p);
+    p += al256(a.B * a.D * 4);
+    if (a.own_ckpt) a.ckpt = reinterpret_cast<float*>(p);
 }
 
 }  // namespace ssm

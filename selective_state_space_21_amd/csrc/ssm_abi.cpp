@@ -30,7 +30,14 @@ int s6_fwd_impl(const void* u, const void* delta, const float* A, const void* Bm
                 const float* h0, void* y, float* h_last, const int32_t* seq_lens,
                 int64_t B, int64_t L, int64_t D, int64_t N, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream, void* const* events,
-                bool static_scratch = false);
+                bool static_scratch = false, float* ckpt = nullptr);
+
+int s6_bwd_impl(const void* u, const void* delta, const float* A, const void* Bm, const void* Cm,
+                const float* Dskip, const void* z, const float* delta_bias, unsigned flags,
+                const float* h0, const void* dy, const float* dh_last, void* du, void* ddelta,
+                float* dA, float* dB, float* dC, float* dDskip, void* dz, float* ddelta_bias,
+                float* dh0, const float* ckpt, int64_t B, int64_t L, int64_t D, int64_t N,
+                int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 int s6_check_sizes(int64_t B, int64_t L, int64_t D, int64_t N, int dtype) {
     if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_BAD_DTYPE;
@@ -165,6 +172,28 @@ int ssm_selective_scan_fwd_timed(const void* u, const void* delta, const float* 
                        B, L, D, N, dtype, workspace, workspace_bytes, stream, events);
 }
 
+size_t ssm_selective_scan_ckpt_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int dtype) {
+    if (s6_bwd_check_sizes(B, L, D, N, dtype) != SSM_OK) return 0;
+    return (size_t)(B * D * ((L + 15) / 16) * N) * sizeof(float);
+}
+
+int ssm_selective_scan_fwd_ckpt(const void* u, const void* delta, const float* A,
+                                const void* Bm, const void* Cm, const float* Dskip,
+                                const void* z, const float* delta_bias, unsigned flags,
+                                const float* h0, void* y, float* h_last, float* ckpt,
+                                int64_t B, int64_t L, int64_t D, int64_t N, int dtype,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    // the sizes and flags the backward takes
+    const int rc = s6_bwd_check_sizes(B, L, D, N, dtype);
+    if (rc != SSM_OK) return rc;
+    if (flags & ~(unsigned)SSM_FLAG_DELTA_SOFTPLUS) return SSM_ERR_UNSUPPORTED;
+    if (L > 0 && !ckpt) return SSM_ERR_NULL_ARG;
+    if (ckpt && !aligned(ckpt, 16)) return SSM_ERR_MISALIGNED;
+    return s6_fwd_impl(u, delta, A, Bm, Cm, Dskip, z, delta_bias, flags, h0, y, h_last, nullptr,
+                       B, L, D, N, dtype, workspace, workspace_bytes, stream, nullptr, false,
+                       L > 0 ? ckpt : nullptr);
+}
+
 }  // extern "C"
 
 namespace {
@@ -174,7 +203,7 @@ int s6_fwd_impl(const void* u, const void* delta, const float* A, const void* Bm
                 const float* h0, void* y, float* h_last, const int32_t* seq_lens,
                 int64_t B, int64_t L, int64_t D, int64_t N, int dtype,
                 void* workspace, size_t workspace_bytes, void* stream, void* const* events,
-                bool static_scratch) {
+                bool static_scratch, float* ckpt) {
     int rc = s6_check_sizes(B, L, D, N, dtype);
     if (rc != SSM_OK) return rc;
     if (flags & ~(unsigned)(SSM_FLAG_DELTA_SOFTPLUS | SSM_FLAG_ZOH)) return SSM_ERR_UNSUPPORTED;
@@ -209,7 +238,21 @@ int s6_fwd_impl(const void* u, const void* delta, const float* A, const void* Bm
     a.events = reinterpret_cast<hipEvent_t const*>(events);
     a.seq_lens = seq_lens;
     ssm::s6_carve(a, workspace);
-    const hipError_t e = ssm::launch_s6(a, static_cast<hipStream_t>(stream));
+    // checkpoints for the backward: written by the one-pass state-per-lane
+    // scan itself where it runs (its per-channel run of checkpoints addressed
+    // with 32-bit offsets), else by the backward's forward sweep afterwards
+    const int64_t nck = (L + ssm::plan::kBwdTile - 1) / ssm::plan::kBwdTile;
+    const bool fused = ckpt && a.lanes && a.S == 1 && ssm::plan::kLanesChans * nck * 64 < (int64_t)1 << 31;
+    a.ckpt = fused ? ckpt : nullptr;
+    a.ckpt_blocks = nck;
+    hipError_t e = ssm::launch_s6(a, static_cast<hipStream_t>(stream));
+    if (e == hipSuccess && ckpt && !fused && L > 0) {
+        ssm::S6BwdArgs c{};
+        c.u = u; c.delta = delta; c.A = A; c.Bm = Bm; c.delta_bias = delta_bias; c.h0 = h0;
+        c.B = B; c.L = L; c.D = D; c.N = N; c.flags = flags; c.bf16 = dtype == SSM_BF16;
+        c.ckpt = ckpt;
+        e = ssm::launch_s6_bwd_ckpt(c, static_cast<hipStream_t>(stream));
+    }
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
@@ -322,7 +365,7 @@ int ssm_selective_state_update(float* state, const void* u, const void* delta, c
 size_t ssm_selective_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
                                               int dtype) {
     if (s6_bwd_check_sizes(B, L, D, N, dtype) != SSM_OK) return 0;
-    return ssm::s6_bwd_workspace_bytes(B, L, D, N);
+    return ssm::s6_bwd_workspace_bytes(B, L, D, N, true);
 }
 
 int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* Bm,
@@ -333,31 +376,30 @@ int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, con
                            float* ddelta_bias, float* dh0, int64_t B, int64_t L, int64_t D,
                            int64_t N, int dtype, void* workspace, size_t workspace_bytes,
                            void* stream) {
-    int rc = s6_bwd_check_sizes(B, L, D, N, dtype);
-    if (rc != SSM_OK) return rc;
-    if (flags & ~(unsigned)SSM_FLAG_DELTA_SOFTPLUS) return SSM_ERR_UNSUPPORTED;
-    if (!A || !dA) return SSM_ERR_NULL_ARG;
-    if (L > 0 && (!u || !delta || !Bm || !Cm || !dy || !du || !ddelta || !dB || !dC))
-        return SSM_ERR_NULL_ARG;
-    if (L > 0 && z && !dz) return SSM_ERR_NULL_ARG;
-    const void* big[] = {u, delta, Bm, Cm, z, dy, du, ddelta, dB, dC, dz};
-    for (const void* p : big)
-        if (p && !aligned(p, 16)) return SSM_ERR_MISALIGNED;
-    const void* vec[] = {A, Dskip, delta_bias, h0, dh_last, dA, dDskip, ddelta_bias, dh0};
-    for (const void* p : vec)
-        if (p && !aligned(p, 4)) return SSM_ERR_MISALIGNED;
-    const size_t need = ssm::s6_bwd_workspace_bytes(B, L, D, N);
-    if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
-    if (!aligned(workspace, 256)) return SSM_ERR_MISALIGNED;
-    ssm::S6BwdArgs a{};
-    a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip;
-    a.z = L > 0 ? z : nullptr; a.delta_bias = delta_bias; a.h0 = h0; a.dy = dy;
-    a.dh_last = dh_last; a.du = du; a.ddelta = ddelta; a.dA = dA; a.dB = dB; a.dC = dC;
-    a.dDskip = dDskip; a.dz = dz; a.ddelta_bias = ddelta_bias; a.dh0 = dh0;
-    a.B = B; a.L = L; a.D = D; a.N = N; a.flags = flags; a.bf16 = dtype == SSM_BF16;
-    ssm::s6_bwd_carve(a, workspace);
-    const hipError_t e = ssm::launch_s6_bwd(a, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+    return s6_bwd_impl(u, delta, A, Bm, Cm, Dskip, z, delta_bias, flags, h0, dy, dh_last, du,
+                       ddelta, dA, dB, dC, dDskip, dz, ddelta_bias, dh0, nullptr, B, L, D, N,
+                       dtype, workspace, workspace_bytes, stream);
+}
+
+size_t ssm_selective_scan_bwd_ckpt_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
+                                                   int dtype) {
+    if (s6_bwd_check_sizes(B, L, D, N, dtype) != SSM_OK) return 0;
+    return ssm::s6_bwd_workspace_bytes(B, L, D, N, false);
+}
+
+int ssm_selective_scan_bwd_ckpt(const void* u, const void* delta, const float* A, const void* Bm,
+                                const void* Cm, const float* Dskip, const void* z,
+                                const float* delta_bias, unsigned flags, const float* h0,
+                                const float* ckpt, const void* dy, const float* dh_last,
+                                void* du, void* ddelta, float* dA, float* dB, float* dC,
+                                float* dDskip, void* dz, float* ddelta_bias, float* dh0,
+                                int64_t B, int64_t L, int64_t D, int64_t N, int dtype,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    if (L > 0 && !ckpt) return SSM_ERR_NULL_ARG;
+    if (ckpt && !aligned(ckpt, 16)) return SSM_ERR_MISALIGNED;
+    return s6_bwd_impl(u, delta, A, Bm, Cm, Dskip, z, delta_bias, flags, h0, dy, dh_last, du,
+                       ddelta, dA, dB, dC, dDskip, dz, ddelta_bias, dh0, L > 0 ? ckpt : nullptr,
+                       B, L, D, N, dtype, workspace, workspace_bytes, stream);
 }
 
 int ssm_causal_conv1d_silu(const void* x, const float* weight, const float* bias,
@@ -388,3 +430,43 @@ int ssm_causal_conv1d_silu(const void* x, const float* weight, const float* bias
 }
 
 }  // extern "C"
+
+namespace {
+
+int s6_bwd_impl(const void* u, const void* delta, const float* A, const void* Bm, const void* Cm,
+                const float* Dskip, const void* z, const float* delta_bias, unsigned flags,
+                const float* h0, const void* dy, const float* dh_last, void* du, void* ddelta,
+                float* dA, float* dB, float* dC, float* dDskip, void* dz, float* ddelta_bias,
+                float* dh0, const float* ckpt, int64_t B, int64_t L, int64_t D, int64_t N,
+                int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = s6_bwd_check_sizes(B, L, D, N, dtype);
+    if (rc != SSM_OK) return rc;
+    if (flags & ~(unsigned)SSM_FLAG_DELTA_SOFTPLUS) return SSM_ERR_UNSUPPORTED;
+    if (!A || !dA) return SSM_ERR_NULL_ARG;
+    if (L > 0 && (!u || !delta || !Bm || !Cm || !dy || !du || !ddelta || !dB || !dC))
+        return SSM_ERR_NULL_ARG;
+    if (L > 0 && z && !dz) return SSM_ERR_NULL_ARG;
+    const void* big[] = {u, delta, Bm, Cm, z, dy, du, ddelta, dB, dC, dz};
+    for (const void* p : big)
+        if (p && !aligned(p, 16)) return SSM_ERR_MISALIGNED;
+    const void* vec[] = {A, Dskip, delta_bias, h0, dh_last, dA, dDskip, ddelta_bias, dh0};
+    for (const void* p : vec)
+        if (p && !aligned(p, 4)) return SSM_ERR_MISALIGNED;
+    const bool own = ckpt == nullptr;
+    const size_t need = ssm::s6_bwd_workspace_bytes(B, L, D, N, own);
+    if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return SSM_ERR_MISALIGNED;
+    ssm::S6BwdArgs a{};
+    a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip;
+    a.z = L > 0 ? z : nullptr; a.delta_bias = delta_bias; a.h0 = h0; a.dy = dy;
+    a.dh_last = dh_last; a.du = du; a.ddelta = ddelta; a.dA = dA; a.dB = dB; a.dC = dC;
+    a.dDskip = dDskip; a.dz = dz; a.ddelta_bias = ddelta_bias; a.dh0 = dh0;
+    a.B = B; a.L = L; a.D = D; a.N = N; a.flags = flags; a.bf16 = dtype == SSM_BF16;
+    a.own_ckpt = own;
+    a.ckpt = const_cast<float*>(ckpt);
+    ssm::s6_bwd_carve(a, workspace);
+    const hipError_t e = ssm::launch_s6_bwd(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // namespace

@@ -44,6 +44,10 @@ struct S6Args {
     int64_t conv_K;
     const int32_t* seq_lens;    // [B] tokens per batch row (device), or NULL: all L
     bool lanes;                 // state-per-lane kernel for N = 16 without ZOH
+    // the state entering every 16-token tile, [B, D, ckpt_blocks, 16] fp32,
+    // written by the one-pass state-per-lane scan (NULL: not written)
+    float* ckpt;
+    int64_t ckpt_blocks;        // ceil(L / 16)
 };
 
 struct S6Plan {
@@ -149,17 +153,26 @@ struct S6BwdArgs {
     int64_t B, L, D, N;
     unsigned flags;
     int bf16;
+    // the state before each 16-token tile, [B, D, ceil(L/16), N]: carved
+    // from the workspace and written by the call's own forward sweep, or
+    // given by the caller (own_ckpt false: the sweep is skipped)
+    float* ckpt;
+    bool own_ckpt;
     // workspace, carved by s6_bwd_carve
-    float* ckpt;       // [B, D, ceil(L/16), N] state before each 16-token tile
     float* part_bc;    // [2][ceil(D/16)][B, L, N] per-channel-group dB, dC
     float* part_dA;    // [B, D, N]
     float* part_dD;    // [B, D]
     float* part_db;    // [B, D]
 };
 
-size_t s6_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N);
+// Workspace of a backward call: the partial sums, then (own_ckpt) the
+// checkpoints.
+size_t s6_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, bool own_ckpt);
 void s6_bwd_carve(S6BwdArgs& a, void* workspace);
 hipError_t launch_s6_bwd(const S6BwdArgs& a, hipStream_t stream);
+// The backward's forward sweep alone: fills a.ckpt (reads u, delta, A, Bm,
+// delta_bias, h0, flags and the sizes).
+hipError_t launch_s6_bwd_ckpt(const S6BwdArgs& a, hipStream_t stream);
 
 // Causal depthwise conv1d (+ SiLU) over tokens.
 struct ConvArgs {

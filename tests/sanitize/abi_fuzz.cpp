@@ -79,6 +79,8 @@ int main(int argc, char** argv) {
             ++g_failures;
         }
         (void)ssm_selective_scan_bwd_workspace_bytes(B, L, D, N, dtype);
+        (void)ssm_selective_scan_bwd_ckpt_workspace_bytes(B, L, D, N, dtype);
+        (void)ssm_selective_scan_ckpt_bytes(B, L, D, N, dtype);
         void* wsp = (next() & 1) ? kOk : nullptr;
         const size_t wsb = (next() & 1) ? ws : (size_t)next();
         // forward scan family: y misaligned
@@ -105,6 +107,15 @@ int main(int argc, char** argv) {
                             kOk, kOk, kOkF, kOk, kOk, nullptr, nullptr, nullptr, flags, nullptr,
                             kOk, nullptr, kMis, kOk, kOkF, kOkF, kOkF, nullptr, nullptr, nullptr,
                             nullptr, B, L, D, N, dtype, wsp, wsb, nullptr), B, L, D, N);
+        expect_rejected("fwd_ckpt", ssm_selective_scan_fwd_ckpt(
+                            kOk, kOk, kOkF, kOk, kOk, nullptr, nullptr, nullptr, flags, nullptr,
+                            kMis, nullptr, reinterpret_cast<float*>(kOk), B, L, D, N, dtype, wsp,
+                            wsb, nullptr), B, L, D, N);
+        expect_rejected("bwd_ckpt", ssm_selective_scan_bwd_ckpt(
+                            kOk, kOk, kOkF, kOk, kOk, nullptr, nullptr, nullptr, flags, nullptr,
+                            reinterpret_cast<const float*>(kOk), kOk, nullptr, kMis, kOk, kOkF,
+                            kOkF, kOkF, nullptr, nullptr, nullptr, nullptr, B, L, D, N, dtype, wsp,
+                            wsb, nullptr), B, L, D, N);
         expect_rejected("state_update", ssm_selective_state_update(
                             kOkF, kOk, kOk, kOkF, kOk, kOk, nullptr, nullptr, nullptr, flags,
                             kMis, B, D, N, dtype, nullptr), B, D, N, 0);

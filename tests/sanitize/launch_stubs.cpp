@@ -19,5 +19,6 @@ hipError_t noalloc_scratch(void**) { reached("noalloc_scratch"); }
 hipError_t launch_ssd(const SSDArgs&, hipStream_t) { reached("launch_ssd"); }
 hipError_t launch_s6_step(const StepArgs&, hipStream_t) { reached("launch_s6_step"); }
 hipError_t launch_s6_bwd(const S6BwdArgs&, hipStream_t) { reached("launch_s6_bwd"); }
+hipError_t launch_s6_bwd_ckpt(const S6BwdArgs&, hipStream_t) { reached("launch_s6_bwd_ckpt"); }
 hipError_t launch_conv1d(const ConvArgs&, hipStream_t) { reached("launch_conv1d"); }
 }  // namespace ssm

@@ -266,6 +266,62 @@ def test_bwd_validation_errors(lib):
     assert lib.ssm_selective_scan_bwd_workspace_bytes(8, 2048, 1536, 17, 1) == 0
 
 
+def fwd_ckpt(lib, **kw):
+    a = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None,
+             flags=1, h0=None, y=FAKE, h_last=None, ck=FAKE, Bt=2, L=64, Dm=128, N=16, dtype=1,
+             ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.ssm_selective_scan_fwd_ckpt(
+        a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["flags"],
+        a["h0"], a["y"], a["h_last"], a["ck"], a["Bt"], a["L"], a["Dm"], a["N"], a["dtype"],
+        a["ws"], a["ws_bytes"], a["stream"])
+
+
+def bwd_ckpt(lib, **kw):
+    a = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, flags=1,
+             h0=None, ck=FAKE, dy=FAKE, dh=None, du=FAKE, dd=FAKE, dA=FAKE, dB=FAKE, dC=FAKE,
+             dD=None, dz=None, dbias=None, dh0=None, Bt=2, L=64, Dm=128, N=16, dtype=1,
+             ws=0x100000, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return lib.ssm_selective_scan_bwd_ckpt(
+        a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["flags"],
+        a["h0"], a["ck"], a["dy"], a["dh"], a["du"], a["dd"], a["dA"], a["dB"], a["dC"], a["dD"],
+        a["dz"], a["dbias"], a["dh0"], a["Bt"], a["L"], a["Dm"], a["N"], a["dtype"], a["ws"],
+        a["ws_bytes"], a["stream"])
+
+
+def test_ckpt_validation_errors(lib):
+    # the forward for training takes the backward's sizes and flags
+    assert fwd_ckpt(lib, ck=None) == 1
+    assert fwd_ckpt(lib, y=None) == 1
+    assert fwd_ckpt(lib, Bt=0) == 2
+    assert fwd_ckpt(lib, dtype=7) == 3
+    assert fwd_ckpt(lib, N=17) == 4
+    assert fwd_ckpt(lib, flags=3) == 4          # ZOH
+    assert fwd_ckpt(lib, ck=FAKE + 4) == 5
+    assert fwd_ckpt(lib, y=FAKE_MIS) == 5
+    assert fwd_ckpt(lib, ws=None) == 6
+    assert bwd_ckpt(lib, ck=None) == 1
+    assert bwd_ckpt(lib, dy=None) == 1
+    assert bwd_ckpt(lib, N=17) == 4
+    assert bwd_ckpt(lib, flags=2) == 4
+    assert bwd_ckpt(lib, ck=FAKE + 8) == 5
+    assert bwd_ckpt(lib, du=FAKE_MIS) == 5
+    assert bwd_ckpt(lib, ws_bytes=16) == 6
+
+
+def test_ckpt_sizes(lib):
+    for (Bt, L, Dm, N) in [(8, 2048, 1536, 16), (3, 513, 40, 5), (1, 1, 16, 1), (2, 0, 16, 16)]:
+        nck = (L + 15) // 16
+        assert lib.ssm_selective_scan_ckpt_bytes(Bt, L, Dm, N, 1) == Bt * Dm * nck * N * 4
+        full = lib.ssm_selective_scan_bwd_workspace_bytes(Bt, L, Dm, N, 1)
+        part = lib.ssm_selective_scan_bwd_ckpt_workspace_bytes(Bt, L, Dm, N, 1)
+        # the checkpoints are the last region of the self-contained call's workspace
+        assert full - part == (Bt * Dm * nck * N * 4 + 255) // 256 * 256
+    assert lib.ssm_selective_scan_ckpt_bytes(8, 2048, 1536, 17, 1) == 0
+    assert lib.ssm_selective_scan_bwd_ckpt_workspace_bytes(8, 2048, 1536, 17, 1) == 0
+
+
 def conv(lib, **kw):
     a = dict(x=FAKE, w=FAKE, b=None, si=None, silu=1, u=FAKE, so=None, Bt=2, L=64, Dm=128, K=4,
              dtype=1, stream=None)
