@@ -172,3 +172,35 @@ def test_full_size_training_pair():
     assert torch.equal(y, y0)
     for k in a:
         assert torch.equal(a[k], b[k]), k
+
+
+def _draw(i):
+    r = np.random.default_rng(4000 + i)
+    return dict(Bt=int(r.integers(1, 5)), L=int(r.integers(1, 1500)), Dm=16 * int(r.integers(1, 9)),
+                dtype=str(r.choice(["f32", "bf16"])), extras=bool(r.random() < 0.6),
+                softplus=bool(r.random() < 0.8), seed=i)
+
+
+RANDOM = [_draw(i) for i in range(16)]
+
+
+@pytest.mark.parametrize("c", RANDOM, ids=lambda c: "B{Bt}L{L}D{Dm}{dtype}".format(**c))
+def test_random_fused_training_pair(c, monkeypatch):
+    # one segment forced, so the state-per-lane scan stores the checkpoints:
+    # they must equal the sweep's, and the pair must reproduce the plain
+    # forward and the self-contained backward bit for bit
+    inp = _inputs(c["Bt"], c["L"], c["Dm"], 16, c["dtype"], extras=c["extras"],
+                  softplus=c["softplus"], seed=c["seed"])
+    d = to_dev(inp)
+    _env(monkeypatch, ONE)
+    y0, h0l = _fwd(d, False)
+    y, hl, ck = _fwd(d, True)
+    got = _bwd(d, ckpt=ck)
+    ref = _bwd(d)
+    _env(monkeypatch, {"SSM_S6_LANES": "0"})
+    _, _, swept = _fwd(d, True)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0) and torch.equal(hl, h0l)
+    assert torch.equal(ck, swept)
+    for k in ref:
+        assert torch.equal(got[k], ref[k]), k
