@@ -255,6 +255,22 @@ int ssm_ssd_chunk_fwd(const void* X, const void* delta, const float* A,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Variable-length batch for the SSD form, as ssm_selective_scan_fwd_varlen
+ * for the scan: row b runs only its first seq_lens[b] tokens (seq_lens:
+ * device int32 [B], values clamped to [0, L]) of the [B, L, ...] layout
+ * right-padded to the longest; Y at t >= seq_lens[b] is left untouched, the
+ * padding is never read, and h_last is the state after the row's last token.
+ * Otherwise as ssm_ssd_chunk_fwd.
+ */
+int ssm_ssd_chunk_fwd_varlen(const void* X, const void* delta, const float* A,
+                             const void* Bm, const void* Cm, const float* Dskip,
+                             const void* z, const float* delta_bias, unsigned flags,
+                             const float* h0, void* Y, float* h_last, const int32_t* seq_lens,
+                             int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                             int64_t N, int64_t chunk, int dtype,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * ---------------------------------------------------------------- S6 backward
  * Gradients of the selective scan (the operation of ssm_selective_scan_fwd,
  * Euler input term) for L = sum(dy * y) + sum(dh_last * h_last).  The states

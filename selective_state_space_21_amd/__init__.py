@@ -241,12 +241,15 @@ def ssd_chunk_fwd(X: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torc
                   z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None,
                   delta_softplus: bool = True, h0: Optional[torch.Tensor] = None,
                   chunk: int = 256, return_last_state: bool = True,
-                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  seq_lens: Optional[torch.Tensor] = None
                   ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Mamba-2 SSD chunked forward (ssm_ssd_chunk_fwd).
 
     X, z: [Bt, L, H, P]; delta: [Bt, L, H]; A: [H] fp32; B, C: [Bt, L, G, N];
     D, delta_bias: [H] fp32; h0: [Bt, H, P, N] fp32.  Returns (Y, h_last).
+    seq_lens: optional int32 [Bt] -- row b runs its first seq_lens[b] tokens
+    (ssm_ssd_chunk_fwd_varlen); later positions of Y are left untouched.
     """
     dt = _act_dtype("X", X)
     if X.dim() != 4 or not isinstance(B, torch.Tensor) or B.dim() != 4:
@@ -258,18 +261,22 @@ def ssd_chunk_fwd(X: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torc
                 ("A", A, (H,), _F32), ("B", B, (Bt, L, G, N), dt), ("C", C, (Bt, L, G, N), dt),
                 ("z", z, (Bt, L, H, P), dt), ("D", D, (H,), _F32),
                 ("delta_bias", delta_bias, (H,), _F32), ("h0", h0, (Bt, H, P, N), _F32),
-                ("out", out, (Bt, L, H, P), dt))
+                ("out", out, (Bt, L, H, P), dt), ("seq_lens", seq_lens, (Bt,), torch.int32))
     lib = _native.load()
     ws_need = int(lib.ssm_ssd_chunk_workspace_bytes(Bt, L, H, P, G, N, chunk, _DT[dt]))
     workspace, ws_bytes = _workspace(workspace, ws_need, dev)
     Y = out if out is not None else torch.empty((Bt, L, H, P), dtype=dt, device=dev)
     h_last = torch.empty((Bt, H, P, N), dtype=_F32, device=dev) if return_last_state else None
     flags = _native.FLAG_DELTA_SOFTPLUS if delta_softplus else 0
-    rc = lib.ssm_ssd_chunk_fwd(
-        _ptr(X), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-        flags, _ptr(h0), _ptr(Y), _ptr(h_last), Bt, L, H, P, G, N, chunk, _DT[dt],
-        _ptr(workspace), ws_bytes, _stream_handle(dev))
-    _native.check(rc, "ssm_ssd_chunk_fwd")
+    head = (_ptr(X), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            flags, _ptr(h0), _ptr(Y), _ptr(h_last))
+    tail = (Bt, L, H, P, G, N, chunk, _DT[dt], _ptr(workspace), ws_bytes, _stream_handle(dev))
+    if seq_lens is not None:
+        rc = lib.ssm_ssd_chunk_fwd_varlen(*head, _ptr(seq_lens), *tail)
+        _native.check(rc, "ssm_ssd_chunk_fwd_varlen")
+    else:
+        rc = lib.ssm_ssd_chunk_fwd(*head, *tail)
+        _native.check(rc, "ssm_ssd_chunk_fwd")
     return Y, h_last
 
 

@@ -49,6 +49,9 @@ SIGNATURES = {
     "ssm_ssd_chunk_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64, _i64, _i]),
     "ssm_ssd_chunk_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _u, _vp, _vp, _vp,
                                _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i, _vp, _sz, _vp]),
+    "ssm_ssd_chunk_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _u, _vp, _vp, _vp,
+                                      _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i, _vp,
+                                      _sz, _vp]),
     "ssm_selective_scan_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i]),
     "ssm_selective_scan_bwd": (_i, [_vp] * 21 + [_i64, _i64, _i64, _i64, _i, _vp, _sz, _vp]),
     "ssm_selective_scan_ckpt_bytes": (_sz, [_i64, _i64, _i64, _i64, _i]),

@@ -186,6 +186,9 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
     const int64_t h = bh % p.H;
     const int64_t grp = h / (p.H / p.G);
     const int64_t L = p.L;
+    // tokens of this batch row: all L, or its own length in a variable-length
+    // batch (right-padded to L); the row's tensors keep their [L, ...] strides
+    const int64_t Lr = p.seq_lens ? min(max((int64_t)p.seq_lens[b], (int64_t)0), L) : L;
     const int64_t H = p.H;
     const int64_t G = p.G;
 
@@ -218,13 +221,13 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
         sm.H[pp * Lds::kHStride + nn] = bf(p.h0 ? p.h0[(bh * P + pbase + pp) * N + nn] : 0.0f);
     }
 
-    // ---- inputs through buffer resources based at batch row b: a read past
-    // the end of the sequence (chunk tail) returns zero, so no load is guarded
+    // ---- inputs through buffer resources over batch row b's Lr tokens: a
+    // read past them (chunk tail, padding) returns zero, so no load is guarded
     static_assert(TL::XGROUP <= kThreads, "one X group per thread at most");
-    const auto rX = make_rsrc(X + b * L * H * P, (uint32_t)(L * H * P * 2));
-    const auto rB = make_rsrc(Bg + b * L * G * N, (uint32_t)(L * G * N * 2));
-    const auto rC = make_rsrc(Cg + b * L * G * N, (uint32_t)(L * G * N * 2));
-    const auto rD = make_rsrc(Dl + b * L * H, (uint32_t)(L * H * 2));
+    const auto rX = make_rsrc(X + b * L * H * P, (uint32_t)(Lr * H * P * 2));
+    const auto rB = make_rsrc(Bg + b * L * G * N, (uint32_t)(Lr * G * N * 2));
+    const auto rC = make_rsrc(Cg + b * L * G * N, (uint32_t)(Lr * G * N * 2));
+    const auto rD = make_rsrc(Dl + b * L * H, (uint32_t)(Lr * H * 2));
     uint32_t dbits = 0;                  // step of this thread's token, bf16 bits
     uint4 bpre[TL::BPIECE];
     uint4 xpre[TL::XPIECE];
@@ -276,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
         }
     };
 
-    const int64_t nchunks = (L + Q - 1) / Q;
+    const int64_t nchunks = (Lr + Q - 1) / Q;
     if (nchunks > 0) {
         prefetch(0);
         prefetch_b(0, std::integral_constant<int, TL::BEARLY>{},
@@ -289,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
         load_c(ch, cop);
         // ---- 1. steps and in-chunk cumulative decay (log2 units)
         float dtv = 0.0f, a2 = 0.0f;
-        if (tid < Q && tc + tid < L) {              // past the end: no step, no decay
+        if (tid < Q && tc + tid < Lr) {             // past the end: no step, no decay
             const float x = bf16_bits_to_f32(dbits) + bias;
             dtv = softplus ? softplus_f(x) : x;
             a2 = dtv * A2;
@@ -363,7 +366,7 @@ __global__ __launch_bounds__(kThreads) void ssd_chunk_kernel(SSDArgs p) {
         auto store_tile = [&](int ti, const f32x4 (&yacc)[JP]) __attribute__((always_inline)) {
             const int tl = 16 * ti + c;
             const int64_t t = tc + tl;
-            if (t >= L) return;
+            if (t >= Lr) return;
 #pragma unroll
             for (int j = 0; j < JP; ++j) {
                 const int p0 = 16 * j + 4 * g;

@@ -39,6 +39,12 @@ int s6_bwd_impl(const void* u, const void* delta, const float* A, const void* Bm
                 float* dh0, const float* ckpt, int64_t B, int64_t L, int64_t D, int64_t N,
                 int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+int ssd_fwd_impl(const void* X, const void* delta, const float* A, const void* Bm, const void* Cm,
+                 const float* Dskip, const void* z, const float* delta_bias, unsigned flags,
+                 const float* h0, void* Y, float* h_last, const int32_t* seq_lens, int64_t B,
+                 int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int64_t chunk, int dtype,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
 int s6_check_sizes(int64_t B, int64_t L, int64_t D, int64_t N, int dtype) {
     if (dtype != SSM_F32 && dtype != SSM_BF16) return SSM_ERR_BAD_DTYPE;
     if (B < 1 || D < 1 || N < 1 || L < 0) return SSM_ERR_BAD_SHAPE;
@@ -315,26 +321,21 @@ int ssm_ssd_chunk_fwd(const void* X, const void* delta, const float* A,
                       int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
                       int64_t N, int64_t chunk, int dtype,
                       void* workspace, size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
-    int rc = ssd_check_sizes(B, L, H, P, G, N, chunk, dtype);
-    if (rc != SSM_OK) return rc;
-    if (flags & ~(unsigned)SSM_FLAG_DELTA_SOFTPLUS) return SSM_ERR_UNSUPPORTED;
-    if (!A) return SSM_ERR_NULL_ARG;
-    if (L > 0 && (!X || !delta || !Bm || !Cm || !Y)) return SSM_ERR_NULL_ARG;
-    const void* big[] = {X, delta, Bm, Cm, z, Y};
-    for (const void* p : big)
-        if (p && !aligned(p, 16)) return SSM_ERR_MISALIGNED;
-    const void* vec[] = {A, Dskip, delta_bias, h0, h_last};
-    for (const void* p : vec)
-        if (p && !aligned(p, 4)) return SSM_ERR_MISALIGNED;
-    ssm::SSDArgs a{};
-    a.X = X; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.z = z;
-    a.delta_bias = delta_bias; a.h0 = h0; a.Y = Y; a.h_last = h_last;
-    a.B = B; a.L = L; a.H = H; a.P = P; a.G = G; a.N = N; a.chunk = chunk; a.flags = flags;
-    const hipError_t e = ssm::launch_ssd(a, static_cast<hipStream_t>(stream));
-    if (e == hipErrorNotSupported) return SSM_ERR_UNSUPPORTED;
-    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+    return ssd_fwd_impl(X, delta, A, Bm, Cm, Dskip, z, delta_bias, flags, h0, Y, h_last, nullptr,
+                        B, L, H, P, G, N, chunk, dtype, workspace, workspace_bytes, stream);
+}
+
+int ssm_ssd_chunk_fwd_varlen(const void* X, const void* delta, const float* A,
+                             const void* Bm, const void* Cm, const float* Dskip,
+                             const void* z, const float* delta_bias, unsigned flags,
+                             const float* h0, void* Y, float* h_last, const int32_t* seq_lens,
+                             int64_t B, int64_t L, int64_t H, int64_t P, int64_t G,
+                             int64_t N, int64_t chunk, int dtype,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    if (!seq_lens) return SSM_ERR_NULL_ARG;
+    if (!aligned(seq_lens, 4)) return SSM_ERR_MISALIGNED;
+    return ssd_fwd_impl(X, delta, A, Bm, Cm, Dskip, z, delta_bias, flags, h0, Y, h_last, seq_lens,
+                        B, L, H, P, G, N, chunk, dtype, workspace, workspace_bytes, stream);
 }
 
 int ssm_selective_state_update(float* state, const void* u, const void* delta, const float* A,
@@ -466,6 +467,34 @@ int s6_bwd_impl(const void* u, const void* delta, const float* A, const void* Bm
     a.ckpt = const_cast<float*>(ckpt);
     ssm::s6_bwd_carve(a, workspace);
     const hipError_t e = ssm::launch_s6_bwd(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+int ssd_fwd_impl(const void* X, const void* delta, const float* A, const void* Bm, const void* Cm,
+                 const float* Dskip, const void* z, const float* delta_bias, unsigned flags,
+                 const float* h0, void* Y, float* h_last, const int32_t* seq_lens, int64_t B,
+                 int64_t L, int64_t H, int64_t P, int64_t G, int64_t N, int64_t chunk, int dtype,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    int rc = ssd_check_sizes(B, L, H, P, G, N, chunk, dtype);
+    if (rc != SSM_OK) return rc;
+    if (flags & ~(unsigned)SSM_FLAG_DELTA_SOFTPLUS) return SSM_ERR_UNSUPPORTED;
+    if (!A) return SSM_ERR_NULL_ARG;
+    if (L > 0 && (!X || !delta || !Bm || !Cm || !Y)) return SSM_ERR_NULL_ARG;
+    const void* big[] = {X, delta, Bm, Cm, z, Y};
+    for (const void* p : big)
+        if (p && !aligned(p, 16)) return SSM_ERR_MISALIGNED;
+    const void* vec[] = {A, Dskip, delta_bias, h0, h_last};
+    for (const void* p : vec)
+        if (p && !aligned(p, 4)) return SSM_ERR_MISALIGNED;
+    ssm::SSDArgs a{};
+    a.X = X; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.z = z;
+    a.delta_bias = delta_bias; a.h0 = h0; a.Y = Y; a.h_last = h_last;
+    a.B = B; a.L = L; a.H = H; a.P = P; a.G = G; a.N = N; a.chunk = chunk; a.flags = flags;
+    a.seq_lens = seq_lens;
+    const hipError_t e = ssm::launch_ssd(a, static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported) return SSM_ERR_UNSUPPORTED;
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

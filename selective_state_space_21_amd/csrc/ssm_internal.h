@@ -105,6 +105,7 @@ struct SSDArgs {
     float* h_last;
     int64_t B, L, H, P, G, N, chunk;
     unsigned flags;
+    const int32_t* seq_lens;    // [B] tokens per batch row (device), or NULL: all L
 };
 
 hipError_t launch_ssd(const SSDArgs& a, hipStream_t stream);

@@ -130,6 +130,10 @@ int main(int argc, char** argv) {
                                                  nullptr, flags & 1u, nullptr, kMis, nullptr, B,
                                                  L, H, P, G, N, chunk, dtype, nullptr, 0, nullptr),
                         B, L, H, P);
+        expect_rejected("ssd_varlen", ssm_ssd_chunk_fwd_varlen(
+                            kOk, kOk, kOkF, kOk, kOk, nullptr, nullptr, nullptr, flags & 1u,
+                            nullptr, kMis, nullptr, reinterpret_cast<const int32_t*>(kOk), B, L,
+                            H, P, G, N, chunk, dtype, nullptr, 0, nullptr), B, L, H, P);
     }
     if (g_failures) {
         fprintf(stderr, "%d unexpected results\n", g_failures);

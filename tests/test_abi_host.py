@@ -374,6 +374,20 @@ def test_varlen_validation_errors(lib):
     assert call(FAKE + 2) == 5
     assert call(FAKE, Bt=0) == 2
 
+    def ssd_call(sl, **kw):
+        a = dict(Bt=1, L=256, H=8, P=64, G=1, N=128, chunk=256, dtype=1, Y=FAKE)
+        a.update(kw)
+        return lib.ssm_ssd_chunk_fwd_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 1,
+                                            None, a["Y"], None, sl, a["Bt"], a["L"], a["H"],
+                                            a["P"], a["G"], a["N"], a["chunk"], a["dtype"], None,
+                                            0, None)
+    assert ssd_call(None) == 1
+    assert ssd_call(FAKE + 2) == 5
+    assert ssd_call(FAKE, Bt=0) == 2
+    assert ssd_call(FAKE, dtype=0) == 4          # fp32 storage: not implemented
+    assert ssd_call(FAKE, N=48) == 4
+    assert ssd_call(FAKE, Y=FAKE_MIS) == 5
+
 
 def test_python_wrapper_rejects_host_tensors():
     import torch

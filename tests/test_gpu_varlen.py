@@ -1,8 +1,8 @@
-"""GPU parity of the variable-length S6 scan (ssm_selective_scan_fwd_varlen):
-each batch row runs its own number of tokens; the reference is the oracle run
-on each row truncated to its length.  Bar as the forward (1e-5 fp32, 2e-2
-bf16); positions past a row's length are untouched (checked bit for bit
-against a sentinel)."""
+"""GPU parity of the variable-length S6 scan (ssm_selective_scan_fwd_varlen)
+and SSD form (ssm_ssd_chunk_fwd_varlen): each batch row runs its own number
+of tokens; the reference is the oracle run on each row truncated to its
+length.  Bar as the forward (1e-5 fp32, 2e-2 bf16); positions past a row's
+length are untouched (checked bit for bit against a sentinel)."""
 import numpy as np
 import pytest
 import torch
@@ -56,3 +56,58 @@ def test_varlen_full_lengths_equal_plain_call():
                                     seq_lens=torch.full((3,), 512, dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(h1, h2)
+
+
+# ---- SSD (ssm_ssd_chunk_fwd_varlen).  The padding of every input is NaN, so
+# a single read past a row's length would show in Y or h_last.
+def _ssd_case(lens, L, H, G, P, N, chunk, seed):
+    w = W.SSD_MAMBA2.scaled(B=len(lens), L=L, H=H, G=G, P=P, N=N, chunk=chunk)
+    inp = W.make_ssd_inputs(w, seed=seed)
+    g = torch.Generator().manual_seed(seed)
+    inp["D"] = 1.0 + 0.1 * torch.randn(H, generator=g)
+    inp["z"] = torch.randn(len(lens), L, H, P, generator=g).to(torch.bfloat16)
+    inp["delta_bias"] = torch.empty(H).uniform_(-1.0, 0.5, generator=g)
+    inp["h0"] = 0.3 * torch.randn(len(lens), H, P, N, generator=g)
+    padded = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    nan = float("nan")
+    for b, n in enumerate(lens):
+        for k in ("X", "delta", "B", "C", "z"):
+            padded[k][b, n:] = nan
+    return inp, padded
+
+
+@pytest.mark.parametrize("chunk,N", [(64, 128), (256, 128), (128, 64)])
+def test_ssd_varlen_parity(chunk, N):
+    lens = [700, 1, 0, 333, 1000, 256]
+    Bt, L, H, G, P = len(lens), 1000, 4, 2, 64
+    inp, padded = _ssd_case(lens, L, H, G, P, N, chunk, seed=chunk + N)
+    d = to_dev(padded)
+    sentinel = 3.0
+    Y = torch.full((Bt, L, H, P), sentinel, device="cuda").to(torch.bfloat16)
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    _, h = ssm.ssd_chunk_fwd(d["X"], d["delta"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
+                             delta_bias=d["delta_bias"], h0=d["h0"], chunk=chunk, out=Y,
+                             seq_lens=sl)
+    torch.cuda.synchronize()
+    Y = Y.float().cpu().numpy()
+    h = h.cpu().numpy()
+    assert np.all(np.isfinite(h))
+    for b, n in enumerate(lens):
+        cut = lambda t: None if t is None else t[b:b + 1, :n]
+        Yr, hr = oracle.ssd_fwd(cut(inp["X"]), cut(inp["delta"]), inp["A"], cut(inp["B"]),
+                                cut(inp["C"]), D=inp["D"], z=cut(inp["z"]),
+                                delta_bias=inp["delta_bias"], h0=inp["h0"][b:b + 1])
+        if n > 0:
+            assert normwise_err(Y[b:b + 1, :n], Yr) <= 2e-2, b
+        assert normwise_err(h[b:b + 1], hr) <= 2e-2, b
+        assert np.all(Y[b, n:] == sentinel), b
+
+
+def test_ssd_varlen_full_lengths_equal_plain_call():
+    w = W.SSD_MAMBA2.scaled(B=2, L=600, H=4)
+    d = to_dev(W.make_ssd_inputs(w, seed=5))
+    Y1, h1 = ssm.ssd_chunk_fwd(d["X"], d["delta"], d["A"], d["B"], d["C"], chunk=w.chunk)
+    Y2, h2 = ssm.ssd_chunk_fwd(d["X"], d["delta"], d["A"], d["B"], d["C"], chunk=w.chunk,
+                               seq_lens=torch.full((2,), 600, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2) and torch.equal(h1, h2)
