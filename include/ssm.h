@@ -308,6 +308,24 @@ int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, con
                            void* stream);
 
 /*
+ * Variable-length batch (the backward of ssm_selective_scan_fwd_varlen): row
+ * b has only its first seq_lens[b] tokens (device int32 [B], values clamped
+ * to [0, L]), dh_last is the gradient of the state after its last one, and
+ * the padding of the [B, L, ...] inputs is never read.  The gradients at
+ * t >= seq_lens[b] (du, ddelta, dz, dB, dC) are written as zeros.  Otherwise
+ * as ssm_selective_scan_bwd (same workspace query).
+ */
+int ssm_selective_scan_bwd_varlen(const void* u, const void* delta, const float* A,
+                                  const void* Bm, const void* Cm, const float* Dskip,
+                                  const void* z, const float* delta_bias, unsigned flags,
+                                  const float* h0, const void* dy, const float* dh_last, void* du,
+                                  void* ddelta, float* dA, float* dB, float* dC, float* dDskip,
+                                  void* dz, float* ddelta_bias, float* dh0,
+                                  const int32_t* seq_lens, int64_t B, int64_t L, int64_t D,
+                                  int64_t N, int dtype, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/*
  * -------------------------------------------- S6 forward and backward, training
  * A training step runs the forward and then the backward over the same
  * inputs; the backward above starts with a forward sweep of its own that

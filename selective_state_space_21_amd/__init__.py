@@ -321,19 +321,25 @@ def selective_scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B:
                        delta_bias: Optional[torch.Tensor] = None, delta_softplus: bool = True,
                        h0: Optional[torch.Tensor] = None, dh_last: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None,
-                       ckpt: Optional[torch.Tensor] = None) -> dict:
+                       ckpt: Optional[torch.Tensor] = None,
+                       seq_lens: Optional[torch.Tensor] = None) -> dict:
     """Gradients of the S6 scan (ssm_selective_scan_bwd), states recomputed.
 
     Inputs as selective_scan_fwd plus dy [Bt, L, Dm] (dtype of u) and
     dh_last [Bt, Dm, N] fp32.  With ckpt (fp32 [Bt, Dm, ceil(L/16), N] from
     selective_scan_fwd_ckpt over the same inputs) the call is
-    ssm_selective_scan_bwd_ckpt, which skips its own forward sweep.  Returns a
+    ssm_selective_scan_bwd_ckpt, which skips its own forward sweep.  With
+    seq_lens (int32 [Bt]) it is ssm_selective_scan_bwd_varlen: row b has its
+    first seq_lens[b] tokens, and the gradients past them are zeros.  Returns a
     dict with du, ddelta (dtype of u), dA [Dm, N], dB, dC [Bt, L, N] (fp32),
     and dD, dz, ddelta_bias, dh0 for the optional inputs that were given.
     """
     dt, dev, Bt, L, Dm, N = _s6_prepare(u, delta, A, B, C, D, z, delta_bias, h0, None)
     _check_args(dev, ("dy", dy, (Bt, L, Dm), dt), ("dh_last", dh_last, (Bt, Dm, N), _F32),
-                ("ckpt", ckpt, (Bt, Dm, (L + 15) // 16, N), _F32))
+                ("ckpt", ckpt, (Bt, Dm, (L + 15) // 16, N), _F32),
+                ("seq_lens", seq_lens, (Bt,), torch.int32))
+    if ckpt is not None and seq_lens is not None:
+        raise ValueError("the backward from checkpoints takes no seq_lens")
     lib = _native.load()
     if ckpt is not None:
         need = int(lib.ssm_selective_scan_bwd_ckpt_workspace_bytes(Bt, L, Dm, N, _DT[dt]))
@@ -364,6 +370,9 @@ def selective_scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B:
     if ckpt is not None:
         rc = lib.ssm_selective_scan_bwd_ckpt(*head, _ptr(ckpt), *grads, *tail)
         _native.check(rc, "ssm_selective_scan_bwd_ckpt")
+    elif seq_lens is not None:
+        rc = lib.ssm_selective_scan_bwd_varlen(*head, *grads, _ptr(seq_lens), *tail)
+        _native.check(rc, "ssm_selective_scan_bwd_varlen")
     else:
         rc = lib.ssm_selective_scan_bwd(*head, *grads, *tail)
         _native.check(rc, "ssm_selective_scan_bwd")

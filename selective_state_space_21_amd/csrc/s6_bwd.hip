@@ -61,6 +61,7 @@ static_assert(kTile == plan::kBwdTile && kMainChans == plan::kBwdChans,
 struct LaneId {
     int w, l, row, n;
     int64_t b, grp, d, dc; // grp: channel group; dc: d clamped into range for addressing
+    int64_t len;           // tokens of batch row b: L, or its own length (variable-length batch)
     bool chan_ok, ok;      // channel exists; channel and state exist
 };
 
@@ -85,6 +86,7 @@ __device__ __forceinline__ LaneId lane_id(const S6BwdArgs& p) {
     id.chan_ok = id.d < p.D;
     id.dc = id.chan_ok ? id.d : p.D - 1;
     id.ok = id.chan_ok && id.n < p.N;
+    id.len = p.seq_lens ? min(max((int64_t)p.seq_lens[id.b], (int64_t)0), p.L) : p.L;
     return id;
 }
 
@@ -127,15 +129,16 @@ __device__ __forceinline__ float sigmoid_f(float x) {
 
 // Per-channel inputs of token t0 + j, loaded by lane j of the row (raw, so
 // that they can be fetched a tile ahead).  Buffer resources over batch row b
-// make every load unconditional: tokens past L read as zero, so no branch
-// (and no wait at its join) separates a prefetch from the work it overlaps.
+// make every load unconditional: tokens past the row's length read as zero
+// (so no padding of a variable-length batch is ever read), and no branch (and
+// no wait at its join) separates a prefetch from the work it overlaps.
 struct RowRsrc {
     __amdgpu_buffer_rsrc_t delta, u, z, dy;
 };
 
 template <typename T>
-__device__ __forceinline__ RowRsrc row_rsrc(const S6BwdArgs& p, int64_t b) {
-    const uint32_t bytes = (uint32_t)(p.L * p.D * sizeof(T));
+__device__ __forceinline__ RowRsrc row_rsrc(const S6BwdArgs& p, int64_t b, int64_t len) {
+    const uint32_t bytes = (uint32_t)(len * p.D * sizeof(T));
     const int64_t off = b * p.L * p.D;
     RowRsrc r;
     r.delta = make_rsrc(static_cast<const T*>(p.delta) + off, bytes);
@@ -184,7 +187,7 @@ struct TileScalars {
     template <typename T, typename R>
     __device__ __forceinline__ void from(const R& r, const S6BwdArgs& p, const LaneId& id,
                                          int64_t t0, float bias) {
-        const bool in = id.chan_ok && t0 + id.n < p.L;
+        const bool in = id.chan_ok && t0 + id.n < id.len;
         const float x = Bits<T>::f32(r.delta) + bias;
         u = in ? Bits<T>::f32(r.u) : 0.0f;
         dt = in ? (SOFTPLUS ? softplus_f(x) : x) : 0.0f;
@@ -250,12 +253,12 @@ template <> __device__ __forceinline__ uint32_t elem_bits<float>(float v) { retu
 
 // B or C [B, L, N] of a tile is shared by every channel of the workgroup:
 // thread (j, n) = (tid / 16, tid % 16) loads element (t0 + j, n) through a
-// buffer resource over batch row b (tokens past L and n >= N read as zero),
-// and the tile is staged in LDS as [token][n].
+// buffer resource over the len tokens of batch row b (tokens past them and
+// n >= N read as zero), and the tile is staged in LDS as [token][n].
 template <typename T>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t bc_rsrc(const S6BwdArgs& p, int64_t b,
-                                                          const void* src) {
-    return make_rsrc(static_cast<const T*>(src) + b * p.L * p.N, (uint32_t)(p.L * p.N * sizeof(T)));
+                                                          int64_t len, const void* src) {
+    return make_rsrc(static_cast<const T*>(src) + b * p.L * p.N, (uint32_t)(len * p.N * sizeof(T)));
 }
 
 // LDS tile of B or C stored per state n as 16 consecutive tokens, rows padded
@@ -346,9 +349,9 @@ __global__ __launch_bounds__(kThreads) void s6_bwd_ckpt(S6BwdArgs p) {
     const int64_t nblk = (p.L + kTile - 1) / kTile;
     const int64_t nsup = (nblk + kSuper - 1) / kSuper;
     float h = (id.ok && p.h0) ? p.h0[(id.b * p.D + id.d) * p.N + id.n] : 0.0f;
-    const auto rB = bc_rsrc<T>(p, id.b, p.Bm);
+    const auto rB = bc_rsrc<T>(p, id.b, id.len, p.Bm);
     float* ck = p.ckpt + (id.b * p.D + id.dc) * nblk * p.N + id.n;
-    const RowRsrc rr = row_rsrc<T>(p, id.b);
+    const RowRsrc rr = row_rsrc<T>(p, id.b, id.len);
     SuperRaw<T, VEC> nxt;
     if (nsup > 0) nxt.load(p, id, rr, 0, rB);
     for (int64_t sg = 0; sg < nsup; ++sg) {
@@ -439,12 +442,12 @@ void s6_bwd_main(S6BwdArgs p) {
     // n clamped: lanes past N read a valid (ignored) checkpoint
     const float* ck = p.ckpt + (id.b * p.D + id.dc) * nblk * p.N + (id.n < p.N ? id.n : 0);
     const int64_t G = (p.D + kChans - 1) / kChans;
-    const RowRsrc rr = row_rsrc<T>(p, id.b);
+    const RowRsrc rr = row_rsrc<T>(p, id.b, id.len);
     T* du_out = static_cast<T*>(p.du);
     T* dd_out = static_cast<T*>(p.ddelta);
     T* dz_out = static_cast<T*>(p.dz);
-    const auto rB = bc_rsrc<T>(p, id.b, p.Bm);
-    const auto rC = bc_rsrc<T>(p, id.b, p.Cm);
+    const auto rB = bc_rsrc<T>(p, id.b, id.len, p.Bm);
+    const auto rC = bc_rsrc<T>(p, id.b, id.len, p.Cm);
 
     float mu = (id.ok && p.dh_last) ? p.dh_last[(id.b * p.D + id.d) * p.N + id.n] : 0.0f;
     float dA_acc = 0.0f, dD_acc = 0.0f, db_acc = 0.0f;
@@ -563,14 +566,16 @@ void s6_bwd_main(S6BwdArgs p) {
         {
             const int64_t t = t0 + id.n;
             const float r = r_y + dsk * s.u;
-            const float dd = r_ddt * s.sig;
+            // past a row's end in a variable-length batch every term is zero
+            // except the carried adjoint's m h a A: its step has no gradient
+            const float dd = t < id.len ? r_ddt * s.sig : 0.0f;
             Elem<T>::store(&outst[0][id.n][0], cl, fmaf(s.g, dsk, s.dt * r_su));
             Elem<T>::store(&outst[1][id.n][0], cl, dd);
             if constexpr (HAS_Z) {
                 const float sz = sigmoid_f(s.z);
                 Elem<T>::store(&outst[2][id.n][0], cl, s.dy * r * (sz * fmaf(s.z, 1.0f - sz, 1.0f)));
             }
-            if (id.chan_ok && t < p.L) {
+            if (id.chan_ok && t < id.len) {
                 db_acc += dd;
                 dD_acc = fmaf(s.g, s.u, dD_acc);
             }

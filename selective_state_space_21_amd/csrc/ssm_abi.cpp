@@ -36,8 +36,9 @@ int s6_bwd_impl(const void* u, const void* delta, const float* A, const void* Bm
                 const float* Dskip, const void* z, const float* delta_bias, unsigned flags,
                 const float* h0, const void* dy, const float* dh_last, void* du, void* ddelta,
                 float* dA, float* dB, float* dC, float* dDskip, void* dz, float* ddelta_bias,
-                float* dh0, const float* ckpt, int64_t B, int64_t L, int64_t D, int64_t N,
-                int dtype, void* workspace, size_t workspace_bytes, void* stream);
+                float* dh0, const float* ckpt, const int32_t* seq_lens, int64_t B, int64_t L,
+                int64_t D, int64_t N, int dtype, void* workspace, size_t workspace_bytes,
+                void* stream);
 
 int ssd_fwd_impl(const void* X, const void* delta, const float* A, const void* Bm, const void* Cm,
                  const float* Dskip, const void* z, const float* delta_bias, unsigned flags,
@@ -378,8 +379,24 @@ int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, con
                            int64_t N, int dtype, void* workspace, size_t workspace_bytes,
                            void* stream) {
     return s6_bwd_impl(u, delta, A, Bm, Cm, Dskip, z, delta_bias, flags, h0, dy, dh_last, du,
-                       ddelta, dA, dB, dC, dDskip, dz, ddelta_bias, dh0, nullptr, B, L, D, N,
-                       dtype, workspace, workspace_bytes, stream);
+                       ddelta, dA, dB, dC, dDskip, dz, ddelta_bias, dh0, nullptr, nullptr, B, L,
+                       D, N, dtype, workspace, workspace_bytes, stream);
+}
+
+int ssm_selective_scan_bwd_varlen(const void* u, const void* delta, const float* A,
+                                  const void* Bm, const void* Cm, const float* Dskip,
+                                  const void* z, const float* delta_bias, unsigned flags,
+                                  const float* h0, const void* dy, const float* dh_last, void* du,
+                                  void* ddelta, float* dA, float* dB, float* dC, float* dDskip,
+                                  void* dz, float* ddelta_bias, float* dh0,
+                                  const int32_t* seq_lens, int64_t B, int64_t L, int64_t D,
+                                  int64_t N, int dtype, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+    if (!seq_lens) return SSM_ERR_NULL_ARG;
+    if (!aligned(seq_lens, 4)) return SSM_ERR_MISALIGNED;
+    return s6_bwd_impl(u, delta, A, Bm, Cm, Dskip, z, delta_bias, flags, h0, dy, dh_last, du,
+                       ddelta, dA, dB, dC, dDskip, dz, ddelta_bias, dh0, nullptr, seq_lens, B, L,
+                       D, N, dtype, workspace, workspace_bytes, stream);
 }
 
 size_t ssm_selective_scan_bwd_ckpt_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
@@ -400,7 +417,7 @@ int ssm_selective_scan_bwd_ckpt(const void* u, const void* delta, const float* A
     if (ckpt && !aligned(ckpt, 16)) return SSM_ERR_MISALIGNED;
     return s6_bwd_impl(u, delta, A, Bm, Cm, Dskip, z, delta_bias, flags, h0, dy, dh_last, du,
                        ddelta, dA, dB, dC, dDskip, dz, ddelta_bias, dh0, L > 0 ? ckpt : nullptr,
-                       B, L, D, N, dtype, workspace, workspace_bytes, stream);
+                       nullptr, B, L, D, N, dtype, workspace, workspace_bytes, stream);
 }
 
 int ssm_causal_conv1d_silu(const void* x, const float* weight, const float* bias,
@@ -438,8 +455,9 @@ int s6_bwd_impl(const void* u, const void* delta, const float* A, const void* Bm
                 const float* Dskip, const void* z, const float* delta_bias, unsigned flags,
                 const float* h0, const void* dy, const float* dh_last, void* du, void* ddelta,
                 float* dA, float* dB, float* dC, float* dDskip, void* dz, float* ddelta_bias,
-                float* dh0, const float* ckpt, int64_t B, int64_t L, int64_t D, int64_t N,
-                int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                float* dh0, const float* ckpt, const int32_t* seq_lens, int64_t B, int64_t L,
+                int64_t D, int64_t N, int dtype, void* workspace, size_t workspace_bytes,
+                void* stream) {
     int rc = s6_bwd_check_sizes(B, L, D, N, dtype);
     if (rc != SSM_OK) return rc;
     if (flags & ~(unsigned)SSM_FLAG_DELTA_SOFTPLUS) return SSM_ERR_UNSUPPORTED;
@@ -465,6 +483,7 @@ int s6_bwd_impl(const void* u, const void* delta, const float* A, const void* Bm
     a.B = B; a.L = L; a.D = D; a.N = N; a.flags = flags; a.bf16 = dtype == SSM_BF16;
     a.own_ckpt = own;
     a.ckpt = const_cast<float*>(ckpt);
+    a.seq_lens = seq_lens;
     ssm::s6_bwd_carve(a, workspace);
     const hipError_t e = ssm::launch_s6_bwd(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;

@@ -154,6 +154,7 @@ struct S6BwdArgs {
     int64_t B, L, D, N;
     unsigned flags;
     int bf16;
+    const int32_t* seq_lens;   // [B] tokens per batch row (device), or NULL: all L
     // the state before each 16-token tile, [B, D, ceil(L/16), N]: carved
     // from the workspace and written by the call's own forward sweep, or
     // given by the caller (own_ckpt false: the sweep is skipped)

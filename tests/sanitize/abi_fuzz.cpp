@@ -107,6 +107,11 @@ int main(int argc, char** argv) {
                             kOk, kOk, kOkF, kOk, kOk, nullptr, nullptr, nullptr, flags, nullptr,
                             kOk, nullptr, kMis, kOk, kOkF, kOkF, kOkF, nullptr, nullptr, nullptr,
                             nullptr, B, L, D, N, dtype, wsp, wsb, nullptr), B, L, D, N);
+        expect_rejected("bwd_varlen", ssm_selective_scan_bwd_varlen(
+                            kOk, kOk, kOkF, kOk, kOk, nullptr, nullptr, nullptr, flags, nullptr,
+                            kOk, nullptr, kMis, kOk, kOkF, kOkF, kOkF, nullptr, nullptr, nullptr,
+                            nullptr, reinterpret_cast<const int32_t*>(kOk), B, L, D, N, dtype,
+                            wsp, wsb, nullptr), B, L, D, N);
         expect_rejected("fwd_ckpt", ssm_selective_scan_fwd_ckpt(
                             kOk, kOk, kOkF, kOk, kOk, nullptr, nullptr, nullptr, flags, nullptr,
                             kMis, nullptr, reinterpret_cast<float*>(kOk), B, L, D, N, dtype, wsp,

@@ -381,6 +381,17 @@ def test_varlen_validation_errors(lib):
                                             None, a["Y"], None, sl, a["Bt"], a["L"], a["H"],
                                             a["P"], a["G"], a["N"], a["chunk"], a["dtype"], None,
                                             0, None)
+    def bwd_call(sl, **kw):
+        a = dict(Bt=2, L=64, Dm=128, N=16, dtype=1, du=FAKE)
+        a.update(kw)
+        return lib.ssm_selective_scan_bwd_varlen(
+            FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 1, None, FAKE, None, a["du"], FAKE,
+            FAKE, FAKE, FAKE, None, None, None, None, sl, a["Bt"], a["L"], a["Dm"], a["N"],
+            a["dtype"], 0x100000, 1 << 40, None)
+    assert bwd_call(None) == 1
+    assert bwd_call(FAKE + 2) == 5
+    assert bwd_call(FAKE, N=17) == 4
+    assert bwd_call(FAKE, du=FAKE_MIS) == 5
     assert ssd_call(None) == 1
     assert ssd_call(FAKE + 2) == 5
     assert ssd_call(FAKE, Bt=0) == 2

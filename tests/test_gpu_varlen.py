@@ -111,3 +111,64 @@ def test_ssd_varlen_full_lengths_equal_plain_call():
                                seq_lens=torch.full((2,), 600, dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     assert torch.equal(Y1, Y2) and torch.equal(h1, h2)
+
+
+# ---- S6 backward (ssm_selective_scan_bwd_varlen).  NaN padding again; the
+# batch-summed gradients (dA, dD, ddelta_bias) are checked against the sum of
+# the oracle's per-row gradients.
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N,Dm", [(16, 96), (5, 80)])
+def test_bwd_varlen_parity(dtype, N, Dm):
+    from oracle.backward import s6_bwd as oracle_bwd
+    lens = [300, 1, 0, 157, 512]
+    Bt, L = len(lens), 512
+    w = W.S6_MAMBA130M.scaled(B=Bt, L=L, D=Dm, N=N, dtype=dtype)
+    inp = W.make_s6_inputs(w, seed=Dm + N)
+    g = torch.Generator().manual_seed(11)
+    inp["h0"] = 0.3 * torch.randn(Bt, Dm, N, generator=g)
+    inp["dy"] = torch.randn(Bt, L, Dm, generator=g).to(inp["u"].dtype)
+    inp["dh_last"] = torch.randn(Bt, Dm, N, generator=g)
+    padded = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    for b, n in enumerate(lens):
+        for k in ("u", "delta", "B", "C", "z", "dy"):
+            padded[k][b, n:] = float("nan")
+    d = to_dev(padded)
+    got = ssm.selective_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], d["dy"], D=d["D"],
+                                 z=d["z"], delta_bias=d["delta_bias"], h0=d["h0"],
+                                 dh_last=d["dh_last"],
+                                 seq_lens=torch.tensor(lens, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    got = {k: v.float().cpu().numpy() for k, v in got.items()}
+    tol_act = 1e-5 if dtype == "f32" else 2e-2
+    summed = {}
+    for b, n in enumerate(lens):
+        row = lambda t: None if t is None else t[b:b + 1, :n]
+        ref = oracle_bwd(row(inp["u"]), row(inp["delta"]), inp["A"], row(inp["B"]), row(inp["C"]),
+                         row(inp["dy"]), D=inp["D"], z=row(inp["z"]), delta_bias=inp["delta_bias"],
+                         h0=inp["h0"][b:b + 1], dh_last=inp["dh_last"][b:b + 1])
+        for k in ("du", "ddelta", "dz", "dB", "dC"):
+            if k not in ref:
+                continue
+            if n > 0:
+                tol = 1e-5 if k in ("dB", "dC") else tol_act
+                assert normwise_err(got[k][b:b + 1, :n], ref[k].numpy()) <= tol, (k, b)
+            assert np.all(got[k][b, n:] == 0.0), (k, b)
+        assert normwise_err(got["dh0"][b:b + 1], ref["dh0"].numpy()) <= 1e-5, b
+        for k in ("dA", "dD", "ddelta_bias"):
+            summed[k] = summed.get(k, 0.0) + ref[k].numpy().astype(np.float64)
+    for k, v in summed.items():
+        assert normwise_err(got[k], v) <= 1e-5, k
+
+
+def test_bwd_varlen_full_lengths_equal_plain_call():
+    w = W.S6_MAMBA130M.scaled(B=3, L=400, D=96)
+    inp = W.make_s6_inputs(w, seed=4)
+    d = to_dev(inp)
+    dy = torch.randn(3, 400, 96, generator=torch.Generator().manual_seed(2)).to(torch.bfloat16).cuda()
+    kw = dict(D=d["D"], z=d["z"], delta_bias=d["delta_bias"])
+    a = ssm.selective_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], dy, **kw)
+    b = ssm.selective_scan_bwd(d["u"], d["delta"], d["A"], d["B"], d["C"], dy, **kw,
+                               seq_lens=torch.full((3,), 400, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
