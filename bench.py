@@ -344,14 +344,19 @@ def bench_decode(args, ctx):
                 state_updates_per_s=round(w.B * w.D * w.N / (ms * 1e-3), 1))
 
 
-def bench_bwd(args, ctx):
+def bench_bwd(args, ctx, long=False):
+    """The backward at the Mamba-130M layer, or (long) at the long fp32
+    sequence, where the planner cuts the sequence into segments."""
     torch, ssm, W = ctx["torch"], ctx["ssm"], ctx["W"]
-    w = W.S6_MAMBA130M
+    w = W.S6_LONG_FP32 if long else W.S6_MAMBA130M
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
     t = W.make_s6_inputs(w, seed=0)
     d = {k: (v.to("cuda:0") if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
     g = torch.Generator().manual_seed(1)
-    dy = torch.randn(w.B, w.L, w.D, generator=g).to(torch.bfloat16).to("cuda:0")
-    need = int(ssm._native.load().ssm_selective_scan_bwd_workspace_bytes(w.B, w.L, w.D, w.N, 1))
+    dy = torch.randn(w.B, w.L, w.D, generator=g).to(dt).to("cuda:0")
+    lib = ssm._native.load()
+    code = 0 if dt == torch.float32 else 1
+    need = int(lib.ssm_selective_scan_bwd_workspace_bytes(w.B, w.L, w.D, w.N, code))
     ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
 
     def step():
@@ -359,13 +364,15 @@ def bench_bwd(args, ctx):
                                z=d["z"], delta_bias=d["delta_bias"], workspace=ws)
 
     ms = ctx["timer"].run(step, args.steps, args.warmup, ctx["flusher"].clean)["mean"]
-    e = 2
-    # inputs u, delta, z, dy, B, C read and du, ddelta, dz written once (bf16);
+    e = 2 if dt == torch.bfloat16 else 4
+    # inputs u, delta, (z,) dy, B, C read and du, ddelta, (dz) written once;
     # dB, dC fp32; A, dA and the per-channel vectors are negligible
-    nbytes = 7 * w.B * w.L * w.D * e + 2 * w.B * w.L * w.N * (e + 4)
+    acts = 7 if w.gate else 5
+    nbytes = acts * w.B * w.L * w.D * e + 2 * w.B * w.L * w.N * (e + 4)
     return dict(status="ok", workload=w.name, ms=round(ms, 5), algorithmic_bytes=nbytes,
                 gbs=round(nbytes / (ms * 1e-3) / 1e9, 2),
-                gtokch=round(w.tok_ch / (ms * 1e-3) / 1e9, 3), workspace_bytes=need)
+                gtokch=round(w.tok_ch / (ms * 1e-3) / 1e9, 3), workspace_bytes=need,
+                segments=int(lib.ssm_selective_scan_bwd_segments(w.B, w.L, w.D, w.N)))
 
 
 def bench_train(args, ctx):
@@ -586,7 +593,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-paths", action="store_true", help="the headline S6 workload only")
     ap.add_argument("--only", choices=["s6", "s6_2p8b", "s6_long", "ssd", "decode", "bwd",
-                                       "train", "conv", "conv_scan", "copy"],
+                                       "bwd_long", "train", "conv", "conv_scan", "copy"],
                     help="run one part alone and print its result")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 256 MiB device copy three times, the "
@@ -619,7 +626,8 @@ def main():
              "s6_2p8b": lambda: bench_s6(args, ctx, W.S6_MAMBA2P8B),
              "s6_long": lambda: bench_s6(args, ctx, W.S6_LONG_FP32),
              "ssd": lambda: bench_ssd(args, ctx), "decode": lambda: bench_decode(args, ctx),
-             "bwd": lambda: bench_bwd(args, ctx), "train": lambda: bench_train(args, ctx),
+             "bwd": lambda: bench_bwd(args, ctx), "bwd_long": lambda: bench_bwd(args, ctx, True),
+             "train": lambda: bench_train(args, ctx),
              "conv": lambda: bench_conv(args, ctx),
              "conv_scan": lambda: bench_conv_scan(args, ctx),
              "copy": lambda: bench_copy(args, ctx, W.s6_algorithmic_bytes(W.S6_MAMBA130M))}
@@ -635,7 +643,8 @@ def main():
     if not args.no_paths:
         for name, key in [("s6_mamba2.8b_layer", "s6_2p8b"), ("s6_long_fp32", "s6_long"),
                           ("ssd_chunk_fwd", "ssd"), ("selective_state_update", "decode"),
-                          ("selective_scan_bwd", "bwd"), ("training_step_fwd_bwd", "train"),
+                          ("selective_scan_bwd", "bwd"), ("selective_scan_bwd_long_fp32", "bwd_long"),
+                          ("training_step_fwd_bwd", "train"),
                           ("causal_conv1d_silu", "conv"),
                           ("selective_scan_conv_fwd", "conv_scan")]:
             paths[name] = parts[key]()

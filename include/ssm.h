@@ -291,12 +291,28 @@ int ssm_ssd_chunk_fwd_varlen(const void* X, const void* delta, const float* A,
  *   dDskip, ddelta_bias : [D]  fp32 or NULL (not computed)
  *   dh0            : [B, D, N] fp32 or NULL
  * Supported: 1 <= N <= 16; flags SSM_FLAG_DELTA_SOFTPLUS only (no ZOH).
+ * Both sweeps (a forward one storing the state every 16 tokens, then the
+ * adjoint one) run one workgroup per channel group and batch row.  When
+ * there are fewer than 128 adjoint-sweep workgroups (B * ceil(D/48)) and at
+ * least 2048 tokens, the sequence is cut into segments (whole 128-token
+ * multiples, at most 64, as many as keep the adjoint sweep within one
+ * workgroup per CU; see ssm_selective_scan_bwd_segments): each segment's
+ * forward pair (its end state from zero) and adjoint pair (its adjoint from
+ * zero at its end) are computed in parallel, folded in segment order into
+ * every segment's incoming state and adjoint (both decaying over a segment by
+ * exp(A * its sum of dt)), and then all segments are swept from those.
  * The workspace (query below; 256-byte aligned) holds per-channel-group
- * partial sums and a state checkpoint every 16 tokens; results are
- * deterministic (no atomics).
+ * partial sums, the segment buffers and a state checkpoint every 16 tokens;
+ * results are deterministic (no atomics).
  */
 size_t ssm_selective_scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
                                               int dtype);
+
+/* Number of sequence segments a backward call uses at these sizes (1 = one
+ * pass); 0 for sizes the backward does not take.  The environment variable
+ * SSM_BWD_SEGMENTS (1..64) overrides the choice, for this query and the call
+ * (capped at one segment per 16 tokens). */
+int ssm_selective_scan_bwd_segments(int64_t B, int64_t L, int64_t D, int64_t N);
 
 int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* Bm,
                            const void* Cm, const float* Dskip, const void* z,

@@ -22,7 +22,8 @@ __all__ = ["selective_scan_fwd", "selective_scan_fwd_noalloc", "selective_scan_c
            "selective_scan_bwd", "selective_scan_fwd_ckpt", "selective_scan_ckpt_bytes",
            "ssd_chunk_fwd", "selective_state_update",
            "causal_conv1d_silu", "selective_scan_workspace_bytes",
-           "selective_scan_segments", "selective_scan_lanes", "ssd_chunk_workspace_bytes",
+           "selective_scan_segments", "selective_scan_lanes", "selective_scan_bwd_segments",
+           "ssd_chunk_workspace_bytes",
            "SSMError"]
 
 _DT = {torch.float32: _native.SSM_F32, torch.bfloat16: _native.SSM_BF16}
@@ -108,6 +109,11 @@ def selective_scan_workspace_bytes(B: int, L: int, D: int, N: int, dtype=torch.b
 
 def selective_scan_segments(B: int, L: int, D: int, N: int) -> int:
     return int(_native.load().ssm_selective_scan_segments(B, L, D, N))
+
+
+def selective_scan_bwd_segments(B: int, L: int, D: int, N: int) -> int:
+    """Sequence segments a backward call uses at these sizes (1: one pass)."""
+    return int(_native.load().ssm_selective_scan_bwd_segments(B, L, D, N))
 
 
 def selective_scan_lanes(B: int, L: int, D: int, N: int) -> bool:

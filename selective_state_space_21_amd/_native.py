@@ -54,6 +54,7 @@ SIGNATURES = {
                                       _sz, _vp]),
     "ssm_selective_scan_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i]),
     "ssm_selective_scan_bwd": (_i, [_vp] * 21 + [_i64, _i64, _i64, _i64, _i, _vp, _sz, _vp]),
+    "ssm_selective_scan_bwd_segments": (_i, [_i64, _i64, _i64, _i64]),
     "ssm_selective_scan_bwd_varlen": (_i, [_vp] * 8 + [_u] + [_vp] * 13 +
                                       [_i64, _i64, _i64, _i64, _i, _vp, _sz, _vp]),
     "ssm_selective_scan_ckpt_bytes": (_sz, [_i64, _i64, _i64, _i64, _i]),

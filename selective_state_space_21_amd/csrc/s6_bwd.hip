@@ -336,9 +336,14 @@ struct SuperRaw {
     }
 };
 
-template <typename T, bool SOFTPLUS, bool VEC>
+// PAIR: the segment's forward pair instead of checkpoints: its state at the
+// end from a zero state at its start (the carry pass folds these into every
+// segment's incoming state).  Otherwise the segment is scanned from its
+// incoming state (h0 for the first) and the state before each tile stored.
+template <typename T, bool SOFTPLUS, bool VEC, bool PAIR>
 __global__ __launch_bounds__(kThreads) void s6_bwd_ckpt(S6BwdArgs p) {
     static_assert(kThreads == kTile * 16, "one tile element per thread");
+    static_assert(kSuper == plan::kBwdSuper, "the planner's segment rounding");
     constexpr int kSpan = kSuper * kTile;
     __shared__ __attribute__((aligned(16))) float bt[kSuper][16 * kPitch];
     __shared__ __attribute__((aligned(16))) T actc[VEC ? 2 : 1][kChans][kSpan + 8];
@@ -347,13 +352,22 @@ __global__ __launch_bounds__(kThreads) void s6_bwd_ckpt(S6BwdArgs p) {
     const float a2 = id.ok ? p.A[id.dc * p.N + id.n] * kLog2e : 0.0f;
     const float bias = p.delta_bias ? p.delta_bias[id.dc] : 0.0f;
     const int64_t nblk = (p.L + kTile - 1) / kTile;
-    const int64_t nsup = (nblk + kSuper - 1) / kSuper;
-    float h = (id.ok && p.h0) ? p.h0[(id.b * p.D + id.d) * p.N + id.n] : 0.0f;
+    // segment s: tiles [k0, k1)
+    const int seg = (int)blockIdx.z;
+    const int64_t k0 = (int64_t)seg * p.seg_tiles;
+    const int64_t k1 = k0 + p.seg_tiles < nblk ? k0 + p.seg_tiles : nblk;
+    const int64_t nsup = k1 > k0 ? (k1 - k0 + kSuper - 1) / kSuper : 0;
+    const int64_t chain = (((int64_t)seg * p.B + id.b) * p.D + id.dc) * p.N + id.n;
+    float h = 0.0f;
+    if (!PAIR && id.ok) {
+        if (seg == 0) h = p.h0 ? p.h0[(id.b * p.D + id.d) * p.N + id.n] : 0.0f;
+        else h = p.seg_hin[chain];
+    }
     const auto rB = bc_rsrc<T>(p, id.b, id.len, p.Bm);
     float* ck = p.ckpt + (id.b * p.D + id.dc) * nblk * p.N + id.n;
     const RowRsrc rr = row_rsrc<T>(p, id.b, id.len);
     SuperRaw<T, VEC> nxt;
-    if (nsup > 0) nxt.load(p, id, rr, 0, rB);
+    if (nsup > 0) nxt.load(p, id, rr, k0 * kTile, rB);
     for (int64_t sg = 0; sg < nsup; ++sg) {
         const SuperRaw<T, VEC> cur = nxt;
         lds_barrier();                    // previous super-tile's LDS reads done
@@ -375,12 +389,12 @@ __global__ __launch_bounds__(kThreads) void s6_bwd_ckpt(S6BwdArgs p) {
         lds_barrier();
         // travels meanwhile; issued unconditionally (past the end it reads
         // zeros) so that no branch join makes the compiler wait for it here
-        nxt.load(p, id, rr, (sg + 1) * kSpan, rB);
+        nxt.load(p, id, rr, k0 * kTile + (sg + 1) * kSpan, rB);
 #pragma unroll
         for (int i = 0; i < kSuper; ++i) {
-            const int64_t k = sg * kSuper + i;
-            if (k >= nblk) break;
-            if (id.ok) ck[k * p.N] = h;
+            const int64_t k = k0 + sg * kSuper + i;
+            if (k >= k1) break;
+            if (!PAIR && id.ok) ck[k * p.N] = h;
             TileRaw<T, false, false> r;
             if constexpr (VEC) {
                 r.delta = elem_bits<T>(actc[0][cl][kTile * i + id.n]);
@@ -404,11 +418,22 @@ __global__ __launch_bounds__(kThreads) void s6_bwd_ckpt(S6BwdArgs p) {
             for (int j = 0; j < kTile; ++j) h = fmaf(dA[j], h, bv[j]);
         }
     }
+    if (PAIR && id.ok) p.seg_fend[chain] = h;
 }
 
-template <typename T, bool HAS_Z, bool SOFTPLUS, bool VEC>
+// MODE kWhole: one segment, from dh_last.  kSegment: segment blockIdx.z of
+// several, from its carried adjoint.  kPairs: the segment's adjoint pair
+// only: the adjoint recurrence run back through the segment from zero at its
+// end, without the states or any gradient (the carry pass folds these into
+// every segment's incoming adjoint), plus the segment's sum of steps.  (The
+// whole-sequence kernel is compiled apart: with the segment bounds and
+// buffers at run time its tile loop measured 3% slower.)
+enum { kWhole = 0, kSegment = 1, kPairs = 2 };
+
+template <typename T, bool HAS_Z, bool SOFTPLUS, bool VEC, int MODE>
 __global__ __launch_bounds__(kMainThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void s6_bwd_main(S6BwdArgs p) {
+    constexpr bool PAIRS = MODE == kPairs;
     constexpr int kWaves = kMainWaves, kThreads = kMainThreads, kChans = kMainChans;
     // dB and dC terms of the tile per channel, [dB|dC][token][state][channel]:
     // each lane writes its own two terms per token, and the sums over the
@@ -439,6 +464,13 @@ void s6_bwd_main(S6BwdArgs p) {
     const float bias = p.delta_bias ? p.delta_bias[id.dc] : 0.0f;
     const float dsk = p.Dskip ? p.Dskip[id.dc] : 0.0f;
     const int64_t nblk = (p.L + kTile - 1) / kTile;
+    // segment s: tiles [k0, k1), walked from k1 - 1 down
+    const int seg = MODE == kWhole ? 0 : (int)blockIdx.z;
+    const int64_t k0 = MODE == kWhole ? 0 : (int64_t)seg * p.seg_tiles;
+    const int64_t k1 = MODE == kWhole ? nblk : (k0 + p.seg_tiles < nblk ? k0 + p.seg_tiles : nblk);
+    // this lane's (segment, b, d, n) chain in the segment buffers, formed
+    // where used (kept live across the tile loop it slowed the loop by 3%)
+    auto chain = [&]() { return (((int64_t)seg * p.B + id.b) * p.D + id.dc) * p.N + id.n; };
     // n clamped: lanes past N read a valid (ignored) checkpoint
     const float* ck = p.ckpt + (id.b * p.D + id.dc) * nblk * p.N + (id.n < p.N ? id.n : 0);
     const int64_t G = (p.D + kChans - 1) / kChans;
@@ -449,8 +481,12 @@ void s6_bwd_main(S6BwdArgs p) {
     const auto rB = bc_rsrc<T>(p, id.b, id.len, p.Bm);
     const auto rC = bc_rsrc<T>(p, id.b, id.len, p.Cm);
 
-    float mu = (id.ok && p.dh_last) ? p.dh_last[(id.b * p.D + id.d) * p.N + id.n] : 0.0f;
-    float dA_acc = 0.0f, dD_acc = 0.0f, db_acc = 0.0f;
+    // a_{t+1} m_{t+1} entering the segment's last token: dh_last for one
+    // segment, the carried value for several, zero for the pair
+    float mu = 0.0f;
+    if constexpr (MODE == kWhole) mu = (id.ok && p.dh_last) ? p.dh_last[(id.b * p.D + id.d) * p.N + id.n] : 0.0f;
+    if constexpr (MODE == kSegment) mu = id.ok ? p.seg_qin[chain()] : 0.0f;
+    float dA_acc = 0.0f, dD_acc = 0.0f, db_acc = 0.0f, dt_sum = 0.0f;
     TileRaw<T, HAS_Z, true> raw;
     uint32_t bpre = 0, cpre = 0;
     float hck = 0.0f;
@@ -467,14 +503,14 @@ void s6_bwd_main(S6BwdArgs p) {
         const int64_t t = act_lane ? t0 + at : -1;
         apre.load(rs_act, quad_off<T, kChans>(p, id.grp, t, aq));
     };
-    if (nblk > 0) {
-        if constexpr (VEC) load_act((nblk - 1) * kTile);
-        else raw.load(p, id, rr, (nblk - 1) * kTile);
-        bpre = load_bc_bits<T>(p, (nblk - 1) * kTile, rB);
-        cpre = load_bc_bits<T>(p, (nblk - 1) * kTile, rC);
-        hck = ck[(nblk - 1) * p.N];
+    if (k1 > k0) {
+        if constexpr (VEC) load_act((k1 - 1) * kTile);
+        else raw.load(p, id, rr, (k1 - 1) * kTile);
+        bpre = load_bc_bits<T>(p, (k1 - 1) * kTile, rB);
+        cpre = load_bc_bits<T>(p, (k1 - 1) * kTile, rC);
+        if constexpr (!PAIRS) hck = ck[(k1 - 1) * p.N];
     }
-    for (int64_t k = nblk - 1; k >= 0; --k) {
+    for (int64_t k = k1 - 1; k >= k0; --k) {
         const int64_t t0 = k * kTile;
         const float hprev0 = id.ok ? hck : 0.0f;
         TileScalars<HAS_Z, SOFTPLUS, true> s;
@@ -510,6 +546,19 @@ void s6_bwd_main(S6BwdArgs p) {
         else raw.load(p, id, rr, t0 - kTile);
         bpre = load_bc_bits<T>(p, t0 - kTile, rB);
         cpre = load_bc_bits<T>(p, t0 - kTile, rC);
+        if constexpr (PAIRS) {
+            // the adjoint alone: m_t = g_t C_t + mu, mu = a_t m_t
+            float cv[kTile];
+            tile_row(bct[1], id.n, cv);
+#pragma unroll
+            for (int j = kTile - 1; j >= 0; --j) {
+                const float m = fmac_bcast(mu, s.g, cv[j], j);
+                mu = fast_exp2(row_bcast(s.dt, j) * a2) * m;
+            }
+            dt_sum += s.dt;
+            lds_barrier();                  // this tile's reads of bct and actst done
+            continue;
+        }
         hck = ck[(k > 0 ? k - 1 : 0) * p.N];
         // states of the tile, recomputed from its checkpoint
         float hs[kTile], da[kTile];
@@ -617,20 +666,52 @@ void s6_bwd_main(S6BwdArgs p) {
             }
         }
     }
+    const int64_t bd = ((int64_t)seg * p.B + id.b) * p.D + id.d;   // (segment, b, d)
+    if constexpr (PAIRS) {
+        dt_sum = row_sum(dt_sum);
+        if (id.ok) p.seg_radj[chain()] = mu;
+        if (id.chan_ok && id.n == 0) p.seg_dsum[bd] = dt_sum;
+        return;
+    }
     if (id.ok) {
-        p.part_dA[(id.b * p.D + id.d) * p.N + id.n] = dA_acc;
-        if (p.dh0) p.dh0[(id.b * p.D + id.d) * p.N + id.n] = mu;
+        p.part_dA[chain()] = dA_acc;
+        if (p.dh0 && seg == 0) p.dh0[(id.b * p.D + id.d) * p.N + id.n] = mu;
     }
     dD_acc = row_sum(dD_acc);
     db_acc = row_sum(db_acc);
     if (id.chan_ok && id.n == 0) {
-        p.part_dD[id.b * p.D + id.d] = dD_acc;
-        p.part_db[id.b * p.D + id.d] = db_acc;
+        p.part_dD[bd] = dD_acc;
+        p.part_db[bd] = db_acc;
+    }
+}
+
+// The segment pairs folded into every segment's incoming state (left to
+// right, from h0) and incoming adjoint (right to left, from dh_last): one
+// thread per (b, d, n) chain.  Over segment s both the state and the adjoint
+// decay by exp2(A log2(e) sum of the segment's steps).
+__global__ __launch_bounds__(256) void s6_bwd_carry(S6BwdArgs p) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t chains = p.B * p.D * p.N;
+    if (i >= chains) return;
+    const int64_t bd = i / p.N, d = bd % p.D, n = i % p.N;
+    const float a2 = p.A[d * p.N + n] * kLog2e;
+    const int64_t nbd = p.B * p.D;
+    if (p.own_ckpt) {
+        float h = p.h0 ? p.h0[i] : 0.0f;
+        for (int s = 0; s < p.S; ++s) {
+            p.seg_hin[s * chains + i] = h;
+            h = fmaf(fast_exp2(a2 * p.seg_dsum[s * nbd + bd]), h, p.seg_fend[s * chains + i]);
+        }
+    }
+    float q = p.dh_last ? p.dh_last[i] : 0.0f;
+    for (int s = p.S - 1; s >= 0; --s) {
+        p.seg_qin[s * chains + i] = q;
+        q = fmaf(fast_exp2(a2 * p.seg_dsum[s * nbd + bd]), q, p.seg_radj[s * chains + i]);
     }
 }
 
 // dB, dC [B, L, N]: sums over the channel groups; dA [D, N], dD, dbias [D]:
-// sums over the batch rows.  One thread per output element.
+// sums over the segments and batch rows.  One thread per output element.
 __global__ __launch_bounds__(256) void s6_bwd_reduce(S6BwdArgs p) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t G = (p.D + kMainChans - 1) / kMainChans;
@@ -655,21 +736,22 @@ __global__ __launch_bounds__(256) void s6_bwd_reduce(S6BwdArgs p) {
     if (j < p.D * p.N) {
         float v = 0.0f;
         int64_t b = 0;
-        for (; b + 8 <= p.B; b += 8) {
+        const int64_t rows = (int64_t)p.S * p.B;     // (segment, batch row) partials
+        for (; b + 8 <= rows; b += 8) {
             float t[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) t[k] = p.part_dA[(b + k) * p.D * p.N + j];
 #pragma unroll
             for (int k = 0; k < 8; ++k) v += t[k];
         }
-        for (; b < p.B; ++b) v += p.part_dA[b * p.D * p.N + j];
+        for (; b < rows; ++b) v += p.part_dA[b * p.D * p.N + j];
         p.dA[j] = v;
         return;
     }
     const int64_t k = j - p.D * p.N;
     if (k < p.D) {
         float v = 0.0f, w = 0.0f;
-        for (int64_t b = 0; b < p.B; ++b) {
+        for (int64_t b = 0; b < (int64_t)p.S * p.B; ++b) {
             v += p.part_dD[b * p.D + k];
             w += p.part_db[b * p.D + k];
         }
@@ -678,23 +760,37 @@ __global__ __launch_bounds__(256) void s6_bwd_reduce(S6BwdArgs p) {
     }
 }
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool PAIR>
 void launch_ckpt_sweep(const S6BwdArgs& a, hipStream_t stream) {
-    const dim3 grid((unsigned)((a.D + kChans - 1) / kChans), (unsigned)a.B);
-    if (a.flags & SSM_FLAG_DELTA_SOFTPLUS) s6_bwd_ckpt<T, true, VEC><<<grid, kThreads, 0, stream>>>(a);
-    else s6_bwd_ckpt<T, false, VEC><<<grid, kThreads, 0, stream>>>(a);
+    const dim3 grid((unsigned)((a.D + kChans - 1) / kChans), (unsigned)a.B, (unsigned)a.S);
+    if (a.flags & SSM_FLAG_DELTA_SOFTPLUS) s6_bwd_ckpt<T, true, VEC, PAIR><<<grid, kThreads, 0, stream>>>(a);
+    else s6_bwd_ckpt<T, false, VEC, PAIR><<<grid, kThreads, 0, stream>>>(a);
+}
+
+template <typename T, bool VEC, int MODE>
+void launch_main(const S6BwdArgs& a, hipStream_t stream) {
+    const bool sp = (a.flags & SSM_FLAG_DELTA_SOFTPLUS) != 0;
+    const dim3 mgrid((unsigned)((a.D + kMainChans - 1) / kMainChans), (unsigned)a.B, (unsigned)a.S);
+    const bool hz = a.z != nullptr;
+    if (hz && sp) s6_bwd_main<T, true, true, VEC, MODE><<<mgrid, kMainThreads, 0, stream>>>(a);
+    else if (hz) s6_bwd_main<T, true, false, VEC, MODE><<<mgrid, kMainThreads, 0, stream>>>(a);
+    else if (sp) s6_bwd_main<T, false, true, VEC, MODE><<<mgrid, kMainThreads, 0, stream>>>(a);
+    else s6_bwd_main<T, false, false, VEC, MODE><<<mgrid, kMainThreads, 0, stream>>>(a);
 }
 
 template <typename T, bool VEC>
 void launch_sweeps(const S6BwdArgs& a, hipStream_t stream) {
-    const bool sp = (a.flags & SSM_FLAG_DELTA_SOFTPLUS) != 0;
-    if (a.own_ckpt) launch_ckpt_sweep<T, VEC>(a, stream);
-    const dim3 mgrid((unsigned)((a.D + kMainChans - 1) / kMainChans), (unsigned)a.B);
-    const bool hz = a.z != nullptr;
-    if (hz && sp) s6_bwd_main<T, true, true, VEC><<<mgrid, kMainThreads, 0, stream>>>(a);
-    else if (hz) s6_bwd_main<T, true, false, VEC><<<mgrid, kMainThreads, 0, stream>>>(a);
-    else if (sp) s6_bwd_main<T, false, true, VEC><<<mgrid, kMainThreads, 0, stream>>>(a);
-    else s6_bwd_main<T, false, false, VEC><<<mgrid, kMainThreads, 0, stream>>>(a);
+    if (a.S > 1) {
+        // the segments' adjoint pairs and step sums, their forward pairs, and
+        // the carry of both into every segment's incoming state and adjoint
+        launch_main<T, VEC, kPairs>(a, stream);
+        if (a.own_ckpt) launch_ckpt_sweep<T, VEC, true>(a, stream);
+        const int64_t chains = a.B * a.D * a.N;
+        s6_bwd_carry<<<(unsigned)((chains + 255) / 256), 256, 0, stream>>>(a);
+    }
+    if (a.own_ckpt) launch_ckpt_sweep<T, VEC, false>(a, stream);
+    if (a.S > 1) launch_main<T, VEC, kSegment>(a, stream);
+    else launch_main<T, VEC, kWhole>(a, stream);
 }
 
 template <typename T>
@@ -713,13 +809,17 @@ hipError_t launch_s6_bwd(const S6BwdArgs& a, hipStream_t stream) {
     return a.bf16 ? launch_t<uint16_t>(a, stream) : launch_t<float>(a, stream);
 }
 
-hipError_t launch_s6_bwd_ckpt(const S6BwdArgs& a, hipStream_t stream) {
+hipError_t launch_s6_bwd_ckpt(const S6BwdArgs& args, hipStream_t stream) {
+    // one segment: the whole sequence from h0
+    S6BwdArgs a = args;
+    a.S = 1;
+    a.seg_tiles = (a.L + kTile - 1) / kTile;
     if (a.bf16) {
-        if ((a.D * 2) % 16 == 0) launch_ckpt_sweep<uint16_t, true>(a, stream);
-        else launch_ckpt_sweep<uint16_t, false>(a, stream);
+        if ((a.D * 2) % 16 == 0) launch_ckpt_sweep<uint16_t, true, false>(a, stream);
+        else launch_ckpt_sweep<uint16_t, false, false>(a, stream);
     } else {
-        if ((a.D * 4) % 16 == 0) launch_ckpt_sweep<float, true>(a, stream);
-        else launch_ckpt_sweep<float, false>(a, stream);
+        if ((a.D * 4) % 16 == 0) launch_ckpt_sweep<float, true, false>(a, stream);
+        else launch_ckpt_sweep<float, false, false>(a, stream);
     }
     return hipGetLastError();
 }

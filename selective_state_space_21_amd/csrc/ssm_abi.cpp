@@ -399,6 +399,11 @@ int ssm_selective_scan_bwd_varlen(const void* u, const void* delta, const float*
                        D, N, dtype, workspace, workspace_bytes, stream);
 }
 
+int ssm_selective_scan_bwd_segments(int64_t B, int64_t L, int64_t D, int64_t N) {
+    if (s6_bwd_check_sizes(B, L, D, N, SSM_F32) != SSM_OK) return 0;
+    return ssm::plan_s6_bwd(B, L, D, N).S;
+}
+
 size_t ssm_selective_scan_bwd_ckpt_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N,
                                                    int dtype) {
     if (s6_bwd_check_sizes(B, L, D, N, dtype) != SSM_OK) return 0;
@@ -484,6 +489,9 @@ int s6_bwd_impl(const void* u, const void* delta, const float* A, const void* Bm
     a.own_ckpt = own;
     a.ckpt = const_cast<float*>(ckpt);
     a.seq_lens = seq_lens;
+    const ssm::S6BwdPlan plan = ssm::plan_s6_bwd(B, L, D, N);
+    a.S = plan.S;
+    a.seg_tiles = plan.seg_tiles;
     ssm::s6_bwd_carve(a, workspace);
     const hipError_t e = ssm::launch_s6_bwd(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;

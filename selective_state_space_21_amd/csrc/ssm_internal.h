@@ -77,6 +77,8 @@ constexpr int kLanesChans = 16;           // state-per-lane kernel: channels per
 constexpr int kFixChunk = 1024;           // state-per-lane fix-up: tokens per workgroup
 constexpr int kBwdTile = 16;              // backward: tokens per state checkpoint
 constexpr int kBwdChans = 48;             // backward: channels per adjoint-sweep workgroup
+constexpr int kBwdSuper = 8;              // backward: tiles per super-tile of the checkpoint sweep
+constexpr int kBwdMaxSegments = 64;       // backward: sequence segments at most
 // SIMDs the S6 planner balances wavefronts over: MI355X has 256 CUs of four
 // SIMDs.  A constant, so that the plan (and the workspace size it implies) is
 // a pure function of the sizes and no HIP call is needed before validation.
@@ -160,15 +162,33 @@ struct S6BwdArgs {
     // given by the caller (own_ckpt false: the sweep is skipped)
     float* ckpt;
     bool own_ckpt;
+    // sequence segments (S = 1: none): segment s holds the 16-token tiles
+    // [s * seg_tiles, (s + 1) * seg_tiles), all scanned in parallel from the
+    // state and adjoint that the carry pass folds from the segment pairs
+    int S;
+    int64_t seg_tiles;
+    float* seg_dsum;   // [S, B, D]    sum of the steps over the segment
+    float* seg_fend;   // [S, B, D, N] state at the segment's end, from zero at its start
+    float* seg_radj;   // [S, B, D, N] a_t m_t after its first token, from zero at its end
+    float* seg_hin;    // [S, B, D, N] state entering the segment
+    float* seg_qin;    // [S, B, D, N] a m entering the segment from its right (dh_last for the last)
     // workspace, carved by s6_bwd_carve
     float* part_bc;    // [2][ceil(D/16)][B, L, N] per-channel-group dB, dC
-    float* part_dA;    // [B, D, N]
-    float* part_dD;    // [B, D]
-    float* part_db;    // [B, D]
+    float* part_dA;    // [S, B, D, N]
+    float* part_dD;    // [S, B, D]
+    float* part_db;    // [S, B, D]
 };
 
-// Workspace of a backward call: the partial sums, then (own_ckpt) the
-// checkpoints.
+// Sequence segments of a backward call: a pure function of the sizes (and
+// the SSM_BWD_SEGMENTS override), like the forward's plan.
+struct S6BwdPlan {
+    int S;
+    int64_t seg_tiles;
+};
+S6BwdPlan plan_s6_bwd(int64_t B, int64_t L, int64_t D, int64_t N);
+
+// Workspace of a backward call: the partial sums, the segment buffers, then
+// (own_ckpt) the checkpoints.
 size_t s6_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, bool own_ckpt);
 void s6_bwd_carve(S6BwdArgs& a, void* workspace);
 hipError_t launch_s6_bwd(const S6BwdArgs& a, hipStream_t stream);
