@@ -72,10 +72,10 @@ ISSUE_PEAK_ELEMS_PER_S = 6.52e12
 # reports traffic null until its counters are taken again.
 COUNTER_TRAFFIC = {
     # kernel@workload: (bytes, sources, sha1 of the sources)
-    "s6_lanes@s6_mamba130m_layer_bf16": (205375500, ['s6_fwd.hip', 's6_plan.cpp', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "70fe76047dc6"),
-    "s6_lanes@s6_mamba2.8b_layer_bf16": (686176417, ['s6_fwd.hip', 's6_plan.cpp', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "70fe76047dc6"),
-    "s6_lanes@s6_long_fp32": (3518709622, ['s6_fwd.hip', 's6_plan.cpp', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "70fe76047dc6"),
-    "ssd@ssd_mamba2_bf16": (597919701, ['ssd_fwd.hip', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "0d3cde8848fd"),
+    "s6_lanes@s6_mamba130m_layer_bf16": (205377321, ['s6_fwd.hip', 's6_plan.cpp', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "535a2c4eb322"),
+    "s6_lanes@s6_mamba2.8b_layer_bf16": (686000558, ['s6_fwd.hip', 's6_plan.cpp', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "535a2c4eb322"),
+    "s6_lanes@s6_long_fp32": (3510319544, ['s6_fwd.hip', 's6_plan.cpp', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "535a2c4eb322"),
+    "ssd@ssd_mamba2_bf16": (597913808, ['ssd_fwd.hip', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "30dbde4d412f"),
 }
 
 

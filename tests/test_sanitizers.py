@@ -2,9 +2,10 @@
 
 * The C oracle with a driver that gives every tensor its own exactly sized heap
   block (tests/sanitize/oracle_asan.c).
-* The C-ABI layer's validation and planning (ssm_abi.cpp, s6_plan.cpp), built
-  host-only, with kernel launches replaced by stand-ins that abort, driven by
-  a fuzzer over edge and random sizes (tests/sanitize/abi_fuzz.cpp).  Every
+* The C-ABI layer's validation and planning (ssm_abi.cpp, s6_plan.cpp,
+  s6_bwd_plan.cpp), built host-only, with kernel launches replaced by
+  stand-ins that abort, driven by a fuzzer over edge and random sizes
+  (tests/sanitize/abi_fuzz.cpp).  Every
   fuzzed call must be refused before it could reach the HIP runtime, and the
   size arithmetic must not overflow.
 
@@ -51,6 +52,7 @@ def test_abi_validation_under_sanitizers(tmp_path):
              "-I" + os.path.join(ROOT, "include"), "-I" + CSRC, "-x", "hip"]
     objs = []
     for src in (os.path.join(CSRC, "ssm_abi.cpp"), os.path.join(CSRC, "s6_plan.cpp"),
+                os.path.join(CSRC, "s6_bwd_plan.cpp"),
                 os.path.join(HERE, "launch_stubs.cpp"), os.path.join(HERE, "abi_fuzz.cpp")):
         obj = str(tmp_path / (os.path.basename(src) + ".o"))
         _run([HIPCC, *flags, "-c", src, "-o", obj])
