@@ -151,3 +151,26 @@ def test_long_single_sequence(monkeypatch):
     for k, idx in pick.items():
         g = got[k].float().cpu()[idx].numpy()
         assert normwise_err(g, ref[k].numpy()) <= 1e-5, k
+
+
+def _draw(i):
+    r = np.random.default_rng(5000 + i)
+    return dict(Bt=int(r.integers(1, 4)), L=int(r.integers(1100, 2500)), Dm=int(r.integers(1, 120)),
+                N=int(r.choice([1, 4, 8, 13, 16])), dtype=str(r.choice(["f32", "bf16"])),
+                S=int(r.integers(2, 21)), extras=bool(r.random() < 0.7),
+                softplus=bool(r.random() < 0.8), seed=i)
+
+
+RANDOM = [_draw(i) for i in range(12)]
+
+
+@pytest.mark.parametrize("c", RANDOM, ids=lambda c: "B{Bt}L{L}D{Dm}N{N}{dtype}S{S}".format(**c))
+def test_random_segmented_backward(c, monkeypatch):
+    monkeypatch.setenv("SSM_BWD_SEGMENTS", str(c["S"]))
+    inp = _inputs(c["Bt"], c["L"], c["Dm"], c["N"], c["dtype"], extras=c["extras"],
+                  softplus=c["softplus"], seed=c["seed"])
+    assert ssm.selective_scan_bwd_segments(c["Bt"], c["L"], c["Dm"], c["N"]) > 1
+    d = to_dev(inp)
+    got = _bwd(d)
+    torch.cuda.synchronize()
+    _check(got, inp, c["dtype"])
