@@ -363,8 +363,11 @@ int ssm_selective_scan_bwd_varlen(const void* u, const void* delta, const float*
  * SSM_FLAG_DELTA_SOFTPLUS).  Where the one-pass state-per-lane scan runs, it
  * stores each checkpoint itself (one 4-byte store per lane and tile); on
  * every other path the call runs the backward's forward sweep after the
- * scan.  Either way the values are those the backward's own sweep computes,
- * bit for bit.  ckpt may be NULL only when L = 0; 16-byte aligned.
+ * scan, as one segment (so for long sequences with few channels, where the
+ * scan is segmented, this pair is slower than the plain forward and the
+ * self-contained backward).  On one-segment sweeps the values are those the
+ * backward's own sweep computes, bit for bit.  ckpt may be NULL only when
+ * L = 0; 16-byte aligned.
  *
  * ssm_selective_scan_bwd_ckpt: ssm_selective_scan_bwd (same arguments,
  * results and errors) reading the checkpoints from ckpt, as written by
