@@ -365,17 +365,19 @@ int ssm_selective_scan_bwd_varlen(const void* u, const void* delta, const float*
  * every other path the call runs the backward's forward sweep after the
  * scan, as one segment (so for long sequences with few channels, where the
  * scan is segmented, this pair is slower than the plain forward and the
- * self-contained backward).  On one-segment sweeps the values are those the
- * backward's own sweep computes, bit for bit.  ckpt may be NULL only when
- * L = 0; 16-byte aligned.
+ * self-contained backward).  Either way the values are those the backward's
+ * sweep computes when it runs as one segment, bit for bit (split into
+ * segments it starts each from a carried state, which rounds differently).
+ * ckpt may be NULL only when L = 0; 16-byte aligned.
  *
  * ssm_selective_scan_bwd_ckpt: ssm_selective_scan_bwd (same arguments,
  * results and errors) reading the checkpoints from ckpt, as written by
  * ssm_selective_scan_fwd_ckpt over the same inputs (or by any forward of the
- * same operation); its forward sweep is skipped and its workspace
- * (ssm_selective_scan_bwd_ckpt_workspace_bytes) holds only the partial sums.
- * With identical checkpoints the gradients equal ssm_selective_scan_bwd's bit
- * for bit.  ckpt may be NULL only when L = 0; 16-byte aligned.
+ * same operation); its forward sweeps are skipped and its workspace
+ * (ssm_selective_scan_bwd_ckpt_workspace_bytes) holds the partial sums and
+ * the segment buffers.  Where ssm_selective_scan_bwd runs as one segment and
+ * its checkpoints equal these, the gradients are equal bit for bit.  ckpt may
+ * be NULL only when L = 0; 16-byte aligned.
  */
 size_t ssm_selective_scan_ckpt_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int dtype);
 
