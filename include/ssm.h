@@ -360,15 +360,15 @@ int ssm_selective_scan_bwd_varlen(const void* u, const void* delta, const float*
  * ssm_selective_scan_fwd_ckpt: ssm_selective_scan_fwd (same arguments,
  * results, workspace query and errors) that also writes ckpt.  Sizes, flags
  * and dtype: those of ssm_selective_scan_bwd (1 <= N <= 16; only
- * SSM_FLAG_DELTA_SOFTPLUS).  Where the one-pass state-per-lane scan runs, it
- * stores each checkpoint itself (one 4-byte store per lane and tile); on
- * every other path the call runs the backward's forward sweep after the
- * scan, as one segment (so for long sequences with few channels, where the
- * scan is segmented, this pair is slower than the plain forward and the
- * self-contained backward).  Either way the values are those the backward's
- * sweep computes when it runs as one segment, bit for bit (split into
- * segments it starts each from a carried state, which rounds differently).
- * ckpt may be NULL only when L = 0; 16-byte aligned.
+ * SSM_FLAG_DELTA_SOFTPLUS).  Where the state-per-lane scan runs, it stores
+ * each checkpoint itself (one 4-byte store per lane and tile); when it runs
+ * in segments, those after the first store their states from zero and the
+ * fix-up pass adds exp(A * cumsum dt) * h_in to each, as it does to y.  On
+ * the split path the call runs the backward's forward sweep after the scan,
+ * as one segment.  The one-pass scan and that sweep give the values the
+ * backward's own sweep computes when it runs as one segment, bit for bit;
+ * the segmented scan's values round differently.  ckpt may be NULL only when
+ * L = 0; 16-byte aligned.
  *
  * ssm_selective_scan_bwd_ckpt: ssm_selective_scan_bwd (same arguments,
  * results and errors) reading the checkpoints from ckpt, as written by

@@ -569,11 +569,12 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
     // state is added to y afterwards, by the fix-up pass)
     float h = (s == 0 && p.h0) ? p.h0[(b * D + d) * 16 + n] : 0.0f;
     float dt_sum = 0.0f;                  // segments: this lane's share of the segment's sum of dt
-    // CKPT (one pass, no convolution): the state entering every 16-token tile
-    // for the backward pass, one 4-byte store per lane and tile, through a
-    // buffer resource over the workgroup's 16 channels; a tile past the row's
-    // end stores at an offset past the resource, which is dropped
-    static_assert(!CKPT || (!SEG && !CONV), "checkpoints are written by the one-pass scan");
+    // CKPT (no convolution): the state entering every 16-token tile for the
+    // backward pass, one 4-byte store per lane and tile, through a buffer
+    // resource over the workgroup's 16 channels; a tile past the row's end
+    // stores at an offset past the resource, which is dropped.  A segment
+    // after the first stores its states from zero, which the fix-up completes.
+    static_assert(!CKPT || !CONV, "checkpoints are written by the scan without the convolution");
     const int64_t nck = CKPT ? p.ckpt_blocks : 0;
     const auto rck = make_rsrc(CKPT ? p.ckpt + (b * D + grp * kChans) * nck * 16 : nullptr,
                                CKPT ? (uint32_t)(kChans * nck * 64) : 0u);
@@ -681,7 +682,7 @@ void s6_lanes(S6Args p, const T* __restrict__ u_, const T* __restrict__ delta_,
         for (int i = 0; i < kSuper; ++i) {
             const int tl = kTile * i + n;   // this lane's token within the super-tile
             if constexpr (CKPT) {
-                uint32_t off = ck_lane + (uint32_t)(((st0 - t0) / kTile + i) * 64);
+                uint32_t off = ck_lane + (uint32_t)((st0 / kTile + i) * 64);
                 if constexpr (kTail) off = st0 + kTile * i < t1 ? off : 0x80000000u;
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(h), rck, (int)off, 0, 0);
             }
@@ -1021,7 +1022,7 @@ constexpr int kPad = 4;                    // LDS row padding (floats)
 }  // namespace fixup
 static_assert(plan::kFixChunk % fixup::kBlock == 0, "fix-up chunks are whole blocks");
 
-template <typename T, bool HAS_Z, bool SOFTPLUS>
+template <typename T, bool HAS_Z, bool SOFTPLUS, bool CKPT>
 __global__ __launch_bounds__(256) void s6_fixup(S6Args p, const T* __restrict__ delta_,
                                                 const T* __restrict__ z_,
                                                 const T* __restrict__ Cm_, T* __restrict__ y_) {
@@ -1098,6 +1099,12 @@ __global__ __launch_bounds__(256) void s6_fixup(S6Args p, const T* __restrict__ 
     const int64_t hb = (int64_t)s * (p.B * D * 16) + (b * D + d) * 16;
 #pragma unroll
     for (int n = 0; n < 16; ++n) hin[n] = p.seg_b[hb + n];
+    // CKPT: lane j of a channel completes state j of the checkpoint of every
+    // tile (stored from zero by the scan): + exp2(A log2(e) cum) h_in, with
+    // cum the segment's sum of dt before the tile
+    const float a2_ck = CKPT ? p.A[d * 16 + j] * kLog2e : 0.0f;
+    const float hin_ck = CKPT ? p.seg_b[hb + j] : 0.0f;
+    float* const ck_row = CKPT ? p.ckpt + (b * D + d) * p.ckpt_blocks * 16 + j : nullptr;
     const float bias = p.delta_bias ? p.delta_bias[d] : 0.0f;
     // buffer resources over the row's tokens (32-bit offsets as in the scan)
     const int64_t rowoff = b * p.L * D;
@@ -1195,6 +1202,14 @@ __global__ __launch_bounds__(256) void s6_fixup(S6Args p, const T* __restrict__ 
             x += dpp_shr<2>(x);
             x += dpp_shr<4>(x);
             x += dpp_shr<8>(x);
+            if constexpr (CKPT) {
+                // carry: the sum before the tile; a term exactly 0 changes nothing
+                const float add = fast_exp2(a2_ck * carry) * hin_ck;
+                if (tt + 16 * i < t1 && add != 0.0f) {
+                    float* const e = ck_row + ((tt + 16 * i) / 16) * 16;
+                    *e += add;
+                }
+            }
             cum[i] = x + carry;
             carry = row_bcast_c<15>(cum[i]);
             corr[i] = 0.0f;
@@ -1288,10 +1303,17 @@ void launch_carry_fixup(const S6Args& a, hipStream_t stream) {
     const T* Z = static_cast<const T*>(a.z);
     const T* Cp = static_cast<const T*>(a.Cm);
     T* Y = static_cast<T*>(a.y);
-    if (a.z)
-        hipLaunchKernelGGL((s6_fixup<T, true, SP>), fgrid, dim3(256), 0, stream, a, Dl, Z, Cp, Y);
-    else
-        hipLaunchKernelGGL((s6_fixup<T, false, SP>), fgrid, dim3(256), 0, stream, a, Dl, Z, Cp, Y);
+    if (a.ckpt) {
+        if (a.z)
+            hipLaunchKernelGGL((s6_fixup<T, true, SP, true>), fgrid, dim3(256), 0, stream, a, Dl, Z, Cp, Y);
+        else
+            hipLaunchKernelGGL((s6_fixup<T, false, SP, true>), fgrid, dim3(256), 0, stream, a, Dl, Z, Cp, Y);
+    } else {
+        if (a.z)
+            hipLaunchKernelGGL((s6_fixup<T, true, SP, false>), fgrid, dim3(256), 0, stream, a, Dl, Z, Cp, Y);
+        else
+            hipLaunchKernelGGL((s6_fixup<T, false, SP, false>), fgrid, dim3(256), 0, stream, a, Dl, Z, Cp, Y);
+    }
     mark(a, 3, stream);
 }
 
@@ -1353,6 +1375,9 @@ hipError_t launch_lanes(const S6Args& a, hipStream_t stream) {
     do {                                                                                          \
         if (!(CV_) && a.ckpt && a.S == 1)                                                         \
             hipLaunchKernelGGL((s6_lanes<T, Z_, SP_, false, false, true>), grid, block, 0,        \
+                               stream, a, U, Dl, Z, Bp, Cp, Y);                                   \
+        else if (!(CV_) && a.ckpt)                                                                \
+            hipLaunchKernelGGL((s6_lanes<T, Z_, SP_, false, true, true>), grid, block, 0,         \
                                stream, a, U, Dl, Z, Bp, Cp, Y);                                   \
         else if (a.S > 1)                                                                         \
             hipLaunchKernelGGL((s6_lanes<T, Z_, SP_, CV_, true>), grid, block, 0,                 \

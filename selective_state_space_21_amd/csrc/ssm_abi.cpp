@@ -245,11 +245,12 @@ int s6_fwd_impl(const void* u, const void* delta, const float* A, const void* Bm
     a.events = reinterpret_cast<hipEvent_t const*>(events);
     a.seq_lens = seq_lens;
     ssm::s6_carve(a, workspace);
-    // checkpoints for the backward: written by the one-pass state-per-lane
-    // scan itself where it runs (its per-channel run of checkpoints addressed
-    // with 32-bit offsets), else by the backward's forward sweep afterwards
+    // checkpoints for the backward: written by the state-per-lane scan itself
+    // where it runs (segments after the first completed by the fix-up; its
+    // per-channel run of checkpoints addressed with 32-bit offsets), else by
+    // the backward's forward sweep afterwards
     const int64_t nck = (L + ssm::plan::kBwdTile - 1) / ssm::plan::kBwdTile;
-    const bool fused = ckpt && a.lanes && a.S == 1 && ssm::plan::kLanesChans * nck * 64 < (int64_t)1 << 31;
+    const bool fused = ckpt && a.lanes && ssm::plan::kLanesChans * nck * 64 < (int64_t)1 << 31;
     a.ckpt = fused ? ckpt : nullptr;
     a.ckpt_blocks = nck;
     hipError_t e = ssm::launch_s6(a, static_cast<hipStream_t>(stream));
