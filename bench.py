@@ -72,9 +72,9 @@ ISSUE_PEAK_ELEMS_PER_S = 6.52e12
 # reports traffic null until its counters are taken again.
 COUNTER_TRAFFIC = {
     # kernel@workload: (bytes, sources, sha1 of the sources)
-    "s6_lanes@s6_mamba130m_layer_bf16": (205377321, ['s6_fwd.hip', 's6_plan.cpp', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "535a2c4eb322"),
-    "s6_lanes@s6_mamba2.8b_layer_bf16": (686000558, ['s6_fwd.hip', 's6_plan.cpp', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "535a2c4eb322"),
-    "s6_lanes@s6_long_fp32": (3510319544, ['s6_fwd.hip', 's6_plan.cpp', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "535a2c4eb322"),
+    "s6_lanes@s6_mamba130m_layer_bf16": (205399670, ['s6_fwd.hip', 's6_plan.cpp', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "f78bfbb89634"),
+    "s6_lanes@s6_mamba2.8b_layer_bf16": (686004605, ['s6_fwd.hip', 's6_plan.cpp', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "f78bfbb89634"),
+    "s6_lanes@s6_long_fp32": (3530774542, ['s6_fwd.hip', 's6_plan.cpp', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "f78bfbb89634"),
     "ssd@ssd_mamba2_bf16": (597913808, ['ssd_fwd.hip', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "30dbde4d412f"),
 }
 
@@ -375,33 +375,38 @@ def bench_bwd(args, ctx, long=False):
                 segments=int(lib.ssm_selective_scan_bwd_segments(w.B, w.L, w.D, w.N)))
 
 
-def bench_train(args, ctx):
-    """Forward and backward of one training step at the Mamba-130M layer, two
-    ways: the plain forward then the self-contained backward (which starts
-    with its own forward sweep), and the forward that saves the 16-token
-    checkpoints then the backward that takes them.  Each call alone and each
-    pair as one timed step."""
+def bench_train(args, ctx, long=False):
+    """Forward and backward of one training step at the Mamba-130M layer (or,
+    long, at the long fp32 sequence), two ways: the plain forward then the
+    self-contained backward (which starts with its own forward sweep), and the
+    forward that saves the 16-token checkpoints then the backward that takes
+    them.  Each call alone and each pair as one timed step."""
     torch, ssm, W = ctx["torch"], ctx["ssm"], ctx["W"]
-    w = W.S6_MAMBA130M
+    w = W.S6_LONG_FP32 if long else W.S6_MAMBA130M
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    code = 0 if dt == torch.float32 else 1
     t = W.make_s6_inputs(w, seed=0)
     d = {k: (v.to("cuda:0") if isinstance(v, torch.Tensor) else v) for k, v in t.items()}
     g = torch.Generator().manual_seed(1)
-    dy = torch.randn(w.B, w.L, w.D, generator=g).to(torch.bfloat16).to("cuda:0")
+    dy = torch.randn(w.B, w.L, w.D, generator=g).to(dt).to("cuda:0")
     lib = ssm._native.load()
     y = torch.empty_like(d["u"])
     ck = torch.empty((w.B, w.D, (w.L + 15) // 16, w.N), dtype=torch.float32, device="cuda:0")
-    ws_full = torch.empty(int(lib.ssm_selective_scan_bwd_workspace_bytes(w.B, w.L, w.D, w.N, 1)),
+    ws_full = torch.empty(int(lib.ssm_selective_scan_bwd_workspace_bytes(w.B, w.L, w.D, w.N, code)),
                           dtype=torch.uint8, device="cuda:0")
-    ws_part = torch.empty(int(lib.ssm_selective_scan_bwd_ckpt_workspace_bytes(w.B, w.L, w.D, w.N, 1)),
+    ws_part = torch.empty(int(lib.ssm_selective_scan_bwd_ckpt_workspace_bytes(w.B, w.L, w.D, w.N, code)),
                           dtype=torch.uint8, device="cuda:0")
+    ws_fwd = torch.empty(max(1, int(lib.ssm_selective_scan_workspace_bytes(w.B, w.L, w.D, w.N, code))),
+                         dtype=torch.uint8, device="cuda:0")
     kw = dict(D=d["D"], z=d["z"], delta_bias=d["delta_bias"])
     args_in = (d["u"], d["delta"], d["A"], d["B"], d["C"])
 
     def fwd():
-        ssm.selective_scan_fwd(*args_in, **kw, return_last_state=False, out=y)
+        ssm.selective_scan_fwd(*args_in, **kw, return_last_state=False, out=y, workspace=ws_fwd)
 
     def fwd_ckpt():
-        ssm.selective_scan_fwd_ckpt(*args_in, **kw, return_last_state=False, out=y, ckpt=ck)
+        ssm.selective_scan_fwd_ckpt(*args_in, **kw, return_last_state=False, out=y, ckpt=ck,
+                                    workspace=ws_fwd)
 
     def bwd():
         ssm.selective_scan_bwd(*args_in, dy, **kw, workspace=ws_full)
@@ -593,7 +598,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-paths", action="store_true", help="the headline S6 workload only")
     ap.add_argument("--only", choices=["s6", "s6_2p8b", "s6_long", "ssd", "decode", "bwd",
-                                       "bwd_long", "train", "conv", "conv_scan", "copy"],
+                                       "bwd_long", "train", "train_long", "conv", "conv_scan",
+                                       "copy"],
                     help="run one part alone and print its result")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="also run a plain 256 MiB device copy three times, the "
@@ -628,6 +634,7 @@ def main():
              "ssd": lambda: bench_ssd(args, ctx), "decode": lambda: bench_decode(args, ctx),
              "bwd": lambda: bench_bwd(args, ctx), "bwd_long": lambda: bench_bwd(args, ctx, True),
              "train": lambda: bench_train(args, ctx),
+             "train_long": lambda: bench_train(args, ctx, True),
              "conv": lambda: bench_conv(args, ctx),
              "conv_scan": lambda: bench_conv_scan(args, ctx),
              "copy": lambda: bench_copy(args, ctx, W.s6_algorithmic_bytes(W.S6_MAMBA130M))}
@@ -645,6 +652,7 @@ def main():
                           ("ssd_chunk_fwd", "ssd"), ("selective_state_update", "decode"),
                           ("selective_scan_bwd", "bwd"), ("selective_scan_bwd_long_fp32", "bwd_long"),
                           ("training_step_fwd_bwd", "train"),
+                          ("training_step_fwd_bwd_long_fp32", "train_long"),
                           ("causal_conv1d_silu", "conv"),
                           ("selective_scan_conv_fwd", "conv_scan")]:
             paths[name] = parts[key]()
