@@ -22,20 +22,28 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kRun = 32;       // tokens per thread
-constexpr int kUnroll = 8;     // tokens whose loads are in flight together
+constexpr int kTokensInFlight = 16;   // loads in flight per thread (4-byte vectors)
 
 // x and u are streamed once: nontemporal accesses (48.0 -> 42.5 us at
 // B=8 L=2048 D=1536 bf16, against 30 us for a plain device copy of x).  In
 // bf16 a thread owns two channels (4-byte accesses): four times the threads
-// of one 16-byte vector each, so more loads are in flight per SIMD
-// (42.6 -> 34.4 us; four channels per thread: 36.8 us; one: 59 us).
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// of one 16-byte vector each, so more loads are in flight per SIMD (with 8
+// tokens in flight: 42.6 -> 34.4 us; four channels 36.8 us, one 59 us).
+// Loads are held as loaded and widened at use, which leaves the registers
+// for 16 tokens in flight per thread: 34.4 -> 25.9 us, 3.88 TB/s (32 tokens
+// in flight: the same; 64-token runs: 26.4 us; 8 bf16 channels per thread
+// with 16 in flight: 43.4 us).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// VEC channels of one token: loaded as RAW (the stored bits), widened to fp32
+// by unpack; store narrows VEC fp32 values back to the element type.
 template <typename T, int VEC> struct Vec;
 template <> struct Vec<uint16_t, 2> {
-    static __device__ __forceinline__ void load(const uint16_t* p, float (&v)[2]) {
-        const uint32_t r = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    using Raw = uint32_t;
+    static __device__ __forceinline__ Raw load(const uint16_t* p) {
+        return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    }
+    static __device__ __forceinline__ void unpack(const Raw& r, float (&v)[2]) {
         v[0] = __uint_as_float(r << 16); v[1] = __uint_as_float(r & 0xffff0000u);
     }
     static __device__ __forceinline__ void store(uint16_t* p, const float (&v)[2]) {
@@ -44,8 +52,11 @@ template <> struct Vec<uint16_t, 2> {
     }
 };
 template <> struct Vec<float, 4> {
-    static __device__ __forceinline__ void load(const float* p, float (&v)[4]) {
-        const f32x4 r = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    using Raw = f32x4;
+    static __device__ __forceinline__ Raw load(const float* p) {
+        return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    }
+    static __device__ __forceinline__ void unpack(const Raw& r, float (&v)[4]) {
         v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
     }
     static __device__ __forceinline__ void store(float* p, const float (&v)[4]) {
@@ -53,13 +64,19 @@ template <> struct Vec<float, 4> {
     }
 };
 template <typename T> struct Vec<T, 1> {
-    static __device__ __forceinline__ void load(const T* p, float (&v)[1]) { v[0] = Elem<T>::load(p, 0); }
+    using Raw = float;
+    static __device__ __forceinline__ Raw load(const T* p) { return Elem<T>::load(p, 0); }
+    static __device__ __forceinline__ void unpack(const Raw& r, float (&v)[1]) { v[0] = r; }
     static __device__ __forceinline__ void store(T* p, const float (&v)[1]) { Elem<T>::store(p, 0, v[0]); }
 };
 
 // one thread per (channel vector, b, run), channel vectors fastest
 template <typename T, int VEC, int K, bool SILU>
 __global__ __launch_bounds__(kBlock) void conv1d_silu_kernel(ConvArgs p) {
+    using V = Vec<T, VEC>;
+    // 16 tokens in flight for 4-byte vectors; 16-byte vectors keep 8 (16 of
+    // them would halve the wavefronts per SIMD)
+    constexpr int kUnroll = VEC * (int)sizeof(T) == 16 ? 8 : kTokensInFlight;
     const int64_t groups = (p.D + VEC - 1) / VEC;
     const int64_t nrun = (p.L + kRun - 1) / kRun;
     const int64_t gi = (int64_t)blockIdx.x * kBlock + threadIdx.x;
@@ -84,7 +101,7 @@ __global__ __launch_bounds__(kBlock) void conv1d_silu_kernel(ConvArgs p) {
     for (int i = 0; i < K - 1; ++i) {
         const int64_t t = t0 - (K - 1) + i;
         if (t >= 0) {
-            Vec<T, VEC>::load(x + t * p.D, win[i]);
+            V::unpack(V::load(x + t * p.D), win[i]);
         } else {
 #pragma unroll
             for (int c = 0; c < VEC; ++c)
@@ -93,15 +110,14 @@ __global__ __launch_bounds__(kBlock) void conv1d_silu_kernel(ConvArgs p) {
     }
     const int64_t tend = t0 + kRun < p.L ? t0 + kRun : p.L;
     for (int64_t tb = t0; tb < tend; tb += kUnroll) {
-        float xs[kUnroll][VEC];
+        typename V::Raw xs[kUnroll];
 #pragma unroll
         for (int j = 0; j < kUnroll; ++j)
-            if (tb + j < tend) Vec<T, VEC>::load(x + (tb + j) * p.D, xs[j]);
+            if (tb + j < tend) xs[j] = V::load(x + (tb + j) * p.D);
 #pragma unroll
         for (int j = 0; j < kUnroll; ++j) {
             if (tb + j >= tend) break;
-#pragma unroll
-            for (int c = 0; c < VEC; ++c) win[K - 1][c] = xs[j][c];
+            V::unpack(xs[j], win[K - 1]);
             float o[VEC];
 #pragma unroll
             for (int c = 0; c < VEC; ++c) {
@@ -110,7 +126,7 @@ __global__ __launch_bounds__(kBlock) void conv1d_silu_kernel(ConvArgs p) {
                 for (int k = 0; k < K; ++k) s = fmaf(w[c][k], win[k][c], s);
                 o[c] = SILU ? silu_f(s) : s;
             }
-            Vec<T, VEC>::store(u + (tb + j) * p.D, o);
+            V::store(u + (tb + j) * p.D, o);
 #pragma unroll
             for (int i = 0; i < K - 1; ++i)
 #pragma unroll

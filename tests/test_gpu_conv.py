@@ -28,7 +28,8 @@ def _run(inp, state=None, silu=True, ret_state=True):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", [(2, 100, 64, 4), (1, 1, 8, 4), (3, 2, 16, 4), (2, 77, 40, 3),
-                                   (2, 65, 13, 4), (1, 33, 7, 2), (2, 40, 24, 1)])
+                                   (2, 65, 13, 4), (1, 33, 7, 2), (2, 40, 24, 1), (2, 70, 18, 4),
+                                   (1, 50, 20, 4)])
 def test_conv_parity(dtype, shape):
     Bt, L, Dm, K = shape
     inp = W.make_conv_inputs(W.CONV_MAMBA130M.scaled(B=Bt, L=L, D=Dm, K=K, dtype=dtype), seed=L)
