@@ -44,55 +44,82 @@ template <> struct Quad<uint16_t> {
     }
 };
 
+// Items (channel, group of 4 states) per thread: all their loads are issued
+// before any of them is computed, so a thread keeps kItems 16-byte state
+// loads in flight; item r of a thread is r grid strides past its first, so
+// each load instruction of a wavefront still covers contiguous bytes.
+constexpr int kItems = 4;
+
 template <typename T, int GL, bool ZOH>
 __global__ __launch_bounds__(kBlock) void s6_step_vec(StepArgs p) {
-    const int64_t lane = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    const int64_t ch = lane / GL;                 // flattened (b, d)
-    const int q = (int)(lane % GL);               // which 4 states
-    const bool valid = ch < p.B * p.D;
-    const int64_t chc = valid ? ch : 0;           // in-range address for idle lanes
-    const int64_t b = chc / p.D, d = chc % p.D;
     constexpr int N = 4 * GL;
-
+    const int64_t nitems = p.B * p.D * GL;
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    const int64_t first = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     const T* xs = static_cast<const T*>(p.u);
     const T* dts = static_cast<const T*>(p.delta);
     const T* zs = static_cast<const T*>(p.z);
-    const float u = Elem<T>::load(xs, chc);
-    const float dt = step_dt(Elem<T>::load(dts, chc), p.delta_bias ? p.delta_bias[d] : 0.0f, p.flags);
-    const float dtu = dt * u;
-    // the gate and skip are loaded with everything else, not after the sum
-    const float zval = zs ? Elem<T>::load(zs, chc) : 0.0f;
-    const float dskv = p.Dskip ? p.Dskip[d] : 0.0f;
 
-    // The state is touched once per call: nontemporal accesses keep it from
-    // displacing other data in the caches (18.4 -> 16.3 us for 64 sequences
-    // of a D=5120, N=16 layer; 15.3 us with the gate and skip loads hoisted).
-    float* st = p.state + chc * N + 4 * q;
-    const f32x4 h = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(st));
-    const float4 a = *reinterpret_cast<const float4*>(p.A + d * N + 4 * q);
-    const float4 bv = Quad<T>::load(static_cast<const T*>(p.Bm) + b * N + 4 * q);
-    const float4 cv = Quad<T>::load(static_cast<const T*>(p.Cm) + b * N + 4 * q);
-    const float av[4] = {a.x, a.y, a.z, a.w};
-    const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
-    const float cc[4] = {cv.x, cv.y, cv.z, cv.w};
-    float hh[4] = {h.x, h.y, h.z, h.w};
-    float acc = 0.0f;
+    struct Item {
+        int64_t ch;                 // flattened (b, d); an in-range address for idle items
+        int q;                      // which 4 states
+        bool valid;
+        f32x4 h;
+        float4 a, bv, cv;
+        float u, dtr, bias, zval, dskv;
+    } it[kItems];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-        const float dA = fast_exp2(dt * (av[n] * kLog2e));
-        const float w = ZOH ? dtu * bb[n] * zoh_factor(dt * av[n]) : bb[n] * dtu;
-        hh[n] = fmaf(dA, hh[n], w);
-        acc = fmaf(cc[n], hh[n], acc);
+    for (int r = 0; r < kItems; ++r) {
+        const int64_t item = first + r * stride;
+        it[r].valid = item < nitems;
+        const int64_t ic = it[r].valid ? item : 0;
+        it[r].ch = ic / GL;
+        it[r].q = (int)(ic % GL);
+        const int64_t b = it[r].ch / p.D, d = it[r].ch % p.D;
+        it[r].u = Elem<T>::load(xs, it[r].ch);
+        it[r].dtr = Elem<T>::load(dts, it[r].ch);
+        it[r].bias = p.delta_bias ? p.delta_bias[d] : 0.0f;
+        // the gate and skip are loaded with everything else, not after the sum
+        it[r].zval = zs ? Elem<T>::load(zs, it[r].ch) : 0.0f;
+        it[r].dskv = p.Dskip ? p.Dskip[d] : 0.0f;
+        // The state is touched once per call: nontemporal accesses keep it
+        // from displacing other data in the caches (18.4 -> 16.3 us for 64
+        // sequences of a D=5120, N=16 layer; 15.3 us with the gate and skip
+        // loads hoisted).
+        it[r].h = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(p.state + it[r].ch * N + 4 * it[r].q));
+        it[r].a = *reinterpret_cast<const float4*>(p.A + d * N + 4 * it[r].q);
+        it[r].bv = Quad<T>::load(static_cast<const T*>(p.Bm) + b * N + 4 * it[r].q);
+        it[r].cv = Quad<T>::load(static_cast<const T*>(p.Cm) + b * N + 4 * it[r].q);
     }
-    // the partial sums of a channel's GL lanes, combined pairwise
 #pragma unroll
-    for (int off = 1; off < GL; off <<= 1) acc += __shfl_xor(acc, off, 64);
-    if (!valid) return;
-    __builtin_nontemporal_store((f32x4){hh[0], hh[1], hh[2], hh[3]}, reinterpret_cast<f32x4*>(st));
-    if (q == 0) {
-        acc = fmaf(dskv, u, acc);
-        if (zs) acc *= silu_f(zval);
-        Elem<T>::store(static_cast<T*>(p.y), chc, acc);
+    for (int r = 0; r < kItems; ++r) {
+        const float dt = step_dt(it[r].dtr, it[r].bias, p.flags);
+        const float dtu = dt * it[r].u;
+        const float av[4] = {it[r].a.x, it[r].a.y, it[r].a.z, it[r].a.w};
+        const float bb[4] = {it[r].bv.x, it[r].bv.y, it[r].bv.z, it[r].bv.w};
+        const float cc[4] = {it[r].cv.x, it[r].cv.y, it[r].cv.z, it[r].cv.w};
+        float hh[4] = {it[r].h.x, it[r].h.y, it[r].h.z, it[r].h.w};
+        float acc = 0.0f;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const float dA = fast_exp2(dt * (av[n] * kLog2e));
+            const float w = ZOH ? dtu * bb[n] * zoh_factor(dt * av[n]) : bb[n] * dtu;
+            hh[n] = fmaf(dA, hh[n], w);
+            acc = fmaf(cc[n], hh[n], acc);
+        }
+        // the partial sums of a channel's GL lanes, combined pairwise (every
+        // lane takes part, idle items included)
+#pragma unroll
+        for (int off = 1; off < GL; off <<= 1) acc += __shfl_xor(acc, off, 64);
+        if (!it[r].valid) continue;
+        __builtin_nontemporal_store((f32x4){hh[0], hh[1], hh[2], hh[3]},
+                                    reinterpret_cast<f32x4*>(p.state + it[r].ch * N + 4 * it[r].q));
+        if (it[r].q == 0) {
+            acc = fmaf(it[r].dskv, it[r].u, acc);
+            if (zs) acc *= silu_f(it[r].zval);
+            Elem<T>::store(static_cast<T*>(p.y), it[r].ch, acc);
+        }
     }
 }
 
@@ -130,12 +157,16 @@ template <typename T, bool ZOH>
 hipError_t launch_t(const StepArgs& a, hipStream_t stream) {
     const int64_t chans = a.B * a.D;
     auto blocks = [](int64_t lanes) { return (unsigned)((lanes + kBlock - 1) / kBlock); };
+    // kItems items per thread on the vector path
+    auto vblocks = [](int64_t items) {
+        return (unsigned)((items + (int64_t)kBlock * kItems - 1) / ((int64_t)kBlock * kItems));
+    };
     switch (a.N) {
-        case 4: s6_step_vec<T, 1, ZOH><<<blocks(chans), kBlock, 0, stream>>>(a); break;
-        case 8: s6_step_vec<T, 2, ZOH><<<blocks(chans * 2), kBlock, 0, stream>>>(a); break;
-        case 16: s6_step_vec<T, 4, ZOH><<<blocks(chans * 4), kBlock, 0, stream>>>(a); break;
-        case 32: s6_step_vec<T, 8, ZOH><<<blocks(chans * 8), kBlock, 0, stream>>>(a); break;
-        case 64: s6_step_vec<T, 16, ZOH><<<blocks(chans * 16), kBlock, 0, stream>>>(a); break;
+        case 4: s6_step_vec<T, 1, ZOH><<<vblocks(chans), kBlock, 0, stream>>>(a); break;
+        case 8: s6_step_vec<T, 2, ZOH><<<vblocks(chans * 2), kBlock, 0, stream>>>(a); break;
+        case 16: s6_step_vec<T, 4, ZOH><<<vblocks(chans * 4), kBlock, 0, stream>>>(a); break;
+        case 32: s6_step_vec<T, 8, ZOH><<<vblocks(chans * 8), kBlock, 0, stream>>>(a); break;
+        case 64: s6_step_vec<T, 16, ZOH><<<vblocks(chans * 16), kBlock, 0, stream>>>(a); break;
         default: s6_step_any<T, ZOH><<<blocks(chans), kBlock, 0, stream>>>(a); break;
     }
     return hipGetLastError();
