@@ -75,7 +75,7 @@ COUNTER_TRAFFIC = {
     "s6_lanes@s6_mamba130m_layer_bf16": (205399670, ['s6_fwd.hip', 's6_plan.cpp', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "f78bfbb89634"),
     "s6_lanes@s6_mamba2.8b_layer_bf16": (686004605, ['s6_fwd.hip', 's6_plan.cpp', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "f78bfbb89634"),
     "s6_lanes@s6_long_fp32": (3530774542, ['s6_fwd.hip', 's6_plan.cpp', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "f78bfbb89634"),
-    "ssd@ssd_mamba2_bf16": (597913808, ['ssd_fwd.hip', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "30dbde4d412f"),
+    "ssd@ssd_mamba2_bf16": (600585033, ['ssd_fwd.hip', 'device_math.h', 'lane_ops.h', 'ssm_internal.h'], "744bff51c7ed"),
 }
 
 
