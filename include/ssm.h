@@ -295,8 +295,9 @@ int ssm_ssd_chunk_fwd_varlen(const void* X, const void* delta, const float* A,
  * adjoint one) run one workgroup per channel group and batch row.  When
  * there are fewer than 128 adjoint-sweep workgroups (B * ceil(D/48)) and at
  * least 2048 tokens, the sequence is cut into segments (whole 128-token
- * multiples of at least 1024 tokens, at most 64, about four adjoint-sweep
- * workgroups per CU; see ssm_selective_scan_bwd_segments): each segment's
+ * multiples of at least 1024 tokens, at most 64, as many as keep the
+ * adjoint-sweep workgroups within four per CU over the call; see
+ * ssm_selective_scan_bwd_segments): each segment's
  * forward pair (its end state from zero) and adjoint pair (its adjoint from
  * zero at its end) are computed in parallel, folded in segment order into
  * every segment's incoming state and adjoint (both decaying over a segment by

@@ -20,14 +20,16 @@ S6BwdPlan plan_s6_bwd(int64_t B, int64_t L, int64_t D, int64_t N) {
     // Both sweeps walk the sequence tile by tile, one workgroup per channel
     // group and batch row (the adjoint sweep's take a CU each).  With fewer
     // than 128 of those the sequence is cut into segments of at least 1024
-    // tokens, enough for about four adjoint-sweep workgroups per CU over the
-    // call.  (At B = 1, L = 131072, D = 2048, fp32: 5 segments, one round of
-    // workgroups, 9.28 ms; 8 segments 10.0 ms; 11 7.73; 16 7.80; 22 7.60;
-    // 32 7.65.)
+    // tokens: as many as keep the adjoint-sweep workgroups within four rounds
+    // of one per CU (256 CUs), rounded down, since a fifth round with a few
+    // workgroups costs a whole workgroup's time.  (At B = 1, L = 131072,
+    // D = 2048, fp32, 43 channel groups: 23 segments, 989 workgroups,
+    // 7.33 ms; 24 segments, 1032 workgroups, 7.98 ms; 22 7.58; 21 7.84;
+    // earlier: 5 segments 9.28 ms, 8 10.0, 11 7.73, 16 7.80, 32 7.65.)
     const int64_t wgs = B * ((D + kBwdChans - 1) / kBwdChans);
     int64_t S = 1;
     if (wgs < 128) {
-        S = (1024 + wgs - 1) / wgs;
+        S = 1024 / wgs;
         if (S > nblk / 64) S = nblk / 64;
     }
     const char* env = getenv("SSM_BWD_SEGMENTS");
